@@ -59,7 +59,7 @@ enum {
     OR_BASE_16 = 4,       /* base address not 16-byte aligned                */
     OR_BASE_NULL = 5,     /* base address is 0                               */
     OR_ES = 6,            /* element size not 1, 2, 4 or 8                   */
-    OR_DIM_RANGE = 7,     /* some dim outside [1, 2^32]                      */
+    OR_DIM_RANGE = 7,     /* some dim outside [1, 2^31] (int32 coordinates)  */
     OR_BOX_ZERO = 8,      /* some box dim is 0                               */
     OR_STRIDE_RANGE = 9,  /* some stride 0 or >= 2^40                        */
     OR_ESTRIDE = 10,      /* some element stride != 1                        */
@@ -87,7 +87,7 @@ int oracle_validate(int32_t es, int32_t rank, uint64_t base,
     if (base == 0) return OR_BASE_NULL;
     if (!(es == 1 || es == 2 || es == 4 || es == 8)) return OR_ES;
     for (d = 0; d < rank; ++d)
-        if (dims[d] < 1 || dims[d] > (1ull << 32)) return OR_DIM_RANGE;
+        if (dims[d] < 1 || dims[d] > (1ull << 31)) return OR_DIM_RANGE;
     for (d = 0; d < rank; ++d)
         if (box[d] < 1) return OR_BOX_ZERO;
     for (d = 1; d < rank; ++d)

@@ -313,7 +313,8 @@ def test_validator_rejects_library_rules():
     assert _ok(base=0) == 5
     assert _ok(es=3) == 6
     assert _ok(dims=[0, 64]) == 7
-    assert _ok(dims=[64, (1 << 32) + 1]) == 7
+    assert _ok(dims=[64, (1 << 31) + 1]) == 7
+    assert _ok(dims=[64, 1 << 31]) == 0
     assert _ok(box=[64, 0]) == 8
     assert _ok(strides=[0]) == 9
     assert _ok(strides=[1 << 40]) == 9
