@@ -1,0 +1,227 @@
+/*
+ * tmap.h -- C ABI of libtmap: descriptor-driven tiled bulk copy between HBM
+ * and LDS on AMD Instinct MI355X (gfx950).
+ *
+ * A tensor map describes a strided tensor of up to five dimensions and the
+ * box (tile) to cut from it; a copy moves whole boxes at given corners
+ * between global memory and an on-chip LDS tile, permutes the bytes with an
+ * XOR swizzle as they land, fills out-of-bounds elements with zeros, and
+ * stores back with out-of-bounds elements clipped.  The operations follow
+ * these pages (cited by title and section):
+ *   "TMA -- the async bulk copy engine" (modern_gpu lesson 04)
+ *   "GPU TMA" (aicassindra blog)
+ *   "Day 76: The Tensor Memory Accelerator (TMA)"
+ *   "Understanding TMA loads in CuTe DSL"
+ *
+ * Conventions for every call:
+ *   - Dimensions, box extents and coordinates are innermost (contiguous)
+ *     dimension first ("Day 76", "Pitfalls": x, then y).
+ *   - Coordinates are int32 element offsets of the box corner and may be
+ *     negative or past the end; elements outside [0, dim) read as zero and
+ *     are never written.
+ *   - Pointers named "device" are HIP device pointers; "host" pointers are
+ *     ordinary CPU memory.  The library never takes ownership: a map borrows
+ *     its tensor's address, and the caller keeps tensors, coordinate arrays
+ *     and packed buffers alive until the stream work has completed.
+ *   - The copy calls enqueue on the given HIP stream (NULL = the default
+ *     stream) and return without waiting.  Argument errors are reported
+ *     synchronously, before anything is launched; a failed call launches
+ *     nothing.  n_tiles == 0 is a successful no-op.
+ *   - No call allocates device memory per call.  One 4-byte status word per
+ *     device is allocated on first use and kept until process exit.
+ */
+#ifndef TMAP_H
+#define TMAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* 128 opaque bytes, sixteen 64-bit words, 64-byte aligned
+ * ("Day 76", "The address arithmetic moves into a descriptor": the map is
+ * built once on the host and handed to the kernel by value, which treats it
+ * as opaque).  Filled only by tmap_encode. */
+typedef struct __attribute__((aligned(64))) tmap_t {
+    uint64_t opaque[16];
+} tmap_t;
+
+typedef enum tmap_status {
+    TMAP_SUCCESS = 0,
+    TMAP_ERROR_INVALID_VALUE = 1,      /* a rule or argument check failed            */
+    TMAP_ERROR_UNSUPPORTED_DEVICE = 2, /* no gfx950 device current                   */
+    TMAP_ERROR_LAUNCH = 3,             /* the HIP runtime refused a launch           */
+    TMAP_ERROR_TIMEOUT = 4             /* a kernel's bounded readiness wait expired  */
+} tmap_status;
+
+/* Only the element size matters to the copy; bytes move verbatim. */
+typedef enum tmap_dtype {
+    TMAP_U8 = 0, TMAP_I8 = 1, TMAP_U16 = 2, TMAP_F16 = 3, TMAP_BF16 = 4,
+    TMAP_U32 = 5, TMAP_I32 = 6, TMAP_F32 = 7, TMAP_U64 = 8, TMAP_F64 = 9
+} tmap_dtype;
+
+/* XOR swizzle on tile-local element offsets: the b bits starting at bit m+s
+ * are XORed into the b bits starting at bit m.  b == 0 is the identity
+ * ("Understanding TMA loads in CuTe DSL", "Describe the memory layout
+ * first": make_swizzle(0,4,3) leaves offsets unchanged).  The 128-byte
+ * swizzle of a box with 128-byte rows is (3, log2(16/elem_size), 3). */
+typedef struct tmap_swizzle {
+    uint8_t b, m, s;
+} tmap_swizzle;
+
+/* Launch options; pass NULL for the defaults.  Any field left 0 takes its
+ * default. */
+typedef struct tmap_launch_opts {
+    uint32_t stages;      /* LDS ring depth 1..4 (default: 4, or 2 for boxes over 32 KiB) */
+    uint32_t grid_wgs;    /* workgroups of the persistent grid (default: fill every CU)    */
+    uint32_t flags;       /* TMAP_FLAG_* bits                                              */
+    uint32_t spin_limit;  /* readiness-wait polls before TMAP_ERROR_TIMEOUT (default 2^22) */
+} tmap_launch_opts;
+
+/* Tiles are dealt to workgroups in contiguous runs instead of round-robin. */
+#define TMAP_FLAG_CONTIGUOUS 0x1u
+/* Non-temporal hints on the streaming loads and stores. */
+#define TMAP_FLAG_NONTEMPORAL 0x2u
+/* Test hook: every wave announces 16 bytes more than it delivers, so a
+ * stage never becomes ready and the bounded wait must end the kernel with
+ * TMAP_ERROR_TIMEOUT ("Day 76", "Pitfalls": a byte budget that does not match
+ * the bytes delivered decouples the wait from the data). */
+#define TMAP_FLAG_INJECT_BUDGET_MISMATCH 0x100u
+
+/*
+ * tmap_encode -- validate and pack a tensor map.
+ * ("Day 76", "The address arithmetic moves into a descriptor" and
+ * "Pitfalls"; "GPU TMA", "The architecture: every piece explained";
+ * "TMA -- the async bulk copy engine", "The real toolchain".)
+ *
+ *   map             out: written only on success
+ *   dtype           element type (element size 1, 2, 4 or 8 bytes)
+ *   rank            1..5
+ *   global_address  device address of element (0,..,0); 16-byte aligned
+ *   global_dim      host [rank] elements per dimension, each in [1, 2^31]
+ *                   (coordinates are int32)
+ *   global_strides  host [rank-1] byte strides of dimensions 1..rank-1,
+ *                   multiples of 16, in (0, 2^40); dimension 0 is contiguous
+ *   box_dim         host [rank] box extents, each in [1, 256]
+ *   element_strides host [rank], all 1, or NULL
+ *   swizzle         see tmap_swizzle
+ *
+ * Rules: the pages' four (box <= 256, strides multiple of 16 bytes, base
+ * 16-byte aligned, rank <= 5) plus this library's own: non-NULL base,
+ * dims and strides in range, unit element strides, box rows a whole number
+ * of 16-byte chunks, at most 64 KiB per box, the box's byte footprint
+ * (box[0]*elem + sum (box[d]-1)*stride[d]) below 2 GiB, and for b > 0:
+ * b <= 8, m <= 16, s <= 16, s >= b and the box element count a multiple of
+ * 2^(m+b).  Any violated rule returns TMAP_ERROR_INVALID_VALUE and leaves
+ * *map unmodified; tmap_last_error_detail() names the rule.  Host-only: no
+ * GPU is needed.
+ */
+tmap_status tmap_encode(tmap_t *map, tmap_dtype dtype, uint32_t rank, void *global_address,
+                        const uint64_t *global_dim, const uint64_t *global_strides,
+                        const uint32_t *box_dim, const uint32_t *element_strides,
+                        tmap_swizzle swizzle);
+
+/*
+ * tmap_load_tiles -- copy n_tiles boxes from the map's tensor into LDS and
+ * write each tile's LDS image to packed_out.
+ * ("TMA -- the async bulk copy engine", "What the issuing thread actually
+ * does", "The descriptor records the layout, including the swizzle" and
+ * "Load completion"; "Day 76", "The address arithmetic moves into a
+ * descriptor"; "Understanding TMA loads in CuTe DSL", "The work assigned to
+ * each block" and "Issue the load and wait for its phase".)
+ *
+ *   src        encoded map of the source tensor
+ *   coords     device int32 [n_tiles][rank] box corners, or NULL for a full
+ *              sweep in which case n_tiles must equal tmap_sweep_tiles(src)
+ *              (tile t: innermost tile index fastest)
+ *   n_tiles    >= 0
+ *   packed_out device, n_tiles * tmap_box_bytes(src) bytes, 16-byte aligned;
+ *              tile t's image starts at t * box_bytes; box element e sits at
+ *              byte swizzle(e) * elem_size of its image; out-of-bounds
+ *              elements are zero
+ *   opts       NULL or launch options
+ *   hip_stream hipStream_t to enqueue on (NULL = default stream)
+ *
+ * Each box lands in an LDS stage whose readiness is a per-stage byte count:
+ * the stage is read only after all box_bytes (zero-filled bytes included)
+ * have arrived, and the count's phase parity flips once per fill.
+ */
+tmap_status tmap_load_tiles(const tmap_t *src, const int32_t *coords, int64_t n_tiles,
+                            void *packed_out, const tmap_launch_opts *opts, void *hip_stream);
+
+/*
+ * tmap_store_tiles -- the reverse direction: copy each tile image from
+ * packed_in into LDS and store its in-bounds elements to the map's tensor;
+ * out-of-bounds elements are never written.
+ * ("GPU TMA", "End-to-end flow": the store is the same mechanism in
+ * reverse; "Day 76", "Exercise" and "Solution"; "TMA -- the async bulk copy
+ * engine", "Store completion".)
+ *
+ *   dst        encoded map of the destination tensor
+ *   coords     device int32 [n_tiles][rank], or NULL for a full sweep
+ *   packed_in  device, n_tiles * tmap_box_bytes(dst) bytes, 16-byte aligned,
+ *              laid out as tmap_load_tiles writes it
+ *   Overlapping boxes that write different bytes to one element leave that
+ *   element with one of them (which one is unspecified).
+ */
+tmap_status tmap_store_tiles(const tmap_t *dst, const int32_t *coords, int64_t n_tiles,
+                             const void *packed_in, const tmap_launch_opts *opts,
+                             void *hip_stream);
+
+/*
+ * tmap_roundtrip -- for each tile: load the box from src into LDS (swizzled,
+ * zero-filled) and store it through dst at the same corner (clipped).
+ * ("Day 76", "An exact round trip" with the symmetric write-back of
+ * "Exercise".)  src and dst must have equal element size, rank, box and
+ * swizzle; their dims and strides may differ.  Otherwise as above.
+ */
+tmap_status tmap_roundtrip(const tmap_t *src, const tmap_t *dst, const int32_t *coords,
+                           int64_t n_tiles, const tmap_launch_opts *opts, void *hip_stream);
+
+/* Bytes of one tile image: product of the box extents times the element
+ * size ("Day 76": 64x64 fp32 is 16384 bytes).  0 for a map never encoded. */
+uint64_t tmap_box_bytes(const tmap_t *map);
+
+/* Tiles in a full sweep: product over dimensions of ceil(dim / box).
+ * -1 for a map never encoded. */
+int64_t tmap_sweep_tiles(const tmap_t *map);
+
+/* Host-side count of in-bounds box elements over n_tiles corners (host
+ * int32 [n_tiles][rank], or NULL for the full sweep): the elements a copy
+ * must read or write.  Writes *out_elems; TMAP_ERROR_INVALID_VALUE on bad
+ * arguments. */
+tmap_status tmap_inbounds_elems(const tmap_t *map, const int32_t *host_coords,
+                                int64_t n_tiles, uint64_t *out_elems);
+
+/* Decoded fields of an encoded map (for inspection and tests). */
+typedef struct tmap_info {
+    uint64_t global_address;
+    uint64_t dims[5];
+    uint64_t strides[5];   /* bytes; strides[0] is the element size */
+    uint32_t box[5];
+    uint32_t rank;
+    uint32_t elem_size;
+    uint32_t dtype;
+    tmap_swizzle swizzle;
+} tmap_info;
+tmap_status tmap_query(const tmap_t *map, tmap_info *out);
+
+/* Static text for a status code. */
+const char *tmap_status_string(tmap_status status);
+
+/* Thread-local text describing the last failure of a call on this thread
+ * (the rule that failed, the argument that was wrong); "" after success. */
+const char *tmap_last_error_detail(void);
+
+/* Wait for hip_stream, then read and clear the device status word that
+ * kernels set when a bounded readiness wait expires.  Returns TMAP_SUCCESS
+ * or TMAP_ERROR_TIMEOUT (or TMAP_ERROR_LAUNCH if the stream reports an
+ * error). */
+tmap_status tmap_sync_status(void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TMAP_H */

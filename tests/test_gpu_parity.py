@@ -1,0 +1,334 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, byte for
+byte, on seeded inputs.
+
+* The five workloads at their full sizes, in the launch configuration the
+  benchmark uses; the oracle recomputes every tile where it finishes in
+  seconds (tile64, strips, pad5d) and a sample of tiles otherwise (ragged
+  bf16, 2 GiB bytes), where closed forms cover the rest (a store of the loaded
+  images restores every byte; an exact-tiling round trip is the identity).
+* Seeded random maps of every rank, element size and swizzle (including
+  swizzles that move data inside 16-byte chunks), random corners inside,
+  across and outside the tensor, every ring depth and grid shape.
+* Edge cases: zero tiles, one tile, fully out-of-bounds boxes, the largest box
+  (64 KiB), box extents of 256, rank 1, and the budget-mismatch timeout.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import Map
+from tiled_tensor_bulk_amd import inputs
+from tiled_tensor_bulk_amd import tmap as T
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_tensor(nbytes, fill_seed=None):
+    t = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    if fill_seed is not None:
+        g = torch.Generator(device=DEV)
+        g.manual_seed(fill_seed)
+        n8 = (nbytes + 7) // 8
+        x = torch.randint(-(2**63), 2**63 - 1, (n8,), dtype=torch.int64, generator=g, device=DEV)
+        t.copy_(x.view(torch.uint8)[:nbytes])
+    return t
+
+
+def enc(dtype, t, dims, strides, box, swz=(0, 0, 0)):
+    return T.tmap_encode(dtype, len(dims), t.data_ptr(), dims, strides, box, None, swz)
+
+
+def dt_of(es):
+    return {1: "u8", 2: "f16", 4: "f32", 8: "f64"}[es]
+
+
+def check_ok(stream=None):
+    st = T.tmap_sync_status(stream)
+    assert st == T.SUCCESS, T.tmap_status_string(st)
+
+
+def first_mismatch(a: np.ndarray, b: np.ndarray, bb: int):
+    idx = np.flatnonzero(a != b)
+    if idx.size == 0:
+        return None
+    i = int(idx[0])
+    return f"byte {i} (tile {i // bb}, offset {i % bb}): got {a[i]:#x} want {b[i]:#x}; {idx.size} bytes differ"
+
+
+def gpu_load(m, coords_np, n, **opts):
+    bb = T.tmap_box_bytes(m)
+    out = torch.empty(max(1, n * bb), dtype=torch.uint8, device=DEV)
+    c = None if coords_np is None else torch.from_numpy(np.ascontiguousarray(coords_np, np.int32)).to(DEV)
+    T.tmap_load_tiles(m, c, n, out, **opts)
+    check_ok()
+    return out[: n * bb]
+
+
+# ----------------------------------------------------------------- workloads
+def test_tile64_f32_roundtrip_load_store():
+    w = inputs.WORKLOADS["tile64_f32"]
+    say("tile64_f32: roundtrip, 1 stage, one box at (0,0)")
+    src = inputs.device_bytes(w, DEV)
+    dst = dev_tensor(w.alloc_bytes, fill_seed=101)
+    dst0 = dst.cpu().numpy().copy()
+    ms, md = enc("f32", src, w.dims, w.strides, w.box), enc("f32", dst, w.dims, w.strides, w.box)
+    coords = torch.zeros((1, 2), dtype=torch.int32, device=DEV)
+    T.tmap_roundtrip(ms, md, coords, 1, stages=1)
+    check_ok()
+    om = Map(es=4, dims=w.dims, strides=w.strides, box=w.box)
+    want = dst0.copy()
+    oracle.roundtrip(om, src.cpu().numpy(), om, want, np.zeros((1, 2), np.int32), 1)
+    got = dst.cpu().numpy()
+    assert (m := first_mismatch(got, want, 16384)) is None, m
+    assert got.tobytes() == src.cpu().numpy().tobytes()       # exact tiling: identity
+    packed = gpu_load(ms, np.zeros((1, 2), np.int32), 1, stages=1)
+    assert packed.cpu().numpy().tobytes() == oracle.load_tiles(om, src.cpu().numpy(), np.zeros((1, 2), np.int32), 1).tobytes()
+    dst2 = dev_tensor(w.alloc_bytes, fill_seed=102)
+    T.tmap_store_tiles(enc("f32", dst2, w.dims, w.strides, w.box), coords, 1, packed, stages=1)
+    check_ok()
+    assert dst2.cpu().numpy().tobytes() == src.cpu().numpy().tobytes()
+
+
+def test_strips_f16_load_page_schedule():
+    """924 tiles; 132 workgroups, each walking the 7 column tiles of its strip."""
+    w = inputs.WORKLOADS["strips_f16"]
+    say("strips_f16: load sweep, 2 stages, 132 WGs x 7 tiles contiguous")
+    src = inputs.device_bytes(w, DEV)
+    m = enc("f16", src, w.dims, w.strides, w.box, w.swizzle)
+    n = T.tmap_sweep_tiles(m)
+    assert n == 924
+    om = Map(es=2, dims=w.dims, strides=w.strides, box=w.box, swizzle=w.swizzle)
+    want = oracle.load_tiles(om, src.cpu().numpy(), None, n)
+    for opts in (dict(stages=2, grid_wgs=132, flags=T.FLAG_CONTIGUOUS), dict(stages=2), dict()):
+        got = gpu_load(m, None, n, **opts).cpu().numpy()
+        assert (mm := first_mismatch(got, want, 32768)) is None, (opts, mm)
+
+
+def _sample_tiles(n, extra, k, seed):
+    rng = np.random.default_rng(seed)
+    s = set(int(x) for x in rng.integers(0, n, size=k))
+    s.update(extra)
+    return np.array(sorted(s), dtype=np.int64)
+
+
+def test_ragged_bf16_full_size_sampled():
+    w = inputs.WORKLOADS["ragged_bf16"]
+    say("ragged_bf16: load sweep 65280 tiles, 4 stages; sampled oracle; store back")
+    src = inputs.device_bytes(w, DEV)
+    m = enc("bf16", src, w.dims, w.strides, w.box, w.swizzle)
+    n = T.tmap_sweep_tiles(m)
+    assert n == 65280
+    packed = gpu_load(m, None, n, stages=4)
+    om = Map(es=2, dims=w.dims, strides=w.strides, box=w.box, swizzle=w.swizzle)
+    last_row = list(range(n - 255, n))                       # the ragged strip (63 rows + 1 zero row)
+    tiles = _sample_tiles(n, last_row + [0, 254, 255], 600, 33)
+    corners = np.array([oracle.sweep_coords(om, int(t)) for t in tiles], np.int32)
+    host = src.cpu().numpy()
+    want = oracle.load_tiles(om, host, corners, len(corners)).reshape(len(tiles), -1)
+    got = packed.view(-1, 8192)[torch.from_numpy(tiles).to(DEV)].cpu().numpy()
+    assert np.array_equal(got, want), first_mismatch(got.reshape(-1), want.reshape(-1), 8192)
+    # the zero-filled row of every ragged tile: last 64 columns x 2 bytes of each image
+    # closed form: storing every image back restores every byte of the tensor
+    dst = dev_tensor(w.alloc_bytes, fill_seed=303)
+    T.tmap_store_tiles(enc("bf16", dst, w.dims, w.strides, w.box, w.swizzle), None, n, packed, stages=4)
+    check_ok()
+    assert torch.equal(dst, src)
+
+
+def test_pad5d_f32_random_corners_full():
+    w = inputs.WORKLOADS["pad5d_f32"]
+    say("pad5d_f32: load 1e5 random corners, 4 stages, full oracle; then store")
+    src = inputs.device_bytes(w, DEV)
+    host = src.cpu().numpy()
+    coords = inputs.random_corners(w.dims, w.box, w.n_random, seed=40)
+    m = enc("f32", src, w.dims, w.strides, w.box)
+    om = Map(es=4, dims=w.dims, strides=w.strides, box=w.box)
+    packed = gpu_load(m, coords, len(coords), stages=4)
+    want = oracle.load_tiles(om, host, coords, len(coords))
+    got = packed.cpu().numpy()
+    assert (mm := first_mismatch(got, want, 8192)) is None, mm
+    dst = dev_tensor(w.alloc_bytes, fill_seed=41)
+    want_dst = dst.cpu().numpy().copy()
+    c = torch.from_numpy(coords).to(DEV)
+    T.tmap_store_tiles(enc("f32", dst, w.dims, w.strides, w.box), c, len(coords), packed, stages=4)
+    check_ok()
+    oracle.store_tiles(om, want_dst, coords, len(coords), want)
+    got_dst = dst.cpu().numpy()
+    assert (mm := first_mismatch(got_dst, want_dst, 1 << 30)) is None, mm
+
+
+def test_sweep2g_u8_full_size():
+    w = inputs.WORKLOADS["sweep2g_u8"]
+    say("sweep2g_u8: roundtrip 131072 tiles (2 GiB), 4 stages; load sampled vs oracle; store")
+    src = inputs.device_bytes(w, DEV)
+    ms = enc("u8", src, w.dims, w.strides, w.box, w.swizzle)
+    n = T.tmap_sweep_tiles(ms)
+    assert n == 131072
+    dst = dev_tensor(w.alloc_bytes)
+    dst.fill_(0xA5)
+    T.tmap_roundtrip(ms, enc("u8", dst, w.dims, w.strides, w.box, w.swizzle), None, n, stages=4)
+    check_ok()
+    assert torch.equal(dst, src)                              # exact tiling: identity
+    del dst
+    packed = gpu_load(ms, None, n, stages=4)
+    om = Map(es=1, dims=w.dims, strides=w.strides, box=w.box, swizzle=w.swizzle)
+    tiles = _sample_tiles(n, [0, 1, 511, 512, n - 1], 300, 55)
+    corners = np.array([oracle.sweep_coords(om, int(t)) for t in tiles], np.int32)
+    host = src.cpu().numpy()
+    want = oracle.load_tiles(om, host, corners, len(corners)).reshape(len(tiles), -1)
+    got = packed.view(-1, 16384)[torch.from_numpy(tiles).to(DEV)].cpu().numpy()
+    assert np.array_equal(got, want)
+    del host
+    dst2 = dev_tensor(w.alloc_bytes)
+    dst2.fill_(0x5A)
+    T.tmap_store_tiles(enc("u8", dst2, w.dims, w.strides, w.box, w.swizzle), None, n, packed, stages=4)
+    check_ok()
+    assert torch.equal(dst2, src)
+
+
+# ----------------------------------------------------------------- seeded fuzz
+def _fuzz_case(rng, idx):
+    mp = inputs.random_map(rng)
+    es, dims, strides, box, swz = mp["es"], mp["dims"], mp["strides"], mp["box"], mp["swizzle"]
+    if idx % 7 == 3 and es <= 4:
+        # a swizzle that permutes elements inside 16-byte chunks
+        n_el = int(np.prod(box))
+        for mm in range(0, 4):
+            if (1 << mm) * es < 16 and n_el % (1 << (mm + 1)) == 0:
+                swz = (1, mm, 1 + int(rng.integers(0, 3)))
+                break
+    alloc = mp["alloc_bytes"]
+    ncoords = int(rng.integers(1, 40))
+    coords = inputs.random_corners(dims, box, ncoords, int(rng.integers(1 << 30)))
+    opts = dict(stages=int(rng.integers(1, 5)), grid_wgs=int(rng.choice([0, 1, 2, 3, 7])),
+                flags=int(rng.choice([0, T.FLAG_CONTIGUOUS, T.FLAG_NONTEMPORAL])))
+    return es, dims, strides, box, swz, alloc, coords, opts
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_fuzz_random_maps(chunk):
+    rng = np.random.default_rng(9000 + chunk)
+    for i in range(40):
+        es, dims, strides, box, swz, alloc, coords, opts = _fuzz_case(rng, i)
+        say(f"fuzz chunk {chunk} case {i}: es={es} dims={dims} strides={strides} box={box} swz={swz} "
+            f"n={len(coords)} opts={opts}")
+        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+        src = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        host = src.cpu().numpy()
+        m = enc(dt_of(es), src, dims, strides, box, swz)
+        bb = T.tmap_box_bytes(m)
+        # load
+        packed = gpu_load(m, coords, len(coords), **opts)
+        want = oracle.load_tiles(om, host, coords, len(coords))
+        got = packed.cpu().numpy()
+        assert (mm := first_mismatch(got, want, bb)) is None, mm
+        # round trip into a sentinel-filled tensor of another layout (same box, swizzle)
+        dst = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        want_dst = dst.cpu().numpy().copy()
+        c = torch.from_numpy(coords).to(DEV)
+        T.tmap_roundtrip(m, enc(dt_of(es), dst, dims, strides, box, swz), c, len(coords), **opts)
+        check_ok()
+        oracle.roundtrip(om, host, om, want_dst, coords, len(coords))
+        assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip", mm)
+        # store of random images through a sweep (no two boxes overlap)
+        ns = T.tmap_sweep_tiles(m)
+        imgs = inputs.sentinel_bytes(ns * bb, int(rng.integers(1 << 30)))
+        dst2 = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        want2 = dst2.cpu().numpy().copy()
+        T.tmap_store_tiles(enc(dt_of(es), dst2, dims, strides, box, swz), None, ns,
+                           torch.from_numpy(imgs).to(DEV), **opts)
+        check_ok()
+        oracle.store_tiles(om, want2, None, ns, imgs)
+        assert (mm := first_mismatch(dst2.cpu().numpy(), want2, 1 << 40)) is None, ("store", mm)
+
+
+# ----------------------------------------------------------------- edge cases
+def test_sweep_equals_explicit_coords():
+    say("sweep vs explicit corners")
+    dims, strides, box, swz = [200, 37, 3], [416, 416 * 37], [32, 8, 2], (2, 3, 2)
+    src = dev_tensor(416 * 37 * 3, fill_seed=5)
+    m = enc("u16", src, dims, strides, box, swz)
+    om = Map(es=2, dims=dims, strides=strides, box=box, swizzle=swz)
+    n = T.tmap_sweep_tiles(m)
+    corners = np.array([oracle.sweep_coords(om, t) for t in range(n)], np.int32)
+    a = gpu_load(m, None, n).cpu().numpy()
+    b = gpu_load(m, corners, n).cpu().numpy()
+    assert a.tobytes() == b.tobytes() == oracle.load_tiles(om, src.cpu().numpy(), None, n).tobytes()
+
+
+def test_largest_box_and_wide_rows():
+    say("64 KiB box (16 slots per lane, 2 stages) and 256-wide boxes")
+    cases = [(1, [256, 256], [256], [256, 256], (3, 4, 3)),        # 64 KiB u8 box
+             (4, [300, 70], [1216], [256, 16], (0, 0, 0)),          # 16 KiB, 256 wide, ragged
+             (8, [100, 9], [800], [64, 16], (2, 1, 3))]             # fp64, 8 KiB
+    for es, dims, strides, box, swz in cases:
+        alloc = dims[-1] * strides[-1]
+        src = dev_tensor(alloc, fill_seed=17)
+        m = enc(dt_of(es), src, dims, strides, box, swz)
+        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+        coords = inputs.random_corners(dims, box, 50, 8)
+        for st in ([1, 2] if T.tmap_box_bytes(m) > 32768 else [1, 2, 3, 4]):
+            got = gpu_load(m, coords, len(coords), stages=st).cpu().numpy()
+            want = oracle.load_tiles(om, src.cpu().numpy(), coords, len(coords))
+            assert (mm := first_mismatch(got, want, T.tmap_box_bytes(m))) is None, (es, box, st, mm)
+
+
+def test_rank1_and_fully_out_of_bounds():
+    say("rank 1, boxes wholly outside the tensor")
+    src = dev_tensor(4096, fill_seed=3)
+    m = enc("u8", src, [4000], [], [256])
+    om = Map(es=1, dims=[4000], strides=[], box=[256])
+    coords = np.array([[-256], [4000], [3900], [-100], [0], [1 << 30], [-(1 << 31)]], np.int32)
+    got = gpu_load(m, coords, len(coords)).cpu().numpy()
+    want = oracle.load_tiles(om, src.cpu().numpy(), coords, len(coords))
+    assert got.tobytes() == want.tobytes()
+    assert not got[:256].any() and not got[256:512].any()
+
+
+def test_zero_tiles_launch_nothing():
+    src = dev_tensor(16384, fill_seed=1)
+    m = enc("f32", src, [64, 64], [256], [64, 64])
+    out = dev_tensor(16)
+    T.tmap_load_tiles(m, torch.zeros((1, 2), dtype=torch.int32, device=DEV), 0, out)
+    check_ok()
+
+
+def test_budget_mismatch_times_out_instead_of_hanging():
+    """Announce 16 more bytes than delivered: the stage never becomes ready; the
+    bounded wait ends the kernel and the status reports a timeout."""
+    say("budget mismatch -> TIMEOUT")
+    src = dev_tensor(16384, fill_seed=1)
+    m = enc("f32", src, [64, 64], [256], [64, 64])
+    out = dev_tensor(16384 * 4)
+    coords = torch.zeros((4, 2), dtype=torch.int32, device=DEV)
+    T.tmap_load_tiles(m, coords, 4, out, stages=2, flags=T.FLAG_INJECT_BUDGET_MISMATCH, spin_limit=2000)
+    assert T.tmap_sync_status() == T.TIMEOUT
+    # the library keeps working afterwards
+    T.tmap_load_tiles(m, coords, 4, out, stages=2)
+    check_ok()
+    assert torch.equal(out.view(4, -1)[3], src)
+
+
+def test_repeat_is_deterministic():
+    w = inputs.WORKLOADS["pad5d_f32"]
+    src = inputs.device_bytes(w, DEV)
+    coords = inputs.random_corners(w.dims, w.box, 5000, seed=4)
+    m = enc("f32", src, w.dims, w.strides, w.box)
+    a = gpu_load(m, coords, len(coords))
+    for st in (1, 2, 3, 4):
+        b = gpu_load(m, coords, len(coords), stages=st, grid_wgs=97)
+        assert torch.equal(a, b), st

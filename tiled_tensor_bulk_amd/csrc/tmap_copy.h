@@ -1,0 +1,545 @@
+// tmap_copy.h -- gfx950 kernel template of the descriptor-driven tiled bulk copy.
+// Included by one small .hip file per copy direction, which instantiates the
+// variants of that direction.
+//
+// One kernel template serves the three directions (load to packed images,
+// store from packed images, round trip).  Each workgroup (4 waves) is
+// persistent and walks its share of the tiles through a ring of S LDS
+// stages:
+//
+//   fill    every lane issues one 16-byte direct-to-LDS buffer load per slot
+//           it owns (buffer_load_dwordx4 ... lds).  The tensor map sits in
+//           scalar registers; per tile only the buffer resource is rebased to
+//           the box corner, and each lane reuses the in-box byte offsets it
+//           computed once at kernel start.  Chunks that are out of bounds get
+//           the offset 0x80000000, past num_records, so the hardware writes
+//           zeros into LDS ("GPU TMA", "Why architecture matters here":
+//           out-of-bounds elements are zero-filled by the copy itself).
+//           The swizzle is applied as the bytes land: lane slot p receives
+//           the logical chunk swizzle(p), because a direct-to-LDS load writes
+//           lane l's 16 bytes at M0 + 16*l and the XOR swizzle is its own
+//           inverse ("TMA -- the async bulk copy engine", "The descriptor
+//           records the layout, including the swizzle").
+//   land    the wave waits for its own loads (vmcnt), patches chunks that are
+//           only partly inside the tensor element by element, and reports
+//           the bytes it delivered to the stage's barrier record.
+//   ready   a stage is ready when every wave has announced its byte budget and
+//           the outstanding byte count is back to zero; the record's phase bit
+//           then flips and consumers wait on that parity ("TMA -- the async
+//           bulk copy engine", "Load completion -- the mbarrier and the byte
+//           budget"; "Understanding TMA loads in CuTe DSL", "Issue the load
+//           and wait for its phase").  Consumers read slots another wave
+//           loaded, so the byte count, not the wave's own vmcnt, is what
+//           makes the stage safe to read.
+//   consume load: copy the LDS image out linearly; store / round trip: read
+//           each logical chunk back from its swizzled slot and store it,
+//           clipped to the destination's bounds.
+//   release one s_barrier per tile: no wave refills a stage before every
+//           wave finished reading it ("TMA -- the async bulk copy engine",
+//           "Why this only pays off inside a pipeline").
+//
+// The S stages are separate __shared__ objects and the tile loop is
+// unrolled by S, so the compiler's LDS-DMA tracking can wait for exactly the
+// loads of one stage instead of draining every load in flight.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tmap_internal.h"
+
+namespace tmap {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr uint32_t kOob = 0x80000000u;       // offset past every num_records
+constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, gfx9 family
+constexpr uint64_t kArrive = 1ull << 32;     // one arrival in a barrier record
+constexpr uint64_t kPhase = 1ull << 63;      // phase bit of a barrier record
+constexpr uint32_t kWaitLgkm = 0xC07F;       // s_waitcnt lgkmcnt(0) only
+
+enum Cls : uint32_t { kZero = 0, kFull = 1, kPart = 2 };
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(uint64_t addr, uint32_t nrec) {
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(addr), 0, (int)nrec, kRsrcWord3);
+}
+
+__device__ __forceinline__ uint32_t swizzle(uint32_t e, uint32_t b, uint32_t m, uint32_t s) {
+    return b ? e ^ (((e >> (m + s)) & ((1u << b) - 1u)) << m) : e;
+}
+
+// Per-tile scalar view of one map: byte offset of the box corner and, per
+// dimension, the window [lo, hi) of box indices that fall inside the tensor.
+struct Win {
+    int64_t off;
+    uint32_t lo[kMaxRank];
+    uint32_t hi[kMaxRank];
+    bool interior;
+};
+
+__device__ __forceinline__ void tile_corner(const KArgs &a, const MapImpl &swept, int64_t t,
+                                            int32_t c[kMaxRank]) {
+    if (a.coords) {
+        // Corners are read through the constant address space: uniform
+        // scalar loads (lgkmcnt), so they never wait behind the ring's
+        // direct-to-LDS loads (vmcnt).
+        typedef const __attribute__((address_space(4))) int32_t const_i32;
+        const int r = swept.rank;
+        const_i32 *p = (const_i32 *)(a.coords) + t * r;
+#pragma unroll
+        for (int d = 0; d < kMaxRank; ++d) c[d] = d < r ? p[d] : 0;
+    } else {
+        uint64_t rest = (uint64_t)t;
+#pragma unroll
+        for (int d = 0; d < kMaxRank; ++d) {
+            const uint64_t nt = a.sweep_tiles[d];
+            const uint64_t q = rest / nt;
+            c[d] = (int32_t)((rest - q * nt) * swept.box[d]);
+            rest = q;
+        }
+    }
+}
+
+__device__ __forceinline__ Win window(const MapImpl &m, const int32_t c[kMaxRank]) {
+    Win w;
+    w.off = 0;
+    w.interior = true;
+#pragma unroll
+    for (int d = 0; d < kMaxRank; ++d) {
+        const int64_t cd = c[d];
+        const int64_t b = m.box[d];
+        int64_t lo = -cd;
+        lo = lo < 0 ? 0 : (lo > b ? b : lo);
+        int64_t hi = (int64_t)m.dims[d] - cd;
+        hi = hi < lo ? lo : (hi > b ? b : hi);
+        w.lo[d] = (uint32_t)lo;
+        w.hi[d] = (uint32_t)hi;
+        w.interior = w.interior && lo == 0 && hi == b;
+        w.off += cd * (int64_t)m.strides[d];
+    }
+    return w;
+}
+
+// Packed box indices of a chunk: w0 = x0 | i1 << 16, w1 = i2 | i3 << 8 | i4 << 16,
+// x0 being the first element index of the chunk in dimension 0.
+__device__ __forceinline__ uint32_t classify(uint32_t w0, uint32_t w1, const Win &w, uint32_t k_el) {
+    const uint32_t x0 = w0 & 0xFFFFu, i1 = w0 >> 16;
+    const uint32_t i2 = w1 & 0xFFu, i3 = (w1 >> 8) & 0xFFu, i4 = w1 >> 16;
+    const bool row_in = (i1 - w.lo[1] < w.hi[1] - w.lo[1]) & (i2 - w.lo[2] < w.hi[2] - w.lo[2]) &
+                        (i3 - w.lo[3] < w.hi[3] - w.lo[3]) & (i4 - w.lo[4] < w.hi[4] - w.lo[4]);
+    const bool full0 = (x0 >= w.lo[0]) & (x0 + k_el <= w.hi[0]);
+    const bool any0 = (x0 < w.hi[0]) & (x0 + k_el > w.lo[0]);
+    return !row_in ? kZero : (full0 ? kFull : (any0 ? kPart : kZero));
+}
+
+// Box indices of tile-local element e (innermost fastest).
+__device__ __forceinline__ void unravel(uint32_t e, const MapImpl &m, uint32_t i[kMaxRank]) {
+#pragma unroll
+    for (int d = 0; d < kMaxRank; ++d) {
+        const uint32_t b = m.box[d];
+        const uint32_t q = e / b;
+        i[d] = e - q * b;
+        e = q;
+    }
+}
+
+__device__ __forceinline__ bool inside(const uint32_t i[kMaxRank], const Win &w) {
+    bool ok = true;
+#pragma unroll
+    for (int d = 0; d < kMaxRank; ++d) ok = ok & (i[d] - w.lo[d] < w.hi[d] - w.lo[d]);
+    return ok;
+}
+
+__device__ __forceinline__ uint32_t inbox_offset(const uint32_t i[kMaxRank], const MapImpl &m) {
+    uint64_t o = 0;
+#pragma unroll
+    for (int d = 0; d < kMaxRank; ++d) o += (uint64_t)i[d] * m.strides[d];
+    return (uint32_t)o;
+}
+
+// ---------------------------------------------------------------- barrier record
+// One 8-byte LDS word per stage: bits 0..31 outstanding bytes, bits 32..62
+// arrivals, bit 63 phase.  The operation that leaves (all waves arrived, zero
+// bytes outstanding) resets the counts and flips the phase.
+__device__ __forceinline__ void bar_update(uint64_t *bar, uint64_t delta) {
+    const uint64_t old = __hip_atomic_fetch_add(bar, delta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint64_t now = old + delta;
+    if ((now & ~kPhase) == ((uint64_t)kWaves << 32))
+        __hip_atomic_fetch_add(bar, kPhase - ((uint64_t)kWaves << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// arrive + expect_tx(bytes)
+__device__ __forceinline__ void bar_arrive_expect(uint64_t *bar, uint32_t bytes, uint32_t lane) {
+    if (lane == 0) bar_update(bar, kArrive + bytes);
+}
+
+// complete_tx(bytes): the wave's own loads into the stage have landed
+__device__ __forceinline__ void bar_complete(uint64_t *bar, uint32_t bytes, uint32_t lane) {
+    if (lane == 0 && bytes) bar_update(bar, (uint64_t)0 - (uint64_t)bytes);
+}
+
+// Wait until the phase with parity `parity` has completed; false on timeout.
+__device__ __forceinline__ bool bar_wait(uint64_t *bar, uint32_t parity, uint32_t limit) {
+    for (uint32_t polls = 0;; ++polls) {
+        const uint64_t v = __hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if ((uint32_t)(v >> 63) != parity) return true;
+        if (polls >= limit) return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// ---------------------------------------------------------------- element path
+// Load the elements of LDS slot p one by one (used for chunks that straddle a
+// dimension-0 edge, and for every chunk when the swizzle permutes bytes inside
+// a 16-byte chunk).  Out-of-bounds elements read the out-of-range offset and
+// land as zero.
+__device__ __forceinline__ void load_slot_elements(uint8_t *stage, uint32_t p, const KArgs &a, const MapImpl &m,
+                                                const Win &w, __amdgpu_buffer_rsrc_t r) {
+    const uint32_t es = m.elem_size, k = a.k_el;
+    for (uint32_t j = 0; j < k; ++j) {
+        const uint32_t s = p * k + j;
+        uint32_t i[kMaxRank];
+        unravel(swizzle(s, m.swz_b, m.swz_m, m.swz_s), m, i);
+        const uint32_t off = inside(i, w) ? inbox_offset(i, m) : kOob;
+        uint8_t *dst = stage + (size_t)s * es;
+        if (es == 1) {
+            *dst = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+        } else if (es == 2) {
+            *(uint16_t *)dst = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+        } else if (es == 4) {
+            *(uint32_t *)dst = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+        } else {
+            auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+            *(decltype(v) *)dst = v;
+        }
+    }
+}
+
+// Store the in-bounds elements held in LDS slot p one by one.
+__device__ __forceinline__ void store_slot_elements(const uint8_t *stage, uint32_t p, const KArgs &a,
+                                                 const MapImpl &m, const Win &w, __amdgpu_buffer_rsrc_t r) {
+    const uint32_t es = m.elem_size, k = a.k_el;
+    for (uint32_t j = 0; j < k; ++j) {
+        const uint32_t s = p * k + j;
+        uint32_t i[kMaxRank];
+        unravel(swizzle(s, m.swz_b, m.swz_m, m.swz_s), m, i);
+        if (!inside(i, w)) continue;
+        const uint32_t off = inbox_offset(i, m);
+        const uint8_t *src = stage + (size_t)s * es;
+        if (es == 1) {
+            __builtin_amdgcn_raw_buffer_store_b8(*src, r, off, 0, 0);
+        } else if (es == 2) {
+            __builtin_amdgcn_raw_buffer_store_b16(*(const uint16_t *)src, r, off, 0, 0);
+        } else if (es == 4) {
+            __builtin_amdgcn_raw_buffer_store_b32(*(const uint32_t *)src, r, off, 0, 0);
+        } else {
+            typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+            __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2 *)src, r, off, 0, 0);
+        }
+    }
+}
+
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+// ---------------------------------------------------------------- the kernel
+template <int MODE, int S, int NSLOT>
+struct Copier {
+    static constexpr uint32_t kStageBytes = NSLOT * kWaves * kBlockBytes;
+
+    const KArgs &a;
+    uint32_t lane, wave, my_bytes, parity;
+    int64_t t0, tstep, cnt;
+    bool nt;
+    uint64_t *bars;
+    uint32_t *abort_flag;
+    // producer slots (the slots this lane fills) and consumer slots (the slots
+    // this lane drains: those the next wave filled)
+    uint32_t pslot[NSLOT], poff[NSLOT], pw0[NSLOT], pw1[NSLOT];
+    uint32_t cslot[NSLOT], coff[NSLOT], cw0[NSLOT], cw1[NSLOT];
+
+    __device__ __forceinline__ Copier(const KArgs &args, uint64_t *b, uint32_t *ab) : a(args), bars(b), abort_flag(ab) {}
+
+    __device__ __forceinline__ const MapImpl &swept() const { return MODE == kStore ? a.dst : a.src; }
+
+    __device__ __forceinline__ int64_t tile(int64_t k) const { return t0 + k * tstep; }
+
+    // In-box byte offset (in map m) and packed indices of logical chunk q.
+    __device__ __forceinline__ void chunk_info(uint32_t q, const MapImpl &m, uint32_t &off, uint32_t &w0,
+                                               uint32_t &w1) const {
+        const uint32_t row = q / a.row_chunks;
+        const uint32_t x0 = (q - row * a.row_chunks) * a.k_el;
+        uint32_t i[kMaxRank];
+        i[0] = x0;
+        uint32_t rest = row;
+#pragma unroll
+        for (int d = 1; d < kMaxRank; ++d) {
+            const uint32_t b = m.box[d];
+            const uint32_t qq = rest / b;
+            i[d] = rest - qq * b;
+            rest = qq;
+        }
+        off = inbox_offset(i, m);
+        w0 = x0 | (i[1] << 16);
+        w1 = i[2] | (i[3] << 8) | (i[4] << 16);
+    }
+
+    __device__ __forceinline__ uint32_t logical_chunk(uint32_t p, const MapImpl &m) const {
+        return swizzle(p * a.k_el, m.swz_b, m.swz_m, m.swz_s) / a.k_el;
+    }
+
+    __device__ __forceinline__ void setup() {
+        lane = threadIdx.x & 63u;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        nt = (a.flags & TMAP_FLAG_NONTEMPORAL) != 0;
+        parity = 0;
+        const int64_t n = a.n_tiles;
+        const int64_t G = a.grid, g = blockIdx.x;
+        if (a.flags & TMAP_FLAG_CONTIGUOUS) {
+            const int64_t base = n / G, rem = n % G;
+            cnt = base + (g < rem ? 1 : 0);
+            t0 = g * base + (g < rem ? g : rem);
+            tstep = 1;
+        } else {
+            cnt = g < n ? (n - 1 - g) / G + 1 : 0;
+            t0 = g;
+            tstep = G;
+        }
+        my_bytes = 0;
+        const uint32_t cw = (wave + 1) % kWaves;
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) {
+            const uint32_t pb = (uint32_t)(j * kWaves) + wave;
+            const int32_t valid = (int32_t)a.n_chunks - (int32_t)(pb * 64u);
+            my_bytes += 16u * (uint32_t)(valid <= 0 ? 0 : (valid >= 64 ? 64 : valid));
+            pslot[j] = pb * 64u + lane;
+            cslot[j] = ((uint32_t)(j * kWaves) + cw) * 64u + lane;
+            poff[j] = pw0[j] = pw1[j] = 0;
+            coff[j] = cw0[j] = cw1[j] = 0;
+            if (!a.elemwise) {
+                if (MODE != kStore && pslot[j] < a.n_chunks)
+                    chunk_info(logical_chunk(pslot[j], a.src), a.src, poff[j], pw0[j], pw1[j]);
+                if (MODE != kLoad && cslot[j] < a.n_chunks)
+                    chunk_info(logical_chunk(cslot[j], a.dst), a.dst, coff[j], cw0[j], cw1[j]);
+            }
+        }
+    }
+
+    template <typename T>
+    __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, T *stage, int j, uint32_t voff) const {
+        lds_void_t *blk = (lds_void_t *)(stage + (j * kWaves + wave) * kBlockBytes);
+        if (nt)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, blk, 16, voff, 0, 0, 2);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, blk, 16, voff, 0, 0, 0);
+    }
+
+    // Issue the loads of tile k into `stage`.
+    __device__ __forceinline__ void fill(uint8_t *stage, uint64_t *bar, int64_t k) const {
+        const int64_t t = tile(k);
+        const uint32_t budget = my_bytes + ((a.flags & TMAP_FLAG_INJECT_BUDGET_MISMATCH) ? 16u : 0u);
+        bar_arrive_expect(bar, budget, lane);
+        if (MODE == kStore) {
+            const uint64_t bb = a.dst.box_bytes;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)t * bb, (uint32_t)bb);
+#pragma unroll
+            for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? pslot[j] * 16u : kOob);
+        } else {
+            int32_t c[kMaxRank];
+            tile_corner(a, a.src, t, c);
+            const Win w = window(a.src, c);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)w.off, a.src.span);
+            if (w.interior && !a.elemwise) {
+#pragma unroll
+                for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? poff[j] : kOob);
+            } else {
+#pragma unroll
+                for (int j = 0; j < NSLOT; ++j) {
+                    const bool full = !a.elemwise && pslot[j] < a.n_chunks &&
+                                      classify(pw0[j], pw1[j], w, a.k_el) == kFull;
+                    dma(r, stage, j, full ? poff[j] : kOob);
+                }
+            }
+        }
+    }
+
+    // The wave's loads of tile k into `stage` have landed: patch partial
+    // chunks, then report the delivered bytes.
+    __device__ __forceinline__ void land(uint8_t *stage, uint64_t *bar, int64_t k) const {
+        // A read of this stage object makes the compiler wait (vmcnt) for this
+        // wave's direct-to-LDS loads into it.
+        uint32_t probe = *(volatile uint32_t *)(stage + (wave * 64u + lane) * 16u);
+        asm volatile("" ::"v"(probe) : "memory");
+        if (MODE != kStore) {
+            int32_t c[kMaxRank];
+            tile_corner(a, a.src, tile(k), c);
+            const Win w = window(a.src, c);
+            if (!w.interior || a.elemwise) {
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)w.off, a.src.span);
+#pragma unroll
+                for (int j = 0; j < NSLOT; ++j) {
+                    if (pslot[j] >= a.n_chunks) continue;
+                    if (a.elemwise || classify(pw0[j], pw1[j], w, a.k_el) == kPart)
+                        load_slot_elements(stage, pslot[j], a, a.src, w, r);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+        asm volatile("" ::: "memory");
+        bar_complete(bar, my_bytes, lane);
+    }
+
+    // Read tile k out of `stage`.
+    __device__ __forceinline__ void consume(uint8_t *stage, int64_t k) const {
+        const int64_t t = tile(k);
+        if (MODE == kLoad) {
+            const uint64_t bb = a.src.box_bytes;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)t * bb, (uint32_t)bb);
+#pragma unroll
+            for (int j = 0; j < NSLOT; ++j) {
+                if (cslot[j] < a.n_chunks) {
+                    const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
+                    if (nt)
+                        __builtin_amdgcn_raw_buffer_store_b128(v, r, cslot[j] * 16u, 0, 2);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b128(v, r, cslot[j] * 16u, 0, 0);
+                }
+            }
+        } else {
+            int32_t c[kMaxRank];
+            tile_corner(a, swept(), t, c);
+            const Win w = window(a.dst, c);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.dst.base + (uint64_t)w.off, a.dst.span);
+            if (w.interior && !a.elemwise) {
+#pragma unroll
+                for (int j = 0; j < NSLOT; ++j) {
+                    if (cslot[j] < a.n_chunks) {
+                        const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
+                        if (nt)
+                            __builtin_amdgcn_raw_buffer_store_b128(v, r, coff[j], 0, 2);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b128(v, r, coff[j], 0, 0);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NSLOT; ++j) {
+                    if (cslot[j] >= a.n_chunks) continue;
+                    const uint32_t cls = a.elemwise ? kPart : classify(cw0[j], cw1[j], w, a.k_el);
+                    if (cls == kFull) {
+                        const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
+                        __builtin_amdgcn_raw_buffer_store_b128(v, r, coff[j], 0, 0);
+                    } else if (cls == kPart) {
+                        store_slot_elements(stage, cslot[j], a, a.dst, w, r);
+                    }
+                }
+            }
+        }
+    }
+
+    // One ring step for tile k held in stage X; `fillst` is the stage that
+    // tile k+S-1 goes to (the one tile k-1 just left).  False ends the loop.
+    template <int X>
+    __device__ __forceinline__ bool step(uint8_t *st, uint8_t *fillst, int64_t k) {
+        if (k >= cnt) return false;
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+        __builtin_amdgcn_s_barrier();
+        if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
+        constexpr int XF = (X + S - 1) % S;
+        if (k + S - 1 < cnt) fill(fillst, &bars[XF], k + S - 1);
+        land(st, &bars[X], k);
+        const bool ok = bar_wait(&bars[X], (parity >> X) & 1u, a.spin_limit);
+        parity ^= 1u << X;
+        asm volatile("" ::: "memory");
+        if (ok) {
+            consume(st, k);
+        } else if (lane == 0) {
+            __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return true;
+    }
+};
+
+template <int MODE, int S, int NSLOT>
+__global__ __launch_bounds__(kThreads) void copy_kernel(const KArgs a) {
+    constexpr uint32_t SB = NSLOT * kWaves * kBlockBytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[SB];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[S > 1 ? SB : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? SB : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? SB : 16];
+    __shared__ uint64_t bars[4];
+    __shared__ uint32_t abort_flag;
+
+    Copier<MODE, S, NSLOT> cp(a, bars, &abort_flag);
+    if (threadIdx.x == 0) {
+        for (int i = 0; i < 4; ++i) bars[i] = 0;
+        abort_flag = 0;
+    }
+    cp.setup();
+    __syncthreads();
+    if (cp.cnt <= 0) return;
+
+    // prologue: tiles 0..S-2 go to stages 0..S-2
+    if constexpr (S > 1) cp.fill(st0, &bars[0], 0);
+    if constexpr (S > 2) if (1 < cp.cnt) cp.fill(st1, &bars[1], 1);
+    if constexpr (S > 3) if (2 < cp.cnt) cp.fill(st2, &bars[2], 2);
+
+    for (int64_t kb = 0; kb < cp.cnt; kb += S) {
+        if constexpr (S == 1) {
+            if (!cp.template step<0>(st0, st0, kb)) break;
+        } else if constexpr (S == 2) {
+            if (!cp.template step<0>(st0, st1, kb)) break;
+            if (!cp.template step<1>(st1, st0, kb + 1)) break;
+        } else if constexpr (S == 3) {
+            if (!cp.template step<0>(st0, st2, kb)) break;
+            if (!cp.template step<1>(st1, st0, kb + 1)) break;
+            if (!cp.template step<2>(st2, st1, kb + 2)) break;
+        } else {
+            if (!cp.template step<0>(st0, st3, kb)) break;
+            if (!cp.template step<1>(st1, st0, kb + 1)) break;
+            if (!cp.template step<2>(st2, st1, kb + 2)) break;
+            if (!cp.template step<3>(st3, st2, kb + 3)) break;
+        }
+    }
+    // nothing may still be writing LDS or memory when the wave ends
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+typedef void (*KernelFn)(const KArgs);
+
+template <int MODE, int S>
+KernelFn pick_nslot(int nslot) {
+    switch (nslot) {
+        case 1: return copy_kernel<MODE, S, 1>;
+        case 2: return copy_kernel<MODE, S, 2>;
+        case 4: return copy_kernel<MODE, S, 4>;
+        case 8: return copy_kernel<MODE, S, 8>;
+        case 16:
+            if constexpr (S <= 2) return copy_kernel<MODE, S, 16>;
+            return nullptr;
+        default: return nullptr;
+    }
+}
+
+// Launch the (MODE, stages, nslot) variant; hipError_t as int.
+template <int MODE>
+int launch_mode(int stages, int nslot, const KArgs &a, void *stream) {
+    KernelFn fn = nullptr;
+    switch (stages) {
+        case 1: fn = pick_nslot<MODE, 1>(nslot); break;
+        case 2: fn = pick_nslot<MODE, 2>(nslot); break;
+        case 3: fn = pick_nslot<MODE, 3>(nslot); break;
+        case 4: fn = pick_nslot<MODE, 4>(nslot); break;
+        default: break;
+    }
+    if (!fn) return (int)hipErrorInvalidValue;
+    KArgs copy = a;
+    void *args[] = {&copy};
+    return (int)hipLaunchKernel((const void *)fn, dim3(a.grid), dim3(kThreads), args, 0, (hipStream_t)stream);
+}
+
+}  // namespace
+}  // namespace tmap

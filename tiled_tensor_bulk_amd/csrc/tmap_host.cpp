@@ -1,0 +1,446 @@
+// tmap_host.cpp -- host half of libtmap: tensor-map encode and validation,
+// queries, the gfx950 device gate, launch selection and the status word.
+//
+// Encode follows "Day 76: The Tensor Memory Accelerator (TMA)", sections
+// "The address arithmetic moves into a descriptor" and "Pitfalls": the map is
+// validated and packed once on the host, every rule is checked, and a single
+// failed rule fails the whole call with INVALID_VALUE.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "tmap_internal.h"
+
+using tmap::MapImpl;
+
+namespace {
+
+thread_local std::string g_detail;
+
+tmap_status fail(tmap_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+tmap_status fail(tmap_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return st;
+}
+
+tmap_status ok() {
+    g_detail.clear();
+    return TMAP_SUCCESS;
+}
+
+int elem_size_of(tmap_dtype t) {
+    switch (t) {
+        case TMAP_U8: case TMAP_I8: return 1;
+        case TMAP_U16: case TMAP_F16: case TMAP_BF16: return 2;
+        case TMAP_U32: case TMAP_I32: case TMAP_F32: return 4;
+        case TMAP_U64: case TMAP_F64: return 8;
+    }
+    return 0;
+}
+
+bool decode(const tmap_t *map, MapImpl &m) {
+    if (!map) return false;
+    std::memcpy(&m, map, sizeof m);
+    return m.magic == tmap::kMagic;
+}
+
+// ------------------------------------------------------------------ device
+struct DeviceState {
+    bool probed = false;
+    bool supported = false;
+    int cus = 0;
+    uint32_t lds_per_cu = 0;
+    uint32_t *status = nullptr;  // one word, allocated on first launch
+};
+std::mutex g_dev_mu;
+DeviceState g_dev[64];
+
+// Arch gate: the copy kernels are built for gfx950 only.  The check happens
+// before any allocation or launch ("Day 76", "Checks for the first run": the
+// capability gate is a branch taken before anything is allocated).
+tmap_status device_for_launch(DeviceState **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return fail(TMAP_ERROR_UNSUPPORTED_DEVICE, "no HIP device is available");
+    }
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DeviceState &d = g_dev[dev];
+    if (!d.probed) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(TMAP_ERROR_UNSUPPORTED_DEVICE, "cannot query HIP device %d", dev);
+        }
+        d.probed = true;
+        d.supported = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+        d.cus = p.multiProcessorCount;
+        d.lds_per_cu = (uint32_t)p.maxSharedMemoryPerMultiProcessor;
+        if (d.lds_per_cu == 0) d.lds_per_cu = 160 * 1024;
+    }
+    if (!d.supported)
+        return fail(TMAP_ERROR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+    if (!d.status) {
+        void *p = nullptr;
+        if (hipMalloc(&p, 4) != hipSuccess || hipMemset(p, 0, 4) != hipSuccess) {
+            (void)hipGetLastError();
+            if (p) (void)hipFree(p);
+            return fail(TMAP_ERROR_LAUNCH, "cannot allocate the 4-byte status word");
+        }
+        d.status = (uint32_t *)p;
+    }
+    *out = &d;
+    return TMAP_SUCCESS;
+}
+
+int64_t sweep_count(const MapImpl &m) {
+    int64_t n = 1;
+    for (int d = 0; d < m.rank; ++d) n *= (int64_t)((m.dims[d] + m.box[d] - 1) / m.box[d]);
+    return n;
+}
+
+struct Plan {
+    int nslot, stages;
+    uint32_t grid;
+};
+
+tmap_status plan_launch(const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
+                        const DeviceState &dev, Plan &pl) {
+    const uint32_t per_wave_pass = tmap::kWaves * tmap::kBlockBytes;  // bytes one slot per lane covers
+    const uint32_t need = (m.box_bytes + per_wave_pass - 1) / per_wave_pass;
+    int nslot = 1;
+    while ((uint32_t)nslot < need) nslot *= 2;
+    if (nslot > 16) return fail(TMAP_ERROR_INVALID_VALUE, "box of %u bytes is too large", m.box_bytes);
+    int stages = (opts && opts->stages) ? (int)opts->stages : (nslot >= 16 ? 2 : 4);
+    if (stages < 1 || stages > 4)
+        return fail(TMAP_ERROR_INVALID_VALUE, "stages must be 1..4 (got %d)", stages);
+    const uint32_t lds = tmap::variant_lds_bytes(stages, nslot);
+    if (lds > dev.lds_per_cu || (nslot == 16 && stages > 2))
+        return fail(TMAP_ERROR_INVALID_VALUE, "%d stages of %u bytes do not fit in LDS", stages,
+                    (unsigned)(nslot * per_wave_pass));
+    uint32_t grid = (opts && opts->grid_wgs) ? opts->grid_wgs : 0;
+    if (!grid) {
+        uint32_t per_cu = dev.lds_per_cu / lds;
+        if (per_cu > 4) per_cu = 4;
+        if (per_cu < 1) per_cu = 1;
+        grid = (uint32_t)dev.cus * per_cu;
+    }
+    if ((int64_t)grid > n_tiles) grid = (uint32_t)n_tiles;
+    pl.nslot = nslot;
+    pl.stages = stages;
+    pl.grid = grid;
+    return TMAP_SUCCESS;
+}
+
+tmap_status check_coords_and_count(const MapImpl &swept, const int32_t *coords, int64_t n_tiles) {
+    if (n_tiles < 0) return fail(TMAP_ERROR_INVALID_VALUE, "n_tiles is negative");
+    if (!coords && n_tiles != sweep_count(swept))
+        return fail(TMAP_ERROR_INVALID_VALUE, "a sweep (coords == NULL) needs n_tiles == %lld, got %lld",
+                    (long long)sweep_count(swept), (long long)n_tiles);
+    if (coords && ((uintptr_t)coords & 3u))
+        return fail(TMAP_ERROR_INVALID_VALUE, "coords must be 4-byte aligned");
+    return TMAP_SUCCESS;
+}
+
+void fill_common(tmap::KArgs &a, const MapImpl &swept, const int32_t *coords, int64_t n_tiles) {
+    a.coords = coords;
+    a.n_tiles = n_tiles;
+    for (int d = 0; d < tmap::kMaxRank; ++d)
+        a.sweep_tiles[d] = (uint32_t)((swept.dims[d] + swept.box[d] - 1) / swept.box[d]);
+    a.n_chunks = swept.box_bytes / 16u;
+    a.row_chunks = (uint32_t)swept.box[0] * swept.elem_size / 16u;
+    a.k_el = 16u / swept.elem_size;
+    // The direct-to-LDS path moves whole 16-byte chunks; a swizzle that
+    // permutes elements inside a chunk needs the element path for every chunk.
+    a.elemwise = (swept.swz_b > 0 && ((1u << swept.swz_m) * swept.elem_size) < 16u) ? 1u : 0u;
+}
+
+tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launch_opts *opts,
+                void *stream) {
+    DeviceState *dev = nullptr;
+    tmap_status st = device_for_launch(&dev);
+    if (st != TMAP_SUCCESS) return st;
+    Plan pl;
+    st = plan_launch(swept, a.n_tiles, opts, *dev, pl);
+    if (st != TMAP_SUCCESS) return st;
+    a.status = dev->status;
+    a.grid = pl.grid;
+    a.flags = opts ? opts->flags : 0u;
+    a.spin_limit = (opts && opts->spin_limit) ? opts->spin_limit : (1u << 22);
+    int rc = (int)hipErrorInvalidValue;
+    switch (mode) {
+        case tmap::kLoad: rc = tmap::launch_load(pl.stages, pl.nslot, a, stream); break;
+        case tmap::kStore: rc = tmap::launch_store(pl.stages, pl.nslot, a, stream); break;
+        case tmap::kRoundtrip: rc = tmap::launch_roundtrip(pl.stages, pl.nslot, a, stream); break;
+        default: break;
+    }
+    if (rc != 0) {
+        (void)hipGetLastError();
+        return fail(TMAP_ERROR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)rc));
+    }
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tmap_status_string(tmap_status s) {
+    switch (s) {
+        case TMAP_SUCCESS: return "TMAP_SUCCESS";
+        case TMAP_ERROR_INVALID_VALUE: return "TMAP_ERROR_INVALID_VALUE";
+        case TMAP_ERROR_UNSUPPORTED_DEVICE: return "TMAP_ERROR_UNSUPPORTED_DEVICE";
+        case TMAP_ERROR_LAUNCH: return "TMAP_ERROR_LAUNCH";
+        case TMAP_ERROR_TIMEOUT: return "TMAP_ERROR_TIMEOUT";
+    }
+    return "TMAP_ERROR_UNKNOWN";
+}
+
+const char *tmap_last_error_detail(void) { return g_detail.c_str(); }
+
+tmap_status tmap_encode(tmap_t *map, tmap_dtype dtype, uint32_t rank, void *global_address,
+                        const uint64_t *global_dim, const uint64_t *global_strides,
+                        const uint32_t *box_dim, const uint32_t *element_strides,
+                        tmap_swizzle swizzle) {
+    if (!map) return fail(TMAP_ERROR_INVALID_VALUE, "map is NULL");
+    // the pages' rules
+    if (rank < 1 || rank > (uint32_t)tmap::kMaxRank)
+        return fail(TMAP_ERROR_INVALID_VALUE, "rank %u is outside 1..5", rank);
+    if (!global_dim || !box_dim || (rank > 1 && !global_strides))
+        return fail(TMAP_ERROR_INVALID_VALUE, "dims, strides or box array is NULL");
+    for (uint32_t d = 0; d < rank; ++d)
+        if (box_dim[d] > 256u)
+            return fail(TMAP_ERROR_INVALID_VALUE, "box dim %u is %u, above 256", d, box_dim[d]);
+    for (uint32_t d = 1; d < rank; ++d)
+        if (global_strides[d - 1] % 16u)
+            return fail(TMAP_ERROR_INVALID_VALUE, "stride of dim %u (%llu bytes) is not a multiple of 16", d,
+                        (unsigned long long)global_strides[d - 1]);
+    const uint64_t base = (uint64_t)(uintptr_t)global_address;
+    if (base % 16u)
+        return fail(TMAP_ERROR_INVALID_VALUE, "global address 0x%llx is not 16-byte aligned",
+                    (unsigned long long)base);
+    // this library's rules
+    if (base == 0) return fail(TMAP_ERROR_INVALID_VALUE, "global address is NULL");
+    const int es = elem_size_of(dtype);
+    if (!es) return fail(TMAP_ERROR_INVALID_VALUE, "unknown dtype %d", (int)dtype);
+    for (uint32_t d = 0; d < rank; ++d)
+        if (global_dim[d] < 1 || global_dim[d] > (1ull << 31))
+            return fail(TMAP_ERROR_INVALID_VALUE, "dim %u (%llu) is outside [1, 2^31]", d,
+                        (unsigned long long)global_dim[d]);
+    for (uint32_t d = 0; d < rank; ++d)
+        if (box_dim[d] < 1) return fail(TMAP_ERROR_INVALID_VALUE, "box dim %u is 0", d);
+    for (uint32_t d = 1; d < rank; ++d)
+        if (global_strides[d - 1] == 0 || global_strides[d - 1] >= (1ull << 40))
+            return fail(TMAP_ERROR_INVALID_VALUE, "stride of dim %u is 0 or not below 2^40", d);
+    if (element_strides)
+        for (uint32_t d = 0; d < rank; ++d)
+            if (element_strides[d] != 1u)
+                return fail(TMAP_ERROR_INVALID_VALUE, "element stride of dim %u is %u; only 1 is supported", d,
+                            element_strides[d]);
+    if (((uint64_t)box_dim[0] * (uint64_t)es) % 16u)
+        return fail(TMAP_ERROR_INVALID_VALUE, "box row of %llu bytes is not a whole number of 16-byte chunks",
+                    (unsigned long long)box_dim[0] * es);
+    uint64_t n_el = 1;
+    for (uint32_t d = 0; d < rank; ++d) n_el *= box_dim[d];
+    if (n_el * (uint64_t)es > 65536u)
+        return fail(TMAP_ERROR_INVALID_VALUE, "box of %llu bytes is above 64 KiB",
+                    (unsigned long long)(n_el * es));
+    const uint32_t b = swizzle.b, m = swizzle.m, s = swizzle.s;
+    if (b > 8 || m > 16 || s > 16)
+        return fail(TMAP_ERROR_INVALID_VALUE, "swizzle (%u,%u,%u) is out of range", b, m, s);
+    if (b > 0 && s < b)
+        return fail(TMAP_ERROR_INVALID_VALUE, "swizzle shift %u is below its bit count %u", s, b);
+    if (b > 0 && (n_el % (1ull << (m + b))) != 0)
+        return fail(TMAP_ERROR_INVALID_VALUE, "box of %llu elements is not a multiple of the swizzle period 2^%u",
+                    (unsigned long long)n_el, m + b);
+    uint64_t span = (uint64_t)box_dim[0] * es;
+    for (uint32_t d = 1; d < rank; ++d) span += (uint64_t)(box_dim[d] - 1) * global_strides[d - 1];
+    if (span >= (1ull << 31))
+        return fail(TMAP_ERROR_INVALID_VALUE, "box footprint of %llu bytes is not below 2 GiB",
+                    (unsigned long long)span);
+
+    MapImpl mi;
+    std::memset(&mi, 0, sizeof mi);
+    mi.base = base;
+    for (int d = 0; d < tmap::kMaxRank; ++d) {
+        const bool used = (uint32_t)d < rank;
+        mi.dims[d] = used ? global_dim[d] : 1;
+        mi.strides[d] = !used ? 0 : (d == 0 ? (uint64_t)es : global_strides[d - 1]);
+        mi.box[d] = (uint16_t)(used ? box_dim[d] : 1);
+    }
+    mi.elem_size = (uint8_t)es;
+    mi.rank = (uint8_t)rank;
+    mi.swz_b = (uint8_t)b;
+    mi.swz_m = (uint8_t)m;
+    mi.swz_s = (uint8_t)s;
+    mi.dtype = (uint8_t)dtype;
+    mi.box_bytes = (uint32_t)(n_el * es);
+    mi.span = (uint32_t)span;
+    mi.magic = tmap::kMagic;
+    std::memcpy(map, &mi, sizeof mi);
+    return ok();
+}
+
+uint64_t tmap_box_bytes(const tmap_t *map) {
+    MapImpl m;
+    return decode(map, m) ? m.box_bytes : 0;
+}
+
+int64_t tmap_sweep_tiles(const tmap_t *map) {
+    MapImpl m;
+    return decode(map, m) ? sweep_count(m) : -1;
+}
+
+tmap_status tmap_query(const tmap_t *map, tmap_info *out) {
+    MapImpl m;
+    if (!out || !decode(map, m)) return fail(TMAP_ERROR_INVALID_VALUE, "map is NULL or not encoded");
+    std::memset(out, 0, sizeof *out);
+    out->global_address = m.base;
+    for (int d = 0; d < tmap::kMaxRank; ++d) {
+        out->dims[d] = d < m.rank ? m.dims[d] : 0;
+        out->strides[d] = d < m.rank ? m.strides[d] : 0;
+        out->box[d] = d < m.rank ? m.box[d] : 0;
+    }
+    out->rank = m.rank;
+    out->elem_size = m.elem_size;
+    out->dtype = m.dtype;
+    out->swizzle.b = m.swz_b;
+    out->swizzle.m = m.swz_m;
+    out->swizzle.s = m.swz_s;
+    return ok();
+}
+
+tmap_status tmap_inbounds_elems(const tmap_t *map, const int32_t *host_coords, int64_t n_tiles,
+                                uint64_t *out_elems) {
+    MapImpl m;
+    if (!out_elems || !decode(map, m)) return fail(TMAP_ERROR_INVALID_VALUE, "map is NULL or not encoded");
+    tmap_status st = check_coords_and_count(m, host_coords, n_tiles);
+    if (st != TMAP_SUCCESS) return st;
+    // per tile: product over dimensions of the overlap of [c, c+box) with [0, dim)
+    uint64_t total = 0;
+    int64_t nt[tmap::kMaxRank];
+    for (int d = 0; d < tmap::kMaxRank; ++d) nt[d] = (int64_t)((m.dims[d] + m.box[d] - 1) / m.box[d]);
+    for (int64_t t = 0; t < n_tiles; ++t) {
+        uint64_t prod = 1;
+        int64_t rest = t;
+        for (int d = 0; d < tmap::kMaxRank; ++d) {
+            int64_t c;
+            if (host_coords) {
+                c = d < m.rank ? host_coords[t * m.rank + d] : 0;
+            } else {
+                c = (rest % nt[d]) * (int64_t)m.box[d];
+                rest /= nt[d];
+            }
+            int64_t lo = c < 0 ? 0 : c;
+            int64_t hi = c + (int64_t)m.box[d];
+            if (hi > (int64_t)m.dims[d]) hi = (int64_t)m.dims[d];
+            prod *= hi > lo ? (uint64_t)(hi - lo) : 0u;
+        }
+        total += prod;
+    }
+    *out_elems = total;
+    return ok();
+}
+
+tmap_status tmap_load_tiles(const tmap_t *src, const int32_t *coords, int64_t n_tiles, void *packed_out,
+                            const tmap_launch_opts *opts, void *hip_stream) {
+    MapImpl s;
+    if (!decode(src, s)) return fail(TMAP_ERROR_INVALID_VALUE, "src map is NULL or not encoded");
+    tmap_status st = check_coords_and_count(s, coords, n_tiles);
+    if (st != TMAP_SUCCESS) return st;
+    if (!packed_out || ((uintptr_t)packed_out & 15u))
+        return fail(TMAP_ERROR_INVALID_VALUE, "packed_out is NULL or not 16-byte aligned");
+    if (n_tiles == 0) return ok();
+    tmap::KArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.src = s;
+    a.dst = s;
+    a.packed = (uint8_t *)packed_out;
+    fill_common(a, s, coords, n_tiles);
+    return run(tmap::kLoad, s, a, opts, hip_stream);
+}
+
+tmap_status tmap_store_tiles(const tmap_t *dst, const int32_t *coords, int64_t n_tiles, const void *packed_in,
+                             const tmap_launch_opts *opts, void *hip_stream) {
+    MapImpl d;
+    if (!decode(dst, d)) return fail(TMAP_ERROR_INVALID_VALUE, "dst map is NULL or not encoded");
+    tmap_status st = check_coords_and_count(d, coords, n_tiles);
+    if (st != TMAP_SUCCESS) return st;
+    if (!packed_in || ((uintptr_t)packed_in & 15u))
+        return fail(TMAP_ERROR_INVALID_VALUE, "packed_in is NULL or not 16-byte aligned");
+    if (n_tiles == 0) return ok();
+    tmap::KArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.src = d;
+    a.dst = d;
+    a.packed = (uint8_t *)const_cast<void *>(packed_in);
+    fill_common(a, d, coords, n_tiles);
+    return run(tmap::kStore, d, a, opts, hip_stream);
+}
+
+tmap_status tmap_roundtrip(const tmap_t *src, const tmap_t *dst, const int32_t *coords, int64_t n_tiles,
+                           const tmap_launch_opts *opts, void *hip_stream) {
+    MapImpl s, d;
+    if (!decode(src, s)) return fail(TMAP_ERROR_INVALID_VALUE, "src map is NULL or not encoded");
+    if (!decode(dst, d)) return fail(TMAP_ERROR_INVALID_VALUE, "dst map is NULL or not encoded");
+    // The tile is read back with the layout it was written in: the two maps
+    // must agree on element size, rank, box and swizzle ("TMA -- the async
+    // bulk copy engine", "The descriptor records the layout, including the
+    // swizzle": a swizzle mismatch reads scrambled bytes).
+    const bool same_swizzle = s.swz_b == d.swz_b && (s.swz_b == 0 || (s.swz_m == d.swz_m && s.swz_s == d.swz_s));
+    if (s.elem_size != d.elem_size || s.rank != d.rank || !same_swizzle ||
+        std::memcmp(s.box, d.box, sizeof s.box) != 0)
+        return fail(TMAP_ERROR_INVALID_VALUE,
+                    "src and dst maps differ in element size, rank, box or swizzle");
+    tmap_status st = check_coords_and_count(s, coords, n_tiles);
+    if (st != TMAP_SUCCESS) return st;
+    if (n_tiles == 0) return ok();
+    tmap::KArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.src = s;
+    a.dst = d;
+    a.packed = nullptr;
+    fill_common(a, s, coords, n_tiles);
+    return run(tmap::kRoundtrip, s, a, opts, hip_stream);
+}
+
+tmap_status tmap_sync_status(void *hip_stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return fail(TMAP_ERROR_UNSUPPORTED_DEVICE, "no HIP device is available");
+    }
+    if (hipStreamSynchronize((hipStream_t)hip_stream) != hipSuccess) {
+        const hipError_t e = hipGetLastError();
+        return fail(TMAP_ERROR_LAUNCH, "stream error: %s", hipGetErrorString(e));
+    }
+    uint32_t *word = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        word = g_dev[dev].status;
+    }
+    if (!word) return ok();
+    uint32_t v = 0;
+    if (hipMemcpy(&v, word, 4, hipMemcpyDeviceToHost) != hipSuccess) {
+        const hipError_t e = hipGetLastError();
+        return fail(TMAP_ERROR_LAUNCH, "cannot read the status word: %s", hipGetErrorString(e));
+    }
+    if (v) {
+        (void)hipMemset(word, 0, 4);
+        (void)hipDeviceSynchronize();
+        return fail(TMAP_ERROR_TIMEOUT, "a readiness wait expired (status 0x%x)", v);
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -105,6 +105,35 @@ def tensor_bytes(w: Workload, seed: Optional[int] = None, nbytes: Optional[int] 
     raise ValueError(w.values)
 
 
+def device_bytes(w: Workload, device, seed: Optional[int] = None, nbytes: Optional[int] = None,
+                 values: Optional[str] = None):
+    """Seeded contents of the allocation generated on `device` with torch's
+    counter-based Philox generator (fast at gigabyte sizes).  Same recipes as
+    tensor_bytes(); the values differ from the numpy ones, so a check against
+    the oracle hands the oracle a host copy of these very bytes.  Returns a
+    uint8 torch tensor."""
+    import torch
+    seed = w.seed if seed is None else seed
+    n = w.alloc_bytes if nbytes is None else nbytes
+    values = w.values if values is None else values
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    if values in ("bytes", "u32"):
+        n8 = (n + 7) // 8
+        x = torch.randint(-(2**63), 2**63 - 1, (n8,), dtype=torch.int64, generator=g, device=device)
+        return x.view(torch.uint8)[:n].contiguous() if n8 * 8 != n else x.view(torch.uint8)
+    if values == "normal_f16":
+        assert n % 2 == 0
+        return torch.randn(n // 2, generator=g, device=device, dtype=torch.float32).to(torch.float16).view(torch.uint8)
+    if values == "normal_bf16":
+        assert n % 2 == 0
+        f = torch.randn(n // 2, generator=g, device=device, dtype=torch.float32)
+        u = f.view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+        b = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).to(torch.int32).to(torch.int16)
+        return b.view(torch.uint8)
+    raise ValueError(values)
+
+
 def sentinel_bytes(n: int, seed: int) -> np.ndarray:
     """Seeded uniform bytes used to pre-fill destinations, so that a byte the
     copy never wrote is told apart from one it wrote."""
