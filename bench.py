@@ -1,0 +1,256 @@
+"""Benchmark of the tiled bulk copy on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--op OP]
+
+One step is one pass of the whole copy path over the workload: every tile
+loaded from HBM into an LDS stage (swizzled, zero-filled, byte-counted) and
+written back out.  The default workload is the 2 GiB byte tensor
+(32768 x 65536 u8, 128x128-byte boxes, 128-byte swizzle (3,4,3), 131072 tiles)
+moved by tmap_roundtrip into a second tensor: the large swizzled load/store
+sweep.  Inputs are generated on the device before timing.
+
+Prints one JSON line: achieved GB/s (algorithmic bytes read + written per
+step / step time), tiles/s, the dominant kernel's roofline (HIP-event kernel
+time on the launch stream, against 8 TB/s HBM), HBM traffic from the committed
+rocprofv3 counter summary when it was taken on the current kernel sources,
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (read+write) and % of MI355X peak; tiles/sec"
+PEAK_HBM_GBPS = 8000.0
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_tensor_bulk_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, op: str):
+    """Per-launch HBM bytes from profiles/traffic_<workload>_<op>.txt, if it was
+    measured on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{op}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sweep2g_u8")
+    ap.add_argument("--op", default="roundtrip", choices=["roundtrip", "load", "store"])
+    ap.add_argument("--stages", type=int, default=0)
+    ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the copy shards with no exchange step, so the "
+              "whole-job rate at N GPUs is N times the one-GPU rate; run with --gpus 1.", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from tiled_tensor_bulk_amd import inputs
+    from tiled_tensor_bulk_amd import tmap as T
+
+    T.lib()  # raises if the HIP library is not built
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = inputs.WORKLOADS[args.workload]
+    es = w.es
+    src = inputs.device_bytes(w, dev)
+    ms = T.tmap_encode(w.dtype, w.rank, src.data_ptr(), w.dims, w.strides, w.box, None, w.swizzle)
+    bb = T.tmap_box_bytes(ms)
+    if w.coords == "sweep":
+        n = T.tmap_sweep_tiles(ms)
+        coords_np, coords = None, None
+    elif w.coords == "origin":
+        n = 1
+        coords_np = np.zeros((1, w.rank), np.int32)
+        coords = torch.from_numpy(coords_np).to(dev)
+    else:
+        coords_np = inputs.random_corners(w.dims, w.box, w.n_random, seed=w.seed * 10)
+        n = len(coords_np)
+        coords = torch.from_numpy(coords_np).to(dev)
+    inb = T.tmap_inbounds_elems(ms, coords_np, n) * es
+    opts = dict(stages=args.stages or w.stages, grid_wgs=args.grid, flags=args.flags)
+
+    dst = packed = None
+    if args.op == "roundtrip":
+        dst = torch.empty(w.alloc_bytes, dtype=torch.uint8, device=dev)
+        md = T.tmap_encode(w.dtype, w.rank, dst.data_ptr(), w.dims, w.strides, w.box, None, w.swizzle)
+        algo_bytes = 2 * inb                                   # in-bounds read + in-bounds write
+
+        def launch():
+            T.tmap_roundtrip(ms, md, coords, n, **opts)
+    elif args.op == "load":
+        packed = torch.empty(n * bb, dtype=torch.uint8, device=dev)
+        algo_bytes = inb + n * bb                              # in-bounds read + whole images written
+
+        def launch():
+            T.tmap_load_tiles(ms, coords, n, packed, **opts)
+    else:
+        packed = torch.empty(n * bb, dtype=torch.uint8, device=dev)
+        T.tmap_load_tiles(ms, coords, n, packed, **opts)
+        dst = torch.empty(w.alloc_bytes, dtype=torch.uint8, device=dev)
+        md = T.tmap_encode(w.dtype, w.rank, dst.data_ptr(), w.dims, w.strides, w.box, None, w.swizzle)
+        algo_bytes = n * bb + inb                              # whole images read + in-bounds written
+
+        def launch():
+            T.tmap_store_tiles(md, coords, n, packed, **opts)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        launch()
+    st = T.tmap_sync_status(stream)
+    if st != T.SUCCESS:
+        raise RuntimeError(f"warmup failed: {T.tmap_status_string(st)}")
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = T.tmap_sync_status(stream)
+    if st != T.SUCCESS:
+        raise RuntimeError(f"timed run failed: {T.tmap_status_string(st)}")
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_avg_s = sum(kern_ms) / len(kern_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    value = algo_bytes / (wall / args.steps) / 1e9
+
+    # context: a plain device-to-device copy of the same byte count
+    ref = torch.empty(w.alloc_bytes, dtype=torch.uint8, device=dev)
+    ref.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        ref.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * w.alloc_bytes / (e0.elapsed_time(e1) / 5 / 1e3) / 1e9
+    del ref
+
+    achieved = algo_bytes / kern_avg_s / 1e9
+    traffic = traffic_from_profile(args.workload, args.op)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded on device, torch Philox)",
+        "config": {"workload": w.name, "op": args.op, "dims": list(w.dims), "strides": list(w.strides),
+                   "box": list(w.box), "swizzle": list(w.swizzle), "tiles": n, "box_bytes": bb,
+                   "stages": opts["stages"], "grid_wgs": args.grid or "auto", "flags": args.flags,
+                   "algorithmic_bytes_per_step": algo_bytes},
+        "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBPS, 2),
+        "tiles_per_s": round(n / (wall / args.steps), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic / kern_avg_s / 1e9, 2),
+                     "kernel_ms": round(kern_avg_s * 1e3, 4),
+                     "kernel": f"tmap copy_kernel ({args.op})"},
+        "reference_d2d_copy_GBps": round(copy_gbps, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.op, src, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, op, src, budget_s):
+    """The CPU oracle (single thread, as it stands) on a bounded sample: whole
+    tile rows of the sweep, one after another, until ~budget_s of oracle time.
+    Reported in the same algorithmic GB/s as the GPU line."""
+    import numpy as np
+
+    import oracle
+
+    if w.coords != "sweep" or w.rank != 2:
+        return None
+    row_bytes = w.strides[0] * w.box[1]                       # one tile row of the tensor
+    rows_per_chunk = 4
+    total_t = 0.0
+    total_bytes = 0
+    tiles = 0
+    chunk = 0
+    n_rows = -(-w.dims[1] // w.box[1])
+    while total_t < budget_s and chunk * rows_per_chunk < n_rows:
+        r0 = chunk * rows_per_chunk
+        r1 = min(n_rows, r0 + rows_per_chunk)
+        lo = r0 * row_bytes
+        hi = min(w.alloc_bytes, r1 * row_bytes)
+        host = src[lo:hi].cpu().numpy()
+        sub_rows = min(w.dims[1], r1 * w.box[1]) - r0 * w.box[1]
+        m = oracle.Map(es=w.es, dims=[w.dims[0], sub_rows], strides=w.strides, box=w.box, swizzle=w.swizzle)
+        nt = oracle.sweep_count(m)
+        t0 = time.perf_counter()
+        if op == "roundtrip":
+            dst = np.empty_like(host)
+            oracle.roundtrip(m, host, m, dst, None, nt)
+        elif op == "load":
+            oracle.load_tiles(m, host, None, nt)
+        else:
+            packed = oracle.load_tiles(m, host, None, nt)
+            t0 = time.perf_counter()
+            dst = np.empty_like(host)
+            oracle.store_tiles(m, dst, None, nt, packed)
+        total_t += time.perf_counter() - t0
+        inb = oracle.inb_elems(m, None, nt) * w.es
+        total_bytes += 2 * inb if op == "roundtrip" else inb + nt * oracle.box_bytes(m)
+        tiles += nt
+        chunk += 1
+    return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tiles_per_s": round(tiles / total_t, 1),
+            "sample": f"{tiles} tiles ({chunk * rows_per_chunk} tile rows from the top) of {w.name}, "
+                      f"{op}, {total_t:.1f} s of single-thread oracle time",
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -79,27 +79,74 @@ struct Win {
     bool interior;
 };
 
-__device__ __forceinline__ void tile_corner(const KArgs &a, const MapImpl &swept, int64_t t,
-                                            int32_t c[kMaxRank]) {
+// Position of a workgroup in its tile sequence.  In a sweep the tile index
+// is held as mixed-radix digits over the per-dimension tile counts (innermost
+// fastest) and advanced by the workgroup's step with carries, so no tile ever
+// costs a division; with explicit corners it is a plain index.
+struct Cursor {
+    int64_t t;
+    uint32_t dig[kMaxRank];
+};
+
+__device__ __forceinline__ void cursor_init(const KArgs &a, int64_t t, Cursor &cur) {
+    cur.t = t;
+    uint64_t rest = (uint64_t)t;
+#pragma unroll
+    for (int d = 0; d < kMaxRank; ++d) {
+        const uint64_t nt = a.sweep_tiles[d];
+        const uint64_t q = rest / nt;
+        cur.dig[d] = (uint32_t)(rest - q * nt);
+        rest = q;
+    }
+}
+
+__device__ __forceinline__ void cursor_advance(const KArgs &a, int64_t tstep, Cursor &cur) {
+    cur.t += tstep;
+    uint32_t carry = 0;
+#pragma unroll
+    for (int d = 0; d < kMaxRank; ++d) {
+        const uint32_t v = cur.dig[d] + a.step_digits[d] + carry;
+        carry = v >= a.sweep_tiles[d] ? 1u : 0u;
+        cur.dig[d] = carry ? v - a.sweep_tiles[d] : v;
+    }
+}
+
+// Box corner of the cursor's tile (innermost first).
+__device__ __forceinline__ void cursor_corner(const KArgs &a, const MapImpl &swept, const Cursor &cur,
+                                              int32_t c[kMaxRank]) {
     if (a.coords) {
         // Corners are read through the constant address space: uniform
         // scalar loads (lgkmcnt), so they never wait behind the ring's
         // direct-to-LDS loads (vmcnt).
         typedef const __attribute__((address_space(4))) int32_t const_i32;
         const int r = swept.rank;
-        const_i32 *p = (const_i32 *)(a.coords) + t * r;
+        const_i32 *p = (const_i32 *)(a.coords) + cur.t * r;
 #pragma unroll
         for (int d = 0; d < kMaxRank; ++d) c[d] = d < r ? p[d] : 0;
     } else {
-        uint64_t rest = (uint64_t)t;
 #pragma unroll
-        for (int d = 0; d < kMaxRank; ++d) {
-            const uint64_t nt = a.sweep_tiles[d];
-            const uint64_t q = rest / nt;
-            c[d] = (int32_t)((rest - q * nt) * swept.box[d]);
-            rest = q;
-        }
+        for (int d = 0; d < kMaxRank; ++d) c[d] = (int32_t)(cur.dig[d] * (uint32_t)swept.box[d]);
     }
+}
+
+// Byte offset of the box corner from the base, and whether the whole box lies
+// inside the tensor.
+struct Place {
+    int64_t off;
+    bool interior;
+};
+
+__device__ __forceinline__ Place place(const MapImpl &m, const int32_t c[kMaxRank]) {
+    Place p;
+    p.off = 0;
+    p.interior = true;
+#pragma unroll
+    for (int d = 0; d < kMaxRank; ++d) {
+        const int64_t cd = c[d];
+        p.off += cd * (int64_t)m.strides[d];
+        p.interior = p.interior && cd >= 0 && cd + (int64_t)m.box[d] <= (int64_t)m.dims[d];
+    }
+    return p;
 }
 
 __device__ __forceinline__ Win window(const MapImpl &m, const int32_t c[kMaxRank]) {
@@ -247,14 +294,14 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 // ---------------------------------------------------------------- the kernel
 template <int MODE, int S, int NSLOT>
 struct Copier {
-    static constexpr uint32_t kStageBytes = NSLOT * kWaves * kBlockBytes;
-
     const KArgs &a;
     uint32_t lane, wave, my_bytes, parity;
-    int64_t t0, tstep, cnt;
+    int64_t tstep, cnt;
     bool nt;
     uint64_t *bars;
     uint32_t *abort_flag;
+    Cursor fcur;  // next tile to fill
+    Cursor ccur;  // next tile to land and consume
     // producer slots (the slots this lane fills) and consumer slots (the slots
     // this lane drains: those the next wave filled)
     uint32_t pslot[NSLOT], poff[NSLOT], pw0[NSLOT], pw1[NSLOT];
@@ -263,8 +310,6 @@ struct Copier {
     __device__ __forceinline__ Copier(const KArgs &args, uint64_t *b, uint32_t *ab) : a(args), bars(b), abort_flag(ab) {}
 
     __device__ __forceinline__ const MapImpl &swept() const { return MODE == kStore ? a.dst : a.src; }
-
-    __device__ __forceinline__ int64_t tile(int64_t k) const { return t0 + k * tstep; }
 
     // In-box byte offset (in map m) and packed indices of logical chunk q.
     __device__ __forceinline__ void chunk_info(uint32_t q, const MapImpl &m, uint32_t &off, uint32_t &w0,
@@ -297,6 +342,7 @@ struct Copier {
         parity = 0;
         const int64_t n = a.n_tiles;
         const int64_t G = a.grid, g = blockIdx.x;
+        int64_t t0;
         if (a.flags & TMAP_FLAG_CONTIGUOUS) {
             const int64_t base = n / G, rem = n % G;
             cnt = base + (g < rem ? 1 : 0);
@@ -307,6 +353,8 @@ struct Copier {
             t0 = g;
             tstep = G;
         }
+        cursor_init(a, t0, fcur);
+        ccur = fcur;
         my_bytes = 0;
         const uint32_t cw = (wave + 1) % kWaves;
 #pragma unroll
@@ -336,25 +384,26 @@ struct Copier {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, blk, 16, voff, 0, 0, 0);
     }
 
-    // Issue the loads of tile k into `stage`.
-    __device__ __forceinline__ void fill(uint8_t *stage, uint64_t *bar, int64_t k) const {
-        const int64_t t = tile(k);
+    // Issue the loads of the tile under the fill cursor into `stage`, then
+    // move the cursor on.
+    __device__ __forceinline__ void fill(uint8_t *stage, uint64_t *bar) {
         const uint32_t budget = my_bytes + ((a.flags & TMAP_FLAG_INJECT_BUDGET_MISMATCH) ? 16u : 0u);
         bar_arrive_expect(bar, budget, lane);
         if (MODE == kStore) {
             const uint64_t bb = a.dst.box_bytes;
-            const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)t * bb, (uint32_t)bb);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)fcur.t * bb, (uint32_t)bb);
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? pslot[j] * 16u : kOob);
         } else {
             int32_t c[kMaxRank];
-            tile_corner(a, a.src, t, c);
-            const Win w = window(a.src, c);
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)w.off, a.src.span);
-            if (w.interior && !a.elemwise) {
+            cursor_corner(a, a.src, fcur, c);
+            const Place pl = place(a.src, c);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
+            if (pl.interior && !a.elemwise) {
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? poff[j] : kOob);
             } else {
+                const Win w = window(a.src, c);
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) {
                     const bool full = !a.elemwise && pslot[j] < a.n_chunks &&
@@ -363,21 +412,21 @@ struct Copier {
                 }
             }
         }
+        cursor_advance(a, tstep, fcur);
     }
 
-    // The wave's loads of tile k into `stage` have landed: patch partial
-    // chunks, then report the delivered bytes.
-    __device__ __forceinline__ void land(uint8_t *stage, uint64_t *bar, int64_t k) const {
+    // This wave's loads of the tile at corner c have landed in `stage`:
+    // patch partial chunks, then report the delivered bytes.
+    __device__ __forceinline__ void land(uint8_t *stage, uint64_t *bar, const int32_t c[kMaxRank]) const {
         // A read of this stage object makes the compiler wait (vmcnt) for this
         // wave's direct-to-LDS loads into it.
         uint32_t probe = *(volatile uint32_t *)(stage + (wave * 64u + lane) * 16u);
         asm volatile("" ::"v"(probe) : "memory");
         if (MODE != kStore) {
-            int32_t c[kMaxRank];
-            tile_corner(a, a.src, tile(k), c);
-            const Win w = window(a.src, c);
-            if (!w.interior || a.elemwise) {
-                const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)w.off, a.src.span);
+            const Place pl = place(a.src, c);
+            if (!pl.interior || a.elemwise) {
+                const Win w = window(a.src, c);
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) {
                     if (pslot[j] >= a.n_chunks) continue;
@@ -391,9 +440,16 @@ struct Copier {
         bar_complete(bar, my_bytes, lane);
     }
 
-    // Read tile k out of `stage`.
-    __device__ __forceinline__ void consume(uint8_t *stage, int64_t k) const {
-        const int64_t t = tile(k);
+    template <typename R>
+    __device__ __forceinline__ void store16(const i32x4 &v, R r, uint32_t off) const {
+        if (nt)
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2);
+        else
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+    }
+
+    // Read the tile at corner c (sequence index t) out of `stage`.
+    __device__ __forceinline__ void consume(uint8_t *stage, const int32_t c[kMaxRank], int64_t t) const {
         if (MODE == kLoad) {
             const uint64_t bb = a.src.box_bytes;
             const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)t * bb, (uint32_t)bb);
@@ -401,36 +457,29 @@ struct Copier {
             for (int j = 0; j < NSLOT; ++j) {
                 if (cslot[j] < a.n_chunks) {
                     const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
-                    if (nt)
-                        __builtin_amdgcn_raw_buffer_store_b128(v, r, cslot[j] * 16u, 0, 2);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b128(v, r, cslot[j] * 16u, 0, 0);
+                    store16(v, r, cslot[j] * 16u);
                 }
             }
         } else {
-            int32_t c[kMaxRank];
-            tile_corner(a, swept(), t, c);
-            const Win w = window(a.dst, c);
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.dst.base + (uint64_t)w.off, a.dst.span);
-            if (w.interior && !a.elemwise) {
+            const Place pl = place(a.dst, c);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.dst.base + (uint64_t)pl.off, a.dst.span);
+            if (pl.interior && !a.elemwise) {
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) {
                     if (cslot[j] < a.n_chunks) {
                         const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
-                        if (nt)
-                            __builtin_amdgcn_raw_buffer_store_b128(v, r, coff[j], 0, 2);
-                        else
-                            __builtin_amdgcn_raw_buffer_store_b128(v, r, coff[j], 0, 0);
+                        store16(v, r, coff[j]);
                     }
                 }
             } else {
+                const Win w = window(a.dst, c);
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) {
                     if (cslot[j] >= a.n_chunks) continue;
                     const uint32_t cls = a.elemwise ? kPart : classify(cw0[j], cw1[j], w, a.k_el);
                     if (cls == kFull) {
                         const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
-                        __builtin_amdgcn_raw_buffer_store_b128(v, r, coff[j], 0, 0);
+                        store16(v, r, coff[j]);
                     } else if (cls == kPart) {
                         store_slot_elements(stage, cslot[j], a, a.dst, w, r);
                     }
@@ -448,17 +497,20 @@ struct Copier {
         __builtin_amdgcn_s_barrier();
         if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
         constexpr int XF = (X + S - 1) % S;
-        if (k + S - 1 < cnt) fill(fillst, &bars[XF], k + S - 1);
-        land(st, &bars[X], k);
+        if (k + S - 1 < cnt) fill(fillst, &bars[XF]);
+        int32_t c[kMaxRank];
+        cursor_corner(a, swept(), ccur, c);
+        land(st, &bars[X], c);
         const bool ok = bar_wait(&bars[X], (parity >> X) & 1u, a.spin_limit);
         parity ^= 1u << X;
         asm volatile("" ::: "memory");
         if (ok) {
-            consume(st, k);
+            consume(st, c, ccur.t);
         } else if (lane == 0) {
             __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        cursor_advance(a, tstep, ccur);
         return true;
     }
 };
@@ -483,9 +535,9 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const KArgs a) {
     if (cp.cnt <= 0) return;
 
     // prologue: tiles 0..S-2 go to stages 0..S-2
-    if constexpr (S > 1) cp.fill(st0, &bars[0], 0);
-    if constexpr (S > 2) if (1 < cp.cnt) cp.fill(st1, &bars[1], 1);
-    if constexpr (S > 3) if (2 < cp.cnt) cp.fill(st2, &bars[2], 2);
+    if constexpr (S > 1) cp.fill(st0, &bars[0]);
+    if constexpr (S > 2) if (1 < cp.cnt) cp.fill(st1, &bars[1]);
+    if constexpr (S > 3) if (2 < cp.cnt) cp.fill(st2, &bars[2]);
 
     for (int64_t kb = 0; kb < cp.cnt; kb += S) {
         if constexpr (S == 1) {

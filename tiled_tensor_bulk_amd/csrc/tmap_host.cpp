@@ -176,6 +176,13 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     a.status = dev->status;
     a.grid = pl.grid;
     a.flags = opts ? opts->flags : 0u;
+    // each workgroup advances through the sweep by a fixed step; kernels add
+    // its digits with carries instead of dividing per tile
+    uint64_t step = (a.flags & TMAP_FLAG_CONTIGUOUS) ? 1u : pl.grid;
+    for (int d = 0; d < tmap::kMaxRank; ++d) {
+        a.step_digits[d] = (uint32_t)(step % a.sweep_tiles[d]);
+        step /= a.sweep_tiles[d];
+    }
     a.spin_limit = (opts && opts->spin_limit) ? opts->spin_limit : (1u << 22);
     int rc = (int)hipErrorInvalidValue;
     switch (mode) {

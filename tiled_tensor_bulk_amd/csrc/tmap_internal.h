@@ -48,6 +48,8 @@ struct KArgs {
     uint32_t *status;             // device status word (bit 0: readiness wait expired)
     int64_t n_tiles;
     uint32_t sweep_tiles[kMaxRank];  // ceil(dims/box) per dimension of the swept map
+    uint32_t step_digits[kMaxRank];  // the tile step of one workgroup (grid, or 1 when
+                                     // contiguous) as mixed-radix digits over sweep_tiles
     uint32_t n_chunks;            // box_bytes / 16
     uint32_t row_chunks;          // box[0]*es / 16
     uint32_t k_el;                // elements per 16-byte chunk (16 / es)
@@ -55,7 +57,6 @@ struct KArgs {
     uint32_t grid;                // workgroups launched
     uint32_t flags;               // TMAP_FLAG_*
     uint32_t spin_limit;          // readiness-wait polls before giving up
-    uint32_t pad_;
 };
 
 }  // namespace tmap
