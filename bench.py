@@ -18,7 +18,6 @@ and the CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -29,16 +28,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (read+write) and % of MI355X peak; tiles/sec"
 PEAK_HBM_GBPS = 8000.0
-
-
-def kernel_source_sha() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "tiled_tensor_bulk_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".h", ".hip", ".cpp")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
-    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(workload: str, op: str):
@@ -52,6 +41,7 @@ def traffic_from_profile(workload: str, op: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
+    from tiled_tensor_bulk_amd.profile_summary import kernel_source_sha
     if kv.get("kernel_source_sha") != kernel_source_sha():
         return None
     try:
@@ -69,7 +59,9 @@ def main():
     ap.add_argument("--op", default="roundtrip", choices=["roundtrip", "load", "store"])
     ap.add_argument("--stages", type=int, default=0)
     ap.add_argument("--grid", type=int, default=0)
-    ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--flags", type=int, default=-1,
+                    help="TMAP_FLAG_* bits; default: non-temporal hints when the tensor exceeds the 256 MB MALL")
+    ap.add_argument("--group", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -105,7 +97,9 @@ def main():
         n = len(coords_np)
         coords = torch.from_numpy(coords_np).to(dev)
     inb = T.tmap_inbounds_elems(ms, coords_np, n) * es
-    opts = dict(stages=args.stages or w.stages, grid_wgs=args.grid, flags=args.flags)
+    if args.flags < 0:
+        args.flags = T.FLAG_NONTEMPORAL if w.alloc_bytes > (256 << 20) else 0
+    opts = dict(stages=args.stages or w.stages, grid_wgs=args.grid, flags=args.flags, group=args.group)
 
     dst = packed = None
     if args.op == "roundtrip":
@@ -187,6 +181,7 @@ def main():
         "config": {"workload": w.name, "op": args.op, "dims": list(w.dims), "strides": list(w.strides),
                    "box": list(w.box), "swizzle": list(w.swizzle), "tiles": n, "box_bytes": bb,
                    "stages": opts["stages"], "grid_wgs": args.grid or "auto", "flags": args.flags,
+                   "group": args.group or "auto",
                    "algorithmic_bytes_per_step": algo_bytes},
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBPS, 2),
         "tiles_per_s": round(n / (wall / args.steps), 1),

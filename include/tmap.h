@@ -78,9 +78,16 @@ typedef struct tmap_launch_opts {
     uint32_t grid_wgs;    /* workgroups of the persistent grid (default: fill every CU)    */
     uint32_t flags;       /* TMAP_FLAG_* bits                                              */
     uint32_t spin_limit;  /* readiness-wait polls before TMAP_ERROR_TIMEOUT (default 2^22) */
+    uint32_t group;       /* tiles dealt to a workgroup at a time, a power of two <= 64
+                             (default: enough boxes side by side to span 512 bytes of a
+                             row, at most 8)                                               */
 } tmap_launch_opts;
 
-/* Tiles are dealt to workgroups in contiguous runs instead of round-robin. */
+/* Tile order: tile index t runs innermost-fastest over the sweep (or over the
+ * coords array).  By default the tiles are dealt in groups of `group`
+ * consecutive indices, group after group round-robin over the workgroups, so
+ * that a workgroup's tiles in flight are neighbours in memory.  With this
+ * flag each workgroup instead takes one contiguous run of tiles. */
 #define TMAP_FLAG_CONTIGUOUS 0x1u
 /* Non-temporal hints on the streaming loads and stores. */
 #define TMAP_FLAG_NONTEMPORAL 0x2u

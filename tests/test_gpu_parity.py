@@ -215,7 +215,8 @@ def _fuzz_case(rng, idx):
     ncoords = int(rng.integers(1, 40))
     coords = inputs.random_corners(dims, box, ncoords, int(rng.integers(1 << 30)))
     opts = dict(stages=int(rng.integers(1, 5)), grid_wgs=int(rng.choice([0, 1, 2, 3, 7])),
-                flags=int(rng.choice([0, T.FLAG_CONTIGUOUS, T.FLAG_NONTEMPORAL])))
+                flags=int(rng.choice([0, T.FLAG_CONTIGUOUS, T.FLAG_NONTEMPORAL])),
+                group=int(rng.choice([0, 1, 2, 4, 8, 64])))
     return es, dims, strides, box, swz, alloc, coords, opts
 
 

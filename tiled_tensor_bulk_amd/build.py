@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtmap.so")
 ROOT = os.path.dirname(PKG)
 
-SOURCES = ["tmap_host.cpp", "tmap_load.hip", "tmap_store.hip", "tmap_roundtrip.hip"]
+SOURCES = ["tmap_host.cpp"] + [f"tmap_{m}_r{r}.hip" for m in ("load", "store", "roundtrip") for r in (2, 5)]
 ARCH = "gfx950"
 
 
@@ -38,7 +38,7 @@ def common_flags():
             "-I", os.path.join(ROOT, "include")]
 
 
-def build(jobs: int = 4, verbose: bool = False, incremental: bool = False) -> str:
+def build(jobs: int = 7, verbose: bool = False, incremental: bool = False) -> str:
     """Compile every translation unit (or, with incremental=True, only those
     older than a source or header) and link libtmap.so."""
     os.makedirs(BUILD, exist_ok=True)
@@ -87,7 +87,7 @@ def build(jobs: int = 4, verbose: bool = False, incremental: bool = False) -> st
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--jobs", type=int, default=4)
+    ap.add_argument("--jobs", type=int, default=7)
     ap.add_argument("-v", "--verbose", action="store_true")
     ap.add_argument("--incremental", action="store_true", help="recompile only out-of-date units")
     a = ap.parse_args()

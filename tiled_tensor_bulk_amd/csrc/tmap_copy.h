@@ -1,6 +1,6 @@
 // tmap_copy.h -- gfx950 kernel template of the descriptor-driven tiled bulk copy.
-// Included by one small .hip file per copy direction, which instantiates the
-// variants of that direction.
+// Included by one small .hip file per (copy direction, dimension count), which
+// instantiates the variants of that direction.
 //
 // One kernel template serves the three directions (load to packed images,
 // store from packed images, round trip).  Each workgroup (4 waves) is
@@ -40,7 +40,9 @@
 //
 // The S stages are separate __shared__ objects and the tile loop is
 // unrolled by S, so the compiler's LDS-DMA tracking can wait for exactly the
-// loads of one stage instead of draining every load in flight.
+// loads of one stage instead of draining every load in flight.  R is the
+// number of dimensions the scalar tile arithmetic walks: 2 for maps of rank
+// <= 2, else 5.
 
 #pragma once
 
@@ -53,6 +55,7 @@ namespace tmap {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 constexpr uint32_t kOob = 0x80000000u;       // offset past every num_records
 constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, gfx9 family
@@ -70,29 +73,25 @@ __device__ __forceinline__ uint32_t swizzle(uint32_t e, uint32_t b, uint32_t m, 
     return b ? e ^ (((e >> (m + s)) & ((1u << b) - 1u)) << m) : e;
 }
 
-// Per-tile scalar view of one map: byte offset of the box corner and, per
-// dimension, the window [lo, hi) of box indices that fall inside the tensor.
-struct Win {
-    int64_t off;
-    uint32_t lo[kMaxRank];
-    uint32_t hi[kMaxRank];
-    bool interior;
-};
-
+// ---------------------------------------------------------------- tile cursor
 // Position of a workgroup in its tile sequence.  In a sweep the tile index
 // is held as mixed-radix digits over the per-dimension tile counts (innermost
 // fastest) and advanced by the workgroup's step with carries, so no tile ever
 // costs a division; with explicit corners it is a plain index.
+template <int R>
 struct Cursor {
-    int64_t t;
-    uint32_t dig[kMaxRank];
+    int64_t t;        // tile index
+    uint32_t k;       // position in this workgroup's sequence
+    uint32_t dig[R];  // sweep: tile index per dimension
 };
 
-__device__ __forceinline__ void cursor_init(const KArgs &a, int64_t t, Cursor &cur) {
+template <int R>
+__device__ __forceinline__ void cursor_init(const KArgs &a, int64_t t, Cursor<R> &cur) {
     cur.t = t;
+    cur.k = 0;
     uint64_t rest = (uint64_t)t;
 #pragma unroll
-    for (int d = 0; d < kMaxRank; ++d) {
+    for (int d = 0; d < R; ++d) {
         const uint64_t nt = a.sweep_tiles[d];
         const uint64_t q = rest / nt;
         cur.dig[d] = (uint32_t)(rest - q * nt);
@@ -100,20 +99,26 @@ __device__ __forceinline__ void cursor_init(const KArgs &a, int64_t t, Cursor &c
     }
 }
 
-__device__ __forceinline__ void cursor_advance(const KArgs &a, int64_t tstep, Cursor &cur) {
-    cur.t += tstep;
+// Next tile: +1 inside a group, big_step from the last tile of a group.
+template <int R>
+__device__ __forceinline__ void cursor_advance(const KArgs &a, Cursor<R> &cur) {
+    const bool big = (cur.k & a.group_mask) == a.group_mask;
+    cur.k += 1;
+    cur.t += big ? a.big_step : 1;
+    if (a.coords) return;
     uint32_t carry = 0;
 #pragma unroll
-    for (int d = 0; d < kMaxRank; ++d) {
-        const uint32_t v = cur.dig[d] + a.step_digits[d] + carry;
+    for (int d = 0; d < R; ++d) {
+        const uint32_t v = cur.dig[d] + (big ? a.big_digits[d] : a.step_digits[d]) + carry;
         carry = v >= a.sweep_tiles[d] ? 1u : 0u;
         cur.dig[d] = carry ? v - a.sweep_tiles[d] : v;
     }
 }
 
 // Box corner of the cursor's tile (innermost first).
-__device__ __forceinline__ void cursor_corner(const KArgs &a, const MapImpl &swept, const Cursor &cur,
-                                              int32_t c[kMaxRank]) {
+template <int R>
+__device__ __forceinline__ void cursor_corner(const KArgs &a, const KMap &swept, const Cursor<R> &cur,
+                                              int32_t c[R]) {
     if (a.coords) {
         // Corners are read through the constant address space: uniform
         // scalar loads (lgkmcnt), so they never wait behind the ring's
@@ -122,39 +127,45 @@ __device__ __forceinline__ void cursor_corner(const KArgs &a, const MapImpl &swe
         const int r = swept.rank;
         const_i32 *p = (const_i32 *)(a.coords) + cur.t * r;
 #pragma unroll
-        for (int d = 0; d < kMaxRank; ++d) c[d] = d < r ? p[d] : 0;
+        for (int d = 0; d < R; ++d) c[d] = d < r ? p[d] : 0;
     } else {
 #pragma unroll
-        for (int d = 0; d < kMaxRank; ++d) c[d] = (int32_t)(cur.dig[d] * (uint32_t)swept.box[d]);
+        for (int d = 0; d < R; ++d) c[d] = (int32_t)(cur.dig[d] * (uint32_t)swept.box[d]);
     }
 }
 
 // Byte offset of the box corner from the base, and whether the whole box lies
-// inside the tensor.
+// inside the tensor (0 <= c <= dims - box in every dimension).
 struct Place {
     int64_t off;
     bool interior;
 };
 
-__device__ __forceinline__ Place place(const MapImpl &m, const int32_t c[kMaxRank]) {
+template <int R>
+__device__ __forceinline__ Place place(const KMap &m, const int32_t c[R]) {
     Place p;
     p.off = 0;
     p.interior = true;
 #pragma unroll
-    for (int d = 0; d < kMaxRank; ++d) {
-        const int64_t cd = c[d];
-        p.off += cd * (int64_t)m.strides[d];
-        p.interior = p.interior && cd >= 0 && cd + (int64_t)m.box[d] <= (int64_t)m.dims[d];
+    for (int d = 0; d < R; ++d) {
+        p.off += (int64_t)c[d] * (int64_t)m.strides[d];
+        p.interior = p.interior & (c[d] >= 0) & (c[d] <= m.lim[d]);
     }
     return p;
 }
 
-__device__ __forceinline__ Win window(const MapImpl &m, const int32_t c[kMaxRank]) {
-    Win w;
-    w.off = 0;
-    w.interior = true;
+// Per dimension, the window [lo, hi) of box indices inside the tensor.
+template <int R>
+struct Win {
+    uint32_t lo[R];
+    uint32_t hi[R];
+};
+
+template <int R>
+__device__ __forceinline__ Win<R> window(const KMap &m, const int32_t c[R]) {
+    Win<R> w;
 #pragma unroll
-    for (int d = 0; d < kMaxRank; ++d) {
+    for (int d = 0; d < R; ++d) {
         const int64_t cd = c[d];
         const int64_t b = m.box[d];
         int64_t lo = -cd;
@@ -163,28 +174,31 @@ __device__ __forceinline__ Win window(const MapImpl &m, const int32_t c[kMaxRank
         hi = hi < lo ? lo : (hi > b ? b : hi);
         w.lo[d] = (uint32_t)lo;
         w.hi[d] = (uint32_t)hi;
-        w.interior = w.interior && lo == 0 && hi == b;
-        w.off += cd * (int64_t)m.strides[d];
     }
     return w;
 }
 
 // Packed box indices of a chunk: w0 = x0 | i1 << 16, w1 = i2 | i3 << 8 | i4 << 16,
 // x0 being the first element index of the chunk in dimension 0.
-__device__ __forceinline__ uint32_t classify(uint32_t w0, uint32_t w1, const Win &w, uint32_t k_el) {
-    const uint32_t x0 = w0 & 0xFFFFu, i1 = w0 >> 16;
-    const uint32_t i2 = w1 & 0xFFu, i3 = (w1 >> 8) & 0xFFu, i4 = w1 >> 16;
-    const bool row_in = (i1 - w.lo[1] < w.hi[1] - w.lo[1]) & (i2 - w.lo[2] < w.hi[2] - w.lo[2]) &
-                        (i3 - w.lo[3] < w.hi[3] - w.lo[3]) & (i4 - w.lo[4] < w.hi[4] - w.lo[4]);
+template <int R>
+__device__ __forceinline__ uint32_t classify(uint32_t w0, uint32_t w1, const Win<R> &w, uint32_t k_el) {
+    const uint32_t x0 = w0 & 0xFFFFu;
+    bool row_in = (w0 >> 16) - w.lo[1] < w.hi[1] - w.lo[1];
+    if constexpr (R > 2) {
+        const uint32_t i2 = w1 & 0xFFu, i3 = (w1 >> 8) & 0xFFu, i4 = w1 >> 16;
+        row_in = row_in & (i2 - w.lo[2] < w.hi[2] - w.lo[2]) & (i3 - w.lo[3] < w.hi[3] - w.lo[3]) &
+                 (i4 - w.lo[4] < w.hi[4] - w.lo[4]);
+    }
     const bool full0 = (x0 >= w.lo[0]) & (x0 + k_el <= w.hi[0]);
     const bool any0 = (x0 < w.hi[0]) & (x0 + k_el > w.lo[0]);
     return !row_in ? kZero : (full0 ? kFull : (any0 ? kPart : kZero));
 }
 
 // Box indices of tile-local element e (innermost fastest).
-__device__ __forceinline__ void unravel(uint32_t e, const MapImpl &m, uint32_t i[kMaxRank]) {
+template <int R>
+__device__ __forceinline__ void unravel(uint32_t e, const KMap &m, uint32_t i[R]) {
 #pragma unroll
-    for (int d = 0; d < kMaxRank; ++d) {
+    for (int d = 0; d < R; ++d) {
         const uint32_t b = m.box[d];
         const uint32_t q = e / b;
         i[d] = e - q * b;
@@ -192,17 +206,19 @@ __device__ __forceinline__ void unravel(uint32_t e, const MapImpl &m, uint32_t i
     }
 }
 
-__device__ __forceinline__ bool inside(const uint32_t i[kMaxRank], const Win &w) {
+template <int R>
+__device__ __forceinline__ bool inside(const uint32_t i[R], const Win<R> &w) {
     bool ok = true;
 #pragma unroll
-    for (int d = 0; d < kMaxRank; ++d) ok = ok & (i[d] - w.lo[d] < w.hi[d] - w.lo[d]);
+    for (int d = 0; d < R; ++d) ok = ok & (i[d] - w.lo[d] < w.hi[d] - w.lo[d]);
     return ok;
 }
 
-__device__ __forceinline__ uint32_t inbox_offset(const uint32_t i[kMaxRank], const MapImpl &m) {
+template <int R>
+__device__ __forceinline__ uint32_t inbox_offset(const uint32_t i[R], const KMap &m) {
     uint64_t o = 0;
 #pragma unroll
-    for (int d = 0; d < kMaxRank; ++d) o += (uint64_t)i[d] * m.strides[d];
+    for (int d = 0; d < R; ++d) o += (uint64_t)i[d] * m.strides[d];
     return (uint32_t)o;
 }
 
@@ -218,9 +234,15 @@ __device__ __forceinline__ void bar_update(uint64_t *bar, uint64_t delta) {
                                __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// arrive + expect_tx(bytes)
+// arrive + expect_tx(bytes).  With bytes > 0 this can never complete the
+// phase (this wave's own bytes are still outstanding), so it needs no result.
 __device__ __forceinline__ void bar_arrive_expect(uint64_t *bar, uint32_t bytes, uint32_t lane) {
-    if (lane == 0) bar_update(bar, kArrive + bytes);
+    if (lane == 0) {
+        if (bytes)
+            __hip_atomic_fetch_add(bar, kArrive + bytes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        else
+            bar_update(bar, kArrive);
+    }
 }
 
 // complete_tx(bytes): the wave's own loads into the stage have landed
@@ -243,14 +265,15 @@ __device__ __forceinline__ bool bar_wait(uint64_t *bar, uint32_t parity, uint32_
 // dimension-0 edge, and for every chunk when the swizzle permutes bytes inside
 // a 16-byte chunk).  Out-of-bounds elements read the out-of-range offset and
 // land as zero.
-__device__ __forceinline__ void load_slot_elements(uint8_t *stage, uint32_t p, const KArgs &a, const MapImpl &m,
-                                                const Win &w, __amdgpu_buffer_rsrc_t r) {
+template <int R>
+__device__ __forceinline__ void load_slot_elements(uint8_t *stage, uint32_t p, const KArgs &a, const KMap &m,
+                                                   const Win<R> &w, __amdgpu_buffer_rsrc_t r) {
     const uint32_t es = m.elem_size, k = a.k_el;
     for (uint32_t j = 0; j < k; ++j) {
         const uint32_t s = p * k + j;
-        uint32_t i[kMaxRank];
-        unravel(swizzle(s, m.swz_b, m.swz_m, m.swz_s), m, i);
-        const uint32_t off = inside(i, w) ? inbox_offset(i, m) : kOob;
+        uint32_t i[R];
+        unravel<R>(swizzle(s, m.swz_b, m.swz_m, m.swz_s), m, i);
+        const uint32_t off = inside<R>(i, w) ? inbox_offset<R>(i, m) : kOob;
         uint8_t *dst = stage + (size_t)s * es;
         if (es == 1) {
             *dst = __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
@@ -266,15 +289,16 @@ __device__ __forceinline__ void load_slot_elements(uint8_t *stage, uint32_t p, c
 }
 
 // Store the in-bounds elements held in LDS slot p one by one.
+template <int R>
 __device__ __forceinline__ void store_slot_elements(const uint8_t *stage, uint32_t p, const KArgs &a,
-                                                 const MapImpl &m, const Win &w, __amdgpu_buffer_rsrc_t r) {
+                                                    const KMap &m, const Win<R> &w, __amdgpu_buffer_rsrc_t r) {
     const uint32_t es = m.elem_size, k = a.k_el;
     for (uint32_t j = 0; j < k; ++j) {
         const uint32_t s = p * k + j;
-        uint32_t i[kMaxRank];
-        unravel(swizzle(s, m.swz_b, m.swz_m, m.swz_s), m, i);
-        if (!inside(i, w)) continue;
-        const uint32_t off = inbox_offset(i, m);
+        uint32_t i[R];
+        unravel<R>(swizzle(s, m.swz_b, m.swz_m, m.swz_s), m, i);
+        if (!inside<R>(i, w)) continue;
+        const uint32_t off = inbox_offset<R>(i, m);
         const uint8_t *src = stage + (size_t)s * es;
         if (es == 1) {
             __builtin_amdgcn_raw_buffer_store_b8(*src, r, off, 0, 0);
@@ -289,19 +313,18 @@ __device__ __forceinline__ void store_slot_elements(const uint8_t *stage, uint32
     }
 }
 
-typedef __attribute__((ext_vector_type(4))) int i32x4;
-
 // ---------------------------------------------------------------- the kernel
-template <int MODE, int S, int NSLOT>
+template <int MODE, int S, int NSLOT, int R>
 struct Copier {
     const KArgs &a;
     uint32_t lane, wave, my_bytes, parity;
-    int64_t tstep, cnt;
+    uint32_t edge;  // bit X: the tile in stage X needs the element path when it lands
+    int64_t cnt;
     bool nt;
     uint64_t *bars;
     uint32_t *abort_flag;
-    Cursor fcur;  // next tile to fill
-    Cursor ccur;  // next tile to land and consume
+    Cursor<R> fcur;  // next tile to fill
+    Cursor<R> ccur;  // next tile to land and consume
     // producer slots (the slots this lane fills) and consumer slots (the slots
     // this lane drains: those the next wave filled)
     uint32_t pslot[NSLOT], poff[NSLOT], pw0[NSLOT], pw1[NSLOT];
@@ -309,29 +332,28 @@ struct Copier {
 
     __device__ __forceinline__ Copier(const KArgs &args, uint64_t *b, uint32_t *ab) : a(args), bars(b), abort_flag(ab) {}
 
-    __device__ __forceinline__ const MapImpl &swept() const { return MODE == kStore ? a.dst : a.src; }
+    __device__ __forceinline__ const KMap &swept() const { return MODE == kStore ? a.dst : a.src; }
 
     // In-box byte offset (in map m) and packed indices of logical chunk q.
-    __device__ __forceinline__ void chunk_info(uint32_t q, const MapImpl &m, uint32_t &off, uint32_t &w0,
+    __device__ __forceinline__ void chunk_info(uint32_t q, const KMap &m, uint32_t &off, uint32_t &w0,
                                                uint32_t &w1) const {
         const uint32_t row = q / a.row_chunks;
         const uint32_t x0 = (q - row * a.row_chunks) * a.k_el;
-        uint32_t i[kMaxRank];
-        i[0] = x0;
+        uint32_t i[kMaxRank] = {x0, 0, 0, 0, 0};
         uint32_t rest = row;
 #pragma unroll
-        for (int d = 1; d < kMaxRank; ++d) {
+        for (int d = 1; d < R; ++d) {
             const uint32_t b = m.box[d];
             const uint32_t qq = rest / b;
             i[d] = rest - qq * b;
             rest = qq;
         }
-        off = inbox_offset(i, m);
+        off = inbox_offset<R>(i, m);
         w0 = x0 | (i[1] << 16);
         w1 = i[2] | (i[3] << 8) | (i[4] << 16);
     }
 
-    __device__ __forceinline__ uint32_t logical_chunk(uint32_t p, const MapImpl &m) const {
+    __device__ __forceinline__ uint32_t logical_chunk(uint32_t p, const KMap &m) const {
         return swizzle(p * a.k_el, m.swz_b, m.swz_m, m.swz_s) / a.k_el;
     }
 
@@ -340,20 +362,26 @@ struct Copier {
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         nt = (a.flags & TMAP_FLAG_NONTEMPORAL) != 0;
         parity = 0;
+        edge = 0;
         const int64_t n = a.n_tiles;
         const int64_t G = a.grid, g = blockIdx.x;
         int64_t t0;
-        if (a.flags & TMAP_FLAG_CONTIGUOUS) {
+        if (a.group == 0) {
+            // one contiguous run per workgroup
             const int64_t base = n / G, rem = n % G;
             cnt = base + (g < rem ? 1 : 0);
             t0 = g * base + (g < rem ? g : rem);
-            tstep = 1;
         } else {
-            cnt = g < n ? (n - 1 - g) / G + 1 : 0;
-            t0 = g;
-            tstep = G;
+            // groups of Q consecutive tiles, dealt round-robin: workgroup g
+            // takes tiles [g*Q, g*Q+Q) of every round of G*Q tiles
+            const int64_t Q = a.group, GQ = G * Q;
+            const int64_t rounds = n / GQ, rem = n % GQ;
+            int64_t last = rem - g * Q;
+            last = last < 0 ? 0 : (last > Q ? Q : last);
+            cnt = rounds * Q + last;
+            t0 = g * Q;
         }
-        cursor_init(a, t0, fcur);
+        cursor_init<R>(a, t0, fcur);
         ccur = fcur;
         my_bytes = 0;
         const uint32_t cw = (wave + 1) % kWaves;
@@ -384,8 +412,9 @@ struct Copier {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, blk, 16, voff, 0, 0, 0);
     }
 
-    // Issue the loads of the tile under the fill cursor into `stage`, then
+    // Issue the loads of the tile under the fill cursor into stage XF, then
     // move the cursor on.
+    template <int XF>
     __device__ __forceinline__ void fill(uint8_t *stage, uint64_t *bar) {
         const uint32_t budget = my_bytes + ((a.flags & TMAP_FLAG_INJECT_BUDGET_MISMATCH) ? 16u : 0u);
         bar_arrive_expect(bar, budget, lane);
@@ -395,43 +424,46 @@ struct Copier {
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? pslot[j] * 16u : kOob);
         } else {
-            int32_t c[kMaxRank];
-            cursor_corner(a, a.src, fcur, c);
-            const Place pl = place(a.src, c);
+            int32_t c[R];
+            cursor_corner<R>(a, a.src, fcur, c);
+            const Place pl = place<R>(a.src, c);
             const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
-            if (pl.interior && !a.elemwise) {
+            const bool fast = pl.interior && !a.elemwise;
+            edge = fast ? (edge & ~(1u << XF)) : (edge | (1u << XF));
+            if (fast) {
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? poff[j] : kOob);
             } else {
-                const Win w = window(a.src, c);
+                const Win<R> w = window<R>(a.src, c);
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) {
                     const bool full = !a.elemwise && pslot[j] < a.n_chunks &&
-                                      classify(pw0[j], pw1[j], w, a.k_el) == kFull;
+                                      classify<R>(pw0[j], pw1[j], w, a.k_el) == kFull;
                     dma(r, stage, j, full ? poff[j] : kOob);
                 }
             }
         }
-        cursor_advance(a, tstep, fcur);
+        cursor_advance<R>(a, fcur);
     }
 
-    // This wave's loads of the tile at corner c have landed in `stage`:
+    // This wave's loads of the tile at corner c have landed in stage X:
     // patch partial chunks, then report the delivered bytes.
-    __device__ __forceinline__ void land(uint8_t *stage, uint64_t *bar, const int32_t c[kMaxRank]) const {
+    template <int X>
+    __device__ __forceinline__ void land(uint8_t *stage, uint64_t *bar, const int32_t c[R]) const {
         // A read of this stage object makes the compiler wait (vmcnt) for this
         // wave's direct-to-LDS loads into it.
         uint32_t probe = *(volatile uint32_t *)(stage + (wave * 64u + lane) * 16u);
         asm volatile("" ::"v"(probe) : "memory");
         if (MODE != kStore) {
-            const Place pl = place(a.src, c);
-            if (!pl.interior || a.elemwise) {
-                const Win w = window(a.src, c);
+            if ((edge >> X) & 1u) {
+                const Place pl = place<R>(a.src, c);
+                const Win<R> w = window<R>(a.src, c);
                 const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) {
                     if (pslot[j] >= a.n_chunks) continue;
-                    if (a.elemwise || classify(pw0[j], pw1[j], w, a.k_el) == kPart)
-                        load_slot_elements(stage, pslot[j], a, a.src, w, r);
+                    if (a.elemwise || classify<R>(pw0[j], pw1[j], w, a.k_el) == kPart)
+                        load_slot_elements<R>(stage, pslot[j], a, a.src, w, r);
                 }
             }
         }
@@ -440,8 +472,8 @@ struct Copier {
         bar_complete(bar, my_bytes, lane);
     }
 
-    template <typename R>
-    __device__ __forceinline__ void store16(const i32x4 &v, R r, uint32_t off) const {
+    template <typename Rs>
+    __device__ __forceinline__ void store16(const i32x4 &v, Rs r, uint32_t off) const {
         if (nt)
             __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2);
         else
@@ -449,7 +481,7 @@ struct Copier {
     }
 
     // Read the tile at corner c (sequence index t) out of `stage`.
-    __device__ __forceinline__ void consume(uint8_t *stage, const int32_t c[kMaxRank], int64_t t) const {
+    __device__ __forceinline__ void consume(uint8_t *stage, const int32_t c[R], int64_t t) const {
         if (MODE == kLoad) {
             const uint64_t bb = a.src.box_bytes;
             const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)t * bb, (uint32_t)bb);
@@ -461,7 +493,7 @@ struct Copier {
                 }
             }
         } else {
-            const Place pl = place(a.dst, c);
+            const Place pl = place<R>(a.dst, c);
             const __amdgpu_buffer_rsrc_t r = make_rsrc(a.dst.base + (uint64_t)pl.off, a.dst.span);
             if (pl.interior && !a.elemwise) {
 #pragma unroll
@@ -472,16 +504,16 @@ struct Copier {
                     }
                 }
             } else {
-                const Win w = window(a.dst, c);
+                const Win<R> w = window<R>(a.dst, c);
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) {
                     if (cslot[j] >= a.n_chunks) continue;
-                    const uint32_t cls = a.elemwise ? kPart : classify(cw0[j], cw1[j], w, a.k_el);
+                    const uint32_t cls = a.elemwise ? kPart : classify<R>(cw0[j], cw1[j], w, a.k_el);
                     if (cls == kFull) {
                         const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
                         store16(v, r, coff[j]);
                     } else if (cls == kPart) {
-                        store_slot_elements(stage, cslot[j], a, a.dst, w, r);
+                        store_slot_elements<R>(stage, cslot[j], a, a.dst, w, r);
                     }
                 }
             }
@@ -497,10 +529,10 @@ struct Copier {
         __builtin_amdgcn_s_barrier();
         if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
         constexpr int XF = (X + S - 1) % S;
-        if (k + S - 1 < cnt) fill(fillst, &bars[XF]);
-        int32_t c[kMaxRank];
-        cursor_corner(a, swept(), ccur, c);
-        land(st, &bars[X], c);
+        if (k + S - 1 < cnt) fill<XF>(fillst, &bars[XF]);
+        int32_t c[R];
+        cursor_corner<R>(a, swept(), ccur, c);
+        land<X>(st, &bars[X], c);
         const bool ok = bar_wait(&bars[X], (parity >> X) & 1u, a.spin_limit);
         parity ^= 1u << X;
         asm volatile("" ::: "memory");
@@ -510,12 +542,12 @@ struct Copier {
             __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        cursor_advance(a, tstep, ccur);
+        cursor_advance<R>(a, ccur);
         return true;
     }
 };
 
-template <int MODE, int S, int NSLOT>
+template <int MODE, int S, int NSLOT, int R>
 __global__ __launch_bounds__(kThreads) void copy_kernel(const KArgs a) {
     constexpr uint32_t SB = NSLOT * kWaves * kBlockBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t st0[SB];
@@ -525,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const KArgs a) {
     __shared__ uint64_t bars[4];
     __shared__ uint32_t abort_flag;
 
-    Copier<MODE, S, NSLOT> cp(a, bars, &abort_flag);
+    Copier<MODE, S, NSLOT, R> cp(a, bars, &abort_flag);
     if (threadIdx.x == 0) {
         for (int i = 0; i < 4; ++i) bars[i] = 0;
         abort_flag = 0;
@@ -535,9 +567,9 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const KArgs a) {
     if (cp.cnt <= 0) return;
 
     // prologue: tiles 0..S-2 go to stages 0..S-2
-    if constexpr (S > 1) cp.fill(st0, &bars[0]);
-    if constexpr (S > 2) if (1 < cp.cnt) cp.fill(st1, &bars[1]);
-    if constexpr (S > 3) if (2 < cp.cnt) cp.fill(st2, &bars[2]);
+    if constexpr (S > 1) cp.template fill<0>(st0, &bars[0]);
+    if constexpr (S > 2) if (1 < cp.cnt) cp.template fill<1>(st1, &bars[1]);
+    if constexpr (S > 3) if (2 < cp.cnt) cp.template fill<2>(st2, &bars[2]);
 
     for (int64_t kb = 0; kb < cp.cnt; kb += S) {
         if constexpr (S == 1) {
@@ -562,29 +594,29 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const KArgs a) {
 
 typedef void (*KernelFn)(const KArgs);
 
-template <int MODE, int S>
+template <int MODE, int S, int R>
 KernelFn pick_nslot(int nslot) {
     switch (nslot) {
-        case 1: return copy_kernel<MODE, S, 1>;
-        case 2: return copy_kernel<MODE, S, 2>;
-        case 4: return copy_kernel<MODE, S, 4>;
-        case 8: return copy_kernel<MODE, S, 8>;
+        case 1: return copy_kernel<MODE, S, 1, R>;
+        case 2: return copy_kernel<MODE, S, 2, R>;
+        case 4: return copy_kernel<MODE, S, 4, R>;
+        case 8: return copy_kernel<MODE, S, 8, R>;
         case 16:
-            if constexpr (S <= 2) return copy_kernel<MODE, S, 16>;
+            if constexpr (S <= 2) return copy_kernel<MODE, S, 16, R>;
             return nullptr;
         default: return nullptr;
     }
 }
 
-// Launch the (MODE, stages, nslot) variant; hipError_t as int.
-template <int MODE>
+// Launch the (MODE, stages, nslot, R) variant; hipError_t as int.
+template <int MODE, int R>
 int launch_mode(int stages, int nslot, const KArgs &a, void *stream) {
     KernelFn fn = nullptr;
     switch (stages) {
-        case 1: fn = pick_nslot<MODE, 1>(nslot); break;
-        case 2: fn = pick_nslot<MODE, 2>(nslot); break;
-        case 3: fn = pick_nslot<MODE, 3>(nslot); break;
-        case 4: fn = pick_nslot<MODE, 4>(nslot); break;
+        case 1: fn = pick_nslot<MODE, 1, R>(nslot); break;
+        case 2: fn = pick_nslot<MODE, 2, R>(nslot); break;
+        case 3: fn = pick_nslot<MODE, 3, R>(nslot); break;
+        case 4: fn = pick_nslot<MODE, 4, R>(nslot); break;
         default: break;
     }
     if (!fn) return (int)hipErrorInvalidValue;

@@ -112,6 +112,7 @@ int64_t sweep_count(const MapImpl &m) {
 struct Plan {
     int nslot, stages;
     uint32_t grid;
+    uint32_t group;
 };
 
 tmap_status plan_launch(const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
@@ -128,6 +129,16 @@ tmap_status plan_launch(const MapImpl &m, int64_t n_tiles, const tmap_launch_opt
     if (lds > dev.lds_per_cu || (nslot == 16 && stages > 2))
         return fail(TMAP_ERROR_INVALID_VALUE, "%d stages of %u bytes do not fit in LDS", stages,
                     (unsigned)(nslot * per_wave_pass));
+    // group: enough boxes side by side to cover 512 bytes of a row, so that a
+    // workgroup's tiles in flight read and write neighbouring row segments
+    uint32_t group = (opts && opts->group) ? opts->group : 0;
+    if (group && (group > 64 || (group & (group - 1))))
+        return fail(TMAP_ERROR_INVALID_VALUE, "group must be a power of two <= 64 (got %u)", group);
+    if (!group) {
+        const uint32_t row = (uint32_t)m.box[0] * m.elem_size;
+        group = 1;
+        while (group < 8 && group * row < 512u) group *= 2;
+    }
     uint32_t grid = (opts && opts->grid_wgs) ? opts->grid_wgs : 0;
     if (!grid) {
         uint32_t per_cu = dev.lds_per_cu / lds;
@@ -135,10 +146,13 @@ tmap_status plan_launch(const MapImpl &m, int64_t n_tiles, const tmap_launch_opt
         if (per_cu < 1) per_cu = 1;
         grid = (uint32_t)dev.cus * per_cu;
     }
-    if ((int64_t)grid > n_tiles) grid = (uint32_t)n_tiles;
+    const bool contiguous = opts && (opts->flags & TMAP_FLAG_CONTIGUOUS);
+    const int64_t useful = contiguous ? n_tiles : (n_tiles + group - 1) / group;
+    if ((int64_t)grid > useful) grid = (uint32_t)useful;
     pl.nslot = nslot;
     pl.stages = stages;
     pl.grid = grid;
+    pl.group = group;
     return TMAP_SUCCESS;
 }
 
@@ -176,19 +190,37 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     a.status = dev->status;
     a.grid = pl.grid;
     a.flags = opts ? opts->flags : 0u;
-    // each workgroup advances through the sweep by a fixed step; kernels add
-    // its digits with carries instead of dividing per tile
-    uint64_t step = (a.flags & TMAP_FLAG_CONTIGUOUS) ? 1u : pl.grid;
+    // each workgroup advances through the tiles by +1 inside a group and by
+    // big_step between groups; kernels add the steps' digits with carries
+    // instead of dividing per tile
+    const bool contiguous = (a.flags & TMAP_FLAG_CONTIGUOUS) != 0;
+    a.group = contiguous ? 0u : pl.group;
+    a.group_mask = contiguous ? 0xFFFFFFFFu : pl.group - 1u;
+    a.big_step = contiguous ? 1 : (int64_t)pl.grid * pl.group - pl.group + 1;
+    uint64_t s1 = 1, sb = (uint64_t)a.big_step;
     for (int d = 0; d < tmap::kMaxRank; ++d) {
-        a.step_digits[d] = (uint32_t)(step % a.sweep_tiles[d]);
-        step /= a.sweep_tiles[d];
+        a.step_digits[d] = (uint32_t)(s1 % a.sweep_tiles[d]);
+        s1 /= a.sweep_tiles[d];
+        a.big_digits[d] = (uint32_t)(sb % a.sweep_tiles[d]);
+        sb /= a.sweep_tiles[d];
     }
     a.spin_limit = (opts && opts->spin_limit) ? opts->spin_limit : (1u << 22);
+    // maps of rank <= 2 run the variants that only walk two dimensions
+    const bool r2 = a.src.rank <= 2 && a.dst.rank <= 2;
     int rc = (int)hipErrorInvalidValue;
     switch (mode) {
-        case tmap::kLoad: rc = tmap::launch_load(pl.stages, pl.nslot, a, stream); break;
-        case tmap::kStore: rc = tmap::launch_store(pl.stages, pl.nslot, a, stream); break;
-        case tmap::kRoundtrip: rc = tmap::launch_roundtrip(pl.stages, pl.nslot, a, stream); break;
+        case tmap::kLoad:
+            rc = r2 ? tmap::launch_load_r2(pl.stages, pl.nslot, a, stream)
+                    : tmap::launch_load_r5(pl.stages, pl.nslot, a, stream);
+            break;
+        case tmap::kStore:
+            rc = r2 ? tmap::launch_store_r2(pl.stages, pl.nslot, a, stream)
+                    : tmap::launch_store_r5(pl.stages, pl.nslot, a, stream);
+            break;
+        case tmap::kRoundtrip:
+            rc = r2 ? tmap::launch_roundtrip_r2(pl.stages, pl.nslot, a, stream)
+                    : tmap::launch_roundtrip_r5(pl.stages, pl.nslot, a, stream);
+            break;
         default: break;
     }
     if (rc != 0) {
@@ -370,8 +402,8 @@ tmap_status tmap_load_tiles(const tmap_t *src, const int32_t *coords, int64_t n_
     if (n_tiles == 0) return ok();
     tmap::KArgs a;
     std::memset(&a, 0, sizeof a);
-    a.src = s;
-    a.dst = s;
+    a.src = tmap::kernel_map(s);
+    a.dst = a.src;
     a.packed = (uint8_t *)packed_out;
     fill_common(a, s, coords, n_tiles);
     return run(tmap::kLoad, s, a, opts, hip_stream);
@@ -388,8 +420,8 @@ tmap_status tmap_store_tiles(const tmap_t *dst, const int32_t *coords, int64_t n
     if (n_tiles == 0) return ok();
     tmap::KArgs a;
     std::memset(&a, 0, sizeof a);
-    a.src = d;
-    a.dst = d;
+    a.src = tmap::kernel_map(d);
+    a.dst = a.src;
     a.packed = (uint8_t *)const_cast<void *>(packed_in);
     fill_common(a, d, coords, n_tiles);
     return run(tmap::kStore, d, a, opts, hip_stream);
@@ -414,8 +446,8 @@ tmap_status tmap_roundtrip(const tmap_t *src, const tmap_t *dst, const int32_t *
     if (n_tiles == 0) return ok();
     tmap::KArgs a;
     std::memset(&a, 0, sizeof a);
-    a.src = s;
-    a.dst = d;
+    a.src = tmap::kernel_map(s);
+    a.dst = tmap::kernel_map(d);
     a.packed = nullptr;
     fill_common(a, s, coords, n_tiles);
     return run(tmap::kRoundtrip, s, a, opts, hip_stream);

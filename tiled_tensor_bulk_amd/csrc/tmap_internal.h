@@ -39,17 +39,57 @@ constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;     // 256 lanes
 constexpr int kBlockBytes = 1024;         // one wave-wide 16-byte-per-lane LDS write
 
+// The kernel's form of a tensor map: the fields the copy reads, with 32-bit
+// dims and 16-bit box extents so that it stays small in scalar registers.
+struct KMap {
+    uint64_t base;
+    uint64_t strides[kMaxRank];   // bytes; strides[0] == elem_size; 0 for unused dims
+    uint32_t dims[kMaxRank];      // <= 2^31; 1 for unused dims
+    int32_t lim[kMaxRank];        // dims - box: a corner c is inside in dim d iff 0 <= c <= lim
+    uint32_t span;                // num_records of a buffer resource rebased to a corner
+    uint32_t box_bytes;
+    uint16_t box[kMaxRank];       // 1 for unused dims
+    uint8_t elem_size, rank, swz_b, swz_m, swz_s, pad_[3];
+    uint32_t pad2_[3];
+};
+static_assert(sizeof(KMap) == 128, "KMap layout");
+
+inline KMap kernel_map(const MapImpl &m) {
+    KMap k{};
+    k.base = m.base;
+    for (int d = 0; d < kMaxRank; ++d) {
+        k.strides[d] = m.strides[d];
+        k.dims[d] = (uint32_t)m.dims[d];
+        k.lim[d] = (int32_t)((int64_t)m.dims[d] - (int64_t)m.box[d]);
+        k.box[d] = m.box[d];
+    }
+    k.span = m.span;
+    k.box_bytes = m.box_bytes;
+    k.elem_size = m.elem_size;
+    k.rank = m.rank;
+    k.swz_b = m.swz_b;
+    k.swz_m = m.swz_m;
+    k.swz_s = m.swz_s;
+    return k;
+}
+
 // Everything a copy kernel needs, passed by value.
 struct KArgs {
-    MapImpl src;                  // load / round trip: the source map
-    MapImpl dst;                  // store / round trip: the destination map
+    KMap src;                     // load / round trip: the source map
+    KMap dst;                     // store / round trip: the destination map
     const int32_t *coords;        // [n][rank] corners, or nullptr for a sweep
     uint8_t *packed;              // load: output images; store: input images
     uint32_t *status;             // device status word (bit 0: readiness wait expired)
     int64_t n_tiles;
     uint32_t sweep_tiles[kMaxRank];  // ceil(dims/box) per dimension of the swept map
-    uint32_t step_digits[kMaxRank];  // the tile step of one workgroup (grid, or 1 when
-                                     // contiguous) as mixed-radix digits over sweep_tiles
+    // A workgroup walks tiles t0, t0+1, .. in groups of (group_mask+1); from
+    // the last tile of a group it jumps by big_step.  Both steps are also
+    // given as mixed-radix digits over sweep_tiles for the carry-add cursor.
+    uint32_t step_digits[kMaxRank];  // digits of 1
+    uint32_t big_digits[kMaxRank];   // digits of big_step
+    int64_t big_step;                // grid*group - group + 1
+    uint32_t group;                  // tiles per group (power of two); 0 = contiguous runs
+    uint32_t group_mask;             // group - 1, or 0xFFFFFFFF for contiguous runs
     uint32_t n_chunks;            // box_bytes / 16
     uint32_t row_chunks;          // box[0]*es / 16
     uint32_t k_el;                // elements per 16-byte chunk (16 / es)
@@ -62,13 +102,16 @@ struct KArgs {
 }  // namespace tmap
 
 // Launch one copy-kernel variant (stages in 1..4, nslot in {1,2,4,8,16}:
-// 16-byte chunks per lane per tile).  Each direction's variants live in their
-// own translation unit (tmap_load.hip, tmap_store.hip, tmap_roundtrip.hip).
-// Return a hipError_t as int (0 on success).
+// 16-byte chunks per lane per tile; dims 2 for maps of rank <= 2, else 5).
+// Each direction and dims class has its own translation unit
+// (tmap_{load,store,roundtrip}_r{2,5}.hip).  Return a hipError_t as int.
 namespace tmap {
-int launch_load(int stages, int nslot, const KArgs &a, void *stream);
-int launch_store(int stages, int nslot, const KArgs &a, void *stream);
-int launch_roundtrip(int stages, int nslot, const KArgs &a, void *stream);
+int launch_load_r2(int stages, int nslot, const KArgs &a, void *stream);
+int launch_store_r2(int stages, int nslot, const KArgs &a, void *stream);
+int launch_roundtrip_r2(int stages, int nslot, const KArgs &a, void *stream);
+int launch_load_r5(int stages, int nslot, const KArgs &a, void *stream);
+int launch_store_r5(int stages, int nslot, const KArgs &a, void *stream);
+int launch_roundtrip_r5(int stages, int nslot, const KArgs &a, void *stream);
 
 // LDS bytes one workgroup of a variant uses: the ring plus the barrier words.
 inline uint32_t variant_lds_bytes(int stages, int nslot) {

@@ -1,0 +1,133 @@
+"""Summaries of rocprofv3 runs for profiles/ (kernel time and HBM traffic).
+
+    python -m tiled_tensor_bulk_amd.profile_summary stats  <kernel_stats.csv> --out FILE --cmd "..."
+    python -m tiled_tensor_bulk_amd.profile_summary traffic --fetch <counter_collection.csv>
+        --write <counter_collection.csv> --workload W --op OP --out FILE --cmd "..."
+
+`stats` condenses a --kernel-trace --stats kernel_stats.csv into a short
+markdown table.  `traffic` turns a FETCH_SIZE run and a WRITE_SIZE run (each
+in KiB per dispatch) into HBM bytes per launch of the copy kernel.  Each
+counter is scaled by what it reads for the plain device-to-device copy of a
+known byte count that the same benchmark process runs (torch's copy of the
+whole tensor: it reads and writes exactly alloc_bytes), and the result is
+stamped with the hash of the kernel sources so that bench.py reports it only
+while the kernels are unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import re
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tiled_tensor_bulk_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def short(name: str) -> str:
+    m = re.search(r"copy_kernel<(\d+), (\d+), (\d+), (\d+)>", name)
+    if m:
+        mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
+        return f"tmap copy_kernel<{mode}, stages={m.group(2)}, nslot={m.group(3)}, dims={m.group(4)}>"
+    if "copyBuffer" in name:
+        return "hip copyBuffer (torch d2d copy)"
+    return (name[:60] + "...") if len(name) > 63 else name
+
+
+def cmd_stats(a):
+    rows = list(csv.DictReader(open(a.csv)))
+    out = ["# rocprofv3 kernel statistics", "", f"command: `{a.cmd}`", "",
+           "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or ""
+        calls = int(r.get("Calls", 0))
+        avg = float(r.get("AverageNs", 0)) / 1e3
+        mn = float(r.get("MinNs", 0)) / 1e3
+        mx = float(r.get("MaxNs", 0)) / 1e3
+        pct = float(r.get("Percentage", 0))
+        out.append(f"| {short(name)} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f}% |")
+    open(a.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def per_dispatch(path, counter):
+    rows = list(csv.DictReader(open(path)))
+    agg = defaultdict(float)
+    names = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        agg[d] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    return [(d, names[d], agg[d]) for d in sorted(agg)]
+
+
+def cmd_traffic(a):
+    from tiled_tensor_bulk_amd import inputs
+    w = inputs.WORKLOADS[a.workload]
+    known_kib = w.alloc_bytes / 1024.0                 # the reference copy reads and writes this much
+    res = {}
+    for counter, path in (("FETCH_SIZE", a.fetch), ("WRITE_SIZE", a.write)):
+        d = per_dispatch(path, counter)
+        copies = [v for (_, n, v) in d if "copyBuffer" in n and v > 0.25 * known_kib]
+        kern = [v for (_, n, v) in d if "copy_kernel" in n]
+        if not copies or not kern:
+            sys.exit(f"{path}: no reference copy or copy kernel dispatches with {counter}")
+        factor = known_kib / (sum(copies) / len(copies))
+        res[counter] = (sum(kern) / len(kern), factor)
+    fetch_kib, ff = res["FETCH_SIZE"]
+    write_kib, wf = res["WRITE_SIZE"]
+    hbm = (fetch_kib * ff + write_kib * wf) * 1024.0
+    lines = [
+        f"# HBM traffic of the copy kernel, {a.workload} {a.op} (rocprofv3 --pmc, one counter per run)",
+        f"# command (FETCH_SIZE): {a.cmd}",
+        f"# command (WRITE_SIZE): same with --pmc WRITE_SIZE",
+        f"# scale: the same process copies the whole {w.alloc_bytes}-byte tensor with torch (hip copyBuffer);",
+        f"# each counter is multiplied by known_bytes / counter_reading for that copy.",
+        f"kernel_source_sha: {kernel_source_sha()}",
+        f"fetch_kib_per_dispatch_raw: {fetch_kib:.1f}",
+        f"fetch_scale: {ff:.4f}",
+        f"write_kib_per_dispatch_raw: {write_kib:.1f}",
+        f"write_scale: {wf:.4f}",
+        f"hbm_read_bytes_per_launch: {fetch_kib * ff * 1024.0:.0f}",
+        f"hbm_write_bytes_per_launch: {write_kib * wf * 1024.0:.0f}",
+        f"hbm_bytes_per_launch: {hbm:.0f}",
+    ]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--out", required=True)
+    s.add_argument("--cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--op", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--cmd", required=True)
+    a = ap.parse_args()
+    sys.path.insert(0, ROOT)
+    (cmd_stats if a.what == "stats" else cmd_traffic)(a)
+
+
+if __name__ == "__main__":
+    main()

@@ -40,7 +40,8 @@ class tmap_swizzle(ctypes.Structure):
 
 class tmap_launch_opts(ctypes.Structure):
     _fields_ = [("stages", ctypes.c_uint32), ("grid_wgs", ctypes.c_uint32),
-                ("flags", ctypes.c_uint32), ("spin_limit", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("spin_limit", ctypes.c_uint32),
+                ("group", ctypes.c_uint32)]
 
 
 class tmap_info(ctypes.Structure):
@@ -123,10 +124,10 @@ def _stream(s) -> Optional[int]:
     return int(s.cuda_stream)
 
 
-def _opts(stages=0, grid_wgs=0, flags=0, spin_limit=0):
-    if not (stages or grid_wgs or flags or spin_limit):
+def _opts(stages=0, grid_wgs=0, flags=0, spin_limit=0, group=0):
+    if not (stages or grid_wgs or flags or spin_limit or group):
         return None
-    return ctypes.byref(tmap_launch_opts(stages, grid_wgs, flags, spin_limit))
+    return ctypes.byref(tmap_launch_opts(stages, grid_wgs, flags, spin_limit, group))
 
 
 # ------------------------------------------------------------------- C ABI names
