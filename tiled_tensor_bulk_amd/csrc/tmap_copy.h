@@ -313,6 +313,71 @@ __device__ __forceinline__ void store_slot_elements(const uint8_t *stage, uint32
     }
 }
 
+// Partial chunk of a swizzle whose granule is at least 16 bytes: the slot
+// holds the k = 16/ES consecutive dimension-0 elements x0 .. x0+k-1 of one box
+// row that lies inside the tensor, starting at in-box byte offset `off`;
+// element j is inside iff lo0 <= x0+j < hi0.  Loads land in the slot (the
+// out-of-range ones as zero); stores write only the inside elements.
+template <int ES>
+__device__ __forceinline__ void load_chunk_edge(uint8_t *slot, uint32_t off, uint32_t x0, uint32_t lo0,
+                                                uint32_t hi0, __amdgpu_buffer_rsrc_t r) {
+    constexpr int K = 16 / ES;
+#pragma unroll 4
+    for (int j = 0; j < K; ++j) {
+        const uint32_t voff = (x0 + j - lo0 < hi0 - lo0) ? off + j * ES : kOob;
+        if constexpr (ES == 1) {
+            slot[j] = __builtin_amdgcn_raw_buffer_load_b8(r, voff, 0, 0);
+        } else if constexpr (ES == 2) {
+            ((uint16_t *)slot)[j] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+        } else if constexpr (ES == 4) {
+            ((uint32_t *)slot)[j] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+        } else {
+            auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+            ((decltype(v) *)slot)[j] = v;
+        }
+    }
+}
+
+template <int ES>
+__device__ __forceinline__ void store_chunk_edge(const uint8_t *slot, uint32_t off, uint32_t x0, uint32_t lo0,
+                                                 uint32_t hi0, __amdgpu_buffer_rsrc_t r) {
+    constexpr int K = 16 / ES;
+#pragma unroll 4
+    for (int j = 0; j < K; ++j) {
+        if (x0 + j - lo0 >= hi0 - lo0) continue;
+        if constexpr (ES == 1) {
+            __builtin_amdgcn_raw_buffer_store_b8(slot[j], r, off + j, 0, 0);
+        } else if constexpr (ES == 2) {
+            __builtin_amdgcn_raw_buffer_store_b16(((const uint16_t *)slot)[j], r, off + j * 2, 0, 0);
+        } else if constexpr (ES == 4) {
+            __builtin_amdgcn_raw_buffer_store_b32(((const uint32_t *)slot)[j], r, off + j * 4, 0, 0);
+        } else {
+            typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+            __builtin_amdgcn_raw_buffer_store_b64(((const u32x2 *)slot)[j], r, off + j * 8, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void load_chunk_edge_es(uint32_t es, uint8_t *slot, uint32_t off, uint32_t x0,
+                                                   uint32_t lo0, uint32_t hi0, __amdgpu_buffer_rsrc_t r) {
+    switch (es) {
+        case 1: load_chunk_edge<1>(slot, off, x0, lo0, hi0, r); break;
+        case 2: load_chunk_edge<2>(slot, off, x0, lo0, hi0, r); break;
+        case 4: load_chunk_edge<4>(slot, off, x0, lo0, hi0, r); break;
+        default: load_chunk_edge<8>(slot, off, x0, lo0, hi0, r); break;
+    }
+}
+
+__device__ __forceinline__ void store_chunk_edge_es(uint32_t es, const uint8_t *slot, uint32_t off, uint32_t x0,
+                                                    uint32_t lo0, uint32_t hi0, __amdgpu_buffer_rsrc_t r) {
+    switch (es) {
+        case 1: store_chunk_edge<1>(slot, off, x0, lo0, hi0, r); break;
+        case 2: store_chunk_edge<2>(slot, off, x0, lo0, hi0, r); break;
+        case 4: store_chunk_edge<4>(slot, off, x0, lo0, hi0, r); break;
+        default: store_chunk_edge<8>(slot, off, x0, lo0, hi0, r); break;
+    }
+}
+
 // ---------------------------------------------------------------- the kernel
 template <int MODE, int S, int NSLOT, int R>
 struct Copier {
@@ -459,11 +524,20 @@ struct Copier {
                 const Place pl = place<R>(a.src, c);
                 const Win<R> w = window<R>(a.src, c);
                 const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
-#pragma unroll
+                // slow path, kept out of the unrolled slot arrays: recompute
+                // each slot's chunk, patch the partial ones
+#pragma unroll 1
                 for (int j = 0; j < NSLOT; ++j) {
-                    if (pslot[j] >= a.n_chunks) continue;
-                    if (a.elemwise || classify<R>(pw0[j], pw1[j], w, a.k_el) == kPart)
-                        load_slot_elements<R>(stage, pslot[j], a, a.src, w, r);
+                    const uint32_t p = ((uint32_t)(j * kWaves) + wave) * 64u + lane;
+                    if (p >= a.n_chunks) continue;
+                    if (a.elemwise) {
+                        load_slot_elements<R>(stage, p, a, a.src, w, r);
+                        continue;
+                    }
+                    uint32_t off, w0, w1;
+                    chunk_info(logical_chunk(p, a.src), a.src, off, w0, w1);
+                    if (classify<R>(w0, w1, w, a.k_el) == kPart)
+                        load_chunk_edge_es(a.src.elem_size, stage + p * 16u, off, w0 & 0xFFFFu, w.lo[0], w.hi[0], r);
                 }
             }
         }
@@ -505,16 +579,30 @@ struct Copier {
                 }
             } else {
                 const Win<R> w = window<R>(a.dst, c);
+                if (!a.elemwise) {
 #pragma unroll
-                for (int j = 0; j < NSLOT; ++j) {
-                    if (cslot[j] >= a.n_chunks) continue;
-                    const uint32_t cls = a.elemwise ? kPart : classify<R>(cw0[j], cw1[j], w, a.k_el);
-                    if (cls == kFull) {
-                        const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
-                        store16(v, r, coff[j]);
-                    } else if (cls == kPart) {
-                        store_slot_elements<R>(stage, cslot[j], a, a.dst, w, r);
+                    for (int j = 0; j < NSLOT; ++j) {
+                        if (cslot[j] < a.n_chunks && classify<R>(cw0[j], cw1[j], w, a.k_el) == kFull) {
+                            const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
+                            store16(v, r, coff[j]);
+                        }
                     }
+                }
+                // slow path, kept out of the unrolled slot arrays: recompute
+                // each slot's chunk, store the inside elements of partial ones
+                const uint32_t cw = (wave + 1) % kWaves;
+#pragma unroll 1
+                for (int j = 0; j < NSLOT; ++j) {
+                    const uint32_t p = ((uint32_t)(j * kWaves) + cw) * 64u + lane;
+                    if (p >= a.n_chunks) continue;
+                    if (a.elemwise) {
+                        store_slot_elements<R>(stage, p, a, a.dst, w, r);
+                        continue;
+                    }
+                    uint32_t off, w0, w1;
+                    chunk_info(logical_chunk(p, a.dst), a.dst, off, w0, w1);
+                    if (classify<R>(w0, w1, w, a.k_el) == kPart)
+                        store_chunk_edge_es(a.dst.elem_size, stage + p * 16u, off, w0 & 0xFFFFu, w.lo[0], w.hi[0], r);
                 }
             }
         }
@@ -529,10 +617,18 @@ struct Copier {
         __builtin_amdgcn_s_barrier();
         if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
         constexpr int XF = (X + S - 1) % S;
-        if (k + S - 1 < cnt) fill<XF>(fillst, &bars[XF]);
         int32_t c[R];
         cursor_corner<R>(a, swept(), ccur, c);
-        land<X>(st, &bars[X], c);
+        if (S > 1 && MODE != kStore && ((edge >> X) & 1u)) {
+            // An edge tile's element loads must be waited for (vmcnt); landing
+            // it before the next fill keeps that wait off the fill's loads.
+            // (With one stage the fill of this step is tile k itself.)
+            land<X>(st, &bars[X], c);
+            if (k + S - 1 < cnt) fill<XF>(fillst, &bars[XF]);
+        } else {
+            if (k + S - 1 < cnt) fill<XF>(fillst, &bars[XF]);
+            land<X>(st, &bars[X], c);
+        }
         const bool ok = bar_wait(&bars[X], (parity >> X) & 1u, a.spin_limit);
         parity ^= 1u << X;
         asm volatile("" ::: "memory");

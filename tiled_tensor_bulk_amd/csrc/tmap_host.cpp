@@ -139,10 +139,13 @@ tmap_status plan_launch(const MapImpl &m, int64_t n_tiles, const tmap_launch_opt
         group = 1;
         while (group < 8 && group * row < 512u) group *= 2;
     }
+    // default grid: twice the workgroups that fit in a CU's LDS at once (at
+    // most 16 per CU); the queued half starts as soon as a resident one ends,
+    // which hides per-tile latency on edge-heavy and scattered workloads
     uint32_t grid = (opts && opts->grid_wgs) ? opts->grid_wgs : 0;
     if (!grid) {
-        uint32_t per_cu = dev.lds_per_cu / lds;
-        if (per_cu > 4) per_cu = 4;
+        uint32_t per_cu = 2 * (dev.lds_per_cu / lds);
+        if (per_cu > 16) per_cu = 16;
         if (per_cu < 1) per_cu = 1;
         grid = (uint32_t)dev.cus * per_cu;
     }
