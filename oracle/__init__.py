@@ -80,6 +80,11 @@ def _load():
         lib.oracle_roundtrip.argtypes = [mp, u8p, ctypes.c_uint64, mp, u8p, ctypes.c_uint64,
                                          i32p, ctypes.c_int64, u8p]
         lib.oracle_roundtrip.restype = ctypes.c_int
+        lib.oracle_roundtrip_add_f32.argtypes = [mp, u8p, ctypes.c_uint64, mp, u8p, ctypes.c_uint64,
+                                                 i32p, ctypes.c_int64, ctypes.c_float, u8p]
+        lib.oracle_roundtrip_add_f32.restype = ctypes.c_int
+        lib.oracle_bulk_copy.argtypes = [u8p, u8p, ctypes.c_uint64]
+        lib.oracle_bulk_copy.restype = None
         lib.oracle_inb_elems.argtypes = [mp, i32p, ctypes.c_int64]
         lib.oracle_inb_elems.restype = ctypes.c_uint64
         _lib = lib
@@ -204,3 +209,27 @@ def inb_elems(mp: Map, coords: Optional[np.ndarray], n: int) -> int:
     coords = _coords_arg(mp, coords, n)
     c = mp._c()
     return int(_load().oracle_inb_elems(ctypes.byref(c), _ptr(coords, ctypes.c_int32), n))
+
+
+def roundtrip_add_f32(smap: Map, src: np.ndarray, dmap: Map, dst: np.ndarray,
+                      coords: Optional[np.ndarray], n: int, addend: float) -> None:
+    """Load each box, add `addend` (fp32) to every element of the tile, store
+    it through dmap into dst (in place)."""
+    src = np.ascontiguousarray(src).view(np.uint8).reshape(-1)
+    assert dst.dtype == np.uint8 and dst.flags["C_CONTIGUOUS"]
+    coords = _coords_arg(smap, coords, n)
+    scratch = np.empty(box_bytes(smap), dtype=np.uint8)
+    a, b = smap._c(), dmap._c()
+    rc = _load().oracle_roundtrip_add_f32(ctypes.byref(a), _ptr(src, ctypes.c_uint8), src.size,
+                                          ctypes.byref(b), _ptr(dst, ctypes.c_uint8), dst.size,
+                                          _ptr(coords, ctypes.c_int32), n, float(addend),
+                                          _ptr(scratch, ctypes.c_uint8))
+    if rc:
+        raise ValueError("maps need 4-byte elements and must stay inside their buffers")
+
+
+def bulk_copy(dst: np.ndarray, src: np.ndarray, nbytes: int) -> None:
+    """Copy nbytes from src to dst (uint8 arrays, dst modified in place)."""
+    src = np.ascontiguousarray(src).view(np.uint8).reshape(-1)
+    assert dst.dtype == np.uint8 and dst.flags["C_CONTIGUOUS"] and src.size >= nbytes and dst.size >= nbytes
+    _load().oracle_bulk_copy(_ptr(dst, ctypes.c_uint8), _ptr(src, ctypes.c_uint8), int(nbytes))

@@ -295,6 +295,43 @@ int oracle_roundtrip(const oracle_map *src_map, const uint8_t *src, uint64_t src
     return 0;
 }
 
+/* Fused round trip with an fp32 update in on-chip memory: each tile is
+ * loaded, every element of the tile image gets + addend in single precision,
+ * and the image is stored through dst [DAY76 "An exact round trip": one load
+ * per block, +1.0f per element in shared memory, the tile written back; and
+ * "Solution": the +1.0f becomes a shared-memory update between the load and
+ * the store].  Both maps must have 4-byte elements. */
+int oracle_roundtrip_add_f32(const oracle_map *src_map, const uint8_t *src, uint64_t src_len,
+                             const oracle_map *dst_map, uint8_t *dst, uint64_t dst_len,
+                             const int32_t *coords, int64_t n, float addend, uint8_t *tile_scratch)
+{
+    int64_t t;
+    int32_t c[OR_MAX_RANK];
+    uint64_t e, nb = box_elems(src_map);
+    if (src_map->es != 4 || dst_map->es != 4) return -1;
+    for (t = 0; t < n; ++t) {
+        tile_corner(src_map, coords, t, c);
+        if (load_one_tile(src_map, src, src_len, c, tile_scratch)) return -1;
+        for (e = 0; e < nb; ++e) {
+            float f;
+            memcpy(&f, tile_scratch + e * 4u, 4);
+            f = f + addend;
+            memcpy(tile_scratch + e * 4u, &f, 4);
+        }
+        if (store_one_tile(dst_map, dst, dst_len, c, tile_scratch)) return -1;
+    }
+    return 0;
+}
+
+/* Raw one-dimensional bulk copy of a contiguous byte range [TMA-L04 "The real
+ * toolchain": the plain bulk copy moves a contiguous byte range, with no
+ * tensor map and no swizzle]. */
+void oracle_bulk_copy(uint8_t *dst, const uint8_t *src, uint64_t bytes)
+{
+    uint64_t i;
+    for (i = 0; i < bytes; ++i) dst[i] = src[i];
+}
+
 /* Count of in-bounds box elements over n tiles (the bytes a copy must read or
  * write, divided by es). */
 uint64_t oracle_inb_elems(const oracle_map *mp, const int32_t *coords, int64_t n)

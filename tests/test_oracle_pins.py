@@ -325,3 +325,67 @@ def test_validator_rejects_library_rules():
     assert _ok(swizzle=(3, 2, 2)) == 14
     assert _ok(es=4, box=[4, 1], dims=[64, 64], swizzle=(3, 2, 3)) == 15
     assert _ok(rank=2, box=[4, 256], strides=[(1 << 40) - 16], dims=[64, 300]) == 16
+
+
+# ------------------------------------------------------------- fused +1.0f round trip
+def _as_f32(b):
+    return np.ascontiguousarray(b).view(np.float32)
+
+
+def test_plus_one_on_the_day76_matrix():
+    """The round-trip program's matrix: 256x256 fp32, 16 boxes of 64x64, each
+    element +1.0f in on-chip memory; integer-valued inputs make the result exact."""
+    g = GOLD["roundtrip_matrix_f32"]
+    vals = (np.arange(256 * 256, dtype=np.float32) - 30000.0)
+    src = vals.view(np.uint8).copy()
+    dst = np.zeros_like(src)
+    m = Map(es=4, dims=g["dims"], strides=[g["row_stride"]], box=g["box"])
+    n = oracle.sweep_count(m)
+    assert n == g["tiles"]
+    oracle.roundtrip_add_f32(m, src, m, dst, None, n, 1.0)
+    assert np.array_equal(_as_f32(dst), vals + np.float32(1.0))
+    assert np.all(_as_f32(dst) - vals == 1.0)          # off by exactly 1.0f, never stale
+
+
+def test_plus_addend_matches_numpy_float32_including_specials():
+    rng = np.random.default_rng(17)
+    v = rng.standard_normal(64 * 40).astype(np.float32)
+    v[:8] = np.array([0.0, -0.0, np.inf, -np.inf, 1e-40, -1e-42, 3.4e38, np.nan], np.float32)
+    src = v.view(np.uint8).copy()
+    m = Map(es=4, dims=[64, 40], strides=[256], box=[32, 8], swizzle=(3, 2, 3))
+    for addend in (1.0, -0.5, 1e-38, 65504.0):
+        dst = np.zeros_like(src)
+        oracle.roundtrip_add_f32(m, src, m, dst, None, oracle.sweep_count(m), addend)
+        got, want = _as_f32(dst), v + np.float32(addend)
+        fin = ~np.isnan(want)
+        assert np.array_equal(got[fin].view(np.uint32), want[fin].view(np.uint32))
+        assert np.all(np.isnan(got[~fin]))
+
+
+def test_plus_one_is_clipped_like_the_store():
+    dims, box = [20, 9], [16, 4]
+    v = np.arange(20 * 9, dtype=np.float32)
+    src = np.zeros(9 * 96, np.uint8)
+    npref.tensor_view(src, 4, dims, [96])[:] = v.reshape(9, 20).view(np.uint32)
+    dst0 = inputs.sentinel_bytes(src.size, 9)
+    dst = dst0.copy()
+    corners = np.array([[-5, -2], [10, 7], [4, 2]], np.int32)
+    m = Map(es=4, dims=dims, strides=[96], box=box)
+    oracle.roundtrip_add_f32(m, src, m, dst, corners, 3, 1.0)
+    plain = dst0.copy()
+    oracle.roundtrip(m, src, m, plain, corners, 3)
+    touched = dst != dst0
+    # exactly the bytes a plain round trip rewrites are rewritten, each element + 1.0f
+    assert np.array_equal(touched, plain != dst0)
+    got = npref.tensor_view(dst, 4, dims, [96]).view(np.float32)
+    cov = npref.tensor_view(plain, 4, dims, [96]).view(np.float32)
+    w = npref.tensor_view(dst0, 4, dims, [96]).view(np.float32)
+    mask = npref.tensor_view(plain, 4, dims, [96]) != npref.tensor_view(dst0, 4, dims, [96])
+    assert np.array_equal(got[mask], cov[mask] + np.float32(1.0))
+
+
+def test_bulk_copy_is_a_byte_range_copy():
+    src = inputs.sentinel_bytes(4096, 1)
+    dst = np.zeros(4096, np.uint8)
+    oracle.bulk_copy(dst, src, 3008)
+    assert dst[:3008].tobytes() == src[:3008].tobytes() and not dst[3008:].any()
