@@ -56,7 +56,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sweep2g_u8")
-    ap.add_argument("--op", default="roundtrip", choices=["roundtrip", "load", "store"])
+    ap.add_argument("--op", default="roundtrip", choices=["roundtrip", "load", "store", "roundtrip_add", "bulk"])
     ap.add_argument("--stages", type=int, default=0)
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--flags", type=int, default=-1,
@@ -102,7 +102,23 @@ def main():
     opts = dict(stages=args.stages or w.stages, grid_wgs=args.grid, flags=args.flags, group=args.group)
 
     dst = packed = None
-    if args.op == "roundtrip":
+    if args.op == "bulk":
+        # raw 1-D bulk copy of the whole allocation: no map, no swizzle
+        dst = torch.empty(w.alloc_bytes, dtype=torch.uint8, device=dev)
+        algo_bytes = 2 * w.alloc_bytes
+        n = -(-w.alloc_bytes // 16384)
+        bb = 16384
+
+        def launch():
+            T.tmap_bulk_copy(dst, src, w.alloc_bytes, **opts)
+    elif args.op == "roundtrip_add":
+        dst = torch.empty(w.alloc_bytes, dtype=torch.uint8, device=dev)
+        md = T.tmap_encode(w.dtype, w.rank, dst.data_ptr(), w.dims, w.strides, w.box, None, w.swizzle)
+        algo_bytes = 2 * inb
+
+        def launch():
+            T.tmap_roundtrip_add_f32(ms, md, coords, n, 1.0, **opts)
+    elif args.op == "roundtrip":
         dst = torch.empty(w.alloc_bytes, dtype=torch.uint8, device=dev)
         md = T.tmap_encode(w.dtype, w.rank, dst.data_ptr(), w.dims, w.strides, w.box, None, w.swizzle)
         algo_bytes = 2 * inb                                   # in-bounds read + in-bounds write
@@ -225,9 +241,20 @@ def cpu_baseline(w, op, src, budget_s):
         m = oracle.Map(es=w.es, dims=[w.dims[0], sub_rows], strides=w.strides, box=w.box, swizzle=w.swizzle)
         nt = oracle.sweep_count(m)
         t0 = time.perf_counter()
+        if op == "bulk":
+            dst = np.empty_like(host)
+            oracle.bulk_copy(dst, host, host.size)
+            total_t += time.perf_counter() - t0
+            total_bytes += 2 * host.size
+            tiles += -(-host.size // 16384)
+            chunk += 1
+            continue
         if op == "roundtrip":
             dst = np.empty_like(host)
             oracle.roundtrip(m, host, m, dst, None, nt)
+        elif op == "roundtrip_add":
+            dst = np.empty_like(host)
+            oracle.roundtrip_add_f32(m, host, m, dst, None, nt, 1.0)
         elif op == "load":
             oracle.load_tiles(m, host, None, nt)
         else:
@@ -237,7 +264,7 @@ def cpu_baseline(w, op, src, budget_s):
             oracle.store_tiles(m, dst, None, nt, packed)
         total_t += time.perf_counter() - t0
         inb = oracle.inb_elems(m, None, nt) * w.es
-        total_bytes += 2 * inb if op == "roundtrip" else inb + nt * oracle.box_bytes(m)
+        total_bytes += 2 * inb if op in ("roundtrip", "roundtrip_add") else inb + nt * oracle.box_bytes(m)
         tiles += nt
         chunk += 1
     return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",

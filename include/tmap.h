@@ -187,6 +187,33 @@ tmap_status tmap_store_tiles(const tmap_t *dst, const int32_t *coords, int64_t n
 tmap_status tmap_roundtrip(const tmap_t *src, const tmap_t *dst, const int32_t *coords,
                            int64_t n_tiles, const tmap_launch_opts *opts, void *hip_stream);
 
+/*
+ * tmap_roundtrip_add_f32 -- the round trip with an fp32 update of the tile in
+ * on-chip memory: each box is loaded into LDS, every element gets + addend
+ * (IEEE single precision, round to nearest even) between the LDS read and the
+ * store, and the in-bounds elements are stored through dst.
+ * ("Day 76", "An exact round trip": +1.0f per element in shared memory, a
+ * bit-exact host check; "Solution": the +1.0f is a shared-memory update
+ * between the load and the store.)  Both maps must be TMAP_F32 and agree as
+ * for tmap_roundtrip.  NaN inputs give NaN outputs; their payload bits are the
+ * hardware's.
+ */
+tmap_status tmap_roundtrip_add_f32(const tmap_t *src, const tmap_t *dst, const int32_t *coords,
+                                   int64_t n_tiles, float addend, const tmap_launch_opts *opts,
+                                   void *hip_stream);
+
+/*
+ * tmap_bulk_copy -- raw one-dimensional bulk copy of `bytes` contiguous bytes
+ * from src to dst through the same LDS ring, with no tensor map and no
+ * swizzle ("TMA -- the async bulk copy engine", "The real toolchain": the
+ * plain bulk copy moves a contiguous byte range).  src and dst are device
+ * pointers, 16-byte aligned, not overlapping; bytes is a multiple of 16
+ * (bytes == 0 is a no-op).  Moved in 16 KiB tiles; larger ranges take several
+ * launches of at most 16 GiB each, all on hip_stream.
+ */
+tmap_status tmap_bulk_copy(void *dst, const void *src, uint64_t bytes, const tmap_launch_opts *opts,
+                           void *hip_stream);
+
 /* Bytes of one tile image: product of the box extents times the element
  * size ("Day 76": 64x64 fp32 is 16384 bytes).  0 for a map never encoded. */
 uint64_t tmap_box_bytes(const tmap_t *map);

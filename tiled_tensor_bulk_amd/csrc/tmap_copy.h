@@ -291,7 +291,8 @@ __device__ __forceinline__ void load_slot_elements(uint8_t *stage, uint32_t p, c
 // Store the in-bounds elements held in LDS slot p one by one.
 template <int R>
 __device__ __forceinline__ void store_slot_elements(const uint8_t *stage, uint32_t p, const KArgs &a,
-                                                    const KMap &m, const Win<R> &w, __amdgpu_buffer_rsrc_t r) {
+                                                    const KMap &m, const Win<R> &w, __amdgpu_buffer_rsrc_t r,
+                                                    bool add) {
     const uint32_t es = m.elem_size, k = a.k_el;
     for (uint32_t j = 0; j < k; ++j) {
         const uint32_t s = p * k + j;
@@ -305,7 +306,9 @@ __device__ __forceinline__ void store_slot_elements(const uint8_t *stage, uint32
         } else if (es == 2) {
             __builtin_amdgcn_raw_buffer_store_b16(*(const uint16_t *)src, r, off, 0, 0);
         } else if (es == 4) {
-            __builtin_amdgcn_raw_buffer_store_b32(*(const uint32_t *)src, r, off, 0, 0);
+            uint32_t v = *(const uint32_t *)src;
+            if (add) v = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, v) + a.addend);
+            __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
         } else {
             typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
             __builtin_amdgcn_raw_buffer_store_b64(*(const u32x2 *)src, r, off, 0, 0);
@@ -340,7 +343,7 @@ __device__ __forceinline__ void load_chunk_edge(uint8_t *slot, uint32_t off, uin
 
 template <int ES>
 __device__ __forceinline__ void store_chunk_edge(const uint8_t *slot, uint32_t off, uint32_t x0, uint32_t lo0,
-                                                 uint32_t hi0, __amdgpu_buffer_rsrc_t r) {
+                                                 uint32_t hi0, __amdgpu_buffer_rsrc_t r, bool add, float addend) {
     constexpr int K = 16 / ES;
 #pragma unroll 4
     for (int j = 0; j < K; ++j) {
@@ -350,7 +353,9 @@ __device__ __forceinline__ void store_chunk_edge(const uint8_t *slot, uint32_t o
         } else if constexpr (ES == 2) {
             __builtin_amdgcn_raw_buffer_store_b16(((const uint16_t *)slot)[j], r, off + j * 2, 0, 0);
         } else if constexpr (ES == 4) {
-            __builtin_amdgcn_raw_buffer_store_b32(((const uint32_t *)slot)[j], r, off + j * 4, 0, 0);
+            uint32_t v = ((const uint32_t *)slot)[j];
+            if (add) v = __builtin_bit_cast(uint32_t, __builtin_bit_cast(float, v) + addend);
+            __builtin_amdgcn_raw_buffer_store_b32(v, r, off + j * 4, 0, 0);
         } else {
             typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
             __builtin_amdgcn_raw_buffer_store_b64(((const u32x2 *)slot)[j], r, off + j * 8, 0, 0);
@@ -369,12 +374,13 @@ __device__ __forceinline__ void load_chunk_edge_es(uint32_t es, uint8_t *slot, u
 }
 
 __device__ __forceinline__ void store_chunk_edge_es(uint32_t es, const uint8_t *slot, uint32_t off, uint32_t x0,
-                                                    uint32_t lo0, uint32_t hi0, __amdgpu_buffer_rsrc_t r) {
+                                                    uint32_t lo0, uint32_t hi0, __amdgpu_buffer_rsrc_t r, bool add,
+                                                    float addend) {
     switch (es) {
-        case 1: store_chunk_edge<1>(slot, off, x0, lo0, hi0, r); break;
-        case 2: store_chunk_edge<2>(slot, off, x0, lo0, hi0, r); break;
-        case 4: store_chunk_edge<4>(slot, off, x0, lo0, hi0, r); break;
-        default: store_chunk_edge<8>(slot, off, x0, lo0, hi0, r); break;
+        case 1: store_chunk_edge<1>(slot, off, x0, lo0, hi0, r, false, 0.f); break;
+        case 2: store_chunk_edge<2>(slot, off, x0, lo0, hi0, r, false, 0.f); break;
+        case 4: store_chunk_edge<4>(slot, off, x0, lo0, hi0, r, add, addend); break;
+        default: store_chunk_edge<8>(slot, off, x0, lo0, hi0, r, false, 0.f); break;
     }
 }
 
@@ -554,6 +560,18 @@ struct Copier {
             __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
     }
 
+    // The tile update of the fused round trip: + addend on each fp32 element
+    // read back from the stage ("Day 76", "Solution").
+    __device__ __forceinline__ i32x4 update(i32x4 v) const {
+        if (MODE == kRoundtrip && a.add_f32) {
+            typedef __attribute__((ext_vector_type(4))) float f32x4;
+            f32x4 f = __builtin_bit_cast(f32x4, v);
+            f = f + a.addend;
+            v = __builtin_bit_cast(i32x4, f);
+        }
+        return v;
+    }
+
     // Read the tile at corner c (sequence index t) out of `stage`.
     __device__ __forceinline__ void consume(uint8_t *stage, const int32_t c[R], int64_t t) const {
         if (MODE == kLoad) {
@@ -573,7 +591,7 @@ struct Copier {
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) {
                     if (cslot[j] < a.n_chunks) {
-                        const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
+                        const i32x4 v = update(*(const i32x4 *)(stage + cslot[j] * 16u));
                         store16(v, r, coff[j]);
                     }
                 }
@@ -583,7 +601,7 @@ struct Copier {
 #pragma unroll
                     for (int j = 0; j < NSLOT; ++j) {
                         if (cslot[j] < a.n_chunks && classify<R>(cw0[j], cw1[j], w, a.k_el) == kFull) {
-                            const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
+                            const i32x4 v = update(*(const i32x4 *)(stage + cslot[j] * 16u));
                             store16(v, r, coff[j]);
                         }
                     }
@@ -596,13 +614,14 @@ struct Copier {
                     const uint32_t p = ((uint32_t)(j * kWaves) + cw) * 64u + lane;
                     if (p >= a.n_chunks) continue;
                     if (a.elemwise) {
-                        store_slot_elements<R>(stage, p, a, a.dst, w, r);
+                        store_slot_elements<R>(stage, p, a, a.dst, w, r, MODE == kRoundtrip && a.add_f32);
                         continue;
                     }
                     uint32_t off, w0, w1;
                     chunk_info(logical_chunk(p, a.dst), a.dst, off, w0, w1);
                     if (classify<R>(w0, w1, w, a.k_el) == kPart)
-                        store_chunk_edge_es(a.dst.elem_size, stage + p * 16u, off, w0 & 0xFFFFu, w.lo[0], w.hi[0], r);
+                        store_chunk_edge_es(a.dst.elem_size, stage + p * 16u, off, w0 & 0xFFFFu, w.lo[0], w.hi[0], r,
+                                            MODE == kRoundtrip && a.add_f32, a.addend);
                 }
             }
         }

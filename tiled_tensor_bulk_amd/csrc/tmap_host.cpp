@@ -10,6 +10,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -430,8 +431,69 @@ tmap_status tmap_store_tiles(const tmap_t *dst, const int32_t *coords, int64_t n
     return run(tmap::kStore, d, a, opts, hip_stream);
 }
 
+static tmap_status roundtrip_impl(const tmap_t *src, const tmap_t *dst, const int32_t *coords, int64_t n_tiles,
+                                  bool add, float addend, const tmap_launch_opts *opts, void *hip_stream);
+
 tmap_status tmap_roundtrip(const tmap_t *src, const tmap_t *dst, const int32_t *coords, int64_t n_tiles,
                            const tmap_launch_opts *opts, void *hip_stream) {
+    return roundtrip_impl(src, dst, coords, n_tiles, false, 0.0f, opts, hip_stream);
+}
+
+tmap_status tmap_roundtrip_add_f32(const tmap_t *src, const tmap_t *dst, const int32_t *coords, int64_t n_tiles,
+                                   float addend, const tmap_launch_opts *opts, void *hip_stream) {
+    MapImpl s, d;
+    if (decode(src, s) && decode(dst, d) && (s.dtype != TMAP_F32 || d.dtype != TMAP_F32))
+        return fail(TMAP_ERROR_INVALID_VALUE, "the fp32 update needs TMAP_F32 maps");
+    return roundtrip_impl(src, dst, coords, n_tiles, true, addend, opts, hip_stream);
+}
+
+tmap_status tmap_bulk_copy(void *dst, const void *src, uint64_t bytes, const tmap_launch_opts *opts,
+                           void *hip_stream) {
+    if (bytes == 0) return ok();
+    if (!dst || !src || ((uintptr_t)dst & 15u) || ((uintptr_t)src & 15u))
+        return fail(TMAP_ERROR_INVALID_VALUE, "src and dst must be non-NULL and 16-byte aligned");
+    if (bytes % 16u) return fail(TMAP_ERROR_INVALID_VALUE, "bytes (%llu) must be a multiple of 16",
+                                 (unsigned long long)bytes);
+    const uint64_t lo_d = (uint64_t)(uintptr_t)dst, lo_s = (uint64_t)(uintptr_t)src;
+    if (lo_d < lo_s + bytes && lo_s < lo_d + bytes)
+        return fail(TMAP_ERROR_INVALID_VALUE, "src and dst ranges overlap");
+    // A rank-1 map of 8-byte elements with 16 KiB boxes over each side; ranges
+    // above 16 GiB go in several launches so that dims stay within 2^31.
+    const uint64_t kBox = 2048, kMaxElems = 1ull << 31;
+    uint64_t done = 0;
+    while (done < bytes) {
+        const uint64_t elems = std::min<uint64_t>((bytes - done) / 8u, kMaxElems);
+        MapImpl m;
+        std::memset(&m, 0, sizeof m);
+        m.base = lo_s + done;
+        for (int d = 0; d < tmap::kMaxRank; ++d) {
+            m.dims[d] = d == 0 ? elems : 1;
+            m.strides[d] = d == 0 ? 8u : 0u;
+            m.box[d] = (uint16_t)(d == 0 ? kBox : 1);
+        }
+        m.elem_size = 8;
+        m.rank = 1;
+        m.dtype = TMAP_U64;
+        m.box_bytes = (uint32_t)(kBox * 8u);
+        m.span = m.box_bytes;
+        m.magic = tmap::kMagic;
+        MapImpl md = m;
+        md.base = lo_d + done;
+        tmap::KArgs a;
+        std::memset(&a, 0, sizeof a);
+        a.src = tmap::kernel_map(m);
+        a.dst = tmap::kernel_map(md);
+        const int64_t n = sweep_count(m);
+        fill_common(a, m, nullptr, n);
+        tmap_status st = run(tmap::kRoundtrip, m, a, opts, hip_stream);
+        if (st != TMAP_SUCCESS) return st;
+        done += elems * 8u;
+    }
+    return ok();
+}
+
+static tmap_status roundtrip_impl(const tmap_t *src, const tmap_t *dst, const int32_t *coords, int64_t n_tiles,
+                                  bool add, float addend, const tmap_launch_opts *opts, void *hip_stream) {
     MapImpl s, d;
     if (!decode(src, s)) return fail(TMAP_ERROR_INVALID_VALUE, "src map is NULL or not encoded");
     if (!decode(dst, d)) return fail(TMAP_ERROR_INVALID_VALUE, "dst map is NULL or not encoded");
@@ -452,6 +514,8 @@ tmap_status tmap_roundtrip(const tmap_t *src, const tmap_t *dst, const int32_t *
     a.src = tmap::kernel_map(s);
     a.dst = tmap::kernel_map(d);
     a.packed = nullptr;
+    a.add_f32 = add ? 1u : 0u;
+    a.addend = addend;
     fill_common(a, s, coords, n_tiles);
     return run(tmap::kRoundtrip, s, a, opts, hip_stream);
 }

@@ -97,6 +97,8 @@ struct KArgs {
     uint32_t grid;                // workgroups launched
     uint32_t flags;               // TMAP_FLAG_*
     uint32_t spin_limit;          // readiness-wait polls before giving up
+    uint32_t add_f32;             // round trip: add `addend` to every fp32 element before storing
+    float addend;
 };
 
 }  // namespace tmap

@@ -75,6 +75,10 @@ WORKLOADS = {
     # 2 GiB byte tensor 32768 rows x 65536 cols, 128x128 boxes, 128-byte swizzle
     "sweep2g_u8": Workload("sweep2g_u8", "u8", (65536, 32768), (65536,), (128, 128), (3, 4, 3),
                            "sweep", stages=4, values="bytes", seed=5),
+    # the round-trip program's 64x64 fp32 boxes over a 1 GiB matrix (16384 x 16384),
+    # 128-byte swizzle, for the fused +1.0f update
+    "plus1_f32": Workload("plus1_f32", "f32", (16384, 16384), (65536,), (64, 64), (3, 2, 3),
+                          "sweep", stages=4, values="normal_f32", seed=6),
 }
 
 
@@ -97,6 +101,9 @@ def tensor_bytes(w: Workload, seed: Optional[int] = None, nbytes: Optional[int] 
     if w.values == "normal_f16":
         assert n % 2 == 0
         return rng.standard_normal(n // 2, dtype=np.float32).astype(np.float16).view(np.uint8)
+    if w.values == "normal_f32":
+        assert n % 4 == 0
+        return rng.standard_normal(n // 4, dtype=np.float32).view(np.uint8)
     if w.values == "normal_bf16":
         assert n % 2 == 0
         u = rng.standard_normal(n // 2, dtype=np.float32).view(np.uint32).astype(np.uint64)
@@ -125,6 +132,9 @@ def device_bytes(w: Workload, device, seed: Optional[int] = None, nbytes: Option
     if values == "normal_f16":
         assert n % 2 == 0
         return torch.randn(n // 2, generator=g, device=device, dtype=torch.float32).to(torch.float16).view(torch.uint8)
+    if values == "normal_f32":
+        assert n % 4 == 0
+        return torch.randn(n // 4, generator=g, device=device, dtype=torch.float32).view(torch.uint8)
     if values == "normal_bf16":
         assert n % 2 == 0
         f = torch.randn(n // 2, generator=g, device=device, dtype=torch.float32)

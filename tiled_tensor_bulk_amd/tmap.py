@@ -72,6 +72,11 @@ def lib():
             f.restype = ctypes.c_int
         L.tmap_roundtrip.argtypes = [P(tmap_t), P(tmap_t), vp, i64, P(tmap_launch_opts), vp]
         L.tmap_roundtrip.restype = ctypes.c_int
+        L.tmap_roundtrip_add_f32.argtypes = [P(tmap_t), P(tmap_t), vp, i64, ctypes.c_float,
+                                             P(tmap_launch_opts), vp]
+        L.tmap_roundtrip_add_f32.restype = ctypes.c_int
+        L.tmap_bulk_copy.argtypes = [vp, vp, ctypes.c_uint64, P(tmap_launch_opts), vp]
+        L.tmap_bulk_copy.restype = ctypes.c_int
         L.tmap_box_bytes.argtypes = [P(tmap_t)]
         L.tmap_box_bytes.restype = ctypes.c_uint64
         L.tmap_sweep_tiles.argtypes = [P(tmap_t)]
@@ -164,6 +169,18 @@ def tmap_roundtrip(src: tmap_t, dst: tmap_t, coords, n_tiles: int, stream=None, 
     st = lib().tmap_roundtrip(ctypes.byref(src), ctypes.byref(dst), _ptr(coords), int(n_tiles),
                               _opts(**opts), _stream(stream))
     _check(st, "tmap_roundtrip")
+
+
+def tmap_roundtrip_add_f32(src: tmap_t, dst: tmap_t, coords, n_tiles: int, addend: float, stream=None,
+                           **opts) -> None:
+    st = lib().tmap_roundtrip_add_f32(ctypes.byref(src), ctypes.byref(dst), _ptr(coords), int(n_tiles),
+                                      float(addend), _opts(**opts), _stream(stream))
+    _check(st, "tmap_roundtrip_add_f32")
+
+
+def tmap_bulk_copy(dst, src, nbytes: int, stream=None, **opts) -> None:
+    st = lib().tmap_bulk_copy(_ptr(dst), _ptr(src), int(nbytes), _opts(**opts), _stream(stream))
+    _check(st, "tmap_bulk_copy")
 
 
 def tmap_box_bytes(m: tmap_t) -> int:
