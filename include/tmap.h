@@ -91,6 +91,12 @@ typedef struct tmap_launch_opts {
 #define TMAP_FLAG_CONTIGUOUS 0x1u
 /* Non-temporal hints on the streaming loads and stores. */
 #define TMAP_FLAG_NONTEMPORAL 0x2u
+/* Thread-copy mode: the lanes load each box into registers and write it into
+ * a single LDS stage themselves, publishing it with a workgroup barrier,
+ * instead of direct-to-LDS loads counted by the per-stage byte record
+ * ("TMA -- the async bulk copy engine", "Interactive": thread-copy mode).
+ * Same results; an A/B baseline.  `stages` is ignored. */
+#define TMAP_FLAG_THREAD_COPY 0x4u
 /* Test hook: every wave announces 16 bytes more than it delivers, so a
  * stage never becomes ready and the bounded wait must end the kernel with
  * TMAP_ERROR_TIMEOUT ("Day 76", "Pitfalls": a byte budget that does not match

@@ -215,7 +215,8 @@ def _fuzz_case(rng, idx):
     ncoords = int(rng.integers(1, 40))
     coords = inputs.random_corners(dims, box, ncoords, int(rng.integers(1 << 30)))
     opts = dict(stages=int(rng.integers(1, 5)), grid_wgs=int(rng.choice([0, 1, 2, 3, 7])),
-                flags=int(rng.choice([0, T.FLAG_CONTIGUOUS, T.FLAG_NONTEMPORAL])),
+                flags=int(rng.choice([0, T.FLAG_CONTIGUOUS, T.FLAG_NONTEMPORAL, T.FLAG_THREAD_COPY,
+                                      T.FLAG_THREAD_COPY | T.FLAG_CONTIGUOUS])),
                 group=int(rng.choice([0, 1, 2, 4, 8, 64])))
     return es, dims, strides, box, swz, alloc, coords, opts
 
@@ -333,3 +334,37 @@ def test_repeat_is_deterministic():
     for st in (1, 2, 3, 4):
         b = gpu_load(m, coords, len(coords), stages=st, grid_wgs=97)
         assert torch.equal(a, b), st
+
+
+@pytest.mark.parametrize("name", ["tile64_f32", "strips_f16", "ragged_bf16", "pad5d_f32", "sweep2g_u8"])
+def test_thread_copy_mode_matches_the_staged_copy(name):
+    """The register-path variant gives the same bytes as the direct-to-LDS
+    ring (which the tests above pin to the oracle) for load, store and round
+    trip of every workload."""
+    w = inputs.WORKLOADS[name]
+    say(f"thread-copy vs staged: {name}")
+    src = inputs.device_bytes(w, DEV)
+    m = enc(w.dtype, src, w.dims, w.strides, w.box, w.swizzle)
+    if w.coords == "sweep":
+        cn, n = None, T.tmap_sweep_tiles(m)
+    elif w.coords == "origin":
+        cn, n = np.zeros((1, w.rank), np.int32), 1
+    else:
+        cn = inputs.random_corners(w.dims, w.box, 20000, seed=44)
+        n = len(cn)
+    c = None if cn is None else torch.from_numpy(cn).to(DEV)
+    a = gpu_load(m, cn, n)
+    b = gpu_load(m, cn, n, flags=T.FLAG_THREAD_COPY)
+    assert torch.equal(a, b)
+    d1 = dev_tensor(w.alloc_bytes, fill_seed=7)
+    d2 = d1.clone()
+    T.tmap_store_tiles(enc(w.dtype, d1, w.dims, w.strides, w.box, w.swizzle), c, n, a)
+    T.tmap_store_tiles(enc(w.dtype, d2, w.dims, w.strides, w.box, w.swizzle), c, n, a, flags=T.FLAG_THREAD_COPY)
+    check_ok()
+    assert torch.equal(d1, d2)
+    del a, b
+    d1.copy_(d2)
+    T.tmap_roundtrip(m, enc(w.dtype, d1, w.dims, w.strides, w.box, w.swizzle), c, n)
+    T.tmap_roundtrip(m, enc(w.dtype, d2, w.dims, w.strides, w.box, w.swizzle), c, n, flags=T.FLAG_THREAD_COPY)
+    check_ok()
+    assert torch.equal(d1, d2)

@@ -384,6 +384,31 @@ __device__ __forceinline__ void store_chunk_edge_es(uint32_t es, const uint8_t *
     }
 }
 
+// In-box byte offset (in map m) and packed indices of logical chunk q.
+template <int R>
+__device__ __forceinline__ void chunk_info_of(const KArgs &a, uint32_t q, const KMap &m, uint32_t &off,
+                                              uint32_t &w0, uint32_t &w1) {
+    const uint32_t row = q / a.row_chunks;
+    const uint32_t x0 = (q - row * a.row_chunks) * a.k_el;
+    uint32_t i[kMaxRank] = {x0, 0, 0, 0, 0};
+    uint32_t rest = row;
+#pragma unroll
+    for (int d = 1; d < R; ++d) {
+        const uint32_t b = m.box[d];
+        const uint32_t qq = rest / b;
+        i[d] = rest - qq * b;
+        rest = qq;
+    }
+    off = inbox_offset<R>(i, m);
+    w0 = x0 | (i[1] << 16);
+    w1 = i[2] | (i[3] << 8) | (i[4] << 16);
+}
+
+// Logical chunk held by LDS slot p (the swizzle is its own inverse).
+__device__ __forceinline__ uint32_t logical_chunk_of(const KArgs &a, uint32_t p, const KMap &m) {
+    return swizzle(p * a.k_el, m.swz_b, m.swz_m, m.swz_s) / a.k_el;
+}
+
 // ---------------------------------------------------------------- the kernel
 template <int MODE, int S, int NSLOT, int R>
 struct Copier {
@@ -405,27 +430,13 @@ struct Copier {
 
     __device__ __forceinline__ const KMap &swept() const { return MODE == kStore ? a.dst : a.src; }
 
-    // In-box byte offset (in map m) and packed indices of logical chunk q.
     __device__ __forceinline__ void chunk_info(uint32_t q, const KMap &m, uint32_t &off, uint32_t &w0,
                                                uint32_t &w1) const {
-        const uint32_t row = q / a.row_chunks;
-        const uint32_t x0 = (q - row * a.row_chunks) * a.k_el;
-        uint32_t i[kMaxRank] = {x0, 0, 0, 0, 0};
-        uint32_t rest = row;
-#pragma unroll
-        for (int d = 1; d < R; ++d) {
-            const uint32_t b = m.box[d];
-            const uint32_t qq = rest / b;
-            i[d] = rest - qq * b;
-            rest = qq;
-        }
-        off = inbox_offset<R>(i, m);
-        w0 = x0 | (i[1] << 16);
-        w1 = i[2] | (i[3] << 8) | (i[4] << 16);
+        chunk_info_of<R>(a, q, m, off, w0, w1);
     }
 
     __device__ __forceinline__ uint32_t logical_chunk(uint32_t p, const KMap &m) const {
-        return swizzle(p * a.k_el, m.swz_b, m.swz_m, m.swz_s) / a.k_el;
+        return logical_chunk_of(a, p, m);
     }
 
     __device__ __forceinline__ void setup() {
@@ -525,31 +536,32 @@ struct Copier {
         // wave's direct-to-LDS loads into it.
         uint32_t probe = *(volatile uint32_t *)(stage + (wave * 64u + lane) * 16u);
         asm volatile("" ::"v"(probe) : "memory");
-        if (MODE != kStore) {
-            if ((edge >> X) & 1u) {
-                const Place pl = place<R>(a.src, c);
-                const Win<R> w = window<R>(a.src, c);
-                const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
-                // slow path, kept out of the unrolled slot arrays: recompute
-                // each slot's chunk, patch the partial ones
-#pragma unroll 1
-                for (int j = 0; j < NSLOT; ++j) {
-                    const uint32_t p = ((uint32_t)(j * kWaves) + wave) * 64u + lane;
-                    if (p >= a.n_chunks) continue;
-                    if (a.elemwise) {
-                        load_slot_elements<R>(stage, p, a, a.src, w, r);
-                        continue;
-                    }
-                    uint32_t off, w0, w1;
-                    chunk_info(logical_chunk(p, a.src), a.src, off, w0, w1);
-                    if (classify<R>(w0, w1, w, a.k_el) == kPart)
-                        load_chunk_edge_es(a.src.elem_size, stage + p * 16u, off, w0 & 0xFFFFu, w.lo[0], w.hi[0], r);
-                }
-            }
-        }
+        if (MODE != kStore && ((edge >> X) & 1u)) patch_edge(stage, c);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm);
         asm volatile("" ::: "memory");
         bar_complete(bar, my_bytes, lane);
+    }
+
+    // Edge tile at corner c: fill in the partial chunks of this lane's
+    // producer slots element by element.  Slow path, kept out of the unrolled
+    // slot arrays: each slot's chunk is recomputed.
+    __device__ __forceinline__ void patch_edge(uint8_t *stage, const int32_t c[R]) const {
+        const Place pl = place<R>(a.src, c);
+        const Win<R> w = window<R>(a.src, c);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
+#pragma unroll 1
+        for (int j = 0; j < NSLOT; ++j) {
+            const uint32_t p = ((uint32_t)(j * kWaves) + wave) * 64u + lane;
+            if (p >= a.n_chunks) continue;
+            if (a.elemwise) {
+                load_slot_elements<R>(stage, p, a, a.src, w, r);
+                continue;
+            }
+            uint32_t off, w0, w1;
+            chunk_info(logical_chunk(p, a.src), a.src, off, w0, w1);
+            if (classify<R>(w0, w1, w, a.k_el) == kPart)
+                load_chunk_edge_es(a.src.elem_size, stage + p * 16u, off, w0 & 0xFFFFu, w.lo[0], w.hi[0], r);
+        }
     }
 
     template <typename Rs>
@@ -707,6 +719,108 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const KArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
 }
 
+// ---------------------------------------------------------------- thread-copy variant
+// The register path the pages contrast with the copy engine ("TMA -- the
+// async bulk copy engine", "Interactive": thread-copy mode, the threads drive
+// the copy lane by lane; "Day 76", the diagram's first band: every thread
+// computes its addresses and moves the data through registers).  Each lane
+// loads its chunks into VGPRs (the next tile's loads are in flight while the
+// current tile is handled), writes them into the single LDS stage itself, and
+// a plain workgroup barrier is then enough to publish the tile, because the
+// writes were the threads' own.  Same tile order, bounds, zero fill, swizzle
+// and clipped stores as the staged kernel; used as its A/B baseline.
+template <int MODE, int NSLOT, int R>
+struct ThreadCopier : Copier<MODE, 1, NSLOT, R> {
+    using Base = Copier<MODE, 1, NSLOT, R>;
+    using Base::a;
+    using Base::ccur;
+    using Base::cnt;
+    using Base::fcur;
+    using Base::nt;
+    using Base::poff;
+    using Base::pslot;
+    using Base::pw0;
+    using Base::pw1;
+
+    __device__ __forceinline__ ThreadCopier(const KArgs &args, uint64_t *b, uint32_t *ab) : Base(args, b, ab) {}
+
+    __device__ __forceinline__ i32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) const {
+        return nt ? __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2)
+                  : __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    }
+
+    // Start the register loads of the fill cursor's tile; true for an edge tile.
+    __device__ __forceinline__ bool issue(i32x4 (&v)[NSLOT]) {
+        bool edge = false;
+        if (MODE == kStore) {
+            const uint64_t bb = a.dst.box_bytes;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)fcur.t * bb, (uint32_t)bb);
+#pragma unroll
+            for (int j = 0; j < NSLOT; ++j) v[j] = ld16(r, pslot[j] < a.n_chunks ? pslot[j] * 16u : kOob);
+        } else {
+            int32_t c[R];
+            cursor_corner<R>(a, a.src, fcur, c);
+            const Place pl = place<R>(a.src, c);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
+            edge = !(pl.interior && !a.elemwise);
+            if (!edge) {
+#pragma unroll
+                for (int j = 0; j < NSLOT; ++j) v[j] = ld16(r, pslot[j] < a.n_chunks ? poff[j] : kOob);
+            } else {
+                const Win<R> w = window<R>(a.src, c);
+#pragma unroll
+                for (int j = 0; j < NSLOT; ++j) {
+                    const bool full = !a.elemwise && pslot[j] < a.n_chunks &&
+                                      classify<R>(pw0[j], pw1[j], w, a.k_el) == kFull;
+                    v[j] = ld16(r, full ? poff[j] : kOob);
+                }
+            }
+        }
+        cursor_advance<R>(a, fcur);
+        return edge;
+    }
+
+    // One tile: write `cur` into the stage, publish it with a barrier, drain it.
+    __device__ __forceinline__ bool tile(uint8_t *stage, i32x4 (&cur)[NSLOT], bool cur_edge, i32x4 (&nxt)[NSLOT],
+                                         bool &nxt_edge, int64_t k) {
+        if (k >= cnt) return false;
+        if (k + 1 < cnt) nxt_edge = issue(nxt);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+        __builtin_amdgcn_s_barrier();  // every wave is done reading the previous tile
+        int32_t c[R];
+        cursor_corner<R>(a, this->swept(), ccur, c);
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j)
+            if (pslot[j] < a.n_chunks) *(i32x4 *)(stage + pslot[j] * 16u) = cur[j];
+        if (MODE != kStore && cur_edge) this->patch_edge(stage, c);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+        __builtin_amdgcn_s_barrier();  // the tile is complete in LDS
+        asm volatile("" ::: "memory");
+        this->consume(stage, c, ccur.t);
+        cursor_advance<R>(a, ccur);
+        return true;
+    }
+};
+
+template <int MODE, int NSLOT, int R>
+__global__ __launch_bounds__(kThreads) void thread_kernel(const KArgs a) {
+    constexpr uint32_t SB = NSLOT * kWaves * kBlockBytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t stage[SB];
+    __shared__ uint64_t bars[4];
+    __shared__ uint32_t abort_flag;
+    ThreadCopier<MODE, NSLOT, R> cp(a, bars, &abort_flag);
+    cp.setup();
+    __syncthreads();
+    if (cp.cnt <= 0) return;
+    i32x4 va[NSLOT], vb[NSLOT];
+    bool ea = cp.issue(va), eb = false;
+    for (int64_t k = 0; k < cp.cnt; k += 2) {  // ping-pong, so no register copies
+        if (!cp.tile(stage, va, ea, vb, eb, k)) break;
+        if (!cp.tile(stage, vb, eb, va, ea, k + 1)) break;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 typedef void (*KernelFn)(const KArgs);
 
 template <int MODE, int S, int R>
@@ -723,11 +837,25 @@ KernelFn pick_nslot(int nslot) {
     }
 }
 
-// Launch the (MODE, stages, nslot, R) variant; hipError_t as int.
+template <int MODE, int R>
+KernelFn pick_thread(int nslot) {
+    switch (nslot) {
+        case 1: return thread_kernel<MODE, 1, R>;
+        case 2: return thread_kernel<MODE, 2, R>;
+        case 4: return thread_kernel<MODE, 4, R>;
+        case 8: return thread_kernel<MODE, 8, R>;
+        case 16: return thread_kernel<MODE, 16, R>;
+        default: return nullptr;
+    }
+}
+
+// Launch the (MODE, stages, nslot, R) variant, or with stages == 0 the
+// thread-copy variant; hipError_t as int.
 template <int MODE, int R>
 int launch_mode(int stages, int nslot, const KArgs &a, void *stream) {
     KernelFn fn = nullptr;
     switch (stages) {
+        case 0: fn = pick_thread<MODE, R>(nslot); break;
         case 1: fn = pick_nslot<MODE, 1, R>(nslot); break;
         case 2: fn = pick_nslot<MODE, 2, R>(nslot); break;
         case 3: fn = pick_nslot<MODE, 3, R>(nslot); break;

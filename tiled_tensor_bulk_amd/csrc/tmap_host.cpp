@@ -126,6 +126,8 @@ tmap_status plan_launch(const MapImpl &m, int64_t n_tiles, const tmap_launch_opt
     int stages = (opts && opts->stages) ? (int)opts->stages : (nslot >= 16 ? 2 : 4);
     if (stages < 1 || stages > 4)
         return fail(TMAP_ERROR_INVALID_VALUE, "stages must be 1..4 (got %d)", stages);
+    const bool thread_copy = opts && (opts->flags & TMAP_FLAG_THREAD_COPY);
+    if (thread_copy) stages = 1;  // one LDS stage; the next tile waits in registers
     const uint32_t lds = tmap::variant_lds_bytes(stages, nslot);
     if (lds > dev.lds_per_cu || (nslot == 16 && stages > 2))
         return fail(TMAP_ERROR_INVALID_VALUE, "%d stages of %u bytes do not fit in LDS", stages,
@@ -154,7 +156,7 @@ tmap_status plan_launch(const MapImpl &m, int64_t n_tiles, const tmap_launch_opt
     const int64_t useful = contiguous ? n_tiles : (n_tiles + group - 1) / group;
     if ((int64_t)grid > useful) grid = (uint32_t)useful;
     pl.nslot = nslot;
-    pl.stages = stages;
+    pl.stages = thread_copy ? 0 : stages;
     pl.grid = grid;
     pl.group = group;
     return TMAP_SUCCESS;
