@@ -97,6 +97,12 @@ typedef struct tmap_launch_opts {
  * ("TMA -- the async bulk copy engine", "Interactive": thread-copy mode).
  * Same results; an A/B baseline.  `stages` is ignored. */
 #define TMAP_FLAG_THREAD_COPY 0x4u
+/* Producer-wave mode: one wave of a 5-wave workgroup issues every load of a
+ * box under a single arrive+expect of its bytes; four consumer waves wait on
+ * the stage's byte count, drain it and release it through a second per-stage
+ * record ("GPU TMA", "Warp specialization").  Same results.  Needs boxes of
+ * at most 32 KiB; `stages` 1 is taken as 2. */
+#define TMAP_FLAG_PRODUCER_WAVE 0x8u
 /* Test hook: every wave announces 16 bytes more than it delivers, so a
  * stage never becomes ready and the bounded wait must end the kernel with
  * TMAP_ERROR_TIMEOUT ("Day 76", "Pitfalls": a byte budget that does not match

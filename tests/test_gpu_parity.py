@@ -216,7 +216,8 @@ def _fuzz_case(rng, idx):
     coords = inputs.random_corners(dims, box, ncoords, int(rng.integers(1 << 30)))
     opts = dict(stages=int(rng.integers(1, 5)), grid_wgs=int(rng.choice([0, 1, 2, 3, 7])),
                 flags=int(rng.choice([0, T.FLAG_CONTIGUOUS, T.FLAG_NONTEMPORAL, T.FLAG_THREAD_COPY,
-                                      T.FLAG_THREAD_COPY | T.FLAG_CONTIGUOUS])),
+                                      T.FLAG_THREAD_COPY | T.FLAG_CONTIGUOUS, T.FLAG_PRODUCER_WAVE,
+                                      T.FLAG_PRODUCER_WAVE | T.FLAG_CONTIGUOUS])),
                 group=int(rng.choice([0, 1, 2, 4, 8, 64])))
     return es, dims, strides, box, swz, alloc, coords, opts
 
@@ -309,18 +310,19 @@ def test_zero_tiles_launch_nothing():
     check_ok()
 
 
-def test_budget_mismatch_times_out_instead_of_hanging():
+@pytest.mark.parametrize("mode", [0, T.FLAG_PRODUCER_WAVE])
+def test_budget_mismatch_times_out_instead_of_hanging(mode):
     """Announce 16 more bytes than delivered: the stage never becomes ready; the
     bounded wait ends the kernel and the status reports a timeout."""
-    say("budget mismatch -> TIMEOUT")
+    say(f"budget mismatch -> TIMEOUT (flags {mode})")
     src = dev_tensor(16384, fill_seed=1)
     m = enc("f32", src, [64, 64], [256], [64, 64])
     out = dev_tensor(16384 * 4)
     coords = torch.zeros((4, 2), dtype=torch.int32, device=DEV)
-    T.tmap_load_tiles(m, coords, 4, out, stages=2, flags=T.FLAG_INJECT_BUDGET_MISMATCH, spin_limit=2000)
+    T.tmap_load_tiles(m, coords, 4, out, stages=2, flags=T.FLAG_INJECT_BUDGET_MISMATCH | mode, spin_limit=2000)
     assert T.tmap_sync_status() == T.TIMEOUT
     # the library keeps working afterwards
-    T.tmap_load_tiles(m, coords, 4, out, stages=2)
+    T.tmap_load_tiles(m, coords, 4, out, stages=2, flags=mode)
     check_ok()
     assert torch.equal(out.view(4, -1)[3], src)
 
@@ -336,13 +338,15 @@ def test_repeat_is_deterministic():
         assert torch.equal(a, b), st
 
 
+@pytest.mark.parametrize("mode", ["thread_copy", "producer_wave"])
 @pytest.mark.parametrize("name", ["tile64_f32", "strips_f16", "ragged_bf16", "pad5d_f32", "sweep2g_u8"])
-def test_thread_copy_mode_matches_the_staged_copy(name):
-    """The register-path variant gives the same bytes as the direct-to-LDS
-    ring (which the tests above pin to the oracle) for load, store and round
-    trip of every workload."""
+def test_other_modes_match_the_staged_copy(name, mode):
+    """The register-path and producer-wave variants give the same bytes as the
+    cooperative direct-to-LDS ring (which the tests above pin to the oracle)
+    for load, store and round trip of every workload."""
     w = inputs.WORKLOADS[name]
-    say(f"thread-copy vs staged: {name}")
+    flag = T.FLAG_THREAD_COPY if mode == "thread_copy" else T.FLAG_PRODUCER_WAVE
+    say(f"{mode} vs staged: {name}")
     src = inputs.device_bytes(w, DEV)
     m = enc(w.dtype, src, w.dims, w.strides, w.box, w.swizzle)
     if w.coords == "sweep":
@@ -354,17 +358,17 @@ def test_thread_copy_mode_matches_the_staged_copy(name):
         n = len(cn)
     c = None if cn is None else torch.from_numpy(cn).to(DEV)
     a = gpu_load(m, cn, n)
-    b = gpu_load(m, cn, n, flags=T.FLAG_THREAD_COPY)
+    b = gpu_load(m, cn, n, flags=flag)
     assert torch.equal(a, b)
     d1 = dev_tensor(w.alloc_bytes, fill_seed=7)
     d2 = d1.clone()
     T.tmap_store_tiles(enc(w.dtype, d1, w.dims, w.strides, w.box, w.swizzle), c, n, a)
-    T.tmap_store_tiles(enc(w.dtype, d2, w.dims, w.strides, w.box, w.swizzle), c, n, a, flags=T.FLAG_THREAD_COPY)
+    T.tmap_store_tiles(enc(w.dtype, d2, w.dims, w.strides, w.box, w.swizzle), c, n, a, flags=flag)
     check_ok()
     assert torch.equal(d1, d2)
     del a, b
     d1.copy_(d2)
     T.tmap_roundtrip(m, enc(w.dtype, d1, w.dims, w.strides, w.box, w.swizzle), c, n)
-    T.tmap_roundtrip(m, enc(w.dtype, d2, w.dims, w.strides, w.box, w.swizzle), c, n, flags=T.FLAG_THREAD_COPY)
+    T.tmap_roundtrip(m, enc(w.dtype, d2, w.dims, w.strides, w.box, w.swizzle), c, n, flags=flag)
     check_ok()
     assert torch.equal(d1, d2)

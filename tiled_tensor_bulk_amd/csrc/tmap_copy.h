@@ -49,6 +49,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tmap_internal.h"
 
 namespace tmap {
@@ -226,28 +228,36 @@ __device__ __forceinline__ uint32_t inbox_offset(const uint32_t i[R], const KMap
 // One 8-byte LDS word per stage: bits 0..31 outstanding bytes, bits 32..62
 // arrivals, bit 63 phase.  The operation that leaves (all waves arrived, zero
 // bytes outstanding) resets the counts and flips the phase.
-__device__ __forceinline__ void bar_update(uint64_t *bar, uint64_t delta) {
+// `arrivals` is the number of arrivals a phase needs.
+__device__ __forceinline__ void bar_update(uint64_t *bar, uint64_t delta, uint32_t arrivals = kWaves) {
     const uint64_t old = __hip_atomic_fetch_add(bar, delta, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const uint64_t now = old + delta;
-    if ((now & ~kPhase) == ((uint64_t)kWaves << 32))
-        __hip_atomic_fetch_add(bar, kPhase - ((uint64_t)kWaves << 32), __ATOMIC_RELAXED,
+    if ((now & ~kPhase) == ((uint64_t)arrivals << 32))
+        __hip_atomic_fetch_add(bar, kPhase - ((uint64_t)arrivals << 32), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // arrive + expect_tx(bytes).  With bytes > 0 this can never complete the
 // phase (this wave's own bytes are still outstanding), so it needs no result.
-__device__ __forceinline__ void bar_arrive_expect(uint64_t *bar, uint32_t bytes, uint32_t lane) {
+__device__ __forceinline__ void bar_arrive_expect(uint64_t *bar, uint32_t bytes, uint32_t lane,
+                                                  uint32_t arrivals = kWaves) {
     if (lane == 0) {
         if (bytes)
             __hip_atomic_fetch_add(bar, kArrive + bytes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         else
-            bar_update(bar, kArrive);
+            bar_update(bar, kArrive, arrivals);
     }
 }
 
 // complete_tx(bytes): the wave's own loads into the stage have landed
-__device__ __forceinline__ void bar_complete(uint64_t *bar, uint32_t bytes, uint32_t lane) {
-    if (lane == 0 && bytes) bar_update(bar, (uint64_t)0 - (uint64_t)bytes);
+__device__ __forceinline__ void bar_complete(uint64_t *bar, uint32_t bytes, uint32_t lane,
+                                             uint32_t arrivals = kWaves) {
+    if (lane == 0 && bytes) bar_update(bar, (uint64_t)0 - (uint64_t)bytes, arrivals);
+}
+
+// A plain arrival (no bytes), e.g. a consumer releasing a stage.
+__device__ __forceinline__ void bar_arrive(uint64_t *bar, uint32_t lane, uint32_t arrivals) {
+    if (lane == 0) bar_update(bar, kArrive, arrivals);
 }
 
 // Wait until the phase with parity `parity` has completed; false on timeout.
@@ -439,9 +449,11 @@ struct Copier {
         return logical_chunk_of(a, p, m);
     }
 
-    __device__ __forceinline__ void setup() {
+    // vwave >= 0 makes this lane act as wave vwave of a 4-wave workgroup
+    // (the consumers of the producer-wave variant use it).
+    __device__ __forceinline__ void setup(int vwave = -1) {
         lane = threadIdx.x & 63u;
-        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        wave = vwave >= 0 ? (uint32_t)vwave : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         nt = (a.flags & TMAP_FLAG_NONTEMPORAL) != 0;
         parity = 0;
         edge = 0;
@@ -821,6 +833,223 @@ __global__ __launch_bounds__(kThreads) void thread_kernel(const KArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
 }
 
+// ---------------------------------------------------------------- producer-wave variant
+// A dedicated issuing wave ("GPU TMA", "Warp specialization": producer warps
+// issue the copies, consumer warps work on the tiles that are ready; "TMA --
+// the async bulk copy engine", "Why this only pays off inside a pipeline").
+// Wave 0 issues every direct-to-LDS load of a box under one arrive+expect of
+// the whole box_bytes and completes it once its loads have landed; waves 1..4
+// wait on the stage's full parity, drain it exactly like the cooperative
+// kernel's consumers, and arrive on the stage's empty record, which the
+// producer waits on before it refills the stage.  No workgroup barrier per
+// tile.
+constexpr int kWsConsumers = 4;
+constexpr int kWsThreads = 64 * (kWsConsumers + 1);
+
+template <int MODE, int S, int NSLOT, int R>
+struct WsProducer {
+    static constexpr int NP = NSLOT * kWsConsumers;  // 16-byte slots per producer lane per tile
+    const KArgs &a;
+    uint64_t *full, *empty;
+    uint32_t *abort_flag;
+    uint32_t lane, eparity, edge;
+    int64_t cnt;
+    bool nt;
+    Cursor<R> fcur;
+    uint32_t poff[NP], pw0[NP], pw1[NP];
+
+    __device__ __forceinline__ WsProducer(const KArgs &args, uint64_t *f, uint64_t *e, uint32_t *ab, int64_t n,
+                                          int64_t t0)
+        : a(args), full(f), empty(e), abort_flag(ab), cnt(n) {
+        lane = threadIdx.x & 63u;
+        eparity = 0;
+        edge = 0;
+        nt = (a.flags & TMAP_FLAG_NONTEMPORAL) != 0;
+        cursor_init<R>(a, t0, fcur);
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const uint32_t p = (uint32_t)j * 64u + lane;
+            poff[j] = pw0[j] = pw1[j] = 0;
+            if (MODE != kStore && !a.elemwise && p < a.n_chunks)
+                chunk_info_of<R>(a, logical_chunk_of(a, p, a.src), a.src, poff[j], pw0[j], pw1[j]);
+        }
+    }
+
+    __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint8_t *stage, int j, uint32_t voff) const {
+        lds_void_t *blk = (lds_void_t *)(stage + j * kBlockBytes);
+        if (nt)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, blk, 16, voff, 0, 0, 2);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, blk, 16, voff, 0, 0, 0);
+    }
+
+    // Arm stage X's full record with the box's bytes and issue all its loads.
+    template <int X>
+    __device__ __forceinline__ void fill(uint8_t *stage) {
+        const uint32_t bb = a.src.box_bytes;
+        const uint32_t budget = bb + ((a.flags & TMAP_FLAG_INJECT_BUDGET_MISMATCH) ? 16u : 0u);
+        bar_arrive_expect(&full[X], budget, lane, 1);
+        if (MODE == kStore) {
+            const uint64_t dbb = a.dst.box_bytes;
+            const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)fcur.t * dbb, (uint32_t)dbb);
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                const uint32_t p = (uint32_t)j * 64u + lane;
+                dma(r, stage, j, p < a.n_chunks ? p * 16u : kOob);
+            }
+        } else {
+            int32_t c[R];
+            cursor_corner<R>(a, a.src, fcur, c);
+            const Place pl = place<R>(a.src, c);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
+            const bool fast = pl.interior && !a.elemwise;
+            edge = fast ? (edge & ~(1u << X)) : (edge | (1u << X));
+            if (fast) {
+#pragma unroll
+                for (int j = 0; j < NP; ++j) dma(r, stage, j, (uint32_t)j * 64u + lane < a.n_chunks ? poff[j] : kOob);
+            } else {
+                const Win<R> w = window<R>(a.src, c);
+#pragma unroll
+                for (int j = 0; j < NP; ++j) {
+                    const bool full_chunk = !a.elemwise && (uint32_t)j * 64u + lane < a.n_chunks &&
+                                            classify<R>(pw0[j], pw1[j], w, a.k_el) == kFull;
+                    dma(r, stage, j, full_chunk ? poff[j] : kOob);
+                }
+            }
+        }
+        cursor_advance<R>(a, fcur);
+    }
+
+    // The loads of the tile at corner c have landed in stage X: patch its
+    // partial chunks and complete the stage's byte budget.
+    template <int X>
+    __device__ __forceinline__ void land(uint8_t *stage, const int32_t c[R]) const {
+        uint32_t probe = *(volatile uint32_t *)(stage + lane * 16u);
+        asm volatile("" ::"v"(probe) : "memory");
+        if (MODE != kStore && ((edge >> X) & 1u)) {
+            const Place pl = place<R>(a.src, c);
+            const Win<R> w = window<R>(a.src, c);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
+#pragma unroll 1
+            for (int j = 0; j < NP; ++j) {
+                const uint32_t p = (uint32_t)j * 64u + lane;
+                if (p >= a.n_chunks) continue;
+                if (a.elemwise) {
+                    load_slot_elements<R>(stage, p, a, a.src, w, r);
+                    continue;
+                }
+                uint32_t off, w0, w1;
+                chunk_info_of<R>(a, logical_chunk_of(a, p, a.src), a.src, off, w0, w1);
+                if (classify<R>(w0, w1, w, a.k_el) == kPart)
+                    load_chunk_edge_es(a.src.elem_size, stage + p * 16u, off, w0 & 0xFFFFu, w.lo[0], w.hi[0], r);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+        asm volatile("" ::: "memory");
+        bar_complete(&full[X], a.src.box_bytes, lane, 1);
+    }
+
+    __device__ __forceinline__ bool aborted() const {
+        return __hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+    }
+
+    __device__ __forceinline__ void fail() const {
+        if (lane == 0) {
+            __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // Tile i sits in stage X: land it, then (once the consumers released the
+    // stage) refill the stage with tile i+S.  False ends the loop.
+    template <int X>
+    __device__ __forceinline__ bool step(uint8_t *st, Cursor<R> &lcur, int64_t i) {
+        if (i >= cnt || aborted()) return false;
+        int32_t c[R];
+        cursor_corner<R>(a, MODE == kStore ? a.dst : a.src, lcur, c);
+        land<X>(st, c);
+        cursor_advance<R>(a, lcur);
+        if (i + S < cnt) {
+            if (!bar_wait(&empty[X], (eparity >> X) & 1u, a.spin_limit)) {
+                fail();
+                return false;
+            }
+            eparity ^= 1u << X;
+            asm volatile("" ::: "memory");
+            fill<X>(st);
+        }
+        return true;
+    }
+};
+
+template <int MODE, int S, int NSLOT, int R>
+__global__ __launch_bounds__(kWsThreads) void ws_kernel(const KArgs a) {
+    constexpr uint32_t SB = NSLOT * kWsConsumers * kBlockBytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[SB];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[S > 1 ? SB : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? SB : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? SB : 16];
+    __shared__ uint64_t full[4], empty[4];
+    __shared__ uint32_t abort_flag;
+
+    if (threadIdx.x == 0) {
+        for (int i = 0; i < 4; ++i) full[i] = empty[i] = 0;
+        abort_flag = 0;
+    }
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // the consumers' view: consumer cw = wave-1 drains the slots of the
+    // cooperative kernel's consumer cw, i.e. acts as its wave (cw+3) % 4
+    Copier<MODE, S, NSLOT, R> cons(a, full, &abort_flag);
+    cons.setup(wave == 0 ? 0 : (int)((wave - 1 + kWsConsumers - 1) % kWsConsumers));
+    __syncthreads();
+    if (cons.cnt <= 0) return;
+
+    if (wave == 0) {
+        WsProducer<MODE, S, NSLOT, R> pr(a, full, empty, &abort_flag, cons.cnt, cons.fcur.t);
+        Cursor<R> lcur = pr.fcur;
+        pr.template fill<0>(st0);
+        if constexpr (S > 1) if (1 < pr.cnt) pr.template fill<1>(st1);
+        if constexpr (S > 2) if (2 < pr.cnt) pr.template fill<2>(st2);
+        if constexpr (S > 3) if (3 < pr.cnt) pr.template fill<3>(st3);
+        for (int64_t kb = 0; kb < pr.cnt; kb += S) {
+            if (!pr.template step<0>(st0, lcur, kb)) break;
+            if constexpr (S > 1) if (!pr.template step<1>(st1, lcur, kb + 1)) break;
+            if constexpr (S > 2) if (!pr.template step<2>(st2, lcur, kb + 2)) break;
+            if constexpr (S > 3) if (!pr.template step<3>(st3, lcur, kb + 3)) break;
+        }
+    } else {
+        uint32_t fparity = 0;
+        auto consume = [&](auto xc, uint8_t *st, int64_t i) -> bool {
+            constexpr int X = decltype(xc)::value;
+            if (i >= cons.cnt) return false;
+            if (__hip_atomic_load(&abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
+            if (!bar_wait(&full[X], (fparity >> X) & 1u, a.spin_limit)) {
+                if (cons.lane == 0) {
+                    __hip_atomic_store(&abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                return false;
+            }
+            fparity ^= 1u << X;
+            asm volatile("" ::: "memory");
+            int32_t c[R];
+            cursor_corner<R>(a, cons.swept(), cons.ccur, c);
+            cons.consume(st, c, cons.ccur.t);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm);  // this wave's reads of the stage are done
+            bar_arrive(&empty[X], cons.lane, kWsConsumers);
+            cursor_advance<R>(a, cons.ccur);
+            return true;
+        };
+        for (int64_t kb = 0; kb < cons.cnt; kb += S) {
+            if (!consume(std::integral_constant<int, 0>{}, st0, kb)) break;
+            if constexpr (S > 1) if (!consume(std::integral_constant<int, 1>{}, st1, kb + 1)) break;
+            if constexpr (S > 2) if (!consume(std::integral_constant<int, 2>{}, st2, kb + 2)) break;
+            if constexpr (S > 3) if (!consume(std::integral_constant<int, 3>{}, st3, kb + 3)) break;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 typedef void (*KernelFn)(const KArgs);
 
 template <int MODE, int S, int R>
@@ -849,13 +1078,29 @@ KernelFn pick_thread(int nslot) {
     }
 }
 
-// Launch the (MODE, stages, nslot, R) variant, or with stages == 0 the
-// thread-copy variant; hipError_t as int.
+template <int MODE, int S, int R>
+KernelFn pick_ws(int nslot) {
+    switch (nslot) {
+        case 1: return ws_kernel<MODE, S, 1, R>;
+        case 2: return ws_kernel<MODE, S, 2, R>;
+        case 4: return ws_kernel<MODE, S, 4, R>;
+        case 8: return ws_kernel<MODE, S, 8, R>;
+        default: return nullptr;
+    }
+}
+
+// Launch the (MODE, stages, nslot, R) variant; stages == 0 is the
+// thread-copy variant and stages 12..14 the producer-wave variant with 2..4
+// stages.  hipError_t as int.
 template <int MODE, int R>
 int launch_mode(int stages, int nslot, const KArgs &a, void *stream) {
     KernelFn fn = nullptr;
+    int threads = kThreads;
     switch (stages) {
         case 0: fn = pick_thread<MODE, R>(nslot); break;
+        case 12: fn = pick_ws<MODE, 2, R>(nslot); threads = kWsThreads; break;
+        case 13: fn = pick_ws<MODE, 3, R>(nslot); threads = kWsThreads; break;
+        case 14: fn = pick_ws<MODE, 4, R>(nslot); threads = kWsThreads; break;
         case 1: fn = pick_nslot<MODE, 1, R>(nslot); break;
         case 2: fn = pick_nslot<MODE, 2, R>(nslot); break;
         case 3: fn = pick_nslot<MODE, 3, R>(nslot); break;
@@ -865,7 +1110,7 @@ int launch_mode(int stages, int nslot, const KArgs &a, void *stream) {
     if (!fn) return (int)hipErrorInvalidValue;
     KArgs copy = a;
     void *args[] = {&copy};
-    return (int)hipLaunchKernel((const void *)fn, dim3(a.grid), dim3(kThreads), args, 0, (hipStream_t)stream);
+    return (int)hipLaunchKernel((const void *)fn, dim3(a.grid), dim3(threads), args, 0, (hipStream_t)stream);
 }
 
 }  // namespace

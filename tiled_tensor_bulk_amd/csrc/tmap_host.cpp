@@ -127,7 +127,15 @@ tmap_status plan_launch(const MapImpl &m, int64_t n_tiles, const tmap_launch_opt
     if (stages < 1 || stages > 4)
         return fail(TMAP_ERROR_INVALID_VALUE, "stages must be 1..4 (got %d)", stages);
     const bool thread_copy = opts && (opts->flags & TMAP_FLAG_THREAD_COPY);
+    const bool producer_wave = opts && (opts->flags & TMAP_FLAG_PRODUCER_WAVE);
+    if (thread_copy && producer_wave)
+        return fail(TMAP_ERROR_INVALID_VALUE, "thread-copy and producer-wave modes exclude each other");
     if (thread_copy) stages = 1;  // one LDS stage; the next tile waits in registers
+    if (producer_wave) {
+        if (nslot > 8)
+            return fail(TMAP_ERROR_INVALID_VALUE, "producer-wave mode needs boxes of at most 32 KiB");
+        if (stages < 2) stages = 2;
+    }
     const uint32_t lds = tmap::variant_lds_bytes(stages, nslot);
     if (lds > dev.lds_per_cu || (nslot == 16 && stages > 2))
         return fail(TMAP_ERROR_INVALID_VALUE, "%d stages of %u bytes do not fit in LDS", stages,
@@ -156,7 +164,7 @@ tmap_status plan_launch(const MapImpl &m, int64_t n_tiles, const tmap_launch_opt
     const int64_t useful = contiguous ? n_tiles : (n_tiles + group - 1) / group;
     if ((int64_t)grid > useful) grid = (uint32_t)useful;
     pl.nslot = nslot;
-    pl.stages = thread_copy ? 0 : stages;
+    pl.stages = thread_copy ? 0 : (producer_wave ? 10 + stages : stages);
     pl.grid = grid;
     pl.group = group;
     return TMAP_SUCCESS;

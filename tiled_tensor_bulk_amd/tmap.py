@@ -19,6 +19,7 @@ SUCCESS, INVALID_VALUE, UNSUPPORTED_DEVICE, LAUNCH, TIMEOUT = 0, 1, 2, 3, 4
 FLAG_CONTIGUOUS = 0x1
 FLAG_NONTEMPORAL = 0x2
 FLAG_THREAD_COPY = 0x4
+FLAG_PRODUCER_WAVE = 0x8
 FLAG_INJECT_BUDGET_MISMATCH = 0x100
 
 DTYPES = {"u8": 0, "i8": 1, "u16": 2, "f16": 3, "bf16": 4, "u32": 5, "i32": 6, "f32": 7,
