@@ -99,7 +99,8 @@ def main():
     inb = T.tmap_inbounds_elems(ms, coords_np, n) * es
     if args.flags < 0:
         args.flags = T.FLAG_NONTEMPORAL if w.alloc_bytes > (256 << 20) else 0
-    opts = dict(stages=args.stages or w.stages, grid_wgs=args.grid, flags=args.flags, group=args.group)
+    # 0 = the library's default for stages, grid and group
+    opts = dict(stages=args.stages, grid_wgs=args.grid, flags=args.flags, group=args.group)
 
     dst = packed = None
     if args.op == "bulk":
@@ -140,6 +141,12 @@ def main():
 
         def launch():
             T.tmap_store_tiles(md, coords, n, packed, **opts)
+
+    if args.op == "bulk":
+        schedule = "whole boxes (rank-1 16 KiB tiles)"
+    else:
+        band = T.tmap_band_boxes(ms, None if args.op in ("load", "store") else md, coords is not None, args.flags)
+        schedule = f"band: {band} boxes x 16 rows per stage" if band else "whole boxes"
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -196,7 +203,8 @@ def main():
         "data": "synthetic (seeded on device, torch Philox)",
         "config": {"workload": w.name, "op": args.op, "dims": list(w.dims), "strides": list(w.strides),
                    "box": list(w.box), "swizzle": list(w.swizzle), "tiles": n, "box_bytes": bb,
-                   "stages": opts["stages"], "grid_wgs": args.grid or "auto", "flags": args.flags,
+                   "schedule": schedule, "stages": args.stages or "auto", "grid_wgs": args.grid or "auto",
+                   "flags": args.flags,
                    "group": args.group or "auto",
                    "algorithmic_bytes_per_step": algo_bytes},
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBPS, 2),

@@ -74,14 +74,30 @@ typedef struct tmap_swizzle {
 /* Launch options; pass NULL for the defaults.  Any field left 0 takes its
  * default. */
 typedef struct tmap_launch_opts {
-    uint32_t stages;      /* LDS ring depth 1..4 (default: 4, or 2 for boxes over 32 KiB) */
-    uint32_t grid_wgs;    /* workgroups of the persistent grid (default: fill every CU)    */
+    uint32_t stages;      /* LDS ring depth 1..4 (default 2)                               */
+    uint32_t grid_wgs;    /* workgroups launched; fewer than there are groups makes each
+                             take several (default: one workgroup per group; with
+                             TMAP_FLAG_CONTIGUOUS, twice what fits in LDS per CU)         */
     uint32_t flags;       /* TMAP_FLAG_* bits                                              */
     uint32_t spin_limit;  /* readiness-wait polls before TMAP_ERROR_TIMEOUT (default 2^22) */
-    uint32_t group;       /* tiles dealt to a workgroup at a time, a power of two <= 64
-                             (default: enough boxes side by side to span 512 bytes of a
-                             row, at most 8)                                               */
+    uint32_t group;       /* tiles (band units) dealt to a workgroup at a time, a power of
+                             two <= 64 (default: enough boxes side by side to span 512
+                             bytes of a row, at most 8; band units: 2 for a round trip,
+                             1 for a load or store)                                       */
 } tmap_launch_opts;
+
+/* Band schedule.  A sweep (coords == NULL) of boxes whose rows hold 64 to
+ * 512 bytes, whose dimension-1 extent is 16 times a power of two and whose
+ * higher extents are 1 runs on it unless TMAP_FLAG_WHOLE_BOX, thread-copy or
+ * producer-wave mode is asked for.  A stage then holds the same 16-row band
+ * of the neighbouring boxes that together span 1 KiB of a row (a "unit"),
+ * each box's band being the contiguous piece of that box's swizzled LDS
+ * image that it always is; the swizzle must map each band onto itself
+ * (16 * box[0] a multiple of 2^(m+s+b)) and a row of the sweep must hold a
+ * whole unit.  Every box still passes through LDS in its own layout and the
+ * results are the same; the tensor is read and written 1 KiB wide and 16
+ * rows tall at a time, which HBM serves faster than narrow rows of tall
+ * boxes.  A stage's byte record counts the unit's 16 KiB. */
 
 /* Tile order: tile index t runs innermost-fastest over the sweep (or over the
  * coords array).  By default the tiles are dealt in groups of `group`
@@ -103,6 +119,9 @@ typedef struct tmap_launch_opts {
  * record ("GPU TMA", "Warp specialization").  Same results.  Needs boxes of
  * at most 32 KiB; `stages` 1 is taken as 2. */
 #define TMAP_FLAG_PRODUCER_WAVE 0x8u
+/* One whole box per stage even where the band schedule applies (for A/B
+ * runs, and for a consumer that needs a box's full LDS image at once). */
+#define TMAP_FLAG_WHOLE_BOX 0x10u
 /* Test hook: every wave announces 16 bytes more than it delivers, so a
  * stage never becomes ready and the bounded wait must end the kernel with
  * TMAP_ERROR_TIMEOUT ("Day 76", "Pitfalls": a byte budget that does not match
@@ -240,6 +259,15 @@ int64_t tmap_sweep_tiles(const tmap_t *map);
  * arguments. */
 tmap_status tmap_inbounds_elems(const tmap_t *map, const int32_t *host_coords,
                                 int64_t n_tiles, uint64_t *out_elems);
+
+/* Schedule a copy would take (host only, no device needed): the boxes per
+ * stage on the band schedule described at tmap_launch_opts, or 0 when every
+ * stage holds one whole box.  src is the swept map of a load or round trip
+ * (of a store: the destination map), dst the round trip's destination map or
+ * NULL; coords is non-NULL for explicit corners (any non-NULL pointer: it is
+ * not read); flags are the TMAP_FLAG_* bits the copy would get.  0 for a
+ * map never encoded. */
+uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *coords, uint32_t flags);
 
 /* Decoded fields of an encoded map (for inspection and tests). */
 typedef struct tmap_info {

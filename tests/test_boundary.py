@@ -185,3 +185,60 @@ def test_launch_without_gpu_is_unsupported_device():
 def test_status_strings():
     assert T.tmap_status_string(0) == "TMAP_SUCCESS"
     assert T.tmap_status_string(4) == "TMAP_ERROR_TIMEOUT"
+
+
+def _enc_rows(dt, dims, box, swz=(0, 0, 0), pad_rows=0):
+    """A map over a densely packed tensor (rows padded to 16 bytes)."""
+    es = {"u8": 1, "f16": 2, "bf16": 2, "f32": 4, "f64": 8, "u64": 8}[dt]
+    strides, s = [], -(-dims[0] * es // 16) * 16 + 16 * pad_rows
+    for d in range(1, len(dims)):
+        strides.append(s)
+        s *= dims[d]
+    return T.tmap_encode(dt, len(dims), BASE, dims, strides, box, None, swz)
+
+
+def test_band_schedule_choice():
+    """Which sweeps take the band schedule: boxes with 64..512-byte rows and a
+    dimension-1 extent of 16 times a power of two, swizzles whose period fits
+    a 16-row band, a row of the sweep holding a whole unit, sweeps only, and
+    not in the thread-copy, producer-wave or whole-box modes."""
+    W = inputs.WORKLOADS
+    for name, want in [("sweep2g_u8", 8), ("ragged_bf16", 8), ("strips_f16", 2), ("plus1_f32", 4),
+                       ("tile64_f32", 0), ("pad5d_f32", 0)]:
+        w = W[name]
+        m = T.tmap_encode(w.dtype, w.rank, BASE, w.dims, w.strides, w.box, None, w.swizzle)
+        assert T.tmap_band_boxes(m) == want, name
+        for fl in (T.FLAG_WHOLE_BOX, T.FLAG_THREAD_COPY, T.FLAG_PRODUCER_WAVE):
+            assert T.tmap_band_boxes(m, flags=fl) == 0
+        assert T.tmap_band_boxes(m, flags=T.FLAG_NONTEMPORAL | T.FLAG_CONTIGUOUS) == want
+        assert T.tmap_band_boxes(m, explicit_coords=True) == 0
+        assert T.tmap_band_boxes(m, m) == want
+    # row width: 64..512 bytes, 1 KiB of row per unit
+    for dt, box0, want in [("u8", 32, 0), ("u8", 64, 16), ("u8", 128, 8), ("u8", 256, 4), ("f16", 256, 2),
+                           ("f32", 128, 2), ("f32", 256, 0), ("f64", 8, 16), ("f64", 64, 2), ("f32", 24, 0)]:
+        assert T.tmap_band_boxes(_enc_rows(dt, [box0 * 20, 100], [box0, 16])) == want, (dt, box0)
+    # dimension-1 extent
+    for box1, want in [(8, 0), (16, 8), (24, 0), (32, 8), (48, 0), (64, 8), (128, 8)]:
+        assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, box1])) == want, box1
+    # swizzle period 2^(m+s+b) elements must divide a band of 16 * 128 elements
+    for swz, want in [((3, 4, 3), 8), ((0, 4, 3), 8), ((3, 4, 4), 8), ((2, 4, 5), 8), ((3, 4, 5), 0), ((1, 4, 7), 0)]:
+        assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128], swz)) == want, swz
+    # a swizzle that moves bytes inside 16-byte chunks takes the element path
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128], (3, 0, 3))) == 0
+    # a row of the sweep must hold one whole unit (8 boxes of 128 bytes)
+    assert T.tmap_band_boxes(_enc_rows("u8", [7 * 128, 64], [128, 16])) == 0
+    assert T.tmap_band_boxes(_enc_rows("u8", [7 * 128 + 1, 64], [128, 16])) == 8
+    # higher box extents must be 1
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 1])) == 8
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 2])) == 0
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096], [128])) == 0
+    # a unit must stay within 2^31 bytes of its corner, in both maps: with
+    # this stride a 128x16 box spans 128 + 15 * stride < 2^31 bytes (a valid
+    # map) but a unit 1 KiB wide does not
+    stride = 143165552
+    assert 128 + 15 * stride < 2**31 <= 1024 + 15 * stride
+    far = T.tmap_encode("u8", 2, BASE, [4096, 20], [stride], [128, 16])
+    assert T.tmap_band_boxes(far) == 0
+    near = _enc_rows("u8", [4096, 20], [128, 16])
+    assert T.tmap_band_boxes(near) == 8 and T.tmap_band_boxes(near, far) == 0
+    assert T.tmap_band_boxes(T.tmap_t()) == 0

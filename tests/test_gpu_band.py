@@ -1,0 +1,184 @@
+"""GPU parity of the band schedule (sweeps of narrow boxes staged as 16-row
+bands of neighbouring boxes) against the CPU oracle, byte for byte.
+
+Seeded random maps that take the band schedule (the host query says so for
+every case): element sizes 1..8, box rows of 64..512 bytes, dimension-1
+extents 16..128, ranks 2..5 with higher box extents 1, swizzles whose period
+fits a band, ragged last rows and columns, and rows of the sweep whose last
+unit holds fewer boxes than a full one.  Each case loads, stores and round
+trips (into a destination map of another size and pitch, so that the boxes
+missing from a short last unit would land inside it if they were stored),
+and fp32 cases also run the fused +addend round trip.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import Map
+from tiled_tensor_bulk_amd import inputs
+from tiled_tensor_bulk_amd import tmap as T
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+DEV = "cuda:0"
+DT = {1: "u8", 2: "f16", 4: "f32", 8: "f64"}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_ok():
+    st = T.tmap_sync_status()
+    assert st == T.SUCCESS, T.tmap_status_string(st)
+
+
+def dev_bytes(nbytes, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    n8 = (nbytes + 7) // 8
+    x = torch.randint(-(2**63), 2**63 - 1, (n8,), dtype=torch.int64, generator=g, device=DEV)
+    return x.view(torch.uint8)[:nbytes].contiguous()
+
+
+def first_mismatch(a, b):
+    idx = np.flatnonzero(a != b)
+    return None if idx.size == 0 else f"byte {int(idx[0])}: got {a[idx[0]]:#x} want {b[idx[0]]:#x}; {idx.size} differ"
+
+
+def _strides(rng, dims, es):
+    row = -(-dims[0] * es // 16) * 16 + 16 * int(rng.integers(0, 3))
+    out, s = [], row
+    for d in range(1, len(dims)):
+        out.append(s)
+        s *= dims[d]
+    return out, s
+
+
+def _swizzle(rng, es, box0, box1):
+    n_el = box0 * box1
+    k_el = 16 // es
+    for _ in range(20):
+        b = int(rng.integers(0, 4))
+        if b == 0:
+            return (0, 0, 0)
+        m = int(rng.integers(k_el.bit_length() - 1, 5))
+        s = int(rng.integers(b, 6))
+        if (n_el % (1 << (m + b)) == 0 and (16 * box0) % (1 << (m + s + b)) == 0 and b + m + s <= 20):
+            return (b, m, s)
+    return (0, 0, 0)
+
+
+def _band_case(rng):
+    while True:
+        es = int(rng.choice([1, 2, 4, 8]))
+        rc = int(rng.choice([4, 8, 16, 32]))     # 16-byte chunks per box row
+        box0 = rc * 16 // es
+        if box0 <= 256:
+            break
+    g = 64 // rc
+    box1 = int(rng.choice([16, 32, 64, 128]))
+    while box0 * es * box1 > 65536:
+        box1 //= 2
+    rank = int(rng.choice([2, 2, 2, 3, 4, 5]))
+    tiles0 = int(rng.integers(g, 3 * g + 3))
+    dims0 = tiles0 * box0 - int(rng.integers(0, box0))
+    dims1 = int(rng.integers(1, (3 if rank == 2 else 2) * box1 + 2))
+    dims = [dims0, dims1] + [int(rng.integers(1, 3)) for _ in range(rank - 2)]
+    box = [box0, box1] + [1] * (rank - 2)
+    return es, dims, box, _swizzle(rng, es, box0, box1)
+
+
+def _opts(rng):
+    return dict(stages=int(rng.integers(1, 5)), grid_wgs=int(rng.choice([0, 0, 1, 3, 7])),
+                group=int(rng.choice([0, 1, 2, 4, 8])),
+                flags=int(rng.choice([0, T.FLAG_NONTEMPORAL, T.FLAG_CONTIGUOUS])))
+
+
+@pytest.mark.parametrize("chunk", range(3))
+def test_band_schedule_random_sweeps(chunk):
+    rng = np.random.default_rng(7100 + chunk)
+    for i in range(24):
+        es, dims, box, swz = _band_case(rng)
+        strides, alloc = _strides(rng, dims, es)
+        opts = _opts(rng)
+        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+        src = dev_bytes(alloc, int(rng.integers(1 << 30)))
+        m = T.tmap_encode(DT[es], len(dims), src.data_ptr(), dims, strides, box, None, swz)
+        g = T.tmap_band_boxes(m, None, False, opts["flags"])
+        say(f"band {chunk}/{i}: es={es} dims={dims} strides={strides} box={box} swz={swz} boxes/unit={g} {opts}")
+        assert g == 64 // (box[0] * es // 16)
+        n = T.tmap_sweep_tiles(m)
+        bb = T.tmap_box_bytes(m)
+        host = src.cpu().numpy()
+        # load
+        packed = torch.empty(n * bb, dtype=torch.uint8, device=DEV)
+        T.tmap_load_tiles(m, None, n, packed, **opts)
+        check_ok()
+        want = oracle.load_tiles(om, host, None, n)
+        assert (mm := first_mismatch(packed.cpu().numpy(), want, )) is None, ("load", mm)
+        # store of random images into a sentinel-filled tensor
+        imgs = dev_bytes(n * bb, int(rng.integers(1 << 30)))
+        dst = dev_bytes(alloc, int(rng.integers(1 << 30)))
+        want_dst = dst.cpu().numpy().copy()
+        T.tmap_store_tiles(T.tmap_encode(DT[es], len(dims), dst.data_ptr(), dims, strides, box, None, swz),
+                           None, n, imgs, **opts)
+        check_ok()
+        oracle.store_tiles(om, want_dst, None, n, imgs.cpu().numpy())
+        assert (mm := first_mismatch(dst.cpu().numpy(), want_dst)) is None, ("store", mm)
+        # round trip into a destination of another size and pitch
+        ddims = [max(1, d + int(rng.integers(-b // 2, 2 * b + 1))) for d, b in zip(dims, box)]
+        dstrides, dalloc = _strides(rng, ddims, es)
+        dst2 = dev_bytes(dalloc, int(rng.integers(1 << 30)))
+        want2 = dst2.cpu().numpy().copy()
+        md = T.tmap_encode(DT[es], len(dims), dst2.data_ptr(), ddims, dstrides, box, None, swz)
+        assert T.tmap_band_boxes(m, md, False, opts["flags"]) == g
+        T.tmap_roundtrip(m, md, None, n, **opts)
+        check_ok()
+        omd = Map(es=es, dims=ddims, strides=dstrides, box=box, swizzle=swz)
+        oracle.roundtrip(om, host, omd, want2, None, n)
+        assert (mm := first_mismatch(dst2.cpu().numpy(), want2)) is None, ("roundtrip", ddims, mm)
+        if es == 4:
+            dst3 = dev_bytes(dalloc, int(rng.integers(1 << 30)))
+            want3 = dst3.cpu().numpy().copy()
+            md3 = T.tmap_encode("f32", len(dims), dst3.data_ptr(), ddims, dstrides, box, None, swz)
+            T.tmap_roundtrip_add_f32(m, md3, None, n, 1.0, **opts)
+            check_ok()
+            oracle.roundtrip_add_f32(om, host, omd, want3, None, n, 1.0)
+            got3 = dst3.cpu().numpy()
+            nan = np.isnan(want3.view(np.float32))
+            w32, g32 = want3.view(np.uint32), got3.view(np.uint32)
+            assert np.array_equal(g32[~nan], w32[~nan]), "roundtrip +1.0f"
+            assert np.all(np.isnan(got3.view(np.float32)[nan]))
+
+
+def test_band_and_whole_box_agree_on_a_short_last_unit():
+    """1200 x 50 bytes in 128 x 16 boxes: 10 boxes to a row of the sweep, so
+    the second unit of each row holds 2 boxes of 8 (the last one 48 bytes
+    wide), and the last band of the sweep is partial; the destination is
+    2048 bytes wide, so the unit's 6 missing boxes would be visible."""
+    say("band vs whole box: short last unit")
+    assert -(-1200 // 128) % 8 == 2
+    src = dev_bytes(1200 * 50, 5)
+    dst_a = dev_bytes(2048 * 64, 6)
+    dst_b = dst_a.clone()
+    ms = T.tmap_encode("u8", 2, src.data_ptr(), [1200, 50], [1200], [128, 16], None, (3, 4, 3))
+    n = T.tmap_sweep_tiles(ms)
+    for dst in (dst_a, dst_b):
+        md = T.tmap_encode("u8", 2, dst.data_ptr(), [2048, 64], [2048], [128, 16], None, (3, 4, 3))
+        T.tmap_roundtrip(ms, md, None, n, flags=0 if dst is dst_a else T.FLAG_WHOLE_BOX)
+        check_ok()
+    assert T.tmap_band_boxes(ms, md) == 8
+    assert torch.equal(dst_a, dst_b)
+    want = dev_bytes(2048 * 64, 6).cpu().numpy()
+    om = Map(es=1, dims=[1200, 50], strides=[1200], box=[128, 16], swizzle=(3, 4, 3))
+    omd = Map(es=1, dims=[2048, 64], strides=[2048], box=[128, 16], swizzle=(3, 4, 3))
+    oracle.roundtrip(om, src.cpu().numpy(), omd, want, None, n)
+    assert (mm := first_mismatch(dst_a.cpu().numpy(), want)) is None, mm

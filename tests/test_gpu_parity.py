@@ -127,12 +127,12 @@ def _sample_tiles(n, extra, k, seed):
 
 def test_ragged_bf16_full_size_sampled():
     w = inputs.WORKLOADS["ragged_bf16"]
-    say("ragged_bf16: load sweep 65280 tiles, 4 stages; sampled oracle; store back")
+    say("ragged_bf16: load sweep 65280 tiles (the benchmark's launch); sampled oracle; store back")
     src = inputs.device_bytes(w, DEV)
     m = enc("bf16", src, w.dims, w.strides, w.box, w.swizzle)
     n = T.tmap_sweep_tiles(m)
     assert n == 65280
-    packed = gpu_load(m, None, n, stages=4)
+    packed = gpu_load(m, None, n, flags=T.FLAG_NONTEMPORAL)
     om = Map(es=2, dims=w.dims, strides=w.strides, box=w.box, swizzle=w.swizzle)
     last_row = list(range(n - 255, n))                       # the ragged strip (63 rows + 1 zero row)
     tiles = _sample_tiles(n, last_row + [0, 254, 255], 600, 33)
@@ -144,47 +144,51 @@ def test_ragged_bf16_full_size_sampled():
     # the zero-filled row of every ragged tile: last 64 columns x 2 bytes of each image
     # closed form: storing every image back restores every byte of the tensor
     dst = dev_tensor(w.alloc_bytes, fill_seed=303)
-    T.tmap_store_tiles(enc("bf16", dst, w.dims, w.strides, w.box, w.swizzle), None, n, packed, stages=4)
+    T.tmap_store_tiles(enc("bf16", dst, w.dims, w.strides, w.box, w.swizzle), None, n, packed,
+                       flags=T.FLAG_NONTEMPORAL)
     check_ok()
     assert torch.equal(dst, src)
 
 
 def test_pad5d_f32_random_corners_full():
     w = inputs.WORKLOADS["pad5d_f32"]
-    say("pad5d_f32: load 1e5 random corners, 4 stages, full oracle; then store")
+    say("pad5d_f32: load 1e5 random corners (the benchmark's launch), full oracle; then store")
     src = inputs.device_bytes(w, DEV)
     host = src.cpu().numpy()
     coords = inputs.random_corners(w.dims, w.box, w.n_random, seed=40)
     m = enc("f32", src, w.dims, w.strides, w.box)
     om = Map(es=4, dims=w.dims, strides=w.strides, box=w.box)
-    packed = gpu_load(m, coords, len(coords), stages=4)
+    packed = gpu_load(m, coords, len(coords))
     want = oracle.load_tiles(om, host, coords, len(coords))
     got = packed.cpu().numpy()
     assert (mm := first_mismatch(got, want, 8192)) is None, mm
     dst = dev_tensor(w.alloc_bytes, fill_seed=41)
     want_dst = dst.cpu().numpy().copy()
     c = torch.from_numpy(coords).to(DEV)
-    T.tmap_store_tiles(enc("f32", dst, w.dims, w.strides, w.box), c, len(coords), packed, stages=4)
+    T.tmap_store_tiles(enc("f32", dst, w.dims, w.strides, w.box), c, len(coords), packed)
     check_ok()
     oracle.store_tiles(om, want_dst, coords, len(coords), want)
     got_dst = dst.cpu().numpy()
     assert (mm := first_mismatch(got_dst, want_dst, 1 << 30)) is None, mm
 
 
-def test_sweep2g_u8_full_size():
+@pytest.mark.parametrize("opts", [dict(flags=T.FLAG_NONTEMPORAL),
+                                  dict(stages=4, flags=T.FLAG_NONTEMPORAL | T.FLAG_WHOLE_BOX)],
+                         ids=["benchmark_launch", "whole_box_4_stages"])
+def test_sweep2g_u8_full_size(opts):
     w = inputs.WORKLOADS["sweep2g_u8"]
-    say("sweep2g_u8: roundtrip 131072 tiles (2 GiB), 4 stages; load sampled vs oracle; store")
+    say(f"sweep2g_u8: roundtrip 131072 tiles (2 GiB) {opts}; load sampled vs oracle; store")
     src = inputs.device_bytes(w, DEV)
     ms = enc("u8", src, w.dims, w.strides, w.box, w.swizzle)
     n = T.tmap_sweep_tiles(ms)
     assert n == 131072
     dst = dev_tensor(w.alloc_bytes)
     dst.fill_(0xA5)
-    T.tmap_roundtrip(ms, enc("u8", dst, w.dims, w.strides, w.box, w.swizzle), None, n, stages=4)
+    T.tmap_roundtrip(ms, enc("u8", dst, w.dims, w.strides, w.box, w.swizzle), None, n, **opts)
     check_ok()
     assert torch.equal(dst, src)                              # exact tiling: identity
     del dst
-    packed = gpu_load(ms, None, n, stages=4)
+    packed = gpu_load(ms, None, n, **opts)
     om = Map(es=1, dims=w.dims, strides=w.strides, box=w.box, swizzle=w.swizzle)
     tiles = _sample_tiles(n, [0, 1, 511, 512, n - 1], 300, 55)
     corners = np.array([oracle.sweep_coords(om, int(t)) for t in tiles], np.int32)
@@ -195,7 +199,7 @@ def test_sweep2g_u8_full_size():
     del host
     dst2 = dev_tensor(w.alloc_bytes)
     dst2.fill_(0x5A)
-    T.tmap_store_tiles(enc("u8", dst2, w.dims, w.strides, w.box, w.swizzle), None, n, packed, stages=4)
+    T.tmap_store_tiles(enc("u8", dst2, w.dims, w.strides, w.box, w.swizzle), None, n, packed, **opts)
     check_ok()
     assert torch.equal(dst2, src)
 
@@ -338,14 +342,16 @@ def test_repeat_is_deterministic():
         assert torch.equal(a, b), st
 
 
-@pytest.mark.parametrize("mode", ["thread_copy", "producer_wave"])
+@pytest.mark.parametrize("mode", ["thread_copy", "producer_wave", "whole_box"])
 @pytest.mark.parametrize("name", ["tile64_f32", "strips_f16", "ragged_bf16", "pad5d_f32", "sweep2g_u8"])
 def test_other_modes_match_the_staged_copy(name, mode):
-    """The register-path and producer-wave variants give the same bytes as the
-    cooperative direct-to-LDS ring (which the tests above pin to the oracle)
-    for load, store and round trip of every workload."""
+    """The register-path and producer-wave variants, and the ring on whole
+    boxes, give the same bytes as the default schedule (which the tests above
+    pin to the oracle; the band schedule where it applies) for load, store
+    and round trip of every workload."""
     w = inputs.WORKLOADS[name]
-    flag = T.FLAG_THREAD_COPY if mode == "thread_copy" else T.FLAG_PRODUCER_WAVE
+    flag = {"thread_copy": T.FLAG_THREAD_COPY, "producer_wave": T.FLAG_PRODUCER_WAVE,
+            "whole_box": T.FLAG_WHOLE_BOX}[mode]
     say(f"{mode} vs staged: {name}")
     src = inputs.device_bytes(w, DEV)
     m = enc(w.dtype, src, w.dims, w.strides, w.box, w.swizzle)

@@ -163,13 +163,15 @@ struct Win {
     uint32_t hi[R];
 };
 
-template <int R>
-__device__ __forceinline__ Win<R> window(const KMap &m, const int32_t c[R]) {
+// ext: the extent of the region at corner c per dimension (a box, or a unit
+// of the band schedule).
+template <int R, typename E>
+__device__ __forceinline__ Win<R> window_ext(const KMap &m, const int32_t c[R], const E *ext) {
     Win<R> w;
 #pragma unroll
     for (int d = 0; d < R; ++d) {
         const int64_t cd = c[d];
-        const int64_t b = m.box[d];
+        const int64_t b = ext[d];
         int64_t lo = -cd;
         lo = lo < 0 ? 0 : (lo > b ? b : lo);
         int64_t hi = (int64_t)m.dims[d] - cd;
@@ -178,6 +180,11 @@ __device__ __forceinline__ Win<R> window(const KMap &m, const int32_t c[R]) {
         w.hi[d] = (uint32_t)hi;
     }
     return w;
+}
+
+template <int R>
+__device__ __forceinline__ Win<R> window(const KMap &m, const int32_t c[R]) {
+    return window_ext<R>(m, c, m.box);
 }
 
 // Packed box indices of a chunk: w0 = x0 | i1 << 16, w1 = i2 | i3 << 8 | i4 << 16,
@@ -420,8 +427,11 @@ __device__ __forceinline__ uint32_t logical_chunk_of(const KArgs &a, uint32_t p,
 }
 
 // ---------------------------------------------------------------- the kernel
-template <int MODE, int S, int NSLOT, int R>
+// BAND: the stage holds one unit of the band schedule (see KArgs) instead of
+// one box.
+template <int MODE, int S, int NSLOT, int R, bool BAND = false>
 struct Copier {
+    static_assert(!BAND || NSLOT == kBandSlots, "a band stage is 16 KiB");
     const KArgs &a;
     uint32_t lane, wave, my_bytes, parity;
     uint32_t edge;  // bit X: the tile in stage X needs the element path when it lands
@@ -447,6 +457,109 @@ struct Copier {
 
     __device__ __forceinline__ uint32_t logical_chunk(uint32_t p, const KMap &m) const {
         return logical_chunk_of(a, p, m);
+    }
+
+    // Region offset and packed indices of the chunk in stage slot p.  In the
+    // band schedule, slot p is chunk l = p mod (band chunks) of the band of
+    // the unit's box g = p / (band chunks); the swizzle maps every band of a
+    // box onto itself the same way (a band is a whole number of swizzle
+    // periods), so l's logical chunk is found as in band 0 and the box's
+    // place in the unit is added in dimension 0.
+    __device__ __forceinline__ void slot_info(uint32_t p, const KMap &m, uint32_t &off, uint32_t &w0,
+                                              uint32_t &w1) const {
+        if constexpr (BAND) {
+            const uint32_t g = p >> a.band_lbc;
+            chunk_info(logical_chunk(p & ((1u << a.band_lbc) - 1u), m), m, off, w0, w1);
+            const uint32_t x = g * (uint32_t)m.box[0];
+            off += x * m.elem_size;
+            w0 += x;  // dimension-0 index field: below 2^16
+        } else {
+            chunk_info(logical_chunk(p, m), m, off, w0, w1);
+        }
+    }
+
+    // Offset of slot p's chunk in the packed images, from the unit's base.
+    __device__ __forceinline__ uint32_t slot_packed(uint32_t p, uint32_t bb) const {
+        if constexpr (BAND)
+            return (p >> a.band_lbc) * bb + (p & ((1u << a.band_lbc) - 1u)) * 16u;
+        else
+            return p * 16u;
+    }
+
+    // Corner of the region (box or unit) under cursor cur.
+    __device__ __forceinline__ void corner(const Cursor<R> &cur, int32_t c[R]) const {
+        if constexpr (BAND) {
+#pragma unroll
+            for (int d = 0; d < R; ++d) c[d] = (int32_t)(cur.dig[d] * a.ubox[d]);
+        } else {
+            cursor_corner<R>(a, swept(), cur, c);
+        }
+    }
+
+    // Boxes of the unit under cur that exist (the last unit of a row of the
+    // sweep can reach past its last box); 1 without the band schedule.
+    __device__ __forceinline__ uint32_t unit_boxes(const Cursor<R> &cur) const {
+        if constexpr (BAND) {
+            const uint32_t left = a.tiles[0] - cur.dig[0] * a.band_g;
+            return left < a.band_g ? left : a.band_g;
+        } else {
+            return 1u;
+        }
+    }
+
+    // Buffer resource over the packed images of the region under cur: the
+    // box's image, or the unit's bands (records end after the last existing
+    // box's band, so chunks of missing boxes read zero and are not written).
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t packed_rsrc(const Cursor<R> &cur, uint32_t bb) const {
+        if constexpr (BAND) {
+            uint64_t t = 0;
+#pragma unroll
+            for (int d = R - 1; d >= 1; --d) t = t * a.tiles[d] + (d == 1 ? (cur.dig[1] >> a.band_lnb) : cur.dig[d]);
+            t = t * a.tiles[0] + (uint64_t)cur.dig[0] * a.band_g;
+            const uint32_t j = cur.dig[1] & ((1u << a.band_lnb) - 1u);
+            const uint64_t base = (uint64_t)a.packed + t * bb + (uint64_t)j * a.band_bytes;
+            return make_rsrc(base, (unit_boxes(cur) - 1u) * bb + a.band_bytes);
+        } else {
+            return make_rsrc((uint64_t)a.packed + (uint64_t)cur.t * bb, bb);
+        }
+    }
+
+    // Whether the region at corner c lies inside map m: the whole box, or the
+    // first `boxes` boxes of a unit (a short last unit of a row is inside
+    // when its existing boxes are).
+    __device__ __forceinline__ bool inside_map(const KMap &m, const int32_t c[R], const Place &pl,
+                                               uint32_t boxes) const {
+        if constexpr (BAND) {
+            bool in = (c[0] >= 0) & ((int64_t)c[0] + (int64_t)boxes * m.box[0] <= (int64_t)m.dims[0]);
+#pragma unroll
+            for (int d = 1; d < R; ++d) in = in & (c[d] >= 0) & (c[d] <= m.lim[d]);
+            return in;
+        } else {
+            return pl.interior;
+        }
+    }
+
+    // Whether stage slot p belongs to one of the first `boxes` boxes of the
+    // unit (always, for whole boxes).
+    __device__ __forceinline__ bool slot_present(uint32_t p, uint32_t boxes) const {
+        if constexpr (BAND)
+            return (p >> a.band_lbc) < boxes;
+        else
+            return true;
+    }
+
+    // Window of the region at corner c in map m, limited to the first `boxes`
+    // boxes of a unit.
+    __device__ __forceinline__ Win<R> win(const KMap &m, const int32_t c[R], uint32_t boxes) const {
+        if constexpr (BAND) {
+            Win<R> w = window_ext<R>(m, c, a.ubox);
+            const uint32_t cap = boxes * (uint32_t)m.box[0];
+            w.hi[0] = w.hi[0] < cap ? w.hi[0] : cap;
+            w.lo[0] = w.lo[0] < w.hi[0] ? w.lo[0] : w.hi[0];
+            return w;
+        } else {
+            return window<R>(m, c);
+        }
     }
 
     // vwave >= 0 makes this lane act as wave vwave of a 4-wave workgroup
@@ -488,11 +601,13 @@ struct Copier {
             cslot[j] = ((uint32_t)(j * kWaves) + cw) * 64u + lane;
             poff[j] = pw0[j] = pw1[j] = 0;
             coff[j] = cw0[j] = cw1[j] = 0;
+            // the packed side of a copy reads / writes the slots' image
+            // offsets; the tensor side their region offsets
+            if (MODE == kStore) poff[j] = slot_packed(pslot[j], a.dst.box_bytes);
+            if (MODE == kLoad) coff[j] = slot_packed(cslot[j], a.src.box_bytes);
             if (!a.elemwise) {
-                if (MODE != kStore && pslot[j] < a.n_chunks)
-                    chunk_info(logical_chunk(pslot[j], a.src), a.src, poff[j], pw0[j], pw1[j]);
-                if (MODE != kLoad && cslot[j] < a.n_chunks)
-                    chunk_info(logical_chunk(cslot[j], a.dst), a.dst, coff[j], cw0[j], cw1[j]);
+                if (MODE != kStore && pslot[j] < a.n_chunks) slot_info(pslot[j], a.src, poff[j], pw0[j], pw1[j]);
+                if (MODE != kLoad && cslot[j] < a.n_chunks) slot_info(cslot[j], a.dst, coff[j], cw0[j], cw1[j]);
             }
         }
     }
@@ -513,22 +628,25 @@ struct Copier {
         const uint32_t budget = my_bytes + ((a.flags & TMAP_FLAG_INJECT_BUDGET_MISMATCH) ? 16u : 0u);
         bar_arrive_expect(bar, budget, lane);
         if (MODE == kStore) {
-            const uint64_t bb = a.dst.box_bytes;
-            const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)fcur.t * bb, (uint32_t)bb);
+            const __amdgpu_buffer_rsrc_t r = packed_rsrc(fcur, a.dst.box_bytes);
 #pragma unroll
-            for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? pslot[j] * 16u : kOob);
+            for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? poff[j] : kOob);
         } else {
             int32_t c[R];
-            cursor_corner<R>(a, a.src, fcur, c);
+            corner(fcur, c);
             const Place pl = place<R>(a.src, c);
             const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
-            const bool fast = pl.interior && !a.elemwise;
+            const uint32_t boxes = unit_boxes(fcur);
+            const bool fast = inside_map(a.src, c, pl, boxes) && !a.elemwise;
             edge = fast ? (edge & ~(1u << XF)) : (edge | (1u << XF));
             if (fast) {
 #pragma unroll
-                for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? poff[j] : kOob);
+                for (int j = 0; j < NSLOT; ++j)
+                    dma(r, stage, j, pslot[j] < a.n_chunks && slot_present(pslot[j], boxes) ? poff[j] : kOob);
             } else {
-                const Win<R> w = window<R>(a.src, c);
+                // the source is the swept map: boxes past its last one lie
+                // outside it anyway
+                const Win<R> w = win(a.src, c, a.band_g);
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) {
                     const bool full = !a.elemwise && pslot[j] < a.n_chunks &&
@@ -559,7 +677,7 @@ struct Copier {
     // slot arrays: each slot's chunk is recomputed.
     __device__ __forceinline__ void patch_edge(uint8_t *stage, const int32_t c[R]) const {
         const Place pl = place<R>(a.src, c);
-        const Win<R> w = window<R>(a.src, c);
+        const Win<R> w = win(a.src, c, a.band_g);
         const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
 #pragma unroll 1
         for (int j = 0; j < NSLOT; ++j) {
@@ -570,7 +688,7 @@ struct Copier {
                 continue;
             }
             uint32_t off, w0, w1;
-            chunk_info(logical_chunk(p, a.src), a.src, off, w0, w1);
+            slot_info(p, a.src, off, w0, w1);
             if (classify<R>(w0, w1, w, a.k_el) == kPart)
                 load_chunk_edge_es(a.src.elem_size, stage + p * 16u, off, w0 & 0xFFFFu, w.lo[0], w.hi[0], r);
         }
@@ -596,31 +714,34 @@ struct Copier {
         return v;
     }
 
-    // Read the tile at corner c (sequence index t) out of `stage`.
-    __device__ __forceinline__ void consume(uint8_t *stage, const int32_t c[R], int64_t t) const {
+    // Read the region (box or unit) under cursor cur, at corner c, out of
+    // `stage`.
+    __device__ __forceinline__ void consume(uint8_t *stage, const int32_t c[R], const Cursor<R> &cur) const {
         if (MODE == kLoad) {
-            const uint64_t bb = a.src.box_bytes;
-            const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)t * bb, (uint32_t)bb);
+            const __amdgpu_buffer_rsrc_t r = packed_rsrc(cur, a.src.box_bytes);
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
                 if (cslot[j] < a.n_chunks) {
                     const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
-                    store16(v, r, cslot[j] * 16u);
+                    store16(v, r, coff[j]);
                 }
             }
         } else {
             const Place pl = place<R>(a.dst, c);
             const __amdgpu_buffer_rsrc_t r = make_rsrc(a.dst.base + (uint64_t)pl.off, a.dst.span);
-            if (pl.interior && !a.elemwise) {
+            // a round trip's destination can be larger than the swept
+            // source: only the unit's existing boxes are stored
+            const uint32_t boxes = unit_boxes(cur);
+            if (inside_map(a.dst, c, pl, boxes) && !a.elemwise) {
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) {
-                    if (cslot[j] < a.n_chunks) {
+                    if (cslot[j] < a.n_chunks && slot_present(cslot[j], boxes)) {
                         const i32x4 v = update(*(const i32x4 *)(stage + cslot[j] * 16u));
                         store16(v, r, coff[j]);
                     }
                 }
             } else {
-                const Win<R> w = window<R>(a.dst, c);
+                const Win<R> w = win(a.dst, c, boxes);
                 if (!a.elemwise) {
 #pragma unroll
                     for (int j = 0; j < NSLOT; ++j) {
@@ -642,7 +763,7 @@ struct Copier {
                         continue;
                     }
                     uint32_t off, w0, w1;
-                    chunk_info(logical_chunk(p, a.dst), a.dst, off, w0, w1);
+                    slot_info(p, a.dst, off, w0, w1);
                     if (classify<R>(w0, w1, w, a.k_el) == kPart)
                         store_chunk_edge_es(a.dst.elem_size, stage + p * 16u, off, w0 & 0xFFFFu, w.lo[0], w.hi[0], r,
                                             MODE == kRoundtrip && a.add_f32, a.addend);
@@ -661,7 +782,7 @@ struct Copier {
         if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
         constexpr int XF = (X + S - 1) % S;
         int32_t c[R];
-        cursor_corner<R>(a, swept(), ccur, c);
+        corner(ccur, c);
         if (S > 1 && MODE != kStore && ((edge >> X) & 1u)) {
             // An edge tile's element loads must be waited for (vmcnt); landing
             // it before the next fill keeps that wait off the fill's loads.
@@ -676,7 +797,7 @@ struct Copier {
         parity ^= 1u << X;
         asm volatile("" ::: "memory");
         if (ok) {
-            consume(st, c, ccur.t);
+            consume(st, c, ccur);
         } else if (lane == 0) {
             __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -686,7 +807,7 @@ struct Copier {
     }
 };
 
-template <int MODE, int S, int NSLOT, int R>
+template <int MODE, int S, int NSLOT, int R, bool BAND = false>
 __global__ __launch_bounds__(kThreads) void copy_kernel(const KArgs a) {
     constexpr uint32_t SB = NSLOT * kWaves * kBlockBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t st0[SB];
@@ -696,7 +817,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const KArgs a) {
     __shared__ uint64_t bars[4];
     __shared__ uint32_t abort_flag;
 
-    Copier<MODE, S, NSLOT, R> cp(a, bars, &abort_flag);
+    Copier<MODE, S, NSLOT, R, BAND> cp(a, bars, &abort_flag);
     if (threadIdx.x == 0) {
         for (int i = 0; i < 4; ++i) bars[i] = 0;
         abort_flag = 0;
@@ -808,7 +929,7 @@ struct ThreadCopier : Copier<MODE, 1, NSLOT, R> {
         __builtin_amdgcn_s_waitcnt(kWaitLgkm);
         __builtin_amdgcn_s_barrier();  // the tile is complete in LDS
         asm volatile("" ::: "memory");
-        this->consume(stage, c, ccur.t);
+        this->consume(stage, c, ccur);
         cursor_advance<R>(a, ccur);
         return true;
     }
@@ -1034,7 +1155,7 @@ __global__ __launch_bounds__(kWsThreads) void ws_kernel(const KArgs a) {
             asm volatile("" ::: "memory");
             int32_t c[R];
             cursor_corner<R>(a, cons.swept(), cons.ccur, c);
-            cons.consume(st, c, cons.ccur.t);
+            cons.consume(st, c, cons.ccur);
             __builtin_amdgcn_s_waitcnt(kWaitLgkm);  // this wave's reads of the stage are done
             bar_arrive(&empty[X], cons.lane, kWsConsumers);
             cursor_advance<R>(a, cons.ccur);
@@ -1090,8 +1211,9 @@ KernelFn pick_ws(int nslot) {
 }
 
 // Launch the (MODE, stages, nslot, R) variant; stages == 0 is the
-// thread-copy variant and stages 12..14 the producer-wave variant with 2..4
-// stages.  hipError_t as int.
+// thread-copy variant, stages 12..14 the producer-wave variant with 2..4
+// stages and stages 21..24 the ring with 1..4 stages on the band schedule
+// (nslot is then 4).  hipError_t as int.
 template <int MODE, int R>
 int launch_mode(int stages, int nslot, const KArgs &a, void *stream) {
     KernelFn fn = nullptr;
@@ -1105,6 +1227,10 @@ int launch_mode(int stages, int nslot, const KArgs &a, void *stream) {
         case 2: fn = pick_nslot<MODE, 2, R>(nslot); break;
         case 3: fn = pick_nslot<MODE, 3, R>(nslot); break;
         case 4: fn = pick_nslot<MODE, 4, R>(nslot); break;
+        case 21: fn = copy_kernel<MODE, 1, kBandSlots, R, true>; break;
+        case 22: fn = copy_kernel<MODE, 2, kBandSlots, R, true>; break;
+        case 23: fn = copy_kernel<MODE, 3, kBandSlots, R, true>; break;
+        case 24: fn = copy_kernel<MODE, 4, kBandSlots, R, true>; break;
         default: break;
     }
     if (!fn) return (int)hipErrorInvalidValue;

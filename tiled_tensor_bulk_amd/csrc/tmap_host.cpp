@@ -116,14 +116,72 @@ struct Plan {
     uint32_t group;
 };
 
-tmap_status plan_launch(const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
-                        const DeviceState &dev, Plan &pl) {
+uint32_t log2u(uint32_t v) {
+    uint32_t l = 0;
+    while ((1u << l) < v) ++l;
+    return l;
+}
+
+// Bytes a unit of g boxes of the band schedule reaches from its corner in
+// kernel map k.
+uint64_t band_span(const tmap::KMap &k, uint32_t g) {
+    return (uint64_t)g * k.box[0] * k.elem_size + (uint64_t)(tmap::kBandRows - 1) * k.strides[1];
+}
+
+// Whether a launch runs on the band schedule, and its boxes per unit (g) and
+// bands per box (nb).  It applies to sweeps whose boxes have rows of 64 to
+// 512 bytes and whose dimension-1 extent is a power-of-two multiple of the
+// band height (boxes of rank 2, or with extent 1 above dimension 1), when
+// the swizzle maps each band of a box onto itself and a row of the sweep
+// holds at least one full unit.
+bool band_fits(const MapImpl &m, const tmap::KArgs &a, uint32_t flags, uint32_t &g, uint32_t &nb) {
+    if (a.coords || a.elemwise) return false;
+    if (flags & (TMAP_FLAG_THREAD_COPY | TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WHOLE_BOX)) return false;
+    if (m.rank < 2) return false;
+    for (int d = 2; d < tmap::kMaxRank; ++d)
+        if (m.box[d] != 1) return false;
+    const uint32_t rc = (uint32_t)m.box[0] * m.elem_size / 16u;  // 16-byte chunks per box row
+    if (rc < 4 || rc > 32 || (rc & (rc - 1))) return false;
+    g = 64u / rc;  // a unit row is 1 KiB
+    if (m.box[1] % tmap::kBandRows) return false;
+    nb = m.box[1] / tmap::kBandRows;
+    if (nb & (nb - 1)) return false;
+    if (m.swz_b && (tmap::kBandRows * m.box[0]) % (1u << (m.swz_m + m.swz_s + m.swz_b))) return false;
+    if (a.tiles[0] < g) return false;
+    // a unit's buffer records, like a box's, stay below the out-of-range offset
+    return band_span(a.src, g) < 0x80000000ull && band_span(a.dst, g) < 0x80000000ull;
+}
+
+// Re-point the launch at units of the band schedule.
+void band_setup(const MapImpl &m, tmap::KArgs &a, uint32_t g, uint32_t nb) {
+    const uint32_t bc = tmap::kBandRows * a.row_chunks;
+    a.band_g = g;
+    a.band_lnb = log2u(nb);
+    a.band_lbc = log2u(bc);
+    a.band_bytes = bc * 16u;
+    int64_t units = 1;
+    for (int d = 0; d < tmap::kMaxRank; ++d) {
+        a.sweep_tiles[d] = d == 0 ? (a.tiles[0] + g - 1) / g : (d == 1 ? a.tiles[1] * nb : a.tiles[d]);
+        a.ubox[d] = d == 0 ? g * m.box[0] : (d == 1 ? tmap::kBandRows : m.box[d]);
+        units *= a.sweep_tiles[d];
+    }
+    a.n_tiles = units;
+    a.n_chunks = tmap::kBandSlots * tmap::kWaves * 64u;
+    for (tmap::KMap *k : {&a.src, &a.dst}) {
+        for (int d = 0; d < tmap::kMaxRank; ++d) k->lim[d] = (int32_t)((int64_t)k->dims[d] - (int64_t)a.ubox[d]);
+        k->span = (uint32_t)band_span(*k, g);
+    }
+}
+
+tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
+                        const DeviceState &dev, bool band, Plan &pl) {
     const uint32_t per_wave_pass = tmap::kWaves * tmap::kBlockBytes;  // bytes one slot per lane covers
     const uint32_t need = (m.box_bytes + per_wave_pass - 1) / per_wave_pass;
     int nslot = 1;
     while ((uint32_t)nslot < need) nslot *= 2;
     if (nslot > 16) return fail(TMAP_ERROR_INVALID_VALUE, "box of %u bytes is too large", m.box_bytes);
-    int stages = (opts && opts->stages) ? (int)opts->stages : (nslot >= 16 ? 2 : 4);
+    if (band) nslot = tmap::kBandSlots;  // a stage is one 16 KiB unit
+    int stages = (opts && opts->stages) ? (int)opts->stages : 2;
     if (stages < 1 || stages > 4)
         return fail(TMAP_ERROR_INVALID_VALUE, "stages must be 1..4 (got %d)", stages);
     const bool thread_copy = opts && (opts->flags & TMAP_FLAG_THREAD_COPY);
@@ -140,31 +198,39 @@ tmap_status plan_launch(const MapImpl &m, int64_t n_tiles, const tmap_launch_opt
     if (lds > dev.lds_per_cu || (nslot == 16 && stages > 2))
         return fail(TMAP_ERROR_INVALID_VALUE, "%d stages of %u bytes do not fit in LDS", stages,
                     (unsigned)(nslot * per_wave_pass));
-    // group: enough boxes side by side to cover 512 bytes of a row, so that a
-    // workgroup's tiles in flight read and write neighbouring row segments
+    // group: consecutive tiles (units on the band schedule) a workgroup takes
+    // in a row.  Whole boxes: enough boxes side by side to cover 512 bytes of
+    // a row, so that a workgroup's tiles in flight read and write neighbouring
+    // row segments; units: 2 for a round trip and 1 for a load or store
+    // (measured best on MI355X).
     uint32_t group = (opts && opts->group) ? opts->group : 0;
     if (group && (group > 64 || (group & (group - 1))))
         return fail(TMAP_ERROR_INVALID_VALUE, "group must be a power of two <= 64 (got %u)", group);
+    if (!group && band) group = mode == tmap::kRoundtrip ? 2u : 1u;
     if (!group) {
         const uint32_t row = (uint32_t)m.box[0] * m.elem_size;
         group = 1;
         while (group < 8 && group * row < 512u) group *= 2;
     }
-    // default grid: twice the workgroups that fit in a CU's LDS at once (at
-    // most 16 per CU); the queued half starts as soon as a resident one ends,
-    // which hides per-tile latency on edge-heavy and scattered workloads
+    // default grid: one workgroup per group.  The dispatcher then starts
+    // workgroups in tile order as others finish, so the tiles in flight at
+    // any moment cover a narrow stretch of the tensor (a few rows of tiles),
+    // which HBM serves faster than the spread-out mix that persistent
+    // workgroups drift into.  Contiguous runs keep a persistent grid: twice
+    // the workgroups that fit in a CU's LDS at once (at most 16 per CU).
+    const bool contiguous = opts && (opts->flags & TMAP_FLAG_CONTIGUOUS);
+    const int64_t useful = contiguous ? n_tiles : (n_tiles + group - 1) / group;
     uint32_t grid = (opts && opts->grid_wgs) ? opts->grid_wgs : 0;
-    if (!grid) {
+    if (!grid && contiguous) {
         uint32_t per_cu = 2 * (dev.lds_per_cu / lds);
         if (per_cu > 16) per_cu = 16;
         if (per_cu < 1) per_cu = 1;
         grid = (uint32_t)dev.cus * per_cu;
     }
-    const bool contiguous = opts && (opts->flags & TMAP_FLAG_CONTIGUOUS);
-    const int64_t useful = contiguous ? n_tiles : (n_tiles + group - 1) / group;
+    if (!grid) grid = (uint32_t)std::min<int64_t>(useful, 1 << 30);
     if ((int64_t)grid > useful) grid = (uint32_t)useful;
     pl.nslot = nslot;
-    pl.stages = thread_copy ? 0 : (producer_wave ? 10 + stages : stages);
+    pl.stages = thread_copy ? 0 : (producer_wave ? 10 + stages : (band ? 20 + stages : stages));
     pl.grid = grid;
     pl.group = group;
     return TMAP_SUCCESS;
@@ -183,8 +249,11 @@ tmap_status check_coords_and_count(const MapImpl &swept, const int32_t *coords, 
 void fill_common(tmap::KArgs &a, const MapImpl &swept, const int32_t *coords, int64_t n_tiles) {
     a.coords = coords;
     a.n_tiles = n_tiles;
-    for (int d = 0; d < tmap::kMaxRank; ++d)
-        a.sweep_tiles[d] = (uint32_t)((swept.dims[d] + swept.box[d] - 1) / swept.box[d]);
+    for (int d = 0; d < tmap::kMaxRank; ++d) {
+        a.tiles[d] = (uint32_t)((swept.dims[d] + swept.box[d] - 1) / swept.box[d]);
+        a.sweep_tiles[d] = a.tiles[d];
+        a.ubox[d] = swept.box[d];
+    }
     a.n_chunks = swept.box_bytes / 16u;
     a.row_chunks = (uint32_t)swept.box[0] * swept.elem_size / 16u;
     a.k_el = 16u / swept.elem_size;
@@ -198,8 +267,11 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     DeviceState *dev = nullptr;
     tmap_status st = device_for_launch(&dev);
     if (st != TMAP_SUCCESS) return st;
+    uint32_t g = 0, nb = 0;
+    const bool band = band_fits(swept, a, opts ? opts->flags : 0u, g, nb);
+    if (band) band_setup(swept, a, g, nb);
     Plan pl;
-    st = plan_launch(swept, a.n_tiles, opts, *dev, pl);
+    st = plan_launch(mode, swept, a.n_tiles, opts, *dev, band, pl);
     if (st != TMAP_SUCCESS) return st;
     a.status = dev->status;
     a.grid = pl.grid;
@@ -352,6 +424,19 @@ uint64_t tmap_box_bytes(const tmap_t *map) {
 int64_t tmap_sweep_tiles(const tmap_t *map) {
     MapImpl m;
     return decode(map, m) ? sweep_count(m) : -1;
+}
+
+uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *coords, uint32_t flags) {
+    MapImpl s, d;
+    if (!decode(src, s)) return 0;
+    if (dst && !decode(dst, d)) return 0;
+    tmap::KArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.src = tmap::kernel_map(s);
+    a.dst = dst ? tmap::kernel_map(d) : a.src;
+    fill_common(a, s, coords, 0);
+    uint32_t g = 0, nb = 0;
+    return band_fits(s, a, flags, g, nb) ? g : 0u;
 }
 
 tmap_status tmap_query(const tmap_t *map, tmap_info *out) {

@@ -99,11 +99,27 @@ struct KArgs {
     uint32_t spin_limit;          // readiness-wait polls before giving up
     uint32_t add_f32;             // round trip: add `addend` to every fp32 element before storing
     float addend;
+    // Band schedule (sweeps of boxes with narrow rows).  A unit is the same
+    // band of kBandRows box rows taken from band_g boxes that are neighbours
+    // in dimension 0; a stage holds one unit, each box's band as the
+    // contiguous piece of that box's LDS image it is.  The cursor then walks
+    // units: sweep_tiles/n_tiles count units, ubox is a unit's extent
+    // (band_g*box0, kBandRows, box2, ..) and the maps' lim is dims - ubox.
+    // band_g == 0: one whole box per stage, ubox == box.
+    uint32_t band_g;              // boxes per unit
+    uint32_t band_lnb;            // log2(bands per box)
+    uint32_t band_lbc;            // log2(16-byte chunks in one box's band)
+    uint32_t band_bytes;          // bytes of one box's band
+    uint32_t tiles[kMaxRank];     // ceil(dims/box) per dimension of the swept map
+    uint32_t ubox[kMaxRank];      // extent of a unit per dimension
 };
+
+constexpr uint32_t kBandRows = 16;        // box rows per band
+constexpr int kBandSlots = 4;             // a band stage is 4 slots per lane: 16 KiB
 
 }  // namespace tmap
 
-// Launch one copy-kernel variant (stages in 1..4, nslot in {1,2,4,8,16}:
+// Launch one copy-kernel variant (stages: see launch_mode; nslot in {1,2,4,8,16}:
 // 16-byte chunks per lane per tile; dims 2 for maps of rank <= 2, else 5).
 // Each direction and dims class has its own translation unit
 // (tmap_{load,store,roundtrip}_r{2,5}.hip).  Return a hipError_t as int.

@@ -37,10 +37,11 @@ def kernel_source_sha() -> str:
 
 
 def short(name: str) -> str:
-    m = re.search(r"copy_kernel<(\d+), (\d+), (\d+), (\d+)>", name)
+    m = re.search(r"copy_kernel<(\d+), (\d+), (\d+), (\d+)(?:, (true|false))?>", name)
     if m:
         mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
-        return f"tmap copy_kernel<{mode}, stages={m.group(2)}, nslot={m.group(3)}, dims={m.group(4)}>"
+        sched = ", band" if m.group(5) == "true" else ""
+        return f"tmap copy_kernel<{mode}, stages={m.group(2)}, nslot={m.group(3)}, dims={m.group(4)}{sched}>"
     if "copyBuffer" in name:
         return "hip copyBuffer (torch d2d copy)"
     return (name[:60] + "...") if len(name) > 63 else name

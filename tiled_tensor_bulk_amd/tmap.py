@@ -20,6 +20,7 @@ FLAG_CONTIGUOUS = 0x1
 FLAG_NONTEMPORAL = 0x2
 FLAG_THREAD_COPY = 0x4
 FLAG_PRODUCER_WAVE = 0x8
+FLAG_WHOLE_BOX = 0x10
 FLAG_INJECT_BUDGET_MISMATCH = 0x100
 
 DTYPES = {"u8": 0, "i8": 1, "u16": 2, "f16": 3, "bf16": 4, "u32": 5, "i32": 6, "f32": 7,
@@ -83,6 +84,8 @@ def lib():
         L.tmap_box_bytes.restype = ctypes.c_uint64
         L.tmap_sweep_tiles.argtypes = [P(tmap_t)]
         L.tmap_sweep_tiles.restype = ctypes.c_int64
+        L.tmap_band_boxes.argtypes = [P(tmap_t), P(tmap_t), vp, u32]
+        L.tmap_band_boxes.restype = u32
         L.tmap_inbounds_elems.argtypes = [P(tmap_t), vp, i64, P(ctypes.c_uint64)]
         L.tmap_inbounds_elems.restype = ctypes.c_int
         L.tmap_query.argtypes = [P(tmap_t), P(tmap_info)]
@@ -191,6 +194,14 @@ def tmap_box_bytes(m: tmap_t) -> int:
 
 def tmap_sweep_tiles(m: tmap_t) -> int:
     return int(lib().tmap_sweep_tiles(ctypes.byref(m)))
+
+
+def tmap_band_boxes(src: tmap_t, dst: Optional[tmap_t] = None, explicit_coords: bool = False,
+                    flags: int = 0) -> int:
+    """Boxes per stage on the band schedule a sweep would take, 0 for whole
+    boxes (host only)."""
+    return int(lib().tmap_band_boxes(ctypes.byref(src), None if dst is None else ctypes.byref(dst),
+                                     1 if explicit_coords else None, int(flags)))
 
 
 def tmap_inbounds_elems(m: tmap_t, host_coords, n_tiles: int) -> int:
