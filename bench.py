@@ -9,6 +9,11 @@ written back out.  The default workload is the 2 GiB byte tensor
 moved by tmap_roundtrip into a second tensor: the large swizzled load/store
 sweep.  Inputs are generated on the device before timing.
 
+The default 50 untimed warm-up steps take the GPU past the first tens of
+milliseconds of sustained HBM load, during which launch times swing by up to
+30% as the device's clocks settle; the 100 timed steps then measure the
+steady state a sustained caller sees.
+
 Prints one JSON line: achieved GB/s (algorithmic bytes read + written per
 step / step time), tiles/s, the dominant kernel's roofline (HIP-event kernel
 time on the launch stream, against 8 TB/s HBM), HBM traffic from the committed
@@ -53,8 +58,8 @@ def traffic_from_profile(workload: str, op: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="sweep2g_u8")
     ap.add_argument("--op", default="roundtrip", choices=["roundtrip", "load", "store", "roundtrip_add", "bulk"])
     ap.add_argument("--stages", type=int, default=0)

@@ -74,7 +74,7 @@ typedef struct tmap_swizzle {
 /* Launch options; pass NULL for the defaults.  Any field left 0 takes its
  * default. */
 typedef struct tmap_launch_opts {
-    uint32_t stages;      /* LDS ring depth 1..4 (default 2)                               */
+    uint32_t stages;      /* LDS ring depth 1..4 (default 2; 1 with explicit corners)      */
     uint32_t grid_wgs;    /* workgroups launched; fewer than there are groups makes each
                              take several (default: one workgroup per group; with
                              TMAP_FLAG_CONTIGUOUS, twice what fits in LDS per CU)         */
@@ -82,14 +82,17 @@ typedef struct tmap_launch_opts {
     uint32_t spin_limit;  /* readiness-wait polls before TMAP_ERROR_TIMEOUT (default 2^22) */
     uint32_t group;       /* tiles (band units) dealt to a workgroup at a time, a power of
                              two <= 64 (default: enough boxes side by side to span 512
-                             bytes of a row, at most 8; band units: 2 for a round trip,
-                             1 for a load or store)                                       */
+                             bytes of a row, at least 2 and at most 8; band units: 2 for
+                             a round trip, 1 for a load or store; explicit corners: 8)   */
 } tmap_launch_opts;
 
 /* Band schedule.  A sweep (coords == NULL) of boxes whose rows hold 64 to
  * 512 bytes, whose dimension-1 extent is 16 times a power of two and whose
- * higher extents are 1 runs on it unless TMAP_FLAG_WHOLE_BOX, thread-copy or
- * producer-wave mode is asked for.  A stage then holds the same 16-row band
+ * higher extents are 1 runs on it when the tensor spans at least 256 MiB
+ * (dims[rank-1] * strides[rank-1]; smaller ones fit in the last-level cache
+ * and gain nothing from it) or TMAP_FLAG_BAND asks for it, unless
+ * TMAP_FLAG_WHOLE_BOX, thread-copy or producer-wave mode is asked for.  A
+ * stage then holds the same 16-row band
  * of the neighbouring boxes that together span 1 KiB of a row (a "unit"),
  * each box's band being the contiguous piece of that box's swizzled LDS
  * image that it always is; the swizzle must map each band onto itself
@@ -122,6 +125,9 @@ typedef struct tmap_launch_opts {
 /* One whole box per stage even where the band schedule applies (for A/B
  * runs, and for a consumer that needs a box's full LDS image at once). */
 #define TMAP_FLAG_WHOLE_BOX 0x10u
+/* The band schedule wherever its shape rules allow, whatever the tensor's
+ * size.  Excludes TMAP_FLAG_WHOLE_BOX. */
+#define TMAP_FLAG_BAND 0x20u
 /* Test hook: every wave announces 16 bytes more than it delivers, so a
  * stage never becomes ready and the bounded wait must end the kernel with
  * TMAP_ERROR_TIMEOUT ("Day 76", "Pitfalls": a byte budget that does not match

@@ -201,44 +201,51 @@ def test_band_schedule_choice():
     """Which sweeps take the band schedule: boxes with 64..512-byte rows and a
     dimension-1 extent of 16 times a power of two, swizzles whose period fits
     a 16-row band, a row of the sweep holding a whole unit, sweeps only, and
-    not in the thread-copy, producer-wave or whole-box modes."""
+    not in the thread-copy, producer-wave or whole-box modes; by default only
+    for tensors spanning 256 MiB or more (TMAP_FLAG_BAND lifts that)."""
     W = inputs.WORKLOADS
-    for name, want in [("sweep2g_u8", 8), ("ragged_bf16", 8), ("strips_f16", 2), ("plus1_f32", 4),
-                       ("tile64_f32", 0), ("pad5d_f32", 0)]:
+    B = T.FLAG_BAND
+    for name, want, forced in [("sweep2g_u8", 8, 8), ("ragged_bf16", 8, 8), ("plus1_f32", 4, 4),
+                               ("strips_f16", 0, 2), ("tile64_f32", 0, 0), ("pad5d_f32", 0, 0)]:
         w = W[name]
         m = T.tmap_encode(w.dtype, w.rank, BASE, w.dims, w.strides, w.box, None, w.swizzle)
         assert T.tmap_band_boxes(m) == want, name
+        assert T.tmap_band_boxes(m, flags=B) == forced, name
         for fl in (T.FLAG_WHOLE_BOX, T.FLAG_THREAD_COPY, T.FLAG_PRODUCER_WAVE):
-            assert T.tmap_band_boxes(m, flags=fl) == 0
+            assert T.tmap_band_boxes(m, flags=fl | B) == 0
         assert T.tmap_band_boxes(m, flags=T.FLAG_NONTEMPORAL | T.FLAG_CONTIGUOUS) == want
-        assert T.tmap_band_boxes(m, explicit_coords=True) == 0
+        assert T.tmap_band_boxes(m, explicit_coords=True, flags=B) == 0
         assert T.tmap_band_boxes(m, m) == want
+    # the size threshold: 256 MiB spanned by the outermost dimension
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65536], [128, 128])) == 8
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128])) == 0
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128]), flags=B) == 8
     # row width: 64..512 bytes, 1 KiB of row per unit
     for dt, box0, want in [("u8", 32, 0), ("u8", 64, 16), ("u8", 128, 8), ("u8", 256, 4), ("f16", 256, 2),
                            ("f32", 128, 2), ("f32", 256, 0), ("f64", 8, 16), ("f64", 64, 2), ("f32", 24, 0)]:
-        assert T.tmap_band_boxes(_enc_rows(dt, [box0 * 20, 100], [box0, 16])) == want, (dt, box0)
+        assert T.tmap_band_boxes(_enc_rows(dt, [box0 * 20, 100], [box0, 16]), flags=B) == want, (dt, box0)
     # dimension-1 extent
     for box1, want in [(8, 0), (16, 8), (24, 0), (32, 8), (48, 0), (64, 8), (128, 8)]:
-        assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, box1])) == want, box1
+        assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, box1]), flags=B) == want, box1
     # swizzle period 2^(m+s+b) elements must divide a band of 16 * 128 elements
     for swz, want in [((3, 4, 3), 8), ((0, 4, 3), 8), ((3, 4, 4), 8), ((2, 4, 5), 8), ((3, 4, 5), 0), ((1, 4, 7), 0)]:
-        assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128], swz)) == want, swz
+        assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128], swz), flags=B) == want, swz
     # a swizzle that moves bytes inside 16-byte chunks takes the element path
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128], (3, 0, 3))) == 0
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128], (3, 0, 3)), flags=B) == 0
     # a row of the sweep must hold one whole unit (8 boxes of 128 bytes)
-    assert T.tmap_band_boxes(_enc_rows("u8", [7 * 128, 64], [128, 16])) == 0
-    assert T.tmap_band_boxes(_enc_rows("u8", [7 * 128 + 1, 64], [128, 16])) == 8
+    assert T.tmap_band_boxes(_enc_rows("u8", [7 * 128, 64], [128, 16]), flags=B) == 0
+    assert T.tmap_band_boxes(_enc_rows("u8", [7 * 128 + 1, 64], [128, 16]), flags=B) == 8
     # higher box extents must be 1
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 1])) == 8
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 2])) == 0
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096], [128])) == 0
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 1]), flags=B) == 8
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 2]), flags=B) == 0
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096], [128]), flags=B) == 0
     # a unit must stay within 2^31 bytes of its corner, in both maps: with
     # this stride a 128x16 box spans 128 + 15 * stride < 2^31 bytes (a valid
     # map) but a unit 1 KiB wide does not
     stride = 143165552
     assert 128 + 15 * stride < 2**31 <= 1024 + 15 * stride
     far = T.tmap_encode("u8", 2, BASE, [4096, 20], [stride], [128, 16])
-    assert T.tmap_band_boxes(far) == 0
+    assert T.tmap_band_boxes(far, flags=B) == 0
     near = _enc_rows("u8", [4096, 20], [128, 16])
-    assert T.tmap_band_boxes(near) == 8 and T.tmap_band_boxes(near, far) == 0
+    assert T.tmap_band_boxes(near, flags=B) == 8 and T.tmap_band_boxes(near, far, flags=B) == 0
     assert T.tmap_band_boxes(T.tmap_t()) == 0

@@ -97,9 +97,10 @@ def _band_case(rng):
 
 
 def _opts(rng):
+    # these tensors are small: TMAP_FLAG_BAND takes the band schedule anyway
     return dict(stages=int(rng.integers(1, 5)), grid_wgs=int(rng.choice([0, 0, 1, 3, 7])),
                 group=int(rng.choice([0, 1, 2, 4, 8])),
-                flags=int(rng.choice([0, T.FLAG_NONTEMPORAL, T.FLAG_CONTIGUOUS])))
+                flags=T.FLAG_BAND | int(rng.choice([0, T.FLAG_NONTEMPORAL, T.FLAG_CONTIGUOUS])))
 
 
 @pytest.mark.parametrize("chunk", range(3))
@@ -173,9 +174,9 @@ def test_band_and_whole_box_agree_on_a_short_last_unit():
     n = T.tmap_sweep_tiles(ms)
     for dst in (dst_a, dst_b):
         md = T.tmap_encode("u8", 2, dst.data_ptr(), [2048, 64], [2048], [128, 16], None, (3, 4, 3))
-        T.tmap_roundtrip(ms, md, None, n, flags=0 if dst is dst_a else T.FLAG_WHOLE_BOX)
+        T.tmap_roundtrip(ms, md, None, n, flags=T.FLAG_BAND if dst is dst_a else T.FLAG_WHOLE_BOX)
         check_ok()
-    assert T.tmap_band_boxes(ms, md) == 8
+    assert T.tmap_band_boxes(ms, md, False, T.FLAG_BAND) == 8
     assert torch.equal(dst_a, dst_b)
     want = dev_bytes(2048 * 64, 6).cpu().numpy()
     om = Map(es=1, dims=[1200, 50], strides=[1200], box=[128, 16], swizzle=(3, 4, 3))

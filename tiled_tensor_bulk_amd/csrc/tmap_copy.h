@@ -548,6 +548,17 @@ struct Copier {
             return true;
     }
 
+    // Whether window w cuts through a 16-byte chunk in dimension 0: only
+    // then does some chunk hold elements both inside and outside the tensor
+    // and need the element path.  Chunks start at multiples of k_el, so that
+    // is when a bound of a non-empty window is not such a multiple.
+    __device__ __forceinline__ bool splits_chunks(const Win<R> &w) const {
+        bool rows = true;
+#pragma unroll
+        for (int d = 1; d < R; ++d) rows = rows & (w.lo[d] < w.hi[d]);
+        return rows & (w.lo[0] < w.hi[0]) & (((w.lo[0] | w.hi[0]) & (a.k_el - 1u)) != 0u);
+    }
+
     // Window of the region at corner c in map m, limited to the first `boxes`
     // boxes of a unit.
     __device__ __forceinline__ Win<R> win(const KMap &m, const int32_t c[R], uint32_t boxes) const {
@@ -638,7 +649,8 @@ struct Copier {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
             const uint32_t boxes = unit_boxes(fcur);
             const bool fast = inside_map(a.src, c, pl, boxes) && !a.elemwise;
-            edge = fast ? (edge & ~(1u << XF)) : (edge | (1u << XF));
+            // edge bit: the tile needs the element path when it lands
+            bool patch = false;
             if (fast) {
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j)
@@ -653,7 +665,9 @@ struct Copier {
                                       classify<R>(pw0[j], pw1[j], w, a.k_el) == kFull;
                     dma(r, stage, j, full ? poff[j] : kOob);
                 }
+                patch = a.elemwise || splits_chunks(w);
             }
+            edge = patch ? (edge | (1u << XF)) : (edge & ~(1u << XF));
         }
         cursor_advance<R>(a, fcur);
     }
@@ -753,6 +767,7 @@ struct Copier {
                 }
                 // slow path, kept out of the unrolled slot arrays: recompute
                 // each slot's chunk, store the inside elements of partial ones
+                if (!a.elemwise && !splits_chunks(w)) return;
                 const uint32_t cw = (wave + 1) % kWaves;
 #pragma unroll 1
                 for (int j = 0; j < NSLOT; ++j) {

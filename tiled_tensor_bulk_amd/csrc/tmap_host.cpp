@@ -133,11 +133,18 @@ uint64_t band_span(const tmap::KMap &k, uint32_t g) {
 // 512 bytes and whose dimension-1 extent is a power-of-two multiple of the
 // band height (boxes of rank 2, or with extent 1 above dimension 1), when
 // the swizzle maps each band of a box onto itself and a row of the sweep
-// holds at least one full unit.
+// holds at least one full unit.  By default it is taken only for tensors
+// spanning at least kBandMinSpan bytes: it buys DRAM page locality, which a
+// tensor that fits in the 256 MB last-level cache (MALL) does not need,
+// while its smaller units cost latency there.
+constexpr uint64_t kBandMinSpan = 256ull << 20;
+
 bool band_fits(const MapImpl &m, const tmap::KArgs &a, uint32_t flags, uint32_t &g, uint32_t &nb) {
     if (a.coords || a.elemwise) return false;
     if (flags & (TMAP_FLAG_THREAD_COPY | TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WHOLE_BOX)) return false;
     if (m.rank < 2) return false;
+    const uint64_t span = m.dims[m.rank - 1] * m.strides[m.rank - 1];
+    if (!(flags & TMAP_FLAG_BAND) && span < kBandMinSpan) return false;
     for (int d = 2; d < tmap::kMaxRank; ++d)
         if (m.box[d] != 1) return false;
     const uint32_t rc = (uint32_t)m.box[0] * m.elem_size / 16u;  // 16-byte chunks per box row
@@ -174,20 +181,26 @@ void band_setup(const MapImpl &m, tmap::KArgs &a, uint32_t g, uint32_t nb) {
 }
 
 tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
-                        const DeviceState &dev, bool band, Plan &pl) {
+                        const DeviceState &dev, bool band, bool corners, Plan &pl) {
     const uint32_t per_wave_pass = tmap::kWaves * tmap::kBlockBytes;  // bytes one slot per lane covers
     const uint32_t need = (m.box_bytes + per_wave_pass - 1) / per_wave_pass;
     int nslot = 1;
     while ((uint32_t)nslot < need) nslot *= 2;
     if (nslot > 16) return fail(TMAP_ERROR_INVALID_VALUE, "box of %u bytes is too large", m.box_bytes);
     if (band) nslot = tmap::kBandSlots;  // a stage is one 16 KiB unit
-    int stages = (opts && opts->stages) ? (int)opts->stages : 2;
+    // default ring depth: 2; explicit corners (boxes scattered over the
+    // tensor, many of them cut by its edges): 1, as each box's edge work
+    // leaves little to overlap and the smaller footprint fits more
+    // workgroups (measured best on MI355X)
+    int stages = (opts && opts->stages) ? (int)opts->stages : (corners ? 1 : 2);
     if (stages < 1 || stages > 4)
         return fail(TMAP_ERROR_INVALID_VALUE, "stages must be 1..4 (got %d)", stages);
     const bool thread_copy = opts && (opts->flags & TMAP_FLAG_THREAD_COPY);
     const bool producer_wave = opts && (opts->flags & TMAP_FLAG_PRODUCER_WAVE);
     if (thread_copy && producer_wave)
         return fail(TMAP_ERROR_INVALID_VALUE, "thread-copy and producer-wave modes exclude each other");
+    if (opts && (opts->flags & TMAP_FLAG_BAND) && (opts->flags & TMAP_FLAG_WHOLE_BOX))
+        return fail(TMAP_ERROR_INVALID_VALUE, "TMAP_FLAG_BAND and TMAP_FLAG_WHOLE_BOX exclude each other");
     if (thread_copy) stages = 1;  // one LDS stage; the next tile waits in registers
     if (producer_wave) {
         if (nslot > 8)
@@ -201,15 +214,16 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // group: consecutive tiles (units on the band schedule) a workgroup takes
     // in a row.  Whole boxes: enough boxes side by side to cover 512 bytes of
     // a row, so that a workgroup's tiles in flight read and write neighbouring
-    // row segments; units: 2 for a round trip and 1 for a load or store
-    // (measured best on MI355X).
+    // row segments, and at least 2; units: 2 for a round trip and 1 for a
+    // load or store; explicit corners: 8 (measured best on MI355X).
     uint32_t group = (opts && opts->group) ? opts->group : 0;
     if (group && (group > 64 || (group & (group - 1))))
         return fail(TMAP_ERROR_INVALID_VALUE, "group must be a power of two <= 64 (got %u)", group);
     if (!group && band) group = mode == tmap::kRoundtrip ? 2u : 1u;
+    if (!group && corners) group = 8;
     if (!group) {
         const uint32_t row = (uint32_t)m.box[0] * m.elem_size;
-        group = 1;
+        group = 2;  // at least two, so that the ring overlaps a fill with a drain
         while (group < 8 && group * row < 512u) group *= 2;
     }
     // default grid: one workgroup per group.  The dispatcher then starts
@@ -271,7 +285,7 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     const bool band = band_fits(swept, a, opts ? opts->flags : 0u, g, nb);
     if (band) band_setup(swept, a, g, nb);
     Plan pl;
-    st = plan_launch(mode, swept, a.n_tiles, opts, *dev, band, pl);
+    st = plan_launch(mode, swept, a.n_tiles, opts, *dev, band, a.coords != nullptr, pl);
     if (st != TMAP_SUCCESS) return st;
     a.status = dev->status;
     a.grid = pl.grid;

@@ -21,6 +21,7 @@ FLAG_NONTEMPORAL = 0x2
 FLAG_THREAD_COPY = 0x4
 FLAG_PRODUCER_WAVE = 0x8
 FLAG_WHOLE_BOX = 0x10
+FLAG_BAND = 0x20
 FLAG_INJECT_BUDGET_MISMATCH = 0x100
 
 DTYPES = {"u8": 0, "i8": 1, "u16": 2, "f16": 3, "bf16": 4, "u32": 5, "i32": 6, "f32": 7,
