@@ -314,6 +314,23 @@ def test_zero_tiles_launch_nothing():
     check_ok()
 
 
+def test_budget_mismatch_times_out_on_the_band_schedule():
+    """The same on a band-schedule sweep: each 16 KiB unit's record never
+    reaches zero outstanding bytes."""
+    say("budget mismatch -> TIMEOUT (band schedule)")
+    src = dev_tensor(1024 * 64, fill_seed=2)
+    m = enc("u8", src, [1024, 64], [1024], [128, 16])
+    assert T.tmap_band_boxes(m, None, False, T.FLAG_BAND) == 8
+    n = T.tmap_sweep_tiles(m)
+    out = dev_tensor(n * 2048)
+    T.tmap_load_tiles(m, None, n, out, flags=T.FLAG_INJECT_BUDGET_MISMATCH | T.FLAG_BAND, spin_limit=2000)
+    assert T.tmap_sync_status() == T.TIMEOUT
+    T.tmap_load_tiles(m, None, n, out, flags=T.FLAG_BAND)
+    check_ok()
+    om = Map(es=1, dims=[1024, 64], strides=[1024], box=[128, 16])
+    assert out.cpu().numpy().tobytes() == oracle.load_tiles(om, src.cpu().numpy(), None, n).tobytes()
+
+
 @pytest.mark.parametrize("mode", [0, T.FLAG_PRODUCER_WAVE])
 def test_budget_mismatch_times_out_instead_of_hanging(mode):
     """Announce 16 more bytes than delivered: the stage never becomes ready; the

@@ -197,12 +197,16 @@ def tmap_sweep_tiles(m: tmap_t) -> int:
     return int(lib().tmap_sweep_tiles(ctypes.byref(m)))
 
 
+_ANY_CORNERS = ctypes.c_int32(0)  # a non-NULL corner pointer for the schedule query (never read)
+
+
 def tmap_band_boxes(src: tmap_t, dst: Optional[tmap_t] = None, explicit_coords: bool = False,
                     flags: int = 0) -> int:
-    """Boxes per stage on the band schedule a sweep would take, 0 for whole
+    """Boxes per stage on the band schedule a copy would take, 0 for whole
     boxes (host only)."""
+    corners = ctypes.addressof(_ANY_CORNERS) if explicit_coords else None
     return int(lib().tmap_band_boxes(ctypes.byref(src), None if dst is None else ctypes.byref(dst),
-                                     1 if explicit_coords else None, int(flags)))
+                                     corners, int(flags)))
 
 
 def tmap_inbounds_elems(m: tmap_t, host_coords, n_tiles: int) -> int:
