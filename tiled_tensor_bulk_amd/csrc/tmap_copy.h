@@ -57,6 +57,7 @@ namespace tmap {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 constexpr uint32_t kOob = 0x80000000u;       // offset past every num_records
@@ -67,8 +68,61 @@ constexpr uint32_t kWaitLgkm = 0xC07F;       // s_waitcnt lgkmcnt(0) only
 
 enum Cls : uint32_t { kZero = 0, kFull = 1, kPart = 2 };
 
+// A buffer range as the direct-to-LDS loads take it: base address and
+// number of bytes in range.
+struct Src {
+    uint64_t base;
+    uint32_t nrec;
+};
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(uint64_t addr, uint32_t nrec) {
     return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(addr), 0, (int)nrec, kRsrcWord3);
+}
+
+// ---------------------------------------------------------------- LDS DMA
+// One wave-wide direct-to-LDS load: lane l's 16 bytes at voff land at LDS
+// address lds + 16*l.  Issued from assembly so that the compiler does not
+// guard later LDS accesses against it: lacking alias information it would
+// put vmcnt(0) before every LDS access after it (the barrier records, the
+// consumer's reads), draining the next stage's loads and with them the
+// ring's overlap.  The ring waits for its loads itself (wait_vmcnt), and the
+// "memory" clobber keeps the compiler's own LDS accesses on their side of it.
+// (M0 takes the LDS address and is restored afterwards, since the compiler
+// reserves it; the nops cover the M0 -> LDS-DMA hazard and an SGPR just
+// written by a VALU.)
+__device__ __forceinline__ void dma_lds(uint64_t base, uint32_t nrec, const uint8_t *lds, uint32_t voff, bool nt) {
+    // the buffer descriptor and the LDS address are uniform per wave; say so
+    // explicitly so they are held in SGPRs
+    const i32x4 d = {__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                     __builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xFFFFu)),
+                     __builtin_amdgcn_readfirstlane((int)nrec), kRsrcWord3};
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void_t *)lds);
+    uint32_t saved;
+    if (nt)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0), "v"(voff), "s"(d)
+            : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0), "v"(voff), "s"(d)
+            : "memory");
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (expcnt and lgkmcnt untouched).  Loads complete in issue order, so after
+// issuing k more loads behind a stage's loads, vmcnt(k) guarantees that the
+// stage's loads have landed, whatever stores were issued in between.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    constexpr int n = N > 63 ? 63 : N;
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00);
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ uint32_t swizzle(uint32_t e, uint32_t b, uint32_t m, uint32_t s) {
@@ -441,6 +495,11 @@ struct Copier {
     uint32_t *abort_flag;
     Cursor<R> fcur;  // next tile to fill
     Cursor<R> ccur;  // next tile to land and consume
+    // Corners are read once, one fill ahead (explicit corners cost a scalar
+    // memory round trip each), and kept per stage for landing and draining.
+    int32_t fc[R];     // corner of the tile under the fill cursor
+    int32_t sc[S][R];  // corner of the tile in each stage
+    int64_t nfill;     // tiles this workgroup has filled
     // producer slots (the slots this lane fills) and consumer slots (the slots
     // this lane drains: those the next wave filled)
     uint32_t pslot[NSLOT], poff[NSLOT], pw0[NSLOT], pw1[NSLOT];
@@ -510,20 +569,24 @@ struct Copier {
     // Buffer resource over the packed images of the region under cur: the
     // box's image, or the unit's bands (records end after the last existing
     // box's band, so chunks of missing boxes read zero and are not written).
-    __device__ __forceinline__ __amdgpu_buffer_rsrc_t packed_rsrc(const Cursor<R> &cur, uint32_t bb) const {
+    __device__ __forceinline__ Src packed_src(const Cursor<R> &cur, uint32_t bb) const {
         if constexpr (BAND) {
             uint64_t t = 0;
 #pragma unroll
             for (int d = R - 1; d >= 1; --d) t = t * a.tiles[d] + (d == 1 ? (cur.dig[1] >> a.band_lnb) : cur.dig[d]);
             t = t * a.tiles[0] + (uint64_t)cur.dig[0] * a.band_g;
             const uint32_t j = cur.dig[1] & ((1u << a.band_lnb) - 1u);
-            const uint64_t base = (uint64_t)a.packed + t * bb + (uint64_t)j * a.band_bytes;
-            return make_rsrc(base, (unit_boxes(cur) - 1u) * bb + a.band_bytes);
+            return Src{(uint64_t)a.packed + t * bb + (uint64_t)j * a.band_bytes,
+                       (unit_boxes(cur) - 1u) * bb + a.band_bytes};
         } else {
-            return make_rsrc((uint64_t)a.packed + (uint64_t)cur.t * bb, bb);
+            return Src{(uint64_t)a.packed + (uint64_t)cur.t * bb, bb};
         }
     }
 
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t packed_rsrc(const Cursor<R> &cur, uint32_t bb) const {
+        const Src p = packed_src(cur, bb);
+        return make_rsrc(p.base, p.nrec);
+    }
     // Whether the region at corner c lies inside map m: the whole box, or the
     // first `boxes` boxes of a unit (a short last unit of a row is inside
     // when its existing boxes are).
@@ -601,6 +664,8 @@ struct Copier {
         }
         cursor_init<R>(a, t0, fcur);
         ccur = fcur;
+        nfill = 0;
+        if (cnt > 0) corner(fcur, fc);
         my_bytes = 0;
         const uint32_t cw = (wave + 1) % kWaves;
 #pragma unroll
@@ -624,12 +689,8 @@ struct Copier {
     }
 
     template <typename T>
-    __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, T *stage, int j, uint32_t voff) const {
-        lds_void_t *blk = (lds_void_t *)(stage + (j * kWaves + wave) * kBlockBytes);
-        if (nt)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, blk, 16, voff, 0, 0, 2);
-        else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, blk, 16, voff, 0, 0, 0);
+    __device__ __forceinline__ void dma(const Src &src, T *stage, int j, uint32_t voff) const {
+        dma_lds(src.base, src.nrec, stage + (j * kWaves + wave) * kBlockBytes, voff, nt);
     }
 
     // Issue the loads of the tile under the fill cursor into stage XF, then
@@ -638,15 +699,16 @@ struct Copier {
     __device__ __forceinline__ void fill(uint8_t *stage, uint64_t *bar) {
         const uint32_t budget = my_bytes + ((a.flags & TMAP_FLAG_INJECT_BUDGET_MISMATCH) ? 16u : 0u);
         bar_arrive_expect(bar, budget, lane);
+        int32_t c[R];
+#pragma unroll
+        for (int d = 0; d < R; ++d) c[d] = sc[XF][d] = fc[d];
         if (MODE == kStore) {
-            const __amdgpu_buffer_rsrc_t r = packed_rsrc(fcur, a.dst.box_bytes);
+            const Src r = packed_src(fcur, a.dst.box_bytes);
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? poff[j] : kOob);
         } else {
-            int32_t c[R];
-            corner(fcur, c);
             const Place pl = place<R>(a.src, c);
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
+            const Src r{a.src.base + (uint64_t)pl.off, a.src.span};
             const uint32_t boxes = unit_boxes(fcur);
             const bool fast = inside_map(a.src, c, pl, boxes) && !a.elemwise;
             // edge bit: the tile needs the element path when it lands
@@ -670,16 +732,20 @@ struct Copier {
             edge = patch ? (edge | (1u << XF)) : (edge & ~(1u << XF));
         }
         cursor_advance<R>(a, fcur);
+        // read the next fill's corner now, while this tile's loads fly (never
+        // past this workgroup's last tile: an explicit-corner array ends there)
+        if (++nfill < cnt) corner(fcur, fc);
     }
 
-    // This wave's loads of the tile at corner c have landed in stage X:
-    // patch partial chunks, then report the delivered bytes.
+    // Wait for this wave's loads of the tile at corner c into stage X, patch
+    // its partial chunks, then report the delivered bytes.  `later`: the
+    // S-1 tiles after it have been filled (their loads may stay in flight).
     template <int X>
-    __device__ __forceinline__ void land(uint8_t *stage, uint64_t *bar, const int32_t c[R]) const {
-        // A read of this stage object makes the compiler wait (vmcnt) for this
-        // wave's direct-to-LDS loads into it.
-        uint32_t probe = *(volatile uint32_t *)(stage + (wave * 64u + lane) * 16u);
-        asm volatile("" ::"v"(probe) : "memory");
+    __device__ __forceinline__ void land(uint8_t *stage, uint64_t *bar, const int32_t c[R], bool later) const {
+        if (later)
+            wait_vmcnt<(S - 1) * NSLOT>();
+        else
+            wait_vmcnt<0>();
         if (MODE != kStore && ((edge >> X) & 1u)) patch_edge(stage, c);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm);
         asm volatile("" ::: "memory");
@@ -796,17 +862,22 @@ struct Copier {
         __builtin_amdgcn_s_barrier();
         if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
         constexpr int XF = (X + S - 1) % S;
+        // the tile's corner, recorded when it was filled (with one stage the
+        // fill of this step is tile k itself, so read it after the fill)
         int32_t c[R];
-        corner(ccur, c);
         if (S > 1 && MODE != kStore && ((edge >> X) & 1u)) {
             // An edge tile's element loads must be waited for (vmcnt); landing
             // it before the next fill keeps that wait off the fill's loads.
-            // (With one stage the fill of this step is tile k itself.)
-            land<X>(st, &bars[X], c);
+#pragma unroll
+            for (int d = 0; d < R; ++d) c[d] = sc[X][d];
+            land<X>(st, &bars[X], c, false);
             if (k + S - 1 < cnt) fill<XF>(fillst, &bars[XF]);
         } else {
-            if (k + S - 1 < cnt) fill<XF>(fillst, &bars[XF]);
-            land<X>(st, &bars[X], c);
+            const bool later = k + S - 1 < cnt;
+            if (later) fill<XF>(fillst, &bars[XF]);
+#pragma unroll
+            for (int d = 0; d < R; ++d) c[d] = sc[X][d];
+            land<X>(st, &bars[X], c, later && S > 1);
         }
         const bool ok = bar_wait(&bars[X], (parity >> X) & 1u, a.spin_limit);
         parity ^= 1u << X;
@@ -1011,12 +1082,8 @@ struct WsProducer {
         }
     }
 
-    __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint8_t *stage, int j, uint32_t voff) const {
-        lds_void_t *blk = (lds_void_t *)(stage + j * kBlockBytes);
-        if (nt)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, blk, 16, voff, 0, 0, 2);
-        else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, blk, 16, voff, 0, 0, 0);
+    __device__ __forceinline__ void dma(const Src &src, uint8_t *stage, int j, uint32_t voff) const {
+        dma_lds(src.base, src.nrec, stage + j * kBlockBytes, voff, nt);
     }
 
     // Arm stage X's full record with the box's bytes and issue all its loads.
@@ -1027,7 +1094,7 @@ struct WsProducer {
         bar_arrive_expect(&full[X], budget, lane, 1);
         if (MODE == kStore) {
             const uint64_t dbb = a.dst.box_bytes;
-            const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)fcur.t * dbb, (uint32_t)dbb);
+            const Src r{(uint64_t)a.packed + (uint64_t)fcur.t * dbb, (uint32_t)dbb};
 #pragma unroll
             for (int j = 0; j < NP; ++j) {
                 const uint32_t p = (uint32_t)j * 64u + lane;
@@ -1037,7 +1104,7 @@ struct WsProducer {
             int32_t c[R];
             cursor_corner<R>(a, a.src, fcur, c);
             const Place pl = place<R>(a.src, c);
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
+            const Src r{a.src.base + (uint64_t)pl.off, a.src.span};
             const bool fast = pl.interior && !a.elemwise;
             edge = fast ? (edge & ~(1u << X)) : (edge | (1u << X));
             if (fast) {
@@ -1056,12 +1123,15 @@ struct WsProducer {
         cursor_advance<R>(a, fcur);
     }
 
-    // The loads of the tile at corner c have landed in stage X: patch its
-    // partial chunks and complete the stage's byte budget.
+    // Wait for the loads of the tile at corner c into stage X, patch its
+    // partial chunks and complete the stage's byte budget.  `later`: the S-1
+    // tiles after it have been filled.
     template <int X>
-    __device__ __forceinline__ void land(uint8_t *stage, const int32_t c[R]) const {
-        uint32_t probe = *(volatile uint32_t *)(stage + lane * 16u);
-        asm volatile("" ::"v"(probe) : "memory");
+    __device__ __forceinline__ void land(uint8_t *stage, const int32_t c[R], bool later) const {
+        if (later)
+            wait_vmcnt<(S - 1) * NP>();
+        else
+            wait_vmcnt<0>();
         if (MODE != kStore && ((edge >> X) & 1u)) {
             const Place pl = place<R>(a.src, c);
             const Win<R> w = window<R>(a.src, c);
@@ -1103,7 +1173,7 @@ struct WsProducer {
         if (i >= cnt || aborted()) return false;
         int32_t c[R];
         cursor_corner<R>(a, MODE == kStore ? a.dst : a.src, lcur, c);
-        land<X>(st, c);
+        land<X>(st, c, i + S - 1 < cnt);
         cursor_advance<R>(a, lcur);
         if (i + S < cnt) {
             if (!bar_wait(&empty[X], (eparity >> X) & 1u, a.spin_limit)) {
