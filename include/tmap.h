@@ -74,7 +74,8 @@ typedef struct tmap_swizzle {
 /* Launch options; pass NULL for the defaults.  Any field left 0 takes its
  * default. */
 typedef struct tmap_launch_opts {
-    uint32_t stages;      /* LDS ring depth 1..4 (default 2; 1 with explicit corners)      */
+    uint32_t stages;      /* LDS ring depth 1..4 (default 2; 1 with explicit corners and
+                             when each workgroup takes a single band unit)               */
     uint32_t grid_wgs;    /* workgroups launched; fewer than there are groups makes each
                              take several (default: one workgroup per group; with
                              TMAP_FLAG_CONTIGUOUS, twice what fits in LDS per CU)         */

@@ -221,6 +221,8 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
         return fail(TMAP_ERROR_INVALID_VALUE, "group must be a power of two <= 64 (got %u)", group);
     if (!group && band) group = mode == tmap::kRoundtrip ? 2u : 1u;
     if (!group && corners) group = 8;
+    // a workgroup that takes one band unit has nothing to overlap in its ring
+    if (band && group == 1 && !(opts && opts->stages)) stages = 1;
     if (!group) {
         const uint32_t row = (uint32_t)m.box[0] * m.elem_size;
         group = 2;  // at least two, so that the ring overlaps a fill with a drain
