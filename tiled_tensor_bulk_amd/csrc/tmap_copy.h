@@ -3,9 +3,9 @@
 // instantiates the variants of that direction.
 //
 // One kernel template serves the three directions (load to packed images,
-// store from packed images, round trip).  Each workgroup (4 waves) is
-// persistent and walks its share of the tiles through a ring of S LDS
-// stages:
+// store from packed images, round trip).  Each workgroup (4 waves) walks its
+// share of the tiles (by default one group of neighbouring tiles) through a
+// ring of S LDS stages:
 //
 //   fill    every lane issues one 16-byte direct-to-LDS buffer load per slot
 //           it owns (buffer_load_dwordx4 ... lds).  The tensor map sits in
@@ -39,10 +39,12 @@
 //           "Why this only pays off inside a pipeline").
 //
 // The S stages are separate __shared__ objects and the tile loop is
-// unrolled by S, so the compiler's LDS-DMA tracking can wait for exactly the
-// loads of one stage instead of draining every load in flight.  R is the
-// number of dimensions the scalar tile arithmetic walks: 2 for maps of rank
-// <= 2, else 5.
+// unrolled by S.  The direct-to-LDS loads are issued from assembly and each
+// stage waits for exactly its own loads (vmcnt of the later stages' loads),
+// so a stage drains while the next ones fill.  On the band schedule (sweeps
+// of boxes with narrow rows) a stage holds the same 16-row band of several
+// neighbouring boxes instead of one box.  R is the number of dimensions the
+// scalar tile arithmetic walks: 2 for maps of rank <= 2, else 5.
 
 #pragma once
 

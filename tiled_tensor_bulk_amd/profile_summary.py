@@ -26,13 +26,36 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def _code_only(text: str) -> str:
+    """The source without comments and with whitespace collapsed, so that a
+    comment edit does not mark the measured kernels as changed."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif text[i] == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_tensor_bulk_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.startswith("tmap_") and name.endswith((".h", ".hip", ".cpp")):
             h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+            h.update(_code_only(open(os.path.join(csrc, name), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 
