@@ -219,6 +219,8 @@ def main():
                      "traffic": None if traffic is None else round(traffic / kern_avg_s / 1e9, 2),
                      "kernel_ms": round(kern_avg_s * 1e3, 4),
                      "kernel": f"tmap copy_kernel ({args.op})"},
+        "kernel_ms_median": round(sorted(kern_ms)[len(kern_ms) // 2], 4),
+        "kernel_ms_min": round(min(kern_ms), 4),
         "reference_d2d_copy_GBps": round(copy_gbps, 1),
     }
 
@@ -284,7 +286,17 @@ def cpu_baseline(w, op, src, budget_s):
             "tiles_per_s": round(tiles / total_t, 1),
             "sample": f"{tiles} tiles ({chunk * rows_per_chunk} tile rows from the top) of {w.name}, "
                       f"{op}, {total_t:.1f} s of single-thread oracle time",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

@@ -3,6 +3,8 @@
     python -m tiled_tensor_bulk_amd.profile_summary stats  <kernel_stats.csv> --out FILE --cmd "..."
     python -m tiled_tensor_bulk_amd.profile_summary traffic --fetch <counter_collection.csv>
         --write <counter_collection.csv> --workload W --op OP --out FILE --cmd "..."
+    python -m tiled_tensor_bulk_amd.profile_summary counters <counter_collection.csv>
+        --workload W --op OP --out FILE --cmd "..."
 
 `stats` condenses a --kernel-trace --stats kernel_stats.csv into a short
 markdown table.  `traffic` turns a FETCH_SIZE run and a WRITE_SIZE run (each
@@ -134,9 +136,34 @@ def cmd_traffic(a):
     print("\n".join(lines))
 
 
+def cmd_counters(a):
+    rows = list(csv.DictReader(open(a.csv)))
+    agg = defaultdict(float)
+    disp = set()
+    for r in rows:
+        if "copy_kernel" not in r["Kernel_Name"]:
+            continue
+        disp.add(int(r["Dispatch_Id"]))
+        agg[r["Counter_Name"]] += float(r["Counter_Value"])
+    if not disp:
+        sys.exit(f"{a.csv}: no copy kernel dispatches")
+    lines = [f"# rocprofv3 counters of the copy kernel, {a.workload} {a.op}, averaged over {len(disp)} dispatches",
+             f"# command: {a.cmd}",
+             f"kernel_source_sha: {kernel_source_sha()}"]
+    lines += [f"{k}: {v / len(disp):.0f}" for k, v in sorted(agg.items())]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--op", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("--out", required=True)
@@ -150,7 +177,7 @@ def main():
     t.add_argument("--cmd", required=True)
     a = ap.parse_args()
     sys.path.insert(0, ROOT)
-    (cmd_stats if a.what == "stats" else cmd_traffic)(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
 
 
 if __name__ == "__main__":
