@@ -147,6 +147,18 @@ template <int R>
 __device__ __forceinline__ void cursor_init(const KArgs &a, int64_t t, Cursor<R> &cur) {
     cur.t = t;
     cur.k = 0;
+    if ((uint64_t)t >> 32 == 0) {
+        // the usual case: 32-bit divisions (64-bit ones are long sequences)
+        uint32_t rest = (uint32_t)t;
+#pragma unroll
+        for (int d = 0; d < R; ++d) {
+            const uint32_t nt = a.sweep_tiles[d];
+            const uint32_t q = rest / nt;
+            cur.dig[d] = rest - q * nt;
+            rest = q;
+        }
+        return;
+    }
     uint64_t rest = (uint64_t)t;
 #pragma unroll
     for (int d = 0; d < R; ++d) {
@@ -646,22 +658,20 @@ struct Copier {
         nt = (a.flags & TMAP_FLAG_NONTEMPORAL) != 0;
         parity = 0;
         edge = 0;
-        const int64_t n = a.n_tiles;
-        const int64_t G = a.grid, g = blockIdx.x;
+        const int64_t g = blockIdx.x;
         int64_t t0;
         if (a.group == 0) {
             // one contiguous run per workgroup
-            const int64_t base = n / G, rem = n % G;
+            const int64_t base = a.deal_q, rem = a.deal_r;
             cnt = base + (g < rem ? 1 : 0);
             t0 = g * base + (g < rem ? g : rem);
         } else {
             // groups of Q consecutive tiles, dealt round-robin: workgroup g
-            // takes tiles [g*Q, g*Q+Q) of every round of G*Q tiles
-            const int64_t Q = a.group, GQ = G * Q;
-            const int64_t rounds = n / GQ, rem = n % GQ;
-            int64_t last = rem - g * Q;
+            // takes tiles [g*Q, g*Q+Q) of every round of grid*Q tiles
+            const int64_t Q = a.group;
+            int64_t last = a.deal_r - g * Q;
             last = last < 0 ? 0 : (last > Q ? Q : last);
-            cnt = rounds * Q + last;
+            cnt = a.deal_q * Q + last;
             t0 = g * Q;
         }
         cursor_init<R>(a, t0, fcur);

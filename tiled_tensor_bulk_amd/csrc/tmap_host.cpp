@@ -299,6 +299,9 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     a.group = contiguous ? 0u : pl.group;
     a.group_mask = contiguous ? 0xFFFFFFFFu : pl.group - 1u;
     a.big_step = contiguous ? 1 : (int64_t)pl.grid * pl.group - pl.group + 1;
+    const int64_t deal = contiguous ? (int64_t)pl.grid : (int64_t)pl.grid * pl.group;
+    a.deal_q = a.n_tiles / deal;
+    a.deal_r = a.n_tiles % deal;
     uint64_t s1 = 1, sb = (uint64_t)a.big_step;
     for (int d = 0; d < tmap::kMaxRank; ++d) {
         a.step_digits[d] = (uint32_t)(s1 % a.sweep_tiles[d]);

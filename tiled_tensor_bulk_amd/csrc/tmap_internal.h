@@ -90,6 +90,9 @@ struct KArgs {
     int64_t big_step;                // grid*group - group + 1
     uint32_t group;                  // tiles per group (power of two); 0 = contiguous runs
     uint32_t group_mask;             // group - 1, or 0xFFFFFFFF for contiguous runs
+    // n_tiles / (grid*group) and n_tiles % (grid*group) (contiguous runs: by
+    // grid): the same for every workgroup, so divided once on the host
+    int64_t deal_q, deal_r;
     uint32_t n_chunks;            // box_bytes / 16
     uint32_t row_chunks;          // box[0]*es / 16
     uint32_t k_el;                // elements per 16-byte chunk (16 / es)
