@@ -306,6 +306,34 @@ def test_rank1_and_fully_out_of_bounds():
     assert not got[:256].any() and not got[256:512].any()
 
 
+def test_largest_coordinates():
+    """A dimension of 2^31 elements (the largest a map accepts): boxes ending
+    exactly at the last element, reaching past it, wholly past it and at the
+    most negative corner, in both directions of the copy."""
+    say("2^31-element dimension: corners at the int32 limits")
+    big = 1 << 31
+    src = dev_tensor(big, fill_seed=77)
+    m = enc("u8", src, [big, 1], [big], [128, 1])
+    corners = np.array([[big - 128, 0], [big - 64, 0], [big - 1, 0], [2**31 - 1, 0], [-(2**31), 0],
+                        [-100, 0], [0, 0], [big // 2 + 17, 0], [big - 128, -1], [big - 128, 1]], np.int32)
+    n = len(corners)
+    got = gpu_load(m, corners, n).cpu().numpy()
+    om = Map(es=1, dims=[big, 1], strides=[big], box=[128, 1])
+    host = src.cpu().numpy()
+    want = oracle.load_tiles(om, host, corners, n)
+    assert (mm := first_mismatch(got, want, 128)) is None, mm
+    # store the images back over a zeroed copy: exactly the in-bounds bytes return
+    dst = torch.zeros_like(src)
+    T.tmap_store_tiles(enc("u8", dst, [big, 1], [big], [128, 1]), torch.from_numpy(corners).to(DEV), n,
+                       torch.from_numpy(got).to(DEV))
+    check_ok()
+    want_dst = np.zeros(big, np.uint8)
+    oracle.store_tiles(om, want_dst, corners, n, want)
+    del host
+    d = dst.cpu().numpy()
+    assert (mm := first_mismatch(d, want_dst, 1 << 40)) is None, mm
+
+
 def test_zero_tiles_launch_nothing():
     src = dev_tensor(16384, fill_seed=1)
     m = enc("f32", src, [64, 64], [256], [64, 64])
