@@ -334,6 +334,32 @@ def test_largest_coordinates():
     assert (mm := first_mismatch(d, want_dst, 1 << 40)) is None, mm
 
 
+def test_binding_rejects_buffers_the_copy_would_overrun():
+    """Given tensors, the binding checks sizes before launching: a packed
+    buffer or corner array too small for n_tiles, a host tensor or int64
+    corners never reach the GPU."""
+    say("binding argument guards")
+    src = dev_tensor(64 * 256, fill_seed=1)
+    m = enc("f32", src, [64, 64], [256], [16, 16])
+    n = T.tmap_sweep_tiles(m)
+    bb = T.tmap_box_bytes(m)
+    ok = torch.empty(n * bb, dtype=torch.uint8, device=DEV)
+    cases = [
+        lambda: T.tmap_load_tiles(m, None, n, torch.empty(n * bb - 16, dtype=torch.uint8, device=DEV)),
+        lambda: T.tmap_load_tiles(m, None, n, torch.empty(n * bb, dtype=torch.uint8)),
+        lambda: T.tmap_store_tiles(m, torch.zeros((n, 2), dtype=torch.int64, device=DEV), n, ok),
+        lambda: T.tmap_store_tiles(m, torch.zeros((n - 1, 2), dtype=torch.int32, device=DEV), n, ok),
+        lambda: T.tmap_roundtrip(m, m, torch.zeros((1, 2), dtype=torch.int32, device=DEV), 2),
+        lambda: T.tmap_load_tiles(m, None, n, ok.view(2, -1)[:, ::2]),
+        lambda: T.tmap_bulk_copy(torch.empty(64, dtype=torch.uint8, device=DEV), src, 128),
+    ]
+    for i, bad in enumerate(cases):
+        with pytest.raises(ValueError):
+            bad()
+    T.tmap_load_tiles(m, None, n, ok)
+    check_ok()
+
+
 def test_zero_tiles_launch_nothing():
     src = dev_tensor(16384, fill_seed=1)
     m = enc("f32", src, [64, 64], [256], [64, 64])

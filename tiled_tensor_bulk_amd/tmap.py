@@ -135,6 +135,34 @@ def _stream(s) -> Optional[int]:
     return int(s.cuda_stream)
 
 
+def _is_tensor(x) -> bool:
+    return hasattr(x, "data_ptr") and hasattr(x, "numel") and hasattr(x, "element_size")
+
+
+def _check_buffer(x, need: int, what: str) -> None:
+    """When x is a tensor (not a raw pointer), check that the kernels can
+    touch `need` bytes of it: a device buffer too small would be written or
+    read past its end on the GPU."""
+    if not _is_tensor(x):
+        return
+    if not x.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    have = x.numel() * x.element_size()
+    if have < need:
+        raise ValueError(f"{what} holds {have} bytes, the copy needs {need}")
+
+
+def _check_corners(coords, m: tmap_t, n_tiles: int) -> None:
+    if coords is None or not _is_tensor(coords):
+        return
+    import torch
+    if coords.dtype != torch.int32:
+        raise ValueError("coords must be int32")
+    _check_buffer(coords, 4 * int(n_tiles) * tmap_query(m)["rank"], "coords")
+
+
 def _opts(stages=0, grid_wgs=0, flags=0, spin_limit=0, group=0):
     if not (stages or grid_wgs or flags or spin_limit or group):
         return None
@@ -160,18 +188,23 @@ def tmap_encode(dtype, rank: int, global_address, global_dim: Sequence[int],
 
 
 def tmap_load_tiles(src: tmap_t, coords, n_tiles: int, packed_out, stream=None, **opts) -> None:
+    _check_corners(coords, src, n_tiles)
+    _check_buffer(packed_out, int(n_tiles) * tmap_box_bytes(src), "packed_out")
     st = lib().tmap_load_tiles(ctypes.byref(src), _ptr(coords), int(n_tiles), _ptr(packed_out),
                                _opts(**opts), _stream(stream))
     _check(st, "tmap_load_tiles")
 
 
 def tmap_store_tiles(dst: tmap_t, coords, n_tiles: int, packed_in, stream=None, **opts) -> None:
+    _check_corners(coords, dst, n_tiles)
+    _check_buffer(packed_in, int(n_tiles) * tmap_box_bytes(dst), "packed_in")
     st = lib().tmap_store_tiles(ctypes.byref(dst), _ptr(coords), int(n_tiles), _ptr(packed_in),
                                 _opts(**opts), _stream(stream))
     _check(st, "tmap_store_tiles")
 
 
 def tmap_roundtrip(src: tmap_t, dst: tmap_t, coords, n_tiles: int, stream=None, **opts) -> None:
+    _check_corners(coords, src, n_tiles)
     st = lib().tmap_roundtrip(ctypes.byref(src), ctypes.byref(dst), _ptr(coords), int(n_tiles),
                               _opts(**opts), _stream(stream))
     _check(st, "tmap_roundtrip")
@@ -179,12 +212,15 @@ def tmap_roundtrip(src: tmap_t, dst: tmap_t, coords, n_tiles: int, stream=None, 
 
 def tmap_roundtrip_add_f32(src: tmap_t, dst: tmap_t, coords, n_tiles: int, addend: float, stream=None,
                            **opts) -> None:
+    _check_corners(coords, src, n_tiles)
     st = lib().tmap_roundtrip_add_f32(ctypes.byref(src), ctypes.byref(dst), _ptr(coords), int(n_tiles),
                                       float(addend), _opts(**opts), _stream(stream))
     _check(st, "tmap_roundtrip_add_f32")
 
 
 def tmap_bulk_copy(dst, src, nbytes: int, stream=None, **opts) -> None:
+    _check_buffer(dst, int(nbytes), "dst")
+    _check_buffer(src, int(nbytes), "src")
     st = lib().tmap_bulk_copy(_ptr(dst), _ptr(src), int(nbytes), _opts(**opts), _stream(stream))
     _check(st, "tmap_bulk_copy")
 
