@@ -78,7 +78,8 @@ typedef struct tmap_launch_opts {
                              when each workgroup takes a single band unit)               */
     uint32_t grid_wgs;    /* workgroups launched; fewer than there are groups makes each
                              take several (default: one workgroup per group; with
-                             TMAP_FLAG_CONTIGUOUS, twice what fits in LDS per CU)         */
+                             TMAP_FLAG_CONTIGUOUS, twice what fits in LDS per CU; in
+                             producer-wave mode, 8 per CU)                               */
     uint32_t flags;       /* TMAP_FLAG_* bits                                              */
     uint32_t spin_limit;  /* readiness-wait polls before TMAP_ERROR_TIMEOUT (default 2^22) */
     uint32_t group;       /* tiles (band units) dealt to a workgroup at a time, a power of

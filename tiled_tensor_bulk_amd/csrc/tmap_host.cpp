@@ -243,6 +243,10 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
         if (per_cu < 1) per_cu = 1;
         grid = (uint32_t)dev.cus * per_cu;
     }
+    // producer-wave mode: a persistent grid of 8 workgroups per CU measured
+    // best (each runs a producer wave ahead of four consumer waves, which
+    // needs several tiles per workgroup to pay off)
+    if (!grid && producer_wave) grid = 8u * (uint32_t)dev.cus;
     if (!grid) grid = (uint32_t)std::min<int64_t>(useful, 1 << 30);
     if ((int64_t)grid > useful) grid = (uint32_t)useful;
     pl.nslot = nslot;
