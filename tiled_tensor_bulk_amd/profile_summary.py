@@ -84,6 +84,16 @@ def cmd_stats(a):
         mx = float(r.get("MaxNs", 0)) / 1e3
         pct = float(r.get("Percentage", 0))
         out.append(f"| {short(name)} | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f}% |")
+    if a.trace:
+        # the bench times its last `steps` launches (after the warm-up, whose
+        # first launches run while the clocks settle): average those alone
+        tr = [r for r in csv.DictReader(open(a.trace)) if "copy_kernel" in r["Kernel_Name"]]
+        tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+        last = tr[-a.last:]
+        us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in last]
+        if us:
+            out += ["", f"copy kernel, last {len(us)} launches (the bench's timed steps): "
+                        f"average {sum(us) / len(us):.1f} us, median {sorted(us)[len(us) // 2]:.1f} us"]
     open(a.out, "w").write("\n".join(out) + "\n")
     print("\n".join(out))
 
@@ -168,6 +178,8 @@ def main():
     s.add_argument("csv")
     s.add_argument("--out", required=True)
     s.add_argument("--cmd", required=True)
+    s.add_argument("--trace", help="the run's kernel trace csv (adds the average of the last launches)")
+    s.add_argument("--last", type=int, default=100)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
