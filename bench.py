@@ -67,6 +67,7 @@ def main():
     ap.add_argument("--flags", type=int, default=-1,
                     help="TMAP_FLAG_* bits; default: non-temporal hints when the tensor exceeds the 256 MB MALL")
     ap.add_argument("--group", type=int, default=0)
+    ap.add_argument("--regions", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -105,7 +106,7 @@ def main():
     if args.flags < 0:
         args.flags = T.FLAG_NONTEMPORAL if w.alloc_bytes > (256 << 20) else 0
     # 0 = the library's default for stages, grid and group
-    opts = dict(stages=args.stages, grid_wgs=args.grid, flags=args.flags, group=args.group)
+    opts = dict(stages=args.stages, grid_wgs=args.grid, flags=args.flags, group=args.group, regions=args.regions)
 
     dst = packed = None
     if args.op == "bulk":
@@ -210,7 +211,7 @@ def main():
                    "box": list(w.box), "swizzle": list(w.swizzle), "tiles": n, "box_bytes": bb,
                    "schedule": schedule, "stages": args.stages or "auto", "grid_wgs": args.grid or "auto",
                    "flags": args.flags,
-                   "group": args.group or "auto",
+                   "group": args.group or "auto", "regions": args.regions or "auto",
                    "algorithmic_bytes_per_step": algo_bytes},
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBPS, 2),
         "tiles_per_s": round(n / (wall / args.steps), 1),

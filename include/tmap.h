@@ -86,6 +86,13 @@ typedef struct tmap_launch_opts {
                              two <= 64 (default: enough boxes side by side to span 512
                              bytes of a row, at least 2 and at most 8; band units: 2 for
                              a round trip, 1 for a load or store; explicit corners: 8)   */
+    uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
+                             streams, each sweeping an equal contiguous stretch of the
+                             tiles (workgroup i takes stretch i mod regions), so that the
+                             tiles in flight lie in that many places of the tensor
+                             instead of one.  How the addresses in flight fall on the
+                             HBM channels decides which is faster (default: 2 for loads
+                             and stores on the band schedule, else 1)                  */
 } tmap_launch_opts;
 
 /* Band schedule.  A sweep (coords == NULL) of boxes whose rows hold 64 to

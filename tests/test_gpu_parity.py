@@ -222,7 +222,8 @@ def _fuzz_case(rng, idx):
                 flags=int(rng.choice([0, T.FLAG_CONTIGUOUS, T.FLAG_NONTEMPORAL, T.FLAG_THREAD_COPY,
                                       T.FLAG_THREAD_COPY | T.FLAG_CONTIGUOUS, T.FLAG_PRODUCER_WAVE,
                                       T.FLAG_PRODUCER_WAVE | T.FLAG_CONTIGUOUS])),
-                group=int(rng.choice([0, 1, 2, 4, 8, 64])))
+                group=int(rng.choice([0, 1, 2, 4, 8, 64])),
+                regions=int(rng.choice([0, 1, 2, 3, 8, 64])))
     return es, dims, strides, box, swz, alloc, coords, opts
 
 
@@ -368,6 +369,27 @@ def test_zero_tiles_launch_nothing():
     check_ok()
 
 
+def test_launch_options_out_of_range_are_rejected():
+    """Launch options outside their documented ranges give INVALID_VALUE
+    before anything is launched, and the destination stays untouched."""
+    src = dev_tensor(16384, fill_seed=1)
+    m = enc("f32", src, [64, 64], [256], [16, 16])
+    n = T.tmap_sweep_tiles(m)
+    out = dev_tensor(n * 1024, fill_seed=2)
+    before = out.clone()
+    for bad in (dict(stages=5), dict(group=3), dict(group=128), dict(regions=65),
+                dict(flags=T.FLAG_BAND | T.FLAG_WHOLE_BOX),
+                dict(flags=T.FLAG_THREAD_COPY | T.FLAG_PRODUCER_WAVE)):
+        with pytest.raises(T.TmapError) as e:
+            T.tmap_load_tiles(m, None, n, out, **bad)
+        assert e.value.status == T.INVALID_VALUE, bad
+    check_ok()
+    assert torch.equal(out, before)
+    for ok in (dict(regions=64), dict(regions=1), dict(group=64, regions=7)):
+        T.tmap_load_tiles(m, None, n, out, **ok)
+        check_ok()
+
+
 def test_budget_mismatch_times_out_on_the_band_schedule():
     """The same on a band-schedule sweep: each 16 KiB unit's record never
     reaches zero outstanding bytes."""
@@ -413,16 +435,18 @@ def test_repeat_is_deterministic():
         assert torch.equal(a, b), st
 
 
-@pytest.mark.parametrize("mode", ["thread_copy", "producer_wave", "whole_box"])
+@pytest.mark.parametrize("mode", ["thread_copy", "producer_wave", "whole_box", "regions_3", "regions_1"])
 @pytest.mark.parametrize("name", ["tile64_f32", "strips_f16", "ragged_bf16", "pad5d_f32", "sweep2g_u8"])
 def test_other_modes_match_the_staged_copy(name, mode):
-    """The register-path and producer-wave variants, and the ring on whole
-    boxes, give the same bytes as the default schedule (which the tests above
-    pin to the oracle; the band schedule where it applies) for load, store
-    and round trip of every workload."""
+    """The register-path and producer-wave variants, the ring on whole boxes,
+    and other deals of the groups to the grid (regions), give the same bytes
+    as the default schedule (which the tests above pin to the oracle; the
+    band schedule where it applies) for load, store and round trip of every
+    workload."""
     w = inputs.WORKLOADS[name]
-    flag = {"thread_copy": T.FLAG_THREAD_COPY, "producer_wave": T.FLAG_PRODUCER_WAVE,
-            "whole_box": T.FLAG_WHOLE_BOX}[mode]
+    alt = {"thread_copy": dict(flags=T.FLAG_THREAD_COPY), "producer_wave": dict(flags=T.FLAG_PRODUCER_WAVE),
+           "whole_box": dict(flags=T.FLAG_WHOLE_BOX), "regions_3": dict(regions=3),
+           "regions_1": dict(regions=1)}[mode]
     say(f"{mode} vs staged: {name}")
     src = inputs.device_bytes(w, DEV)
     m = enc(w.dtype, src, w.dims, w.strides, w.box, w.swizzle)
@@ -435,17 +459,17 @@ def test_other_modes_match_the_staged_copy(name, mode):
         n = len(cn)
     c = None if cn is None else torch.from_numpy(cn).to(DEV)
     a = gpu_load(m, cn, n)
-    b = gpu_load(m, cn, n, flags=flag)
+    b = gpu_load(m, cn, n, **alt)
     assert torch.equal(a, b)
     d1 = dev_tensor(w.alloc_bytes, fill_seed=7)
     d2 = d1.clone()
     T.tmap_store_tiles(enc(w.dtype, d1, w.dims, w.strides, w.box, w.swizzle), c, n, a)
-    T.tmap_store_tiles(enc(w.dtype, d2, w.dims, w.strides, w.box, w.swizzle), c, n, a, flags=flag)
+    T.tmap_store_tiles(enc(w.dtype, d2, w.dims, w.strides, w.box, w.swizzle), c, n, a, **alt)
     check_ok()
     assert torch.equal(d1, d2)
     del a, b
     d1.copy_(d2)
     T.tmap_roundtrip(m, enc(w.dtype, d1, w.dims, w.strides, w.box, w.swizzle), c, n)
-    T.tmap_roundtrip(m, enc(w.dtype, d2, w.dims, w.strides, w.box, w.swizzle), c, n, flags=flag)
+    T.tmap_roundtrip(m, enc(w.dtype, d2, w.dims, w.strides, w.box, w.swizzle), c, n, **alt)
     check_ok()
     assert torch.equal(d1, d2)

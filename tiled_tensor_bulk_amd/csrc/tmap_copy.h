@@ -658,7 +658,15 @@ struct Copier {
         nt = (a.flags & TMAP_FLAG_NONTEMPORAL) != 0;
         parity = 0;
         edge = 0;
-        const int64_t g = blockIdx.x;
+        // workgroup index -> place in the deal: with R regions the first
+        // R*(grid/R) workgroups are dealt as R interleaved streams, workgroup
+        // i taking the next place of stretch i mod R (a permutation of
+        // 0..grid-1, so every place is still taken once)
+        int64_t g = blockIdx.x;
+        if (a.regions > 1) {
+            const uint32_t per = gridDim.x / a.regions;
+            if ((uint32_t)g < per * a.regions) g = (int64_t)((uint32_t)g % a.regions) * per + (uint32_t)g / a.regions;
+        }
         int64_t t0;
         if (a.group == 0) {
             // one contiguous run per workgroup

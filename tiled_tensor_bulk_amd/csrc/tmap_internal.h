@@ -98,6 +98,7 @@ struct KArgs {
     uint32_t k_el;                // elements per 16-byte chunk (16 / es)
     uint32_t elemwise;            // 1 when the swizzle moves data inside 16-byte chunks
     uint32_t grid;                // workgroups launched
+    uint32_t regions;             // interleaved streams the groups are dealt as (1: none)
     uint32_t flags;               // TMAP_FLAG_*
     uint32_t spin_limit;          // readiness-wait polls before giving up
     uint32_t add_f32;             // round trip: add `addend` to every fp32 element before storing

@@ -45,7 +45,7 @@ class tmap_swizzle(ctypes.Structure):
 class tmap_launch_opts(ctypes.Structure):
     _fields_ = [("stages", ctypes.c_uint32), ("grid_wgs", ctypes.c_uint32),
                 ("flags", ctypes.c_uint32), ("spin_limit", ctypes.c_uint32),
-                ("group", ctypes.c_uint32)]
+                ("group", ctypes.c_uint32), ("regions", ctypes.c_uint32)]
 
 
 class tmap_info(ctypes.Structure):
@@ -163,10 +163,10 @@ def _check_corners(coords, m: tmap_t, n_tiles: int) -> None:
     _check_buffer(coords, 4 * int(n_tiles) * tmap_query(m)["rank"], "coords")
 
 
-def _opts(stages=0, grid_wgs=0, flags=0, spin_limit=0, group=0):
-    if not (stages or grid_wgs or flags or spin_limit or group):
+def _opts(stages=0, grid_wgs=0, flags=0, spin_limit=0, group=0, regions=0):
+    if not (stages or grid_wgs or flags or spin_limit or group or regions):
         return None
-    return ctypes.byref(tmap_launch_opts(stages, grid_wgs, flags, spin_limit, group))
+    return ctypes.byref(tmap_launch_opts(stages, grid_wgs, flags, spin_limit, group, regions))
 
 
 # ------------------------------------------------------------------- C ABI names
