@@ -68,6 +68,7 @@ def main():
                     help="TMAP_FLAG_* bits; default: non-temporal hints when the tensor exceeds the 256 MB MALL")
     ap.add_argument("--group", type=int, default=0)
     ap.add_argument("--regions", type=int, default=0)
+    ap.add_argument("--band-rows", type=int, default=0, help="box rows per band on the band schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -106,7 +107,8 @@ def main():
     if args.flags < 0:
         args.flags = T.FLAG_NONTEMPORAL if w.alloc_bytes > (256 << 20) else 0
     # 0 = the library's default for stages, grid and group
-    opts = dict(stages=args.stages, grid_wgs=args.grid, flags=args.flags, group=args.group, regions=args.regions)
+    opts = dict(stages=args.stages, grid_wgs=args.grid, flags=args.flags, group=args.group, regions=args.regions,
+                band_rows=args.band_rows)
 
     dst = packed = None
     if args.op == "bulk":
@@ -151,8 +153,10 @@ def main():
     if args.op == "bulk":
         schedule = "whole boxes (rank-1 16 KiB tiles)"
     else:
-        band = T.tmap_band_boxes(ms, None if args.op in ("load", "store") else md, coords is not None, args.flags)
-        schedule = f"band: {band} boxes x 16 rows per stage" if band else "whole boxes"
+        band = T.tmap_band_boxes(ms, None if args.op in ("load", "store") else md, coords is not None, args.flags,
+                                 args.band_rows)
+        rows = 16384 // (band * w.box[0] * es) if band else 0
+        schedule = f"band: {band} boxes x {rows} rows per stage" if band else "whole boxes"
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -212,6 +216,7 @@ def main():
                    "schedule": schedule, "stages": args.stages or "auto", "grid_wgs": args.grid or "auto",
                    "flags": args.flags,
                    "group": args.group or "auto", "regions": args.regions or "auto",
+                   "band_rows": args.band_rows or "auto",
                    "algorithmic_bytes_per_step": algo_bytes},
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBPS, 2),
         "tiles_per_s": round(n / (wall / args.steps), 1),

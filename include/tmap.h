@@ -93,23 +93,33 @@ typedef struct tmap_launch_opts {
                              instead of one.  How the addresses in flight fall on the
                              HBM channels decides which is faster (default: 2 for loads
                              and stores on the band schedule, else 1)                  */
+    uint32_t band_rows;   /* band schedule: box rows per band, a power of two.  A unit is
+                             then 16 KiB / (band_rows * box row bytes) boxes side by
+                             side.  Default: 4 for a round trip (units 4 KiB wide), 8
+                             for a load or store (2 KiB wide), or the next taller
+                             height that fits.  An explicit height that does not fit
+                             the box, the swizzle or the sweep (see below) is
+                             TMAP_ERROR_INVALID_VALUE where the band schedule applies,
+                             and ignored elsewhere                                       */
 } tmap_launch_opts;
 
 /* Band schedule.  A sweep (coords == NULL) of boxes whose rows hold 64 to
- * 512 bytes, whose dimension-1 extent is 16 times a power of two and whose
- * higher extents are 1 runs on it when the tensor spans at least 256 MiB
- * (dims[rank-1] * strides[rank-1]; smaller ones fit in the last-level cache
- * and gain nothing from it) or TMAP_FLAG_BAND asks for it, unless
- * TMAP_FLAG_WHOLE_BOX, thread-copy or producer-wave mode is asked for.  A
- * stage then holds the same 16-row band
- * of the neighbouring boxes that together span 1 KiB of a row (a "unit"),
- * each box's band being the contiguous piece of that box's swizzled LDS
- * image that it always is; the swizzle must map each band onto itself
- * (16 * box[0] a multiple of 2^(m+s+b)) and a row of the sweep must hold a
- * whole unit.  Every box still passes through LDS in its own layout and the
- * results are the same; the tensor is read and written 1 KiB wide and 16
- * rows tall at a time, which HBM serves faster than narrow rows of tall
- * boxes.  A stage's byte record counts the unit's 16 KiB. */
+ * 512 bytes, whose dimension-1 extent is the band height times a power of
+ * two and whose higher extents are 1 runs on it when the tensor spans at
+ * least 256 MiB (dims[rank-1] * strides[rank-1]; smaller ones fit in the
+ * last-level cache and gain nothing from it) or TMAP_FLAG_BAND asks for it,
+ * unless TMAP_FLAG_WHOLE_BOX, thread-copy or producer-wave mode is asked
+ * for.  A stage then holds the same band of band_rows rows of the
+ * neighbouring boxes that together fill 16 KiB (a "unit"), each box's band
+ * being the contiguous piece of that box's swizzled LDS image that it
+ * always is.  The swizzle must map each band onto itself (band_rows * box[0]
+ * a multiple of 2^(m+b): the swizzle only changes element-offset bits
+ * [m, m+b)), and a row of the sweep must hold a whole unit.  Every box's
+ * image is unchanged; the tensor is read and written in wide, short pieces
+ * (4 rows of 4 KiB, or 8 rows of 2 KiB, by default), which HBM serves faster
+ * than narrow rows of tall boxes.  A stage's byte record counts the unit's
+ * 16 KiB.  In a round trip, where no image leaves the workgroup, every band
+ * is staged in the arrangement of a box's first band. */
 
 /* Tile order: tile index t runs innermost-fastest over the sweep (or over the
  * coords array).  By default the tiles are dealt in groups of `group`
@@ -279,10 +289,12 @@ tmap_status tmap_inbounds_elems(const tmap_t *map, const int32_t *host_coords,
  * stage on the band schedule described at tmap_launch_opts, or 0 when every
  * stage holds one whole box.  src is the swept map of a load or round trip
  * (of a store: the destination map), dst the round trip's destination map or
- * NULL; coords is non-NULL for explicit corners (any non-NULL pointer: it is
- * not read); flags are the TMAP_FLAG_* bits the copy would get.  0 for a
- * map never encoded. */
-uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *coords, uint32_t flags);
+ * NULL for a load or store; coords is non-NULL for explicit corners (any non-NULL pointer: it is
+ * not read); opts are the launch options the copy would get (NULL: the
+ * defaults).  0 for a map never encoded, and for a band_rows the launch
+ * would reject. */
+uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *coords,
+                         const tmap_launch_opts *opts);
 
 /* Decoded fields of an encoded map (for inspection and tests). */
 typedef struct tmap_info {

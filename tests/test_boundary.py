@@ -199,14 +199,18 @@ def _enc_rows(dt, dims, box, swz=(0, 0, 0), pad_rows=0):
 
 def test_band_schedule_choice():
     """Which sweeps take the band schedule: boxes with 64..512-byte rows and a
-    dimension-1 extent of 16 times a power of two, swizzles whose period fits
-    a 16-row band, a row of the sweep holding a whole unit, sweeps only, and
-    not in the thread-copy, producer-wave or whole-box modes; by default only
-    for tensors spanning 256 MiB or more (TMAP_FLAG_BAND lifts that)."""
+    dimension-1 extent of the band height (16 rows by default) times a power
+    of two, swizzles that map a band onto itself, a row of the sweep holding a
+    whole unit, sweeps only, and not in the thread-copy, producer-wave or
+    whole-box modes; by default only for tensors spanning 256 MiB or more
+    (TMAP_FLAG_BAND lifts that)."""
     W = inputs.WORKLOADS
     B = T.FLAG_BAND
-    for name, want, forced in [("sweep2g_u8", 8, 8), ("ragged_bf16", 8, 8), ("plus1_f32", 4, 4),
-                               ("strips_f16", 0, 2), ("tile64_f32", 0, 0), ("pad5d_f32", 0, 0)]:
+    # (name, boxes per unit of a load or store (8-row bands), of a round trip
+    # (4-row bands), of a load forced onto the band schedule)
+    for name, want, want_rt, forced in [("sweep2g_u8", 16, 32, 16), ("ragged_bf16", 16, 32, 16),
+                                        ("plus1_f32", 8, 16, 8), ("strips_f16", 0, 0, 4),
+                                        ("tile64_f32", 0, 0, 1), ("pad5d_f32", 0, 0, 0)]:
         w = W[name]
         m = T.tmap_encode(w.dtype, w.rank, BASE, w.dims, w.strides, w.box, None, w.swizzle)
         assert T.tmap_band_boxes(m) == want, name
@@ -215,37 +219,60 @@ def test_band_schedule_choice():
             assert T.tmap_band_boxes(m, flags=fl | B) == 0
         assert T.tmap_band_boxes(m, flags=T.FLAG_NONTEMPORAL | T.FLAG_CONTIGUOUS) == want
         assert T.tmap_band_boxes(m, explicit_coords=True, flags=B) == 0
-        assert T.tmap_band_boxes(m, m) == want
+        assert T.tmap_band_boxes(m, m) == want_rt
     # the size threshold: 256 MiB spanned by the outermost dimension
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65536], [128, 128])) == 8
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65536], [128, 128])) == 16
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128])) == 0
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128]), flags=B) == 8
-    # row width: 64..512 bytes, 1 KiB of row per unit
-    for dt, box0, want in [("u8", 32, 0), ("u8", 64, 16), ("u8", 128, 8), ("u8", 256, 4), ("f16", 256, 2),
-                           ("f32", 128, 2), ("f32", 256, 0), ("f64", 8, 16), ("f64", 64, 2), ("f32", 24, 0)]:
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128]), flags=B) == 16
+    # row width: 64..512 bytes; units of 8 rows (2 KiB wide), or taller bands
+    # when a row of the sweep (20 boxes here) is narrower than that
+    for dt, box0, want in [("u8", 32, 0), ("u8", 64, 16), ("u8", 128, 16), ("u8", 256, 8), ("f16", 256, 4),
+                           ("f32", 128, 4), ("f32", 256, 0), ("f64", 8, 16), ("f64", 64, 4), ("f32", 24, 0)]:
         assert T.tmap_band_boxes(_enc_rows(dt, [box0 * 20, 100], [box0, 16]), flags=B) == want, (dt, box0)
-    # dimension-1 extent
-    for box1, want in [(8, 0), (16, 8), (24, 0), (32, 8), (48, 0), (64, 8), (128, 8)]:
+    # dimension-1 extent: the band height times a power of two
+    for box1, want in [(4, 0), (8, 16), (16, 16), (24, 0), (32, 16), (48, 0), (64, 16), (128, 16)]:
         assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, box1]), flags=B) == want, box1
-    # swizzle period 2^(m+s+b) elements must divide a band of 16 * 128 elements
-    for swz, want in [((3, 4, 3), 8), ((0, 4, 3), 8), ((3, 4, 4), 8), ((2, 4, 5), 8), ((3, 4, 5), 0), ((1, 4, 7), 0)]:
-        assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128], swz), flags=B) == want, swz
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 4]), flags=B, band_rows=4) == 32
+    # the swizzle only changes element-offset bits [m, m+b): a band of
+    # 16 * 128 elements must be a whole number of 2^(m+b) blocks
+    for swz, want in [((3, 4, 3), 8), ((0, 4, 3), 8), ((3, 4, 4), 8), ((2, 4, 5), 8), ((3, 4, 5), 8), ((1, 4, 7), 8),
+                      ((7, 4, 7), 8), ((8, 4, 8), 0)]:
+        assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128], swz), flags=B, band_rows=16) == want, swz
+    # ... which a taller band can satisfy: by default the next height that fits
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128], (8, 4, 8)), flags=B, band_rows=32) == 4
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128], (8, 4, 8)), flags=B) == 4
+    # band height: a power of two dividing box[1], at most a 16 KiB stage, and
+    # a unit of 16 KiB / (rows * row bytes) boxes fitting a row of the sweep
+    wide = _enc_rows("u8", [65536, 300], [128, 128], (3, 4, 3))
+    for rows, want in [(0, 16), (1, 128), (2, 64), (4, 32), (8, 16), (16, 8), (32, 4), (64, 2), (128, 1), (256, 0),
+                       (3, 0), (48, 0)]:
+        assert T.tmap_band_boxes(wide, flags=B, band_rows=rows) == want, rows
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128]), flags=B, band_rows=1) == 0  # 32 boxes a row
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128]), flags=B, band_rows=4) == 32
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 48]), flags=B, band_rows=16) == 0  # 48 = 16 * 3
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 48]), flags=B, band_rows=0) == 0
+    # a 64-byte row with the (3,4,3) swizzle: its 128-element blocks span 2 rows
+    assert T.tmap_band_boxes(_enc_rows("u8", [65536, 300], [64, 128], (3, 4, 3)), flags=B, band_rows=1) == 0
+    assert T.tmap_band_boxes(_enc_rows("u8", [65536, 300], [64, 128], (3, 4, 3)), flags=B, band_rows=2) == 128
     # a swizzle that moves bytes inside 16-byte chunks takes the element path
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128], (3, 0, 3)), flags=B) == 0
-    # a row of the sweep must hold one whole unit (8 boxes of 128 bytes)
+    # a row of the sweep must hold one whole unit (here 8 boxes of 128 bytes
+    # at the tallest height a 16-row box allows)
     assert T.tmap_band_boxes(_enc_rows("u8", [7 * 128, 64], [128, 16]), flags=B) == 0
     assert T.tmap_band_boxes(_enc_rows("u8", [7 * 128 + 1, 64], [128, 16]), flags=B) == 8
     # higher box extents must be 1
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 1]), flags=B) == 8
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 1]), flags=B) == 16
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 2]), flags=B) == 0
     assert T.tmap_band_boxes(_enc_rows("u8", [4096], [128]), flags=B) == 0
     # a unit must stay within 2^31 bytes of its corner, in both maps: with
     # this stride a 128x16 box spans 128 + 15 * stride < 2^31 bytes (a valid
-    # map) but a unit 1 KiB wide does not
+    # map) but a 16-row unit 1 KiB wide does not (an 8-row one does)
     stride = 143165552
     assert 128 + 15 * stride < 2**31 <= 1024 + 15 * stride
     far = T.tmap_encode("u8", 2, BASE, [4096, 20], [stride], [128, 16])
-    assert T.tmap_band_boxes(far, flags=B) == 0
+    assert T.tmap_band_boxes(far, flags=B, band_rows=16) == 0
+    assert T.tmap_band_boxes(far, flags=B) == 16
     near = _enc_rows("u8", [4096, 20], [128, 16])
-    assert T.tmap_band_boxes(near, flags=B) == 8 and T.tmap_band_boxes(near, far, flags=B) == 0
+    assert T.tmap_band_boxes(near, flags=B, band_rows=16) == 8
+    assert T.tmap_band_boxes(near, far, flags=B, band_rows=16) == 0
     assert T.tmap_band_boxes(T.tmap_t()) == 0

@@ -1,11 +1,14 @@
-"""GPU parity of the band schedule (sweeps of narrow boxes staged as 16-row
-bands of neighbouring boxes) against the CPU oracle, byte for byte.
+"""GPU parity of the band schedule (sweeps of narrow boxes staged as bands
+of rows of neighbouring boxes, 16 KiB to a stage) against the CPU oracle,
+byte for byte.
 
 Seeded random maps that take the band schedule (the host query says so for
 every case): element sizes 1..8, box rows of 64..512 bytes, dimension-1
-extents 16..128, ranks 2..5 with higher box extents 1, swizzles whose period
-fits a band, ragged last rows and columns, and rows of the sweep whose last
-unit holds fewer boxes than a full one.  Each case loads, stores and round
+extents 16..128, band heights 1..64 rows, ranks 2..5 with higher box extents
+1, swizzles that map a band onto itself (often with a period longer than a
+band, so that the bands of a box differ by an XOR), ragged last rows and
+columns, and rows of the sweep whose last unit holds fewer boxes than a full
+one.  Each case loads, stores and round
 trips (into a destination map of another size and pitch, so that the boxes
 missing from a short last unit would land inside it if they were stored),
 and fp32 cases also run the fused +addend round trip.
@@ -62,7 +65,10 @@ def _strides(rng, dims, es):
     return out, s
 
 
-def _swizzle(rng, es, box0, box1):
+def _swizzle(rng, es, box0, box1, rows):
+    """A random swizzle the encoder accepts that maps a band of `rows` box
+    rows onto itself (rows * box0 a multiple of 2^(m+b)); often one whose
+    period is longer than a band, so that bands differ by an XOR."""
     n_el = box0 * box1
     k_el = 16 // es
     for _ in range(20):
@@ -70,52 +76,61 @@ def _swizzle(rng, es, box0, box1):
         if b == 0:
             return (0, 0, 0)
         m = int(rng.integers(k_el.bit_length() - 1, 5))
-        s = int(rng.integers(b, 6))
-        if (n_el % (1 << (m + b)) == 0 and (16 * box0) % (1 << (m + s + b)) == 0 and b + m + s <= 20):
+        s = int(rng.integers(b, 7))
+        if n_el % (1 << (m + b)) == 0 and (rows * box0) % (1 << (m + b)) == 0 and b + m + s <= 20:
             return (b, m, s)
     return (0, 0, 0)
 
 
 def _band_case(rng):
+    """(es, dims, box, swizzle, band_rows asked for (0: the default 16),
+    boxes per unit)."""
     while True:
         es = int(rng.choice([1, 2, 4, 8]))
         rc = int(rng.choice([4, 8, 16, 32]))     # 16-byte chunks per box row
         box0 = rc * 16 // es
         if box0 <= 256:
             break
-    g = 64 // rc
     box1 = int(rng.choice([16, 32, 64, 128]))
     while box0 * es * box1 > 65536:
         box1 //= 2
+    want_rows = int(rng.choice([0, 0, 1, 2, 4, 8, 16, 32, 64]))
+    while want_rows > box1 or want_rows * rc > 1024:
+        want_rows //= 2
+    rows = want_rows or 16
+    g = 1024 // (rows * rc)
     rank = int(rng.choice([2, 2, 2, 3, 4, 5]))
     tiles0 = int(rng.integers(g, 3 * g + 3))
     dims0 = tiles0 * box0 - int(rng.integers(0, box0))
     dims1 = int(rng.integers(1, (3 if rank == 2 else 2) * box1 + 2))
     dims = [dims0, dims1] + [int(rng.integers(1, 3)) for _ in range(rank - 2)]
     box = [box0, box1] + [1] * (rank - 2)
-    return es, dims, box, _swizzle(rng, es, box0, box1)
+    return es, dims, box, _swizzle(rng, es, box0, box1, rows), want_rows, g
 
 
-def _opts(rng):
+def _opts(rng, band_rows):
     # these tensors are small: TMAP_FLAG_BAND takes the band schedule anyway
     return dict(stages=int(rng.integers(1, 5)), grid_wgs=int(rng.choice([0, 0, 1, 3, 7])),
-                group=int(rng.choice([0, 1, 2, 4, 8])),
-                flags=T.FLAG_BAND | int(rng.choice([0, T.FLAG_NONTEMPORAL, T.FLAG_CONTIGUOUS])))
+                group=int(rng.choice([0, 1, 2, 4, 8])), regions=int(rng.choice([0, 0, 1, 2, 3])),
+                flags=T.FLAG_BAND | int(rng.choice([0, T.FLAG_NONTEMPORAL, T.FLAG_CONTIGUOUS])),
+                band_rows=band_rows)
 
 
-@pytest.mark.parametrize("chunk", range(3))
+@pytest.mark.parametrize("chunk", range(4))
 def test_band_schedule_random_sweeps(chunk):
     rng = np.random.default_rng(7100 + chunk)
     for i in range(24):
-        es, dims, box, swz = _band_case(rng)
+        es, dims, box, swz, rows, g_want = _band_case(rng)
         strides, alloc = _strides(rng, dims, es)
-        opts = _opts(rng)
+        opts = _opts(rng, rows)
         om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
         src = dev_bytes(alloc, int(rng.integers(1 << 30)))
         m = T.tmap_encode(DT[es], len(dims), src.data_ptr(), dims, strides, box, None, swz)
-        g = T.tmap_band_boxes(m, None, False, opts["flags"])
+        g = T.tmap_band_boxes(m, None, False, opts["flags"], rows)
         say(f"band {chunk}/{i}: es={es} dims={dims} strides={strides} box={box} swz={swz} boxes/unit={g} {opts}")
-        assert g == 64 // (box[0] * es // 16)
+        # an explicit height gives exactly its unit; the default takes the
+        # direction's height or a taller one, at most the 16 rows built for
+        assert g == g_want if rows else g >= g_want
         n = T.tmap_sweep_tiles(m)
         bb = T.tmap_box_bytes(m)
         host = src.cpu().numpy()
@@ -140,7 +155,8 @@ def test_band_schedule_random_sweeps(chunk):
         dst2 = dev_bytes(dalloc, int(rng.integers(1 << 30)))
         want2 = dst2.cpu().numpy().copy()
         md = T.tmap_encode(DT[es], len(dims), dst2.data_ptr(), ddims, dstrides, box, None, swz)
-        assert T.tmap_band_boxes(m, md, False, opts["flags"]) == g
+        g_rt = T.tmap_band_boxes(m, md, False, opts["flags"], rows)
+        assert g_rt == g if rows else g_rt >= g_want
         T.tmap_roundtrip(m, md, None, n, **opts)
         check_ok()
         omd = Map(es=es, dims=ddims, strides=dstrides, box=box, swizzle=swz)
@@ -218,3 +234,64 @@ def test_long_rings_keep_every_stage(stages, flags):
     T.tmap_store_tiles(md, None, n, packed, **opts)
     check_ok()
     assert torch.equal(dst, src)                       # storing every image back restores the tensor
+
+
+@pytest.mark.parametrize("rows", [1, 2, 4, 8, 16, 32, 64, 128])
+def test_every_band_height_of_the_128_byte_swizzle(rows):
+    """16384 x 520 bytes in 128 x 128 boxes with the 128-byte swizzle (3,4,3),
+    whose period is 8 rows: every band height from 1 row (128 boxes to a
+    unit) to a whole box (one box).  Heights under 8 rows stage bands that
+    differ from a box's first band by an XOR.  Load, store and round trip
+    against the oracle; the last tile row is ragged."""
+    dims, strides, box, swz = [16384, 520], [16384], [128, 128], (3, 4, 3)
+    say(f"band height {rows}")
+    src = dev_bytes(16384 * 520, 70 + rows)
+    ms = T.tmap_encode("u8", 2, src.data_ptr(), dims, strides, box, None, swz)
+    assert T.tmap_band_boxes(ms, None, False, T.FLAG_BAND, rows) == 128 // rows
+    n = T.tmap_sweep_tiles(ms)
+    opts = dict(flags=T.FLAG_BAND | T.FLAG_NONTEMPORAL, band_rows=rows)
+    om = Map(es=1, dims=dims, strides=strides, box=box, swizzle=swz)
+    host = src.cpu().numpy()
+    packed = torch.empty(n * 16384, dtype=torch.uint8, device=DEV)
+    T.tmap_load_tiles(ms, None, n, packed, **opts)
+    check_ok()
+    want = oracle.load_tiles(om, host, None, n)
+    assert (mm := first_mismatch(packed.cpu().numpy(), want)) is None, ("load", mm)
+    dst = dev_bytes(16384 * 520, 170 + rows)
+    want_dst = dst.cpu().numpy().copy()
+    md = T.tmap_encode("u8", 2, dst.data_ptr(), dims, strides, box, None, swz)
+    T.tmap_store_tiles(md, None, n, packed, **opts)
+    check_ok()
+    oracle.store_tiles(om, want_dst, None, n, want)
+    assert (mm := first_mismatch(dst.cpu().numpy(), want_dst)) is None, ("store", mm)
+    dst2 = dev_bytes(16384 * 520, 270 + rows)
+    md2 = T.tmap_encode("u8", 2, dst2.data_ptr(), dims, strides, box, None, swz)
+    T.tmap_roundtrip(ms, md2, None, n, **opts)
+    check_ok()
+    assert torch.equal(dst2, src)                      # every byte is inside some box
+
+
+def test_band_rows_that_do_not_fit_are_rejected():
+    """An explicit band height that the box, the swizzle or the sweep cannot
+    take is an argument error on the band schedule (no launch happens), and
+    is ignored where the band schedule does not apply."""
+    say("band rows rejected")
+    t = torch.zeros(4096 * 256, dtype=torch.uint8, device=DEV)
+    m = T.tmap_encode("u8", 2, t.data_ptr(), [4096, 256], [4096], [128, 128], None, (3, 4, 3))
+    n = T.tmap_sweep_tiles(m)
+    packed = torch.empty(n * 16384, dtype=torch.uint8, device=DEV)
+    for rows in (3, 256, 1):     # not a power of two; taller than the box; a unit wider than the row of the sweep
+        with pytest.raises(T.TmapError) as e:
+            T.tmap_load_tiles(m, None, n, packed, flags=T.FLAG_BAND, band_rows=rows)
+        assert e.value.status == T.INVALID_VALUE
+    # whole boxes ignore it
+    T.tmap_load_tiles(m, None, n, packed, flags=T.FLAG_WHOLE_BOX, band_rows=3)
+    check_ok()
+    # a 64-byte box row with the (3,4,3) swizzle: its 128-element blocks span
+    # two rows, so a one-row band is not mapped onto itself
+    m64 = T.tmap_encode("u8", 2, t.data_ptr(), [4096, 256], [4096], [64, 128], None, (3, 4, 3))
+    n64 = T.tmap_sweep_tiles(m64)
+    assert T.tmap_band_boxes(m64, None, False, T.FLAG_BAND, 1) == 0
+    assert T.tmap_band_boxes(m64, None, False, T.FLAG_BAND, 4) == 64
+    with pytest.raises(T.TmapError):
+        T.tmap_load_tiles(m64, None, n64, packed, flags=T.FLAG_BAND, band_rows=1)

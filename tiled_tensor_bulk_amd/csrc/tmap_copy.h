@@ -42,7 +42,7 @@
 // unrolled by S.  The direct-to-LDS loads are issued from assembly and each
 // stage waits for exactly its own loads (vmcnt of the later stages' loads),
 // so a stage drains while the next ones fill.  On the band schedule (sweeps
-// of boxes with narrow rows) a stage holds the same 16-row band of several
+// of boxes with narrow rows) a stage holds the same band of rows of several
 // neighbouring boxes instead of one box.  R is the number of dimensions the
 // scalar tile arithmetic walks: 2 for maps of rank <= 2, else 5.
 
@@ -535,9 +535,9 @@ struct Copier {
     // Region offset and packed indices of the chunk in stage slot p.  In the
     // band schedule, slot p is chunk l = p mod (band chunks) of the band of
     // the unit's box g = p / (band chunks); the swizzle maps every band of a
-    // box onto itself the same way (a band is a whole number of swizzle
-    // periods), so l's logical chunk is found as in band 0 and the box's
-    // place in the unit is added in dimension 0.
+    // box onto itself, so l's logical chunk is found as in band 0 (the
+    // packed side corrects for the band, see band_xor) and the box's place
+    // in the unit is added in dimension 0.
     __device__ __forceinline__ void slot_info(uint32_t p, const KMap &m, uint32_t &off, uint32_t &w0,
                                               uint32_t &w1) const {
         if constexpr (BAND) {
@@ -548,6 +548,24 @@ struct Copier {
             w0 += x;  // dimension-0 index field: below 2^16
         } else {
             chunk_info(logical_chunk(p, m), m, off, w0, w1);
+        }
+    }
+
+    // Band j of a box is swizzled like band 0 but for one extra XOR: the
+    // swizzle changes only element-offset bits [m, m+b), so with a band of
+    // 2^lbe elements (a multiple of 2^(m+b)) the offset j*2^lbe + l goes to
+    // j*2^lbe + (swizzle(l) ^ x_j), x_j = swizzle(j*2^lbe) ^ j*2^lbe.  The
+    // stage's slots follow band 0's arrangement, so a load writes slot p to
+    // image position p ^ x_j of its box's band and a store reads it from
+    // there.  Returns x_j in bytes (a multiple of 16: the swizzle moves whole
+    // chunks on the direct-to-LDS path); 0 without the band schedule.
+    __device__ __forceinline__ uint32_t band_xor(const Cursor<R> &cur) const {
+        if constexpr (BAND) {
+            const KMap &m = swept();
+            const uint32_t jb = (cur.dig[1] & ((1u << a.band_lnb) - 1u)) << a.band_lbe;
+            return (swizzle(jb, m.swz_b, m.swz_m, m.swz_s) ^ jb) * m.elem_size;
+        } else {
+            return 0u;
         }
     }
 
@@ -724,8 +742,9 @@ struct Copier {
         for (int d = 0; d < R; ++d) c[d] = sc[XF][d] = fc[d];
         if (MODE == kStore) {
             const Src r = packed_src(fcur, a.dst.box_bytes);
+            const uint32_t x = band_xor(fcur);
 #pragma unroll
-            for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? poff[j] : kOob);
+            for (int j = 0; j < NSLOT; ++j) dma(r, stage, j, pslot[j] < a.n_chunks ? (poff[j] ^ x) : kOob);
         } else {
             const Place pl = place<R>(a.src, c);
             const Src r{a.src.base + (uint64_t)pl.off, a.src.span};
@@ -819,11 +838,12 @@ struct Copier {
     __device__ __forceinline__ void consume(uint8_t *stage, const int32_t c[R], const Cursor<R> &cur) const {
         if (MODE == kLoad) {
             const __amdgpu_buffer_rsrc_t r = packed_rsrc(cur, a.src.box_bytes);
+            const uint32_t x = band_xor(cur);
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
                 if (cslot[j] < a.n_chunks) {
                     const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
-                    store16(v, r, coff[j]);
+                    store16(v, r, coff[j] ^ x);
                 }
             }
         } else {

@@ -123,24 +123,58 @@ uint32_t log2u(uint32_t v) {
     return l;
 }
 
-// Bytes a unit of g boxes of the band schedule reaches from its corner in
+// Bytes a unit of g boxes, `rows` rows tall, reaches from its corner in
 // kernel map k.
-uint64_t band_span(const tmap::KMap &k, uint32_t g) {
-    return (uint64_t)g * k.box[0] * k.elem_size + (uint64_t)(tmap::kBandRows - 1) * k.strides[1];
+uint64_t band_span(const tmap::KMap &k, uint32_t g, uint32_t rows) {
+    return (uint64_t)g * k.box[0] * k.elem_size + (uint64_t)(rows - 1) * k.strides[1];
 }
 
-// Whether a launch runs on the band schedule, and its boxes per unit (g) and
-// bands per box (nb).  It applies to sweeps whose boxes have rows of 64 to
-// 512 bytes and whose dimension-1 extent is a power-of-two multiple of the
-// band height (boxes of rank 2, or with extent 1 above dimension 1), when
-// the swizzle maps each band of a box onto itself and a row of the sweep
-// holds at least one full unit.  By default it is taken only for tensors
-// spanning at least kBandMinSpan bytes: it buys DRAM page locality, which a
-// tensor that fits in the 256 MB last-level cache (MALL) does not need,
-// while its smaller units cost latency there.
+// Whether a launch runs on the band schedule, and its boxes per unit (g),
+// bands per box (nb) and rows per band.  It applies to sweeps whose boxes
+// have rows of 64 to 512 bytes and whose dimension-1 extent is a power-of-two
+// multiple of the band height (boxes of rank 2, or with extent 1 above
+// dimension 1), when the swizzle maps each band of a box onto itself and a
+// row of the sweep holds at least one full unit.  A unit is one 16 KiB
+// stage: g = 16 KiB / (rows * box row bytes) boxes side by side.  By default
+// it is taken only for tensors spanning at least kBandMinSpan bytes: it buys
+// DRAM page locality, which a tensor that fits in the 256 MB last-level
+// cache (MALL) does not need, while its smaller units cost latency there.
 constexpr uint64_t kBandMinSpan = 256ull << 20;
 
-bool band_fits(const MapImpl &m, const tmap::KArgs &a, uint32_t flags, uint32_t &g, uint32_t &nb) {
+// Default band heights, measured on MI355X over the 2 GiB u8, 1 GiB fp32 and
+// ragged bf16 sweeps: round trips read and write 4-row bands of units 4 KiB
+// wide (0.3-17% faster than 16 rows), loads and stores 8-row bands of units
+// 2 KiB wide (0.5-1.8% faster).  Where that height does not fit the box or
+// the sweep, the next taller one that does is taken.
+constexpr uint32_t kBandRowsRoundtrip = 4;
+constexpr uint32_t kBandRowsLoadStore = 8;
+
+// The checks that depend on the band height; nullptr when `rows` fits,
+// else the reason.  rc: 16-byte chunks per box row.
+const char *band_height_misfit(const MapImpl &m, const tmap::KArgs &a, uint32_t rc, uint32_t rows, uint32_t &g,
+                               uint32_t &nb) {
+    if (!rows || (rows & (rows - 1))) return "band_rows must be a power of two";
+    if (rows * rc > tmap::kBandChunks) return "a band of band_rows box rows exceeds a 16 KiB stage";
+    g = tmap::kBandChunks / (rows * rc);
+    if (m.box[1] % rows) return "band_rows must divide the box's dimension-1 extent";
+    nb = m.box[1] / rows;
+    if (nb & (nb - 1)) return "the box's dimension-1 extent must be band_rows times a power of two";
+    // the swizzle only changes element-offset bits [m, m+b), so it maps each
+    // band onto itself when a band is a whole number of 2^(m+b) blocks
+    if (m.swz_b && ((uint64_t)rows * m.box[0]) % (1ull << (m.swz_m + m.swz_b)))
+        return "the swizzle does not map a band of band_rows rows onto itself";
+    if (a.tiles[0] < g) return "a row of the sweep holds fewer boxes than a unit of band_rows rows";
+    // a unit's buffer records, like a box's, stay below the out-of-range offset
+    if (band_span(a.src, g, rows) >= 0x80000000ull || band_span(a.dst, g, rows) >= 0x80000000ull)
+        return "a unit reaches 2 GiB or more from its corner";
+    return nullptr;
+}
+
+// want_rows: the band height asked for, 0 for the default of the direction.
+// An explicit height that does not fit leaves *why set and returns false;
+// without one the schedule falls back to whole boxes silently.
+bool band_fits(const MapImpl &m, const tmap::KArgs &a, bool roundtrip, uint32_t flags, uint32_t want_rows,
+               uint32_t &g, uint32_t &nb, uint32_t &rows, const char **why = nullptr) {
     if (a.coords || a.elemwise) return false;
     if (flags & (TMAP_FLAG_THREAD_COPY | TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WHOLE_BOX)) return false;
     if (m.rank < 2) return false;
@@ -150,34 +184,36 @@ bool band_fits(const MapImpl &m, const tmap::KArgs &a, uint32_t flags, uint32_t 
         if (m.box[d] != 1) return false;
     const uint32_t rc = (uint32_t)m.box[0] * m.elem_size / 16u;  // 16-byte chunks per box row
     if (rc < 4 || rc > 32 || (rc & (rc - 1))) return false;
-    g = 64u / rc;  // a unit row is 1 KiB
-    if (m.box[1] % tmap::kBandRows) return false;
-    nb = m.box[1] / tmap::kBandRows;
-    if (nb & (nb - 1)) return false;
-    if (m.swz_b && (tmap::kBandRows * m.box[0]) % (1u << (m.swz_m + m.swz_s + m.swz_b))) return false;
-    if (a.tiles[0] < g) return false;
-    // a unit's buffer records, like a box's, stay below the out-of-range offset
-    return band_span(a.src, g) < 0x80000000ull && band_span(a.dst, g) < 0x80000000ull;
+    if (want_rows) {
+        rows = want_rows;
+        const char *w = band_height_misfit(m, a, rc, rows, g, nb);
+        if (w && why) *why = w;
+        return w == nullptr;
+    }
+    for (rows = roundtrip ? kBandRowsRoundtrip : kBandRowsLoadStore; rows <= m.box[1]; rows *= 2)
+        if (!band_height_misfit(m, a, rc, rows, g, nb)) return true;
+    return false;
 }
 
 // Re-point the launch at units of the band schedule.
-void band_setup(const MapImpl &m, tmap::KArgs &a, uint32_t g, uint32_t nb) {
-    const uint32_t bc = tmap::kBandRows * a.row_chunks;
+void band_setup(const MapImpl &m, tmap::KArgs &a, uint32_t g, uint32_t nb, uint32_t rows) {
+    const uint32_t bc = rows * a.row_chunks;
     a.band_g = g;
     a.band_lnb = log2u(nb);
     a.band_lbc = log2u(bc);
+    a.band_lbe = log2u(rows * (uint32_t)m.box[0]);
     a.band_bytes = bc * 16u;
     int64_t units = 1;
     for (int d = 0; d < tmap::kMaxRank; ++d) {
         a.sweep_tiles[d] = d == 0 ? (a.tiles[0] + g - 1) / g : (d == 1 ? a.tiles[1] * nb : a.tiles[d]);
-        a.ubox[d] = d == 0 ? g * m.box[0] : (d == 1 ? tmap::kBandRows : m.box[d]);
+        a.ubox[d] = d == 0 ? g * m.box[0] : (d == 1 ? rows : m.box[d]);
         units *= a.sweep_tiles[d];
     }
     a.n_tiles = units;
     a.n_chunks = tmap::kBandSlots * tmap::kWaves * 64u;
     for (tmap::KMap *k : {&a.src, &a.dst}) {
         for (int d = 0; d < tmap::kMaxRank; ++d) k->lim[d] = (int32_t)((int64_t)k->dims[d] - (int64_t)a.ubox[d]);
-        k->span = (uint32_t)band_span(*k, g);
+        k->span = (uint32_t)band_span(*k, g, rows);
     }
 }
 
@@ -297,9 +333,12 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     DeviceState *dev = nullptr;
     tmap_status st = device_for_launch(&dev);
     if (st != TMAP_SUCCESS) return st;
-    uint32_t g = 0, nb = 0;
-    const bool band = band_fits(swept, a, opts ? opts->flags : 0u, g, nb);
-    if (band) band_setup(swept, a, g, nb);
+    uint32_t g = 0, nb = 0, rows = 0;
+    const char *why = nullptr;
+    const bool band = band_fits(swept, a, mode == tmap::kRoundtrip, opts ? opts->flags : 0u,
+                                opts ? opts->band_rows : 0u, g, nb, rows, &why);
+    if (why) return fail(TMAP_ERROR_INVALID_VALUE, "%s", why);
+    if (band) band_setup(swept, a, g, nb, rows);
     Plan pl;
     st = plan_launch(mode, swept, a.n_tiles, opts, *dev, band, a.coords != nullptr, pl);
     if (st != TMAP_SUCCESS) return st;
@@ -460,7 +499,8 @@ int64_t tmap_sweep_tiles(const tmap_t *map) {
     return decode(map, m) ? sweep_count(m) : -1;
 }
 
-uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *coords, uint32_t flags) {
+uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *coords,
+                         const tmap_launch_opts *opts) {
     MapImpl s, d;
     if (!decode(src, s)) return 0;
     if (dst && !decode(dst, d)) return 0;
@@ -469,8 +509,9 @@ uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *co
     a.src = tmap::kernel_map(s);
     a.dst = dst ? tmap::kernel_map(d) : a.src;
     fill_common(a, s, coords, 0);
-    uint32_t g = 0, nb = 0;
-    return band_fits(s, a, flags, g, nb) ? g : 0u;
+    uint32_t g = 0, nb = 0, rows = 0;
+    return band_fits(s, a, dst != nullptr, opts ? opts->flags : 0u, opts ? opts->band_rows : 0u, g, nb, rows) ? g
+                                                                                                          : 0u;
 }
 
 tmap_status tmap_query(const tmap_t *map, tmap_info *out) {

@@ -1,6 +1,6 @@
 // tmap_internal.h -- private layout of the 128-byte tensor map and of the
 // kernel argument block.  Shared by the host half (tmap_host.cpp) and the
-// device half (tmap_kernels.hip) of libtmap only.
+// device half (tmap_copy.h) of libtmap only.
 #pragma once
 
 #include <stdint.h>
@@ -104,22 +104,23 @@ struct KArgs {
     uint32_t add_f32;             // round trip: add `addend` to every fp32 element before storing
     float addend;
     // Band schedule (sweeps of boxes with narrow rows).  A unit is the same
-    // band of kBandRows box rows taken from band_g boxes that are neighbours
-    // in dimension 0; a stage holds one unit, each box's band as the
-    // contiguous piece of that box's LDS image it is.  The cursor then walks
-    // units: sweep_tiles/n_tiles count units, ubox is a unit's extent
-    // (band_g*box0, kBandRows, box2, ..) and the maps' lim is dims - ubox.
-    // band_g == 0: one whole box per stage, ubox == box.
+    // band of box rows (the band height) taken from band_g boxes that are
+    // neighbours in dimension 0, 16 KiB in all; a stage holds one unit, each
+    // box's band as the contiguous piece of that box's LDS image it is.  The
+    // cursor then walks units: sweep_tiles/n_tiles count units, ubox is a
+    // unit's extent (band_g*box0, band height, box2, ..) and the maps' lim is
+    // dims - ubox.  band_g == 0: one whole box per stage, ubox == box.
     uint32_t band_g;              // boxes per unit
     uint32_t band_lnb;            // log2(bands per box)
     uint32_t band_lbc;            // log2(16-byte chunks in one box's band)
+    uint32_t band_lbe;            // log2(elements in one box's band)
     uint32_t band_bytes;          // bytes of one box's band
     uint32_t tiles[kMaxRank];     // ceil(dims/box) per dimension of the swept map
     uint32_t ubox[kMaxRank];      // extent of a unit per dimension
 };
 
-constexpr uint32_t kBandRows = 16;        // box rows per band
 constexpr int kBandSlots = 4;             // a band stage is 4 slots per lane: 16 KiB
+constexpr uint32_t kBandChunks = kBandSlots * kWaves * 64;  // 16-byte chunks in a band stage
 
 }  // namespace tmap
 

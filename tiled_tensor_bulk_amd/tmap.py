@@ -45,7 +45,8 @@ class tmap_swizzle(ctypes.Structure):
 class tmap_launch_opts(ctypes.Structure):
     _fields_ = [("stages", ctypes.c_uint32), ("grid_wgs", ctypes.c_uint32),
                 ("flags", ctypes.c_uint32), ("spin_limit", ctypes.c_uint32),
-                ("group", ctypes.c_uint32), ("regions", ctypes.c_uint32)]
+                ("group", ctypes.c_uint32), ("regions", ctypes.c_uint32),
+                ("band_rows", ctypes.c_uint32)]
 
 
 class tmap_info(ctypes.Structure):
@@ -85,7 +86,7 @@ def lib():
         L.tmap_box_bytes.restype = ctypes.c_uint64
         L.tmap_sweep_tiles.argtypes = [P(tmap_t)]
         L.tmap_sweep_tiles.restype = ctypes.c_int64
-        L.tmap_band_boxes.argtypes = [P(tmap_t), P(tmap_t), vp, u32]
+        L.tmap_band_boxes.argtypes = [P(tmap_t), P(tmap_t), vp, P(tmap_launch_opts)]
         L.tmap_band_boxes.restype = u32
         L.tmap_inbounds_elems.argtypes = [P(tmap_t), vp, i64, P(ctypes.c_uint64)]
         L.tmap_inbounds_elems.restype = ctypes.c_int
@@ -163,10 +164,10 @@ def _check_corners(coords, m: tmap_t, n_tiles: int) -> None:
     _check_buffer(coords, 4 * int(n_tiles) * tmap_query(m)["rank"], "coords")
 
 
-def _opts(stages=0, grid_wgs=0, flags=0, spin_limit=0, group=0, regions=0):
-    if not (stages or grid_wgs or flags or spin_limit or group or regions):
+def _opts(stages=0, grid_wgs=0, flags=0, spin_limit=0, group=0, regions=0, band_rows=0):
+    if not (stages or grid_wgs or flags or spin_limit or group or regions or band_rows):
         return None
-    return ctypes.byref(tmap_launch_opts(stages, grid_wgs, flags, spin_limit, group, regions))
+    return ctypes.byref(tmap_launch_opts(stages, grid_wgs, flags, spin_limit, group, regions, band_rows))
 
 
 # ------------------------------------------------------------------- C ABI names
@@ -237,12 +238,12 @@ _ANY_CORNERS = ctypes.c_int32(0)  # a non-NULL corner pointer for the schedule q
 
 
 def tmap_band_boxes(src: tmap_t, dst: Optional[tmap_t] = None, explicit_coords: bool = False,
-                    flags: int = 0) -> int:
-    """Boxes per stage on the band schedule a copy would take, 0 for whole
-    boxes (host only)."""
+                    flags: int = 0, band_rows: int = 0) -> int:
+    """Boxes per stage on the band schedule a copy with these launch options
+    would take, 0 for whole boxes (host only)."""
     corners = ctypes.addressof(_ANY_CORNERS) if explicit_coords else None
     return int(lib().tmap_band_boxes(ctypes.byref(src), None if dst is None else ctypes.byref(dst),
-                                     corners, int(flags)))
+                                     corners, _opts(flags=int(flags), band_rows=int(band_rows))))
 
 
 def tmap_inbounds_elems(m: tmap_t, host_coords, n_tiles: int) -> int:
