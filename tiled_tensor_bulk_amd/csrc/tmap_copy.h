@@ -116,10 +116,11 @@ __device__ __forceinline__ void dma_lds(uint64_t base, uint32_t nrec, const uint
             : "memory");
 }
 
-// Wait until at most N vector-memory loads of this wave are outstanding
-// (expcnt and lgkmcnt untouched).  Loads complete in issue order, so after
-// issuing k more loads behind a stage's loads, vmcnt(k) guarantees that the
-// stage's loads have landed, whatever stores were issued in between.
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (expcnt and lgkmcnt untouched).  The counter counts loads (direct-to-LDS
+// ones included) and stores alike and retires them in issue order, so after
+// issuing k more operations behind a stage's loads, vmcnt(k) guarantees that
+// the stage's loads have landed while those k may still be in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     constexpr int n = N > 63 ? 63 : N;
@@ -778,10 +779,17 @@ struct Copier {
 
     // Wait for this wave's loads of the tile at corner c into stage X, patch
     // its partial chunks, then report the delivered bytes.  `later`: the
-    // S-1 tiles after it have been filled (their loads may stay in flight).
+    // S-1 tiles after it have been filled (their NSLOT loads each may stay in
+    // flight).  `drained`: the S-1 tiles before it have also been drained
+    // since it was filled; every drain issues at least NSLOT 16-byte stores
+    // (consume), so those may stay in flight as well and the landing never
+    // waits for a store.
     template <int X>
-    __device__ __forceinline__ void land(uint8_t *stage, uint64_t *bar, const int32_t c[R], bool later) const {
-        if (later)
+    __device__ __forceinline__ void land(uint8_t *stage, uint64_t *bar, const int32_t c[R], bool later,
+                                         bool drained) const {
+        if (later && drained)
+            wait_vmcnt<2 * (S - 1) * NSLOT>();
+        else if (later)
             wait_vmcnt<(S - 1) * NSLOT>();
         else
             wait_vmcnt<0>();
@@ -834,17 +842,17 @@ struct Copier {
     }
 
     // Read the region (box or unit) under cursor cur, at corner c, out of
-    // `stage`.
+    // `stage`.  Every path issues exactly one 16-byte store per consumer slot
+    // (those with nothing to write go to the out-of-range offset, which the
+    // hardware drops), so that land() can count on NSLOT stores per drain.
     __device__ __forceinline__ void consume(uint8_t *stage, const int32_t c[R], const Cursor<R> &cur) const {
         if (MODE == kLoad) {
             const __amdgpu_buffer_rsrc_t r = packed_rsrc(cur, a.src.box_bytes);
             const uint32_t x = band_xor(cur);
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
-                if (cslot[j] < a.n_chunks) {
-                    const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
-                    store16(v, r, coff[j] ^ x);
-                }
+                const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
+                store16(v, r, cslot[j] < a.n_chunks ? (coff[j] ^ x) : kOob);
             }
         } else {
             const Place pl = place<R>(a.dst, c);
@@ -855,21 +863,20 @@ struct Copier {
             if (inside_map(a.dst, c, pl, boxes) && !a.elemwise) {
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j) {
-                    if (cslot[j] < a.n_chunks && slot_present(cslot[j], boxes)) {
-                        const i32x4 v = update(*(const i32x4 *)(stage + cslot[j] * 16u));
-                        store16(v, r, coff[j]);
-                    }
+                    const bool on = cslot[j] < a.n_chunks && slot_present(cslot[j], boxes);
+                    const i32x4 v = update(*(const i32x4 *)(stage + cslot[j] * 16u));
+                    store16(v, r, on ? coff[j] : kOob);
                 }
             } else {
                 const Win<R> w = win(a.dst, c, boxes);
-                if (!a.elemwise) {
+                // whole chunks (none when the swizzle moves elements inside
+                // chunks: the element path below stores everything then)
 #pragma unroll
-                    for (int j = 0; j < NSLOT; ++j) {
-                        if (cslot[j] < a.n_chunks && classify<R>(cw0[j], cw1[j], w, a.k_el) == kFull) {
-                            const i32x4 v = update(*(const i32x4 *)(stage + cslot[j] * 16u));
-                            store16(v, r, coff[j]);
-                        }
-                    }
+                for (int j = 0; j < NSLOT; ++j) {
+                    const bool on = !a.elemwise && cslot[j] < a.n_chunks &&
+                                    classify<R>(cw0[j], cw1[j], w, a.k_el) == kFull;
+                    const i32x4 v = update(*(const i32x4 *)(stage + cslot[j] * 16u));
+                    store16(v, r, on ? coff[j] : kOob);
                 }
                 // slow path, kept out of the unrolled slot arrays: recompute
                 // each slot's chunk, store the inside elements of partial ones
@@ -910,14 +917,16 @@ struct Copier {
             // it before the next fill keeps that wait off the fill's loads.
 #pragma unroll
             for (int d = 0; d < R; ++d) c[d] = sc[X][d];
-            land<X>(st, &bars[X], c, false);
+            land<X>(st, &bars[X], c, false, false);
             if (k + S - 1 < cnt) fill<XF>(fillst, &bars[XF]);
         } else {
             const bool later = k + S - 1 < cnt;
             if (later) fill<XF>(fillst, &bars[XF]);
 #pragma unroll
             for (int d = 0; d < R; ++d) c[d] = sc[X][d];
-            land<X>(st, &bars[X], c, later && S > 1);
+            // tile k was filled S-1 steps ago (or in the prologue), and the
+            // steps since then each drained a tile after filling
+            land<X>(st, &bars[X], c, later && S > 1, k >= S - 1);
         }
         const bool ok = bar_wait(&bars[X], (parity >> X) & 1u, a.spin_limit);
         parity ^= 1u << X;
