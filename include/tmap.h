@@ -75,7 +75,8 @@ typedef struct tmap_swizzle {
  * default. */
 typedef struct tmap_launch_opts {
     uint32_t stages;      /* LDS ring depth 1..4 (default 2; 1 with explicit corners and
-                             when each workgroup takes a single band unit)               */
+                             when each workgroup takes a single band unit; 3 for round
+                             trips on the band schedule)                                 */
     uint32_t grid_wgs;    /* workgroups launched; fewer than there are groups makes each
                              take several (default: one workgroup per group; with
                              TMAP_FLAG_CONTIGUOUS, twice what fits in LDS per CU; in
@@ -84,7 +85,7 @@ typedef struct tmap_launch_opts {
     uint32_t spin_limit;  /* readiness-wait polls before TMAP_ERROR_TIMEOUT (default 2^22) */
     uint32_t group;       /* tiles (band units) dealt to a workgroup at a time, a power of
                              two <= 64 (default: enough boxes side by side to span 512
-                             bytes of a row, at least 2 and at most 8; band units: 2 for
+                             bytes of a row, at least 2 and at most 8; band units: 4 for
                              a round trip, 1 for a load or store; explicit corners: 8)   */
     uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
                              streams, each sweeping an equal contiguous stretch of the
@@ -95,7 +96,7 @@ typedef struct tmap_launch_opts {
                              and stores on the band schedule, else 1)                  */
     uint32_t band_rows;   /* band schedule: box rows per band, a power of two.  A unit is
                              then 16 KiB / (band_rows * box row bytes) boxes side by
-                             side.  Default: 4 for a round trip (units 4 KiB wide), 8
+                             side.  Default: 2 for a round trip (units 8 KiB wide), 8
                              for a load or store (2 KiB wide), or the next taller
                              height that fits.  An explicit height that does not fit
                              the box, the swizzle or the sweep (see below) is
@@ -116,7 +117,7 @@ typedef struct tmap_launch_opts {
  * a multiple of 2^(m+b): the swizzle only changes element-offset bits
  * [m, m+b)), and a row of the sweep must hold a whole unit.  Every box's
  * image is unchanged; the tensor is read and written in wide, short pieces
- * (4 rows of 4 KiB, or 8 rows of 2 KiB, by default), which HBM serves faster
+ * (2 rows of 8 KiB, or 8 rows of 2 KiB, by default), which HBM serves faster
  * than narrow rows of tall boxes.  A stage's byte record counts the unit's
  * 16 KiB.  In a round trip, where no image leaves the workgroup, every band
  * is staged in the arrangement of a box's first band. */

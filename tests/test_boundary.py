@@ -207,9 +207,9 @@ def test_band_schedule_choice():
     W = inputs.WORKLOADS
     B = T.FLAG_BAND
     # (name, boxes per unit of a load or store (8-row bands), of a round trip
-    # (4-row bands), of a load forced onto the band schedule)
-    for name, want, want_rt, forced in [("sweep2g_u8", 16, 32, 16), ("ragged_bf16", 16, 32, 16),
-                                        ("plus1_f32", 8, 16, 8), ("strips_f16", 0, 0, 4),
+    # (2-row bands), of a load forced onto the band schedule)
+    for name, want, want_rt, forced in [("sweep2g_u8", 16, 64, 16), ("ragged_bf16", 16, 64, 16),
+                                        ("plus1_f32", 8, 32, 8), ("strips_f16", 0, 0, 4),
                                         ("tile64_f32", 0, 0, 1), ("pad5d_f32", 0, 0, 0)]:
         w = W[name]
         m = T.tmap_encode(w.dtype, w.rank, BASE, w.dims, w.strides, w.box, None, w.swizzle)

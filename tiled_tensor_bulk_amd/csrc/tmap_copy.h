@@ -782,7 +782,7 @@ struct Copier {
     // S-1 tiles after it have been filled (their NSLOT loads each may stay in
     // flight).  `drained`: the S-1 tiles before it have also been drained
     // since it was filled; every drain issues at least NSLOT 16-byte stores
-    // (consume), so those may stay in flight as well and the landing never
+    // (drain16), so those may stay in flight as well and the landing never
     // waits for a store.
     template <int X>
     __device__ __forceinline__ void land(uint8_t *stage, uint64_t *bar, const int32_t c[R], bool later,
@@ -841,10 +841,21 @@ struct Copier {
         return v;
     }
 
+    // Store slot chunk v at offset off when `on`.  With a ring of several
+    // stages every drain issues the store regardless, sending the chunks
+    // with nothing to write to the out-of-range offset (the hardware drops
+    // them), so that land() can count on NSLOT stores per drain; with one
+    // stage nothing counts on them and they are skipped.
+    template <typename Rs>
+    __device__ __forceinline__ void drain16(const i32x4 &v, Rs r, uint32_t off, bool on) const {
+        if constexpr (S > 1)
+            store16(v, r, on ? off : kOob);
+        else if (on)
+            store16(v, r, off);
+    }
+
     // Read the region (box or unit) under cursor cur, at corner c, out of
-    // `stage`.  Every path issues exactly one 16-byte store per consumer slot
-    // (those with nothing to write go to the out-of-range offset, which the
-    // hardware drops), so that land() can count on NSLOT stores per drain.
+    // `stage`.
     __device__ __forceinline__ void consume(uint8_t *stage, const int32_t c[R], const Cursor<R> &cur) const {
         if (MODE == kLoad) {
             const __amdgpu_buffer_rsrc_t r = packed_rsrc(cur, a.src.box_bytes);
@@ -852,7 +863,7 @@ struct Copier {
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
                 const i32x4 v = *(const i32x4 *)(stage + cslot[j] * 16u);
-                store16(v, r, cslot[j] < a.n_chunks ? (coff[j] ^ x) : kOob);
+                drain16(v, r, coff[j] ^ x, cslot[j] < a.n_chunks);
             }
         } else {
             const Place pl = place<R>(a.dst, c);
@@ -865,7 +876,7 @@ struct Copier {
                 for (int j = 0; j < NSLOT; ++j) {
                     const bool on = cslot[j] < a.n_chunks && slot_present(cslot[j], boxes);
                     const i32x4 v = update(*(const i32x4 *)(stage + cslot[j] * 16u));
-                    store16(v, r, on ? coff[j] : kOob);
+                    drain16(v, r, coff[j], on);
                 }
             } else {
                 const Win<R> w = win(a.dst, c, boxes);
@@ -876,7 +887,7 @@ struct Copier {
                     const bool on = !a.elemwise && cslot[j] < a.n_chunks &&
                                     classify<R>(cw0[j], cw1[j], w, a.k_el) == kFull;
                     const i32x4 v = update(*(const i32x4 *)(stage + cslot[j] * 16u));
-                    store16(v, r, on ? coff[j] : kOob);
+                    drain16(v, r, coff[j], on);
                 }
                 // slow path, kept out of the unrolled slot arrays: recompute
                 // each slot's chunk, store the inside elements of partial ones

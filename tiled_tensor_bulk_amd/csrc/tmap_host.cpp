@@ -142,11 +142,12 @@ uint64_t band_span(const tmap::KMap &k, uint32_t g, uint32_t rows) {
 constexpr uint64_t kBandMinSpan = 256ull << 20;
 
 // Default band heights, measured on MI355X over the 2 GiB u8, 1 GiB fp32 and
-// ragged bf16 sweeps: round trips read and write 4-row bands of units 4 KiB
-// wide (0.3-17% faster than 16 rows), loads and stores 8-row bands of units
-// 2 KiB wide (0.5-1.8% faster).  Where that height does not fit the box or
-// the sweep, the next taller one that does is taken.
-constexpr uint32_t kBandRowsRoundtrip = 4;
+// ragged bf16 sweeps: round trips read and write 2-row bands of units 8 KiB
+// wide (with 3 stages and 4 units per workgroup, see plan_launch), loads and
+// stores 8-row bands of units 2 KiB wide (0.5-1.8% faster than 16 rows).
+// Where that height does not fit the box or the sweep, the next taller one
+// that does is taken.
+constexpr uint32_t kBandRowsRoundtrip = 2;
 constexpr uint32_t kBandRowsLoadStore = 8;
 
 // The checks that depend on the band height; nullptr when `rows` fits,
@@ -230,6 +231,11 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // leaves little to overlap and the smaller footprint fits more
     // workgroups (measured best on MI355X)
     int stages = (opts && opts->stages) ? (int)opts->stages : (corners ? 1 : 2);
+    // band round trips: a ring of 3 stages over 4 units per workgroup (the
+    // group, below) measured 1-4% faster than 2 over 2 on the 2 GiB u8 and
+    // 1 GiB fp32 round trips (one placement-sensitive ragged bf16 round trip
+    // lost 3%); 4 stages fit one workgroup fewer per CU and lose 10%
+    if (band && mode == tmap::kRoundtrip && !(opts && opts->stages)) stages = 3;
     if (stages < 1 || stages > 4)
         return fail(TMAP_ERROR_INVALID_VALUE, "stages must be 1..4 (got %d)", stages);
     const bool thread_copy = opts && (opts->flags & TMAP_FLAG_THREAD_COPY);
@@ -251,12 +257,12 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // group: consecutive tiles (units on the band schedule) a workgroup takes
     // in a row.  Whole boxes: enough boxes side by side to cover 512 bytes of
     // a row, so that a workgroup's tiles in flight read and write neighbouring
-    // row segments, and at least 2; units: 2 for a round trip and 1 for a
+    // row segments, and at least 2; units: 4 for a round trip and 1 for a
     // load or store; explicit corners: 8 (measured best on MI355X).
     uint32_t group = (opts && opts->group) ? opts->group : 0;
     if (group && (group > 64 || (group & (group - 1))))
         return fail(TMAP_ERROR_INVALID_VALUE, "group must be a power of two <= 64 (got %u)", group);
-    if (!group && band) group = mode == tmap::kRoundtrip ? 2u : 1u;
+    if (!group && band) group = mode == tmap::kRoundtrip ? 4u : 1u;
     if (!group && corners) group = 8;
     // a workgroup that takes one band unit has nothing to overlap in its ring
     if (band && group == 1 && !(opts && opts->stages)) stages = 1;
