@@ -150,13 +150,21 @@ def main():
         def launch():
             T.tmap_store_tiles(md, coords, n, packed, **opts)
 
+    plan = None
     if args.op == "bulk":
         schedule = "whole boxes (rank-1 16 KiB tiles)"
     else:
-        band = T.tmap_band_boxes(ms, None if args.op in ("load", "store") else md, coords is not None, args.flags,
-                                 args.band_rows)
-        rows = 16384 // (band * w.box[0] * es) if band else 0
-        schedule = f"band: {band} boxes x {rows} rows per stage" if band else "whole boxes"
+        # the schedule the library chose for these options
+        direction = {"load": "load", "store": "store"}.get(args.op, "roundtrip")
+        swept = md if args.op == "store" else ms
+        plan = T.tmap_plan_launch(direction, swept, md if direction == "roundtrip" else None, coords is not None,
+                                  n, **opts)
+        if plan["band_boxes"]:
+            schedule = f"band: {plan['band_boxes']} boxes x {plan['band_rows']} rows per stage"
+        elif plan["variant"] == "wave_per_box":
+            schedule = "whole boxes, one wave per box"
+        else:
+            schedule = "whole boxes" + ("" if plan["variant"] == "ring" else f" ({plan['variant']})")
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -216,7 +224,7 @@ def main():
                    "schedule": schedule, "stages": args.stages or "auto", "grid_wgs": args.grid or "auto",
                    "flags": args.flags,
                    "group": args.group or "auto", "regions": args.regions or "auto",
-                   "band_rows": args.band_rows or "auto",
+                   "band_rows": args.band_rows or "auto", "plan": plan,
                    "algorithmic_bytes_per_step": algo_bytes},
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBPS, 2),
         "tiles_per_s": round(n / (wall / args.steps), 1),

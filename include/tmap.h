@@ -86,7 +86,8 @@ typedef struct tmap_launch_opts {
     uint32_t group;       /* tiles (band units) dealt to a workgroup at a time, a power of
                              two <= 64 (default: enough boxes side by side to span 512
                              bytes of a row, at least 2 and at most 8; band units: 4 for
-                             a round trip, 1 for a load or store; explicit corners: 8)   */
+                             a round trip, 1 for a load or store; explicit corners: 8,
+                             4 for a wave-per-box store)                                 */
     uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
                              streams, each sweeping an equal contiguous stretch of the
                              tiles (workgroup i takes stretch i mod regions), so that the
@@ -142,8 +143,20 @@ typedef struct tmap_launch_opts {
  * record ("GPU TMA", "Warp specialization").  Same results.  Needs boxes of
  * at most 32 KiB; `stages` 1 is taken as 2. */
 #define TMAP_FLAG_PRODUCER_WAVE 0x8u
-/* One whole box per stage even where the band schedule applies (for A/B
- * runs, and for a consumer that needs a box's full LDS image at once). */
+/* Wave-per-box mode: each of a workgroup's four waves walks its own tiles
+ * through its own ring of one-box stages (stages 1 or 2), issuing all of a
+ * box's direct-to-LDS loads under one arrive+expect of its bytes on its own
+ * stage record, and draining the box itself once the record's phase flips.
+ * The per-box address and bounds work is done once per box instead of once
+ * per wave, and no workgroup barrier is needed.  Same results.  Needs boxes
+ * of at most 16 KiB; grid_wgs then counts waves.  Excludes the thread-copy
+ * and producer-wave modes, TMAP_FLAG_WHOLE_BOX and the band schedule.  The
+ * default for explicit corners of boxes up to 8 KiB (unless stages > 2). */
+#define TMAP_FLAG_WAVE_PER_BOX 0x40u
+/* One whole box per stage, shared by the workgroup's four waves (the
+ * cooperative ring), even where the band schedule or wave-per-box mode
+ * would be the default (for A/B runs, and for a consumer that needs a box's
+ * full LDS image at once). */
 #define TMAP_FLAG_WHOLE_BOX 0x10u
 /* The band schedule wherever its shape rules allow, whatever the tensor's
  * size.  Excludes TMAP_FLAG_WHOLE_BOX. */
@@ -296,6 +309,40 @@ tmap_status tmap_inbounds_elems(const tmap_t *map, const int32_t *host_coords,
  * would reject. */
 uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *coords,
                          const tmap_launch_opts *opts);
+
+/* The schedule a copy would run with (no device memory is touched and
+ * nothing is launched; the plan depends on the current device's CU count
+ * and LDS size, so a gfx950 device must be current, else
+ * TMAP_ERROR_UNSUPPORTED_DEVICE).  Arguments as for the copy call of that
+ * direction: `swept` is the source map of a load or round trip and the
+ * destination map of a store, `dst` the round trip's destination map (NULL
+ * otherwise), `coords` non-NULL for explicit corners (not read), `n_tiles`
+ * checked as the copy checks it.  Errors are those the copy call would
+ * report before launching.  n_tiles == 0 gives an all-zero plan. */
+typedef enum tmap_direction { TMAP_DIR_LOAD = 0, TMAP_DIR_STORE = 1, TMAP_DIR_ROUNDTRIP = 2 } tmap_direction;
+typedef enum tmap_variant {
+    TMAP_VARIANT_RING = 0,          /* workgroup-shared ring of stages (whole boxes or band units) */
+    TMAP_VARIANT_THREAD_COPY = 1,   /* TMAP_FLAG_THREAD_COPY                                       */
+    TMAP_VARIANT_PRODUCER_WAVE = 2, /* TMAP_FLAG_PRODUCER_WAVE                                     */
+    TMAP_VARIANT_WAVE_PER_BOX = 3   /* TMAP_FLAG_WAVE_PER_BOX, or its default                      */
+} tmap_variant;
+typedef struct tmap_plan {
+    uint32_t variant;     /* tmap_variant                                                  */
+    uint32_t band_boxes;  /* boxes per stage on the band schedule, 0 for one box per stage */
+    uint32_t band_rows;   /* box rows per band, 0 without the band schedule                */
+    uint32_t stages;      /* LDS ring depth                                                */
+    uint32_t slots;       /* 16-byte slots per lane and stage                              */
+    uint32_t group;       /* tiles (band units) a walker takes in a row; 0: one contiguous
+                             run per walker (TMAP_FLAG_CONTIGUOUS)                         */
+    uint32_t walkers;     /* tile sequences: workgroups, or waves in wave-per-box mode     */
+    uint32_t workgroups;  /* workgroups launched                                           */
+    uint32_t regions;     /* interleaved streams the groups are dealt as                   */
+    uint32_t lds_bytes;   /* LDS per workgroup                                             */
+    int64_t units;        /* tiles, or band units, dealt to the walkers                    */
+} tmap_plan;
+tmap_status tmap_plan_launch(tmap_direction direction, const tmap_t *swept, const tmap_t *dst,
+                             const int32_t *coords, int64_t n_tiles, const tmap_launch_opts *opts,
+                             tmap_plan *out);
 
 /* Decoded fields of an encoded map (for inspection and tests). */
 typedef struct tmap_info {

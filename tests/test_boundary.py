@@ -182,6 +182,35 @@ def test_launch_without_gpu_is_unsupported_device():
     assert e.value.status == T.UNSUPPORTED_DEVICE
 
 
+def test_plan_query_argument_errors_and_empty_plan():
+    """tmap_plan_launch checks its arguments as the copy calls do, before it
+    looks for a device; a plan of zero tiles is all zeros."""
+    m = T.tmap_encode("f32", 2, BASE, [64, 64], [256], [64, 64])
+    other_box = T.tmap_encode("f32", 2, BASE, [64, 64], [256], [32, 64])
+    bad = [
+        lambda: T.tmap_plan_launch(3, m),                                  # no such direction
+        lambda: T.tmap_plan_launch("load", T.tmap_t()),                    # never encoded
+        lambda: T.tmap_plan_launch("roundtrip", m),                        # round trip without dst
+        lambda: T.tmap_plan_launch("roundtrip", m, other_box),             # boxes differ
+        lambda: T.tmap_plan_launch("load", m, n_tiles=5),                  # sweep count mismatch
+        lambda: T.tmap_plan_launch("store", m, explicit_coords=True, n_tiles=-1),
+    ]
+    for f in bad:
+        with pytest.raises(T.TmapError) as e:
+            f()
+        assert e.value.status == T.INVALID_VALUE
+    p = T.tmap_plan_launch("load", m, explicit_coords=True, n_tiles=0)
+    assert all(v == 0 for k, v in p.items() if k != "variant") and p["variant"] == "ring"
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the device gate on a host without a GPU")
+def test_plan_query_without_gpu_is_unsupported_device():
+    m = T.tmap_encode("f32", 2, BASE, [64, 64], [256], [64, 64])
+    with pytest.raises(T.TmapError) as e:
+        T.tmap_plan_launch("load", m)
+    assert e.value.status == T.UNSUPPORTED_DEVICE
+
+
 def test_status_strings():
     assert T.tmap_status_string(0) == "TMAP_SUCCESS"
     assert T.tmap_status_string(4) == "TMAP_ERROR_TIMEOUT"

@@ -227,11 +227,28 @@ def _fuzz_case(rng, idx):
     return es, dims, strides, box, swz, alloc, coords, opts
 
 
-@pytest.mark.parametrize("chunk", range(4))
+def _wave_case(rng, idx):
+    """A fuzz case for wave-per-box mode: boxes of at most 16 KiB, 1 or 2
+    stages, the grid counting waves."""
+    while True:
+        case = _fuzz_case(rng, idx)
+        if int(np.prod(case[3])) * case[0] <= 16384:
+            break
+    opts = case[7]
+    opts["stages"] = int(rng.integers(1, 3))
+    opts["flags"] = T.FLAG_WAVE_PER_BOX | int(rng.choice([0, T.FLAG_CONTIGUOUS, T.FLAG_NONTEMPORAL]))
+    opts["grid_wgs"] = int(rng.choice([0, 0, 1, 2, 3, 5, 9]))
+    return case
+
+
+@pytest.mark.parametrize("chunk", range(6))
 def test_fuzz_random_maps(chunk):
+    """Seeded random maps of every rank, element size and swizzle, random
+    corners in, across and outside the tensor, random launch options; chunks
+    4 and 5 run wave-per-box mode."""
     rng = np.random.default_rng(9000 + chunk)
     for i in range(40):
-        es, dims, strides, box, swz, alloc, coords, opts = _fuzz_case(rng, i)
+        es, dims, strides, box, swz, alloc, coords, opts = (_fuzz_case if chunk < 4 else _wave_case)(rng, i)
         say(f"fuzz chunk {chunk} case {i}: es={es} dims={dims} strides={strides} box={box} swz={swz} "
             f"n={len(coords)} opts={opts}")
         om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
@@ -361,6 +378,39 @@ def test_binding_rejects_buffers_the_copy_would_overrun():
     check_ok()
 
 
+def test_plan_query_reports_the_schedules():
+    """The schedule each workload's copies take by default, and what the
+    mode flags turn it into, as tmap_plan_launch reports it."""
+    W = inputs.WORKLOADS
+    def plan(name, direction, **opts):
+        w = W[name]
+        m = T.tmap_encode(w.dtype, w.rank, 0x7F0000000000, w.dims, w.strides, w.box, None, w.swizzle)
+        corners = w.coords != "sweep"
+        n = None if not corners else (1 if w.coords == "origin" else w.n_random)
+        return T.tmap_plan_launch(direction, m, m if direction == "roundtrip" else None, corners, n, **opts)
+    say("plan query")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    p = plan("sweep2g_u8", "roundtrip", flags=T.FLAG_NONTEMPORAL)
+    assert (p["variant"], p["band_boxes"], p["band_rows"], p["stages"], p["group"], p["regions"]) == \
+        ("ring", 64, 2, 3, 4, 1)
+    assert p["units"] == 131072 * 64 // 64 and p["walkers"] == p["workgroups"] == p["units"] // 4
+    p = plan("sweep2g_u8", "load", flags=T.FLAG_NONTEMPORAL)
+    assert (p["variant"], p["band_boxes"], p["band_rows"], p["stages"], p["group"], p["regions"]) == \
+        ("ring", 16, 8, 1, 1, 2)
+    p = plan("pad5d_f32", "store")
+    assert (p["variant"], p["stages"], p["slots"], p["group"]) == ("wave_per_box", 1, 8, 4)
+    assert p["walkers"] == -(-100000 // 4) and p["workgroups"] == -(-p["walkers"] // 4)
+    assert plan("pad5d_f32", "load")["group"] == 8 and plan("pad5d_f32", "roundtrip")["variant"] == "wave_per_box"
+    assert plan("pad5d_f32", "load", flags=T.FLAG_WHOLE_BOX)["variant"] == "ring"
+    assert plan("pad5d_f32", "load", stages=3)["variant"] == "ring"
+    assert plan("tile64_f32", "roundtrip")["variant"] == "ring"              # a 16 KiB box: the shared ring
+    assert plan("strips_f16", "load")["band_boxes"] == 0
+    assert plan("strips_f16", "load", flags=T.FLAG_THREAD_COPY)["variant"] == "thread_copy"
+    p = plan("sweep2g_u8", "load", flags=T.FLAG_PRODUCER_WAVE)
+    assert (p["variant"], p["band_boxes"], p["workgroups"]) == ("producer_wave", 0, 8 * cus)
+    assert plan("sweep2g_u8", "load", flags=T.FLAG_CONTIGUOUS | T.FLAG_WHOLE_BOX)["group"] == 0
+
+
 def test_zero_tiles_launch_nothing():
     src = dev_tensor(16384, fill_seed=1)
     m = enc("f32", src, [64, 64], [256], [64, 64])
@@ -379,7 +429,9 @@ def test_launch_options_out_of_range_are_rejected():
     before = out.clone()
     for bad in (dict(stages=5), dict(group=3), dict(group=128), dict(regions=65),
                 dict(flags=T.FLAG_BAND | T.FLAG_WHOLE_BOX),
-                dict(flags=T.FLAG_THREAD_COPY | T.FLAG_PRODUCER_WAVE)):
+                dict(flags=T.FLAG_THREAD_COPY | T.FLAG_PRODUCER_WAVE),
+                dict(flags=T.FLAG_WAVE_PER_BOX | T.FLAG_THREAD_COPY),
+                dict(flags=T.FLAG_WAVE_PER_BOX | T.FLAG_PRODUCER_WAVE), dict(flags=T.FLAG_WAVE_PER_BOX, stages=3)):
         with pytest.raises(T.TmapError) as e:
             T.tmap_load_tiles(m, None, n, out, **bad)
         assert e.value.status == T.INVALID_VALUE, bad
@@ -407,7 +459,7 @@ def test_budget_mismatch_times_out_on_the_band_schedule():
     assert out.cpu().numpy().tobytes() == oracle.load_tiles(om, src.cpu().numpy(), None, n).tobytes()
 
 
-@pytest.mark.parametrize("mode", [0, T.FLAG_PRODUCER_WAVE])
+@pytest.mark.parametrize("mode", [0, T.FLAG_PRODUCER_WAVE, T.FLAG_WAVE_PER_BOX])
 def test_budget_mismatch_times_out_instead_of_hanging(mode):
     """Announce 16 more bytes than delivered: the stage never becomes ready; the
     bounded wait ends the kernel and the status reports a timeout."""
@@ -435,21 +487,30 @@ def test_repeat_is_deterministic():
         assert torch.equal(a, b), st
 
 
-@pytest.mark.parametrize("mode", ["thread_copy", "producer_wave", "whole_box", "regions_3", "regions_1"])
+@pytest.mark.parametrize("mode", ["thread_copy", "producer_wave", "wave_per_box", "whole_box", "regions_3",
+                                  "regions_1"])
 @pytest.mark.parametrize("name", ["tile64_f32", "strips_f16", "ragged_bf16", "pad5d_f32", "sweep2g_u8"])
 def test_other_modes_match_the_staged_copy(name, mode):
-    """The register-path and producer-wave variants, the ring on whole boxes,
-    and other deals of the groups to the grid (regions), give the same bytes
-    as the default schedule (which the tests above pin to the oracle; the
-    band schedule where it applies) for load, store and round trip of every
-    workload."""
+    """The register-path, producer-wave and wave-per-box variants, the ring
+    on whole boxes, and other deals of the groups to the grid (regions), give
+    the same bytes as the default schedule (which the tests above pin to the
+    oracle; the band schedule where it applies) for load, store and round
+    trip of every workload."""
     w = inputs.WORKLOADS[name]
     alt = {"thread_copy": dict(flags=T.FLAG_THREAD_COPY), "producer_wave": dict(flags=T.FLAG_PRODUCER_WAVE),
+           "wave_per_box": dict(flags=T.FLAG_WAVE_PER_BOX),
            "whole_box": dict(flags=T.FLAG_WHOLE_BOX), "regions_3": dict(regions=3),
            "regions_1": dict(regions=1)}[mode]
     say(f"{mode} vs staged: {name}")
     src = inputs.device_bytes(w, DEV)
     m = enc(w.dtype, src, w.dims, w.strides, w.box, w.swizzle)
+    if mode == "wave_per_box" and T.tmap_box_bytes(m) > 16384:
+        # a wave's stage holds at most 16 KiB: rejected before any launch
+        out = torch.empty(T.tmap_box_bytes(m), dtype=torch.uint8, device=DEV)
+        with pytest.raises(T.TmapError) as e:
+            T.tmap_load_tiles(m, torch.zeros((1, w.rank), dtype=torch.int32, device=DEV), 1, out, **alt)
+        assert e.value.status == T.INVALID_VALUE
+        return
     if w.coords == "sweep":
         cn, n = None, T.tmap_sweep_tiles(m)
     elif w.coords == "origin":

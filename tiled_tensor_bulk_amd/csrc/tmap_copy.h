@@ -497,9 +497,12 @@ __device__ __forceinline__ uint32_t logical_chunk_of(const KArgs &a, uint32_t p,
 
 // ---------------------------------------------------------------- the kernel
 // BAND: the stage holds one unit of the band schedule (see KArgs) instead of
-// one box.
-template <int MODE, int S, int NSLOT, int R, bool BAND = false>
+// one box.  W: waves that share a stage (and a tile sequence) -- the whole
+// 4-wave workgroup, or 1 in wave-per-box mode, where every wave of the
+// workgroup walks its own tiles through its own ring.
+template <int MODE, int S, int NSLOT, int R, bool BAND = false, int W = kWaves>
 struct Copier {
+    static_assert(W == kWaves || W == 1, "a stage is shared by the workgroup or owned by one wave");
     static_assert(!BAND || NSLOT == kBandSlots, "a band stage is 16 KiB");
     const KArgs &a;
     uint32_t lane, wave, my_bytes, parity;
@@ -673,17 +676,22 @@ struct Copier {
     // (the consumers of the producer-wave variant use it).
     __device__ __forceinline__ void setup(int vwave = -1) {
         lane = threadIdx.x & 63u;
-        wave = vwave >= 0 ? (uint32_t)vwave : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const uint32_t hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave in the workgroup
+        wave = vwave >= 0 ? (uint32_t)vwave : (W == 1 ? 0u : hw);
         nt = (a.flags & TMAP_FLAG_NONTEMPORAL) != 0;
         parity = 0;
         edge = 0;
-        // workgroup index -> place in the deal: with R regions the first
-        // R*(grid/R) workgroups are dealt as R interleaved streams, workgroup
-        // i taking the next place of stretch i mod R (a permutation of
+        // the tile sequences are dealt to a.grid walkers: the workgroups, or
+        // in wave-per-box mode the waves (workgroup b's wave w is walker
+        // 4b + w; walkers past a.grid in the last workgroup take no tiles).
+        // Walker index -> place in the deal: with R regions the first
+        // R*(grid/R) walkers are dealt as R interleaved streams, walker i
+        // taking the next place of stretch i mod R (a permutation of
         // 0..grid-1, so every place is still taken once)
-        int64_t g = blockIdx.x;
+        int64_t g = W == 1 ? (int64_t)blockIdx.x * kWaves + hw : (int64_t)blockIdx.x;
+        const bool walker = g < (int64_t)a.grid;
         if (a.regions > 1) {
-            const uint32_t per = gridDim.x / a.regions;
+            const uint32_t per = a.grid / a.regions;
             if ((uint32_t)g < per * a.regions) g = (int64_t)((uint32_t)g % a.regions) * per + (uint32_t)g / a.regions;
         }
         int64_t t0;
@@ -701,19 +709,20 @@ struct Copier {
             cnt = a.deal_q * Q + last;
             t0 = g * Q;
         }
+        if (!walker) cnt = 0;
         cursor_init<R>(a, t0, fcur);
         ccur = fcur;
         nfill = 0;
         if (cnt > 0) corner(fcur, fc);
         my_bytes = 0;
-        const uint32_t cw = (wave + 1) % kWaves;
+        const uint32_t cw = (wave + 1) % W;
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
-            const uint32_t pb = (uint32_t)(j * kWaves) + wave;
+            const uint32_t pb = (uint32_t)(j * W) + wave;
             const int32_t valid = (int32_t)a.n_chunks - (int32_t)(pb * 64u);
             my_bytes += 16u * (uint32_t)(valid <= 0 ? 0 : (valid >= 64 ? 64 : valid));
             pslot[j] = pb * 64u + lane;
-            cslot[j] = ((uint32_t)(j * kWaves) + cw) * 64u + lane;
+            cslot[j] = ((uint32_t)(j * W) + cw) * 64u + lane;
             poff[j] = pw0[j] = pw1[j] = 0;
             coff[j] = cw0[j] = cw1[j] = 0;
             // the packed side of a copy reads / writes the slots' image
@@ -723,13 +732,20 @@ struct Copier {
             if (!a.elemwise) {
                 if (MODE != kStore && pslot[j] < a.n_chunks) slot_info(pslot[j], a.src, poff[j], pw0[j], pw1[j]);
                 if (MODE != kLoad && cslot[j] < a.n_chunks) slot_info(cslot[j], a.dst, coff[j], cw0[j], cw1[j]);
+                // a wave that drains its own slots in a round trip (whose
+                // maps share box and swizzle) finds the same box indices on
+                // both sides: hold them once
+                if (W == 1 && MODE == kRoundtrip) {
+                    cw0[j] = pw0[j];
+                    cw1[j] = pw1[j];
+                }
             }
         }
     }
 
     template <typename T>
     __device__ __forceinline__ void dma(const Src &src, T *stage, int j, uint32_t voff) const {
-        dma_lds(src.base, src.nrec, stage + (j * kWaves + wave) * kBlockBytes, voff, nt);
+        dma_lds(src.base, src.nrec, stage + (j * W + wave) * kBlockBytes, voff, nt);
     }
 
     // Issue the loads of the tile under the fill cursor into stage XF, then
@@ -737,7 +753,7 @@ struct Copier {
     template <int XF>
     __device__ __forceinline__ void fill(uint8_t *stage, uint64_t *bar) {
         const uint32_t budget = my_bytes + ((a.flags & TMAP_FLAG_INJECT_BUDGET_MISMATCH) ? 16u : 0u);
-        bar_arrive_expect(bar, budget, lane);
+        bar_arrive_expect(bar, budget, lane, W);
         int32_t c[R];
 #pragma unroll
         for (int d = 0; d < R; ++d) c[d] = sc[XF][d] = fc[d];
@@ -796,7 +812,7 @@ struct Copier {
         if (MODE != kStore && ((edge >> X) & 1u)) patch_edge(stage, c);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm);
         asm volatile("" ::: "memory");
-        bar_complete(bar, my_bytes, lane);
+        bar_complete(bar, my_bytes, lane, W);
     }
 
     // Edge tile at corner c: fill in the partial chunks of this lane's
@@ -808,7 +824,7 @@ struct Copier {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
 #pragma unroll 1
         for (int j = 0; j < NSLOT; ++j) {
-            const uint32_t p = ((uint32_t)(j * kWaves) + wave) * 64u + lane;
+            const uint32_t p = ((uint32_t)(j * W) + wave) * 64u + lane;
             if (p >= a.n_chunks) continue;
             if (a.elemwise) {
                 load_slot_elements<R>(stage, p, a, a.src, w, r);
@@ -892,10 +908,10 @@ struct Copier {
                 // slow path, kept out of the unrolled slot arrays: recompute
                 // each slot's chunk, store the inside elements of partial ones
                 if (!a.elemwise && !splits_chunks(w)) return;
-                const uint32_t cw = (wave + 1) % kWaves;
+                const uint32_t cw = (wave + 1) % W;
 #pragma unroll 1
                 for (int j = 0; j < NSLOT; ++j) {
-                    const uint32_t p = ((uint32_t)(j * kWaves) + cw) * 64u + lane;
+                    const uint32_t p = ((uint32_t)(j * W) + cw) * 64u + lane;
                     if (p >= a.n_chunks) continue;
                     if (a.elemwise) {
                         store_slot_elements<R>(stage, p, a, a.dst, w, r, MODE == kRoundtrip && a.add_f32);
@@ -916,8 +932,11 @@ struct Copier {
     template <int X>
     __device__ __forceinline__ bool step(uint8_t *st, uint8_t *fillst, int64_t k) {
         if (k >= cnt) return false;
+        // this wave's reads of the stage about to be refilled are done; with
+        // a shared stage, every wave's (a wave that owns its stage read it
+        // itself, so its own wait is enough)
         __builtin_amdgcn_s_waitcnt(kWaitLgkm);
-        __builtin_amdgcn_s_barrier();
+        if constexpr (W > 1) __builtin_amdgcn_s_barrier();
         if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
         constexpr int XF = (X + S - 1) % S;
         // the tile's corner, recorded when it was filled (with one stage the
@@ -995,6 +1014,60 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const KArgs a) {
         }
     }
     // nothing may still be writing LDS or memory when the wave ends
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+// ---------------------------------------------------------------- wave-per-box variant
+// Every wave of the workgroup walks its own tile sequence through its own
+// ring of S stages of one box each (NSLOT KiB): it issues all of a box's
+// direct-to-LDS loads, arrives on its own stage record with the box's bytes,
+// completes them once its loads have landed and drains the box after the
+// record's phase flips -- the same byte-count protocol with one arrival per
+// phase, and no workgroup barrier.  The per-box scalar work (corner,
+// address, bounds) is done once per box instead of once per wave, and four
+// boxes are in flight per workgroup and stage.
+template <int MODE, int S, int NSLOT, int R>
+__global__ __launch_bounds__(kThreads) void wave_kernel(const KArgs a) {
+    constexpr uint32_t SB = NSLOT * kBlockBytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kWaves * S * SB];
+    __shared__ uint64_t bars[kWaves * 4];
+    __shared__ uint32_t abort_flag;
+
+    const uint32_t hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Copier<MODE, S, NSLOT, R, false, 1> cp(a, bars + 4 * hw, &abort_flag);
+    if (threadIdx.x == 0) {
+        for (int i = 0; i < kWaves * 4; ++i) bars[i] = 0;
+        abort_flag = 0;
+    }
+    cp.setup();
+    __syncthreads();
+    if (cp.cnt <= 0) return;
+    uint8_t *st0 = ring + hw * (S * SB);
+    uint8_t *st1 = st0 + (S > 1 ? SB : 0);
+    uint8_t *st2 = st0 + (S > 2 ? 2 * SB : 0);
+    uint8_t *st3 = st0 + (S > 3 ? 3 * SB : 0);
+
+    if constexpr (S > 1) cp.template fill<0>(st0, &cp.bars[0]);
+    if constexpr (S > 2) if (1 < cp.cnt) cp.template fill<1>(st1, &cp.bars[1]);
+    if constexpr (S > 3) if (2 < cp.cnt) cp.template fill<2>(st2, &cp.bars[2]);
+
+    for (int64_t kb = 0; kb < cp.cnt; kb += S) {
+        if constexpr (S == 1) {
+            if (!cp.template step<0>(st0, st0, kb)) break;
+        } else if constexpr (S == 2) {
+            if (!cp.template step<0>(st0, st1, kb)) break;
+            if (!cp.template step<1>(st1, st0, kb + 1)) break;
+        } else if constexpr (S == 3) {
+            if (!cp.template step<0>(st0, st2, kb)) break;
+            if (!cp.template step<1>(st1, st0, kb + 1)) break;
+            if (!cp.template step<2>(st2, st1, kb + 2)) break;
+        } else {
+            if (!cp.template step<0>(st0, st3, kb)) break;
+            if (!cp.template step<1>(st1, st0, kb + 1)) break;
+            if (!cp.template step<2>(st2, st1, kb + 2)) break;
+            if (!cp.template step<3>(st3, st2, kb + 3)) break;
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0);
 }
 
@@ -1345,6 +1418,18 @@ KernelFn pick_thread(int nslot) {
 }
 
 template <int MODE, int S, int R>
+KernelFn pick_wave(int nslot) {
+    switch (nslot) {
+        case 1: return wave_kernel<MODE, S, 1, R>;
+        case 2: return wave_kernel<MODE, S, 2, R>;
+        case 4: return wave_kernel<MODE, S, 4, R>;
+        case 8: return wave_kernel<MODE, S, 8, R>;
+        case 16: return wave_kernel<MODE, S, 16, R>;
+        default: return nullptr;
+    }
+}
+
+template <int MODE, int S, int R>
 KernelFn pick_ws(int nslot) {
     switch (nslot) {
         case 1: return ws_kernel<MODE, S, 1, R>;
@@ -1357,12 +1442,14 @@ KernelFn pick_ws(int nslot) {
 
 // Launch the (MODE, stages, nslot, R) variant; stages == 0 is the
 // thread-copy variant, stages 12..14 the producer-wave variant with 2..4
-// stages and stages 21..24 the ring with 1..4 stages on the band schedule
-// (nslot is then 4).  hipError_t as int.
+// stages, stages 21..24 the ring with 1..4 stages on the band schedule
+// (nslot is then 4) and stages 31..32 the wave-per-box variant with 1..2
+// stages of nslot KiB per wave.  hipError_t as int.
 template <int MODE, int R>
 int launch_mode(int stages, int nslot, const KArgs &a, void *stream) {
     KernelFn fn = nullptr;
     int threads = kThreads;
+    uint32_t blocks = a.grid;
     switch (stages) {
         case 0: fn = pick_thread<MODE, R>(nslot); break;
         case 12: fn = pick_ws<MODE, 2, R>(nslot); threads = kWsThreads; break;
@@ -1376,12 +1463,15 @@ int launch_mode(int stages, int nslot, const KArgs &a, void *stream) {
         case 22: fn = copy_kernel<MODE, 2, kBandSlots, R, true>; break;
         case 23: fn = copy_kernel<MODE, 3, kBandSlots, R, true>; break;
         case 24: fn = copy_kernel<MODE, 4, kBandSlots, R, true>; break;
+        // a.grid counts waves here: four to a workgroup
+        case 31: fn = pick_wave<MODE, 1, R>(nslot); blocks = (a.grid + kWaves - 1) / kWaves; break;
+        case 32: fn = pick_wave<MODE, 2, R>(nslot); blocks = (a.grid + kWaves - 1) / kWaves; break;
         default: break;
     }
     if (!fn) return (int)hipErrorInvalidValue;
     KArgs copy = a;
     void *args[] = {&copy};
-    return (int)hipLaunchKernel((const void *)fn, dim3(a.grid), dim3(threads), args, 0, (hipStream_t)stream);
+    return (int)hipLaunchKernel((const void *)fn, dim3(blocks), dim3(threads), args, 0, (hipStream_t)stream);
 }
 
 }  // namespace

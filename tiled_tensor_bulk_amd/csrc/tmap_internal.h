@@ -140,4 +140,9 @@ int launch_roundtrip_r5(int stages, int nslot, const KArgs &a, void *stream);
 inline uint32_t variant_lds_bytes(int stages, int nslot) {
     return (uint32_t)stages * (uint32_t)nslot * kWaves * kBlockBytes + 64u;
 }
+
+// The same for the wave-per-box variant: one ring of one-box stages per wave.
+inline uint32_t wave_lds_bytes(int stages, int nslot) {
+    return (uint32_t)kWaves * (uint32_t)stages * (uint32_t)nslot * kBlockBytes + kWaves * 32u + 4u;
+}
 }  // namespace tmap

@@ -20,6 +20,7 @@ FLAG_CONTIGUOUS = 0x1
 FLAG_NONTEMPORAL = 0x2
 FLAG_THREAD_COPY = 0x4
 FLAG_PRODUCER_WAVE = 0x8
+FLAG_WAVE_PER_BOX = 0x40
 FLAG_WHOLE_BOX = 0x10
 FLAG_BAND = 0x20
 FLAG_INJECT_BUDGET_MISMATCH = 0x100
@@ -47,6 +48,17 @@ class tmap_launch_opts(ctypes.Structure):
                 ("flags", ctypes.c_uint32), ("spin_limit", ctypes.c_uint32),
                 ("group", ctypes.c_uint32), ("regions", ctypes.c_uint32),
                 ("band_rows", ctypes.c_uint32)]
+
+
+class tmap_plan(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_uint32), ("band_boxes", ctypes.c_uint32), ("band_rows", ctypes.c_uint32),
+                ("stages", ctypes.c_uint32), ("slots", ctypes.c_uint32), ("group", ctypes.c_uint32),
+                ("walkers", ctypes.c_uint32), ("workgroups", ctypes.c_uint32), ("regions", ctypes.c_uint32),
+                ("lds_bytes", ctypes.c_uint32), ("units", ctypes.c_int64)]
+
+
+DIRECTIONS = {"load": 0, "store": 1, "roundtrip": 2}
+VARIANTS = {0: "ring", 1: "thread_copy", 2: "producer_wave", 3: "wave_per_box"}
 
 
 class tmap_info(ctypes.Structure):
@@ -90,6 +102,9 @@ def lib():
         L.tmap_band_boxes.restype = u32
         L.tmap_inbounds_elems.argtypes = [P(tmap_t), vp, i64, P(ctypes.c_uint64)]
         L.tmap_inbounds_elems.restype = ctypes.c_int
+        L.tmap_plan_launch.argtypes = [ctypes.c_int, P(tmap_t), P(tmap_t), vp, i64, P(tmap_launch_opts),
+                                       P(tmap_plan)]
+        L.tmap_plan_launch.restype = ctypes.c_int
         L.tmap_query.argtypes = [P(tmap_t), P(tmap_info)]
         L.tmap_query.restype = ctypes.c_int
         L.tmap_status_string.argtypes = [ctypes.c_int]
@@ -244,6 +259,23 @@ def tmap_band_boxes(src: tmap_t, dst: Optional[tmap_t] = None, explicit_coords: 
     corners = ctypes.addressof(_ANY_CORNERS) if explicit_coords else None
     return int(lib().tmap_band_boxes(ctypes.byref(src), None if dst is None else ctypes.byref(dst),
                                      corners, _opts(flags=int(flags), band_rows=int(band_rows))))
+
+
+def tmap_plan_launch(direction, swept: tmap_t, dst: Optional[tmap_t] = None, explicit_coords: bool = False,
+                     n_tiles: Optional[int] = None, **opts) -> dict:
+    """The schedule a copy would run with (needs a gfx950 device; launches
+    nothing).  direction: "load", "store" or "roundtrip"; n_tiles defaults
+    to the full sweep."""
+    d = DIRECTIONS[direction] if isinstance(direction, str) else int(direction)
+    corners = ctypes.addressof(_ANY_CORNERS) if explicit_coords else None
+    n = tmap_sweep_tiles(swept) if n_tiles is None else int(n_tiles)
+    out = tmap_plan()
+    st = lib().tmap_plan_launch(d, ctypes.byref(swept), None if dst is None else ctypes.byref(dst), corners, n,
+                                _opts(**opts), ctypes.byref(out))
+    _check(st, "tmap_plan_launch")
+    r = {f: getattr(out, f) for f, _ in tmap_plan._fields_}
+    r["variant"] = VARIANTS.get(out.variant, str(out.variant))
+    return r
 
 
 def tmap_inbounds_elems(m: tmap_t, host_coords, n_tiles: int) -> int:
