@@ -5,7 +5,8 @@
 // One kernel template serves the three directions (load to packed images,
 // store from packed images, round trip).  Each workgroup (4 waves) walks its
 // share of the tiles (by default one group of neighbouring tiles) through a
-// ring of S LDS stages:
+// ring of S LDS stages -- or, in wave-per-box mode, each wave walks its own
+// share through its own ring of one-box stages:
 //
 //   fill    every lane issues one 16-byte direct-to-LDS buffer load per slot
 //           it owns (buffer_load_dwordx4 ... lds).  The tensor map sits in
@@ -36,11 +37,12 @@
 //           clipped to the destination's bounds.
 //   release one s_barrier per tile: no wave refills a stage before every
 //           wave finished reading it ("TMA -- the async bulk copy engine",
-//           "Why this only pays off inside a pipeline").
+//           "Why this only pays off inside a pipeline"); a wave that owns
+//           its stages only waits for its own reads.
 //
-// The S stages are separate __shared__ objects and the tile loop is
-// unrolled by S.  The direct-to-LDS loads are issued from assembly and each
-// stage waits for exactly its own loads (vmcnt of the later stages' loads),
+// The tile loop is unrolled by S.  The direct-to-LDS loads are issued from
+// assembly and each stage waits for exactly its own loads (a vmcnt that
+// leaves the later stages' loads and the earlier drains' stores in flight),
 // so a stage drains while the next ones fill.  On the band schedule (sweeps
 // of boxes with narrow rows) a stage holds the same band of rows of several
 // neighbouring boxes instead of one box.  R is the number of dimensions the
