@@ -166,6 +166,8 @@ def main():
         else:
             schedule = "whole boxes" + ("" if plan["variant"] == "ring" else f" ({plan['variant']})")
 
+    kernel_name = {"ring": "copy_kernel", "wave_per_box": "wave_kernel", "thread_copy": "thread_kernel",
+                   "producer_wave": "ws_kernel"}[plan["variant"]] if plan else "copy_kernel"
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         launch()
@@ -232,7 +234,7 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic / kern_avg_s / 1e9, 2),
                      "kernel_ms": round(kern_avg_s * 1e3, 4),
-                     "kernel": f"tmap copy_kernel ({args.op})"},
+                     "kernel": f"tmap {kernel_name} ({args.op})"},
         "kernel_ms_median": round(sorted(kern_ms)[len(kern_ms) // 2], 4),
         "kernel_ms_min": round(min(kern_ms), 4),
         "reference_d2d_copy_GBps": round(copy_gbps, 1),

@@ -61,12 +61,24 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+_KERNEL = re.compile(r"\b(copy|wave|thread|ws)_kernel<")
+
+
+def is_copy_kernel(name: str) -> bool:
+    """A dispatch of one of libtmap's copy kernels (any variant)."""
+    return bool(_KERNEL.search(name))
+
+
 def short(name: str) -> str:
     m = re.search(r"copy_kernel<(\d+), (\d+), (\d+), (\d+)(?:, (true|false))?>", name)
     if m:
         mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
         sched = ", band" if m.group(5) == "true" else ""
         return f"tmap copy_kernel<{mode}, stages={m.group(2)}, nslot={m.group(3)}, dims={m.group(4)}{sched}>"
+    m = re.search(r"wave_kernel<(\d+), (\d+), (\d+), (\d+)>", name)
+    if m:
+        mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
+        return f"tmap wave_kernel<{mode}, stages={m.group(2)}, nslot={m.group(3)}, dims={m.group(4)}>"
     if "copyBuffer" in name:
         return "hip copyBuffer (torch d2d copy)"
     return (name[:60] + "...") if len(name) > 63 else name
@@ -87,7 +99,7 @@ def cmd_stats(a):
     if a.trace:
         # the bench times its last `steps` launches (after the warm-up, whose
         # first launches run while the clocks settle): average those alone
-        tr = [r for r in csv.DictReader(open(a.trace)) if "copy_kernel" in r["Kernel_Name"]]
+        tr = [r for r in csv.DictReader(open(a.trace)) if is_copy_kernel(r["Kernel_Name"])]
         tr.sort(key=lambda r: int(r["Start_Timestamp"]))
         last = tr[-a.last:]
         us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in last]
@@ -119,7 +131,7 @@ def cmd_traffic(a):
     for counter, path in (("FETCH_SIZE", a.fetch), ("WRITE_SIZE", a.write)):
         d = per_dispatch(path, counter)
         copies = [v for (_, n, v) in d if "copyBuffer" in n and v > 0.25 * known_kib]
-        kern = [v for (_, n, v) in d if "copy_kernel" in n]
+        kern = [v for (_, n, v) in d if is_copy_kernel(n)]
         if not copies or not kern:
             sys.exit(f"{path}: no reference copy or copy kernel dispatches with {counter}")
         factor = known_kib / (sum(copies) / len(copies))
@@ -151,7 +163,7 @@ def cmd_counters(a):
     agg = defaultdict(float)
     disp = set()
     for r in rows:
-        if "copy_kernel" not in r["Kernel_Name"]:
+        if not is_copy_kernel(r["Kernel_Name"]):
             continue
         disp.add(int(r["Dispatch_Id"]))
         agg[r["Counter_Name"]] += float(r["Counter_Value"])
