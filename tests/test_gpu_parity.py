@@ -125,14 +125,16 @@ def _sample_tiles(n, extra, k, seed):
     return np.array(sorted(s), dtype=np.int64)
 
 
-def test_ragged_bf16_full_size_sampled():
+@pytest.mark.parametrize("opts", [dict(flags=T.FLAG_NONTEMPORAL), dict(stages=4, flags=T.FLAG_NONTEMPORAL)],
+                         ids=["benchmark_launch", "band_4_stages"])
+def test_ragged_bf16_full_size_sampled(opts):
     w = inputs.WORKLOADS["ragged_bf16"]
-    say("ragged_bf16: load sweep 65280 tiles (the benchmark's launch); sampled oracle; store back")
+    say(f"ragged_bf16: load sweep 65280 tiles {opts}; sampled oracle; store back")
     src = inputs.device_bytes(w, DEV)
     m = enc("bf16", src, w.dims, w.strides, w.box, w.swizzle)
     n = T.tmap_sweep_tiles(m)
     assert n == 65280
-    packed = gpu_load(m, None, n, flags=T.FLAG_NONTEMPORAL)
+    packed = gpu_load(m, None, n, **opts)
     om = Map(es=2, dims=w.dims, strides=w.strides, box=w.box, swizzle=w.swizzle)
     last_row = list(range(n - 255, n))                       # the ragged strip (63 rows + 1 zero row)
     tiles = _sample_tiles(n, last_row + [0, 254, 255], 600, 33)
@@ -144,37 +146,38 @@ def test_ragged_bf16_full_size_sampled():
     # the zero-filled row of every ragged tile: last 64 columns x 2 bytes of each image
     # closed form: storing every image back restores every byte of the tensor
     dst = dev_tensor(w.alloc_bytes, fill_seed=303)
-    T.tmap_store_tiles(enc("bf16", dst, w.dims, w.strides, w.box, w.swizzle), None, n, packed,
-                       flags=T.FLAG_NONTEMPORAL)
+    T.tmap_store_tiles(enc("bf16", dst, w.dims, w.strides, w.box, w.swizzle), None, n, packed, **opts)
     check_ok()
     assert torch.equal(dst, src)
 
 
-def test_pad5d_f32_random_corners_full():
+@pytest.mark.parametrize("opts", [dict(), dict(stages=4), dict(stages=2, flags=T.FLAG_WHOLE_BOX)],
+                         ids=["benchmark_launch", "shared_ring_4_stages", "shared_ring_2_stages"])
+def test_pad5d_f32_random_corners_full(opts):
     w = inputs.WORKLOADS["pad5d_f32"]
-    say("pad5d_f32: load 1e5 random corners (the benchmark's launch), full oracle; then store")
+    say(f"pad5d_f32: load 1e5 random corners {opts}, full oracle; then store")
     src = inputs.device_bytes(w, DEV)
     host = src.cpu().numpy()
     coords = inputs.random_corners(w.dims, w.box, w.n_random, seed=40)
     m = enc("f32", src, w.dims, w.strides, w.box)
     om = Map(es=4, dims=w.dims, strides=w.strides, box=w.box)
-    packed = gpu_load(m, coords, len(coords))
+    packed = gpu_load(m, coords, len(coords), **opts)
     want = oracle.load_tiles(om, host, coords, len(coords))
     got = packed.cpu().numpy()
     assert (mm := first_mismatch(got, want, 8192)) is None, mm
     dst = dev_tensor(w.alloc_bytes, fill_seed=41)
     want_dst = dst.cpu().numpy().copy()
     c = torch.from_numpy(coords).to(DEV)
-    T.tmap_store_tiles(enc("f32", dst, w.dims, w.strides, w.box), c, len(coords), packed)
+    T.tmap_store_tiles(enc("f32", dst, w.dims, w.strides, w.box), c, len(coords), packed, **opts)
     check_ok()
     oracle.store_tiles(om, want_dst, coords, len(coords), want)
     got_dst = dst.cpu().numpy()
     assert (mm := first_mismatch(got_dst, want_dst, 1 << 30)) is None, mm
 
 
-@pytest.mark.parametrize("opts", [dict(flags=T.FLAG_NONTEMPORAL),
+@pytest.mark.parametrize("opts", [dict(flags=T.FLAG_NONTEMPORAL), dict(stages=4, flags=T.FLAG_NONTEMPORAL),
                                   dict(stages=4, flags=T.FLAG_NONTEMPORAL | T.FLAG_WHOLE_BOX)],
-                         ids=["benchmark_launch", "whole_box_4_stages"])
+                         ids=["benchmark_launch", "band_4_stages", "whole_box_4_stages"])
 def test_sweep2g_u8_full_size(opts):
     w = inputs.WORKLOADS["sweep2g_u8"]
     say(f"sweep2g_u8: roundtrip 131072 tiles (2 GiB) {opts}; load sampled vs oracle; store")
