@@ -929,6 +929,52 @@ struct Copier {
         }
     }
 
+    // One step of a one-stage ring whose drain is held in registers (a
+    // load of a wave that owns its stage): land tile k, read its image out
+    // of the stage into `held`, refill the stage with tile k+1, and only then
+    // store the image.  The stores of tile k are thus issued after the loads
+    // of tile k+1, and the next landing waits for those loads alone
+    // (vmcnt(NSLOT) leaves tile k's NSLOT stores in flight), where an
+    // ordinary one-stage step would also wait for the previous stores.
+    __device__ __forceinline__ bool step_held(uint8_t *st, int64_t k, i32x4 (&held)[NSLOT]) {
+        static_assert(MODE == kLoad && S == 1 && W == 1, "a one-stage load ring of one wave");
+        if (k >= cnt) return false;
+        if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return false;
+        int32_t c[R];
+#pragma unroll
+        for (int d = 0; d < R; ++d) c[d] = sc[0][d];
+        // after tile k's loads this wave issued tile k-1's NSLOT stores
+        if (k > 0)
+            wait_vmcnt<NSLOT>();
+        else
+            wait_vmcnt<0>();
+        if ((edge & 1u) != 0u) patch_edge(st, c);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+        asm volatile("" ::: "memory");
+        bar_complete(&bars[0], my_bytes, lane, W);
+        const bool ok = bar_wait(&bars[0], parity & 1u, a.spin_limit);
+        parity ^= 1u;
+        asm volatile("" ::: "memory");
+        if (!ok) {
+            if (lane == 0) {
+                __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            return false;
+        }
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) held[j] = *(const i32x4 *)(st + cslot[j] * 16u);
+        // the stage is free once these reads have completed
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+        asm volatile("" ::: "memory");
+        const __amdgpu_buffer_rsrc_t r = packed_rsrc(ccur, a.src.box_bytes);
+        if (k + 1 < cnt) fill<0>(st, &bars[0]);
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) store16(held[j], r, cslot[j] < a.n_chunks ? coff[j] : kOob);
+        cursor_advance<R>(a, ccur);
+        return true;
+    }
+
     // One ring step for tile k held in stage X; `fillst` is the stage that
     // tile k+S-1 goes to (the one tile k-1 just left).  False ends the loop.
     template <int X>
@@ -1049,6 +1095,15 @@ __global__ __launch_bounds__(kThreads) void wave_kernel(const KArgs a) {
     uint8_t *st2 = st0 + (S > 2 ? 2 * SB : 0);
     uint8_t *st3 = st0 + (S > 3 ? 3 * SB : 0);
 
+    if constexpr (MODE == kLoad && S == 1) {
+        // one stage, its drain held in registers while the next tile loads
+        i32x4 held[NSLOT];
+        cp.template fill<0>(st0, &cp.bars[0]);
+        for (int64_t k = 0; k < cp.cnt; ++k)
+            if (!cp.step_held(st0, k, held)) break;
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
     if constexpr (S > 1) cp.template fill<0>(st0, &cp.bars[0]);
     if constexpr (S > 2) if (1 < cp.cnt) cp.template fill<1>(st1, &cp.bars[1]);
     if constexpr (S > 3) if (2 < cp.cnt) cp.template fill<2>(st2, &cp.bars[2]);
