@@ -166,6 +166,12 @@ typedef struct tmap_launch_opts {
  * TMAP_ERROR_TIMEOUT ("Day 76", "Pitfalls": a byte budget that does not match
  * the bytes delivered decouples the wait from the data). */
 #define TMAP_FLAG_INJECT_BUDGET_MISMATCH 0x100u
+/* Debug aid: before the loads of each stage are issued, the stage is filled
+ * with the pattern 0xDEADBEEF, so that a consumer reading it before its byte
+ * count completes would copy the pattern out rather than stale bytes of an
+ * earlier tile.  Same results as without it when the accounting is right;
+ * slower.  Not for the thread-copy mode (it writes the stage itself). */
+#define TMAP_FLAG_DEBUG_POISON 0x200u
 
 /*
  * tmap_encode -- validate and pack a tensor map.

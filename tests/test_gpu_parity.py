@@ -284,6 +284,47 @@ def test_fuzz_random_maps(chunk):
         assert (mm := first_mismatch(dst2.cpu().numpy(), want2, 1 << 40)) is None, ("store", mm)
 
 
+@pytest.mark.parametrize("chunk", range(2))
+def test_poisoned_stages_still_match(chunk):
+    """With every stage filled with 0xDEADBEEF before its loads are issued, a
+    read that the byte count let through too early would copy the pattern
+    out; loads and round trips must still match the oracle byte for byte
+    (shared ring, wave per box, producer wave, band schedule)."""
+    rng = np.random.default_rng(9100 + chunk)
+    for i in range(16):
+        es, dims, strides, box, swz, alloc, coords, opts = (_fuzz_case if i % 2 else _wave_case)(rng, i)
+        if opts["flags"] & T.FLAG_THREAD_COPY:
+            opts["flags"] &= ~T.FLAG_THREAD_COPY
+        opts["flags"] |= T.FLAG_DEBUG_POISON
+        say(f"poison {chunk}/{i}: es={es} dims={dims} box={box} swz={swz} n={len(coords)} opts={opts}")
+        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+        src = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        host = src.cpu().numpy()
+        m = enc(dt_of(es), src, dims, strides, box, swz)
+        got = gpu_load(m, coords, len(coords), **opts).cpu().numpy()
+        want = oracle.load_tiles(om, host, coords, len(coords))
+        assert (mm := first_mismatch(got, want, T.tmap_box_bytes(m))) is None, mm
+        dst = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        want_dst = dst.cpu().numpy().copy()
+        T.tmap_roundtrip(m, enc(dt_of(es), dst, dims, strides, box, swz), torch.from_numpy(coords).to(DEV),
+                         len(coords), **opts)
+        check_ok()
+        oracle.roundtrip(om, host, om, want_dst, coords, len(coords))
+        assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip", mm)
+    # a band-schedule sweep at full size: 2 GiB round trip, 3-stage ring of 16 KiB units
+    w = inputs.WORKLOADS["sweep2g_u8"]
+    if chunk == 0:
+        say("poison: sweep2g_u8 round trip")
+        src = inputs.device_bytes(w, DEV)
+        dst = dev_tensor(w.alloc_bytes)
+        dst.fill_(0)
+        ms = enc("u8", src, w.dims, w.strides, w.box, w.swizzle)
+        T.tmap_roundtrip(ms, enc("u8", dst, w.dims, w.strides, w.box, w.swizzle), None, T.tmap_sweep_tiles(ms),
+                         flags=T.FLAG_NONTEMPORAL | T.FLAG_DEBUG_POISON)
+        check_ok()
+        assert torch.equal(dst, src)
+
+
 # ----------------------------------------------------------------- edge cases
 def test_sweep_equals_explicit_coords():
     say("sweep vs explicit corners")

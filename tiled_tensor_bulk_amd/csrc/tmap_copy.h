@@ -130,6 +130,21 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("" ::: "memory");
 }
 
+// Debug aid (TMAP_FLAG_DEBUG_POISON): fill `blocks` consecutive 1 KiB blocks
+// of LDS from `lds`, this lane's 16 bytes of each, with a recognisable
+// pattern, and wait for the writes, before direct-to-LDS loads refill them.
+// A consumer that read the blocks before the byte count allowed would then
+// copy the pattern into its output, where a comparison with the oracle
+// finds it, instead of stale bytes of an earlier tile.
+constexpr int kPoison = (int)0xDEADBEEFu;
+
+__device__ __forceinline__ void poison_blocks(uint8_t *lds, int blocks, int stride_blocks, uint32_t lane) {
+    const i32x4 v = {kPoison, kPoison, kPoison, kPoison};
+    for (int j = 0; j < blocks; ++j) *(i32x4 *)(lds + (size_t)j * stride_blocks * kBlockBytes + lane * 16u) = v;
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ uint32_t swizzle(uint32_t e, uint32_t b, uint32_t m, uint32_t s) {
     return b ? e ^ (((e >> (m + s)) & ((1u << b) - 1u)) << m) : e;
 }
@@ -755,6 +770,7 @@ struct Copier {
     template <int XF>
     __device__ __forceinline__ void fill(uint8_t *stage, uint64_t *bar) {
         const uint32_t budget = my_bytes + ((a.flags & TMAP_FLAG_INJECT_BUDGET_MISMATCH) ? 16u : 0u);
+        if (a.flags & TMAP_FLAG_DEBUG_POISON) poison_blocks(stage + wave * kBlockBytes, NSLOT, W, lane);
         bar_arrive_expect(bar, budget, lane, W);
         int32_t c[R];
 #pragma unroll
@@ -1281,6 +1297,7 @@ struct WsProducer {
     __device__ __forceinline__ void fill(uint8_t *stage) {
         const uint32_t bb = a.src.box_bytes;
         const uint32_t budget = bb + ((a.flags & TMAP_FLAG_INJECT_BUDGET_MISMATCH) ? 16u : 0u);
+        if (a.flags & TMAP_FLAG_DEBUG_POISON) poison_blocks(stage, NP, 1, lane);
         bar_arrive_expect(&full[X], budget, lane, 1);
         if (MODE == kStore) {
             const uint64_t dbb = a.dst.box_bytes;

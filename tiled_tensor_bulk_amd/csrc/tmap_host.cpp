@@ -6,7 +6,7 @@
 // validated and packed once on the host, every rule is checked, and a single
 // failed rule fails the whole call with INVALID_VALUE.
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cstdarg>
 #include <cstdio>

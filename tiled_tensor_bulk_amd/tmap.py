@@ -24,6 +24,7 @@ FLAG_WAVE_PER_BOX = 0x40
 FLAG_WHOLE_BOX = 0x10
 FLAG_BAND = 0x20
 FLAG_INJECT_BUDGET_MISMATCH = 0x100
+FLAG_DEBUG_POISON = 0x200
 
 DTYPES = {"u8": 0, "i8": 1, "u16": 2, "f16": 3, "bf16": 4, "u32": 5, "i32": 6, "f32": 7,
           "u64": 8, "f64": 9}
