@@ -19,8 +19,11 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# Test hook: TMAP_ORACLE_SRC names another copy of oracle.c, built into a
+# liboracle.so beside it.  The mutation tests use it to run the pins against
+# copies of the oracle with one mistake planted each.
+_SRC = os.environ.get("TMAP_ORACLE_SRC") or os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(os.path.dirname(os.path.abspath(_SRC)), "liboracle.so")
 
 MAX_RANK = 5
 

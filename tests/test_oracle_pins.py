@@ -178,6 +178,52 @@ def test_oob_zero_set_is_exactly_out_of_bounds():
     assert not packed[0].any() and not packed[1].any()       # wholly outside: all zero
 
 
+def test_oob_before_the_base_and_past_the_row_is_zero():
+    """The tensor sits inside a larger buffer whose bytes before its base and
+    in its row padding are nonzero: elements at coordinate -1 (one element
+    before the base in the innermost dimension) and past dims_0 (the padding)
+    must still load as zero, and match the independent numpy formulation."""
+    rng = np.random.default_rng(12)
+    es, dims, pitch, box = 2, [40, 12], 96, [16, 4]
+    prefix = 64
+    big = rng.integers(1, 256, size=prefix + pitch * dims[1] + 64, dtype=np.uint8)  # nothing is zero
+    src = big[prefix:]
+    m = Map(es=es, dims=dims, strides=[pitch], box=box, swizzle=(1, 3, 1))
+    corners = np.array([[-1, 0], [-3, -1], [-1, -3], [30, 9], [-15, 5], [25, -2], [38, 11]], np.int32)
+    got = oracle.load_tiles(m, src, corners, len(corners))
+    want = npref.load_tiles(src, es, dims, [pitch], box, (1, 3, 1), corners)
+    assert np.array_equal(got, want)
+    inv = npref.perm(int(np.prod(box)), (1, 3, 1))
+    tiles = got.view(np.uint16).reshape(len(corners), -1)
+    for t, c in enumerate(corners):
+        mask = npref.inbounds_mask(es, dims, box, c).reshape(-1)
+        assert np.array_equal(tiles[t, inv] != 0, mask)
+
+
+def test_roundtrip_between_layouts_matches_numpy():
+    """A round trip from one layout into another (different dims and pitch,
+    same element size, box and swizzle), over corners in, across and outside
+    both tensors, equals loading each box from the source and storing it
+    through the destination in tile order, in the numpy formulation."""
+    rng = np.random.default_rng(13)
+    es, box, swz = 4, [8, 4, 2], (2, 2, 2)
+    sdims, sstr = [37, 9, 3], [160, 160 * 9]
+    ddims, dstr = [29, 12, 2], [128, 128 * 12]
+    src = rng.integers(0, 256, size=sstr[1] * sdims[2], dtype=np.uint8)
+    dst0 = rng.integers(0, 256, size=dstr[1] * ddims[2], dtype=np.uint8)
+    corners = inputs.random_corners([max(a, b) for a, b in zip(sdims, ddims)], box, 60, seed=14)
+    sm = Map(es=es, dims=sdims, strides=sstr, box=box, swizzle=swz)
+    dm = Map(es=es, dims=ddims, strides=dstr, box=box, swizzle=swz)
+    got = dst0.copy()
+    oracle.roundtrip(sm, src, dm, got, corners, len(corners))
+    want = dst0.copy()
+    for c in corners:
+        tile = npref.load_tiles(src, es, sdims, sstr, box, swz, c[None, :])
+        npref.store_tiles(want, es, ddims, dstr, box, swz, c[None, :], tile)
+    assert np.array_equal(got, want)
+    assert not np.array_equal(got, dst0)
+
+
 # ------------------------------------------------------------- store / round trip
 def test_store_of_load_restores_sweep():
     w = inputs.WORKLOADS["ragged_bf16"]
