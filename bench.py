@@ -253,7 +253,9 @@ def cpu_baseline(w, op, src, budget_s):
 
     import oracle
 
-    if w.coords != "sweep" or w.rank != 2:
+    if w.coords != "sweep":
+        return _cpu_baseline_corners(w, op, src, budget_s)
+    if w.rank != 2:
         return None
     row_bytes = w.strides[0] * w.box[1]                       # one tile row of the tensor
     rows_per_chunk = 4
@@ -302,6 +304,58 @@ def cpu_baseline(w, op, src, budget_s):
             "tiles_per_s": round(tiles / total_t, 1),
             "sample": f"{tiles} tiles ({chunk * rows_per_chunk} tile rows from the top) of {w.name}, "
                       f"{op}, {total_t:.1f} s of single-thread oracle time",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def _cpu_baseline_corners(w, op, src, budget_s):
+    """The oracle on explicit corners: growing prefixes of the corner list
+    (random corners) or repeats of the single box (origin), until ~budget_s
+    of oracle time, in the same algorithmic GB/s as the GPU line."""
+    import numpy as np
+
+    import oracle
+    from tiled_tensor_bulk_amd import inputs
+
+    if op == "bulk":
+        return None
+    host = src.cpu().numpy()
+    m = oracle.Map(es=w.es, dims=w.dims, strides=w.strides, box=w.box, swizzle=w.swizzle)
+    if w.coords == "origin":
+        all_corners = np.zeros((1, w.rank), np.int32)
+    else:
+        all_corners = inputs.random_corners(w.dims, w.box, w.n_random, seed=w.seed * 10)
+    bb = oracle.box_bytes(m)
+    dst = np.empty_like(host)
+    total_t, total_bytes, tiles, start = 0.0, 0, 0, 0
+    chunk = 256
+    while total_t < budget_s:
+        if w.coords == "origin":
+            c = all_corners
+        else:
+            if start >= len(all_corners):
+                break
+            c = np.ascontiguousarray(all_corners[start:start + chunk])
+            start += chunk
+        n = len(c)
+        inb = oracle.inb_elems(m, c, n) * w.es
+        if op == "store":
+            packed = oracle.load_tiles(m, host, c, n)
+        t0 = time.perf_counter()
+        if op == "load":
+            oracle.load_tiles(m, host, c, n)
+        elif op == "store":
+            oracle.store_tiles(m, dst, c, n, packed)
+        elif op == "roundtrip_add":
+            oracle.roundtrip_add_f32(m, host, m, dst, c, n, 1.0)
+        else:
+            oracle.roundtrip(m, host, m, dst, c, n)
+        total_t += time.perf_counter() - t0
+        total_bytes += 2 * inb if op in ("roundtrip", "roundtrip_add") else inb + n * bb
+        tiles += n
+    what = "repeats of the one box" if w.coords == "origin" else f"the first {tiles} of its {len(all_corners)} corners"
+    return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tiles_per_s": round(tiles / total_t, 1),
+            "sample": f"{tiles} tiles ({what}) of {w.name}, {op}, {total_t:.1f} s of single-thread oracle time",
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
