@@ -20,6 +20,7 @@ import pytest
 
 import oracle
 from oracle import Map
+from tests import npref
 from tiled_tensor_bulk_amd import inputs
 from tiled_tensor_bulk_amd import tmap as T
 
@@ -323,6 +324,61 @@ def test_poisoned_stages_still_match(chunk):
                          flags=T.FLAG_NONTEMPORAL | T.FLAG_DEBUG_POISON)
         check_ok()
         assert torch.equal(dst, src)
+
+
+@pytest.mark.parametrize("mode", [dict(), dict(flags=T.FLAG_WHOLE_BOX), dict(flags=T.FLAG_THREAD_COPY)],
+                         ids=["default", "shared_ring", "thread_copy"])
+def test_position_coded_elements_name_their_source(mode):
+    """Every in-bounds element of a padded rank-5 fp32 tensor holds its own
+    linear index + 1 and every padding word 0xFFFFFFFF, so a misplaced byte
+    names where it came from.  Loads at 3000 random corners must put exactly
+    index + 1 (or 0 outside the tensor) at each element's swizzled position,
+    computed here in closed form without the oracle; storing those images
+    into a fresh tensor must restore exactly the union of the boxes'
+    footprints and leave every other word, padding included, untouched."""
+    say(f"position-coded corners {mode}")
+    dims, box, swz = [37, 11, 5, 3, 2], [8, 4, 2, 2, 1], (1, 2, 3)
+    strides = [160, 160 * 11 + 32]
+    strides += [strides[-1] * 5 + 16]
+    strides += [strides[-1] * 3]
+    words = strides[-1] * dims[-1] // 4
+    grid = np.meshgrid(*[np.arange(n) for n in reversed(dims)], indexing="ij")   # outermost first
+    g = [grid[len(dims) - 1 - d].reshape(-1) for d in range(len(dims))]           # innermost first
+    word = sum(g[d] * (strides[d - 1] // 4 if d else 1) for d in range(len(dims)))
+    lin = sum(g[d] * int(np.prod(dims[:d])) for d in range(len(dims)))
+    host = np.full(words, 0xFFFFFFFF, np.uint32)
+    host[word] = (lin + 1).astype(np.uint32)
+    src = torch.from_numpy(host.view(np.uint8)).to(DEV)
+    m = enc("f32", src, dims, strides, box, swz)
+    corners = inputs.random_corners(dims, box, 3000, seed=61)
+    n = len(corners)
+    got = gpu_load(m, corners, n, **mode).cpu().numpy().view(np.uint32).reshape(n, -1)
+    # closed form: box element e at image position perm(e)
+    N = int(np.prod(box))
+    e = np.arange(N)
+    idx = []
+    for d in range(len(box)):
+        idx.append(e % box[d])
+        e = e // box[d]
+    gi = corners[:, None, :].astype(np.int64) + np.stack(idx, axis=1)[None, :, :]
+    inb = np.all((gi >= 0) & (gi < np.array(dims)), axis=2)
+    lin_box = sum(gi[:, :, d] * int(np.prod(dims[:d])) for d in range(len(dims)))
+    want = np.zeros((n, N), np.uint32)
+    want[:, npref.perm(N, swz)] = np.where(inb, lin_box + 1, 0).astype(np.uint32)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+    # store them back into a fresh tensor
+    dst = torch.full((words,), -1, dtype=torch.int32, device=DEV).view(torch.uint8)
+    md = enc("f32", dst, dims, strides, box, swz)
+    T.tmap_store_tiles(md, torch.from_numpy(corners).to(DEV), n, torch.from_numpy(want.view(np.uint8).reshape(-1)).to(DEV),
+                       **mode)
+    check_ok()
+    out = dst.cpu().numpy().view(np.uint32)
+    covered = np.zeros(words, bool)
+    wbox = sum(np.where(inb, gi[:, :, d], 0) * (strides[d - 1] // 4 if d else 1) for d in range(len(dims)))
+    covered[wbox[inb]] = True
+    expect = np.where(covered, host, np.uint32(0xFFFFFFFF))
+    assert np.array_equal(out, expect), np.argwhere(out != expect)[:5]
+    assert covered.sum() < len(word)              # some in-bounds elements stay unwritten
 
 
 # ----------------------------------------------------------------- edge cases
