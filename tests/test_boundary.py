@@ -305,3 +305,21 @@ def test_band_schedule_choice():
     assert T.tmap_band_boxes(near, flags=B, band_rows=16) == 8
     assert T.tmap_band_boxes(near, far, flags=B, band_rows=16) == 0
     assert T.tmap_band_boxes(T.tmap_t()) == 0
+
+
+@pytest.mark.skipif(__import__("shutil").which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("std", ["c99", "c11"])
+def test_plain_c_client_compiles_links_and_runs(std, tmp_path):
+    """include/tmap.h is plain C (strict, warnings as errors) and a C program
+    linked against the shared library encodes, queries and counts on the host
+    (tests/c_client/abi_client.c)."""
+    import subprocess
+    exe = str(tmp_path / "abi_client")
+    libdir = os.path.dirname(T.LIB_PATH)
+    r = subprocess.run(["gcc", f"-std={std}", "-Wall", "-Wextra", "-Wpedantic", "-Werror",
+                        "-I" + os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_client", "abi_client.c"),
+                        "-L" + libdir, "-l:libtmap.so", f"-Wl,-rpath,{libdir}", "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "abi client ok" in r.stdout, r.stdout + r.stderr
