@@ -81,7 +81,7 @@ typedef struct tmap_launch_opts {
                              take several (default: one workgroup per group; with
                              TMAP_FLAG_CONTIGUOUS, twice what fits in LDS per CU; in
                              producer-wave mode, 8 per CU)                               */
-    uint32_t flags;       /* TMAP_FLAG_* bits                                              */
+    uint32_t flags;       /* TMAP_FLAG_* bits; any other bit is TMAP_ERROR_INVALID_VALUE   */
     uint32_t spin_limit;  /* readiness-wait polls before TMAP_ERROR_TIMEOUT (default 2^22) */
     uint32_t group;       /* tiles (band units) dealt to a workgroup at a time, a power of
                              two <= 64 (default: enough boxes side by side to span 512
@@ -311,8 +311,8 @@ tmap_status tmap_inbounds_elems(const tmap_t *map, const int32_t *host_coords,
  * (of a store: the destination map), dst the round trip's destination map or
  * NULL for a load or store; coords is non-NULL for explicit corners (any non-NULL pointer: it is
  * not read); opts are the launch options the copy would get (NULL: the
- * defaults).  0 for a map never encoded, and for a band_rows the launch
- * would reject. */
+ * defaults).  0 for a map never encoded, and for a band_rows or flag bits
+ * the launch would reject. */
 uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *coords,
                          const tmap_launch_opts *opts);
 

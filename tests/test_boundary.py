@@ -247,6 +247,8 @@ def test_band_schedule_choice():
         for fl in (T.FLAG_WHOLE_BOX, T.FLAG_THREAD_COPY, T.FLAG_PRODUCER_WAVE):
             assert T.tmap_band_boxes(m, flags=fl | B) == 0
         assert T.tmap_band_boxes(m, flags=T.FLAG_NONTEMPORAL | T.FLAG_CONTIGUOUS) == want
+        # bits the header does not define: the launch rejects them
+        assert T.tmap_band_boxes(m, flags=B | 0x80) == 0
         assert T.tmap_band_boxes(m, explicit_coords=True, flags=B) == 0
         assert T.tmap_band_boxes(m, m) == want_rt
     # the size threshold: 256 MiB spanned by the outermost dimension

@@ -520,8 +520,9 @@ def test_zero_tiles_launch_nothing():
 
 
 def test_launch_options_out_of_range_are_rejected():
-    """Launch options outside their documented ranges give INVALID_VALUE
-    before anything is launched, and the destination stays untouched."""
+    """Launch options outside their documented ranges (flag bits the header
+    does not define among them) give INVALID_VALUE before anything is
+    launched, and the destination stays untouched."""
     src = dev_tensor(16384, fill_seed=1)
     m = enc("f32", src, [64, 64], [256], [16, 16])
     n = T.tmap_sweep_tiles(m)
@@ -531,7 +532,8 @@ def test_launch_options_out_of_range_are_rejected():
                 dict(flags=T.FLAG_BAND | T.FLAG_WHOLE_BOX),
                 dict(flags=T.FLAG_THREAD_COPY | T.FLAG_PRODUCER_WAVE),
                 dict(flags=T.FLAG_WAVE_PER_BOX | T.FLAG_THREAD_COPY),
-                dict(flags=T.FLAG_WAVE_PER_BOX | T.FLAG_PRODUCER_WAVE), dict(flags=T.FLAG_WAVE_PER_BOX, stages=3)):
+                dict(flags=T.FLAG_WAVE_PER_BOX | T.FLAG_PRODUCER_WAVE), dict(flags=T.FLAG_WAVE_PER_BOX, stages=3),
+                dict(flags=0x80), dict(flags=0x400), dict(flags=T.FLAG_NONTEMPORAL | 0x80000000)):
         with pytest.raises(T.TmapError) as e:
             T.tmap_load_tiles(m, None, n, out, **bad)
         assert e.value.status == T.INVALID_VALUE, bad

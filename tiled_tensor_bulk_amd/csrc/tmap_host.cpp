@@ -222,6 +222,13 @@ void band_setup(const MapImpl &m, tmap::KArgs &a, uint32_t g, uint32_t nb, uint3
     }
 }
 
+// Every flag bit the header defines; a caller's other bits are rejected
+// rather than ignored, so that a misspelt or future flag does not run as a
+// different copy.
+constexpr uint32_t kKnownFlags = TMAP_FLAG_CONTIGUOUS | TMAP_FLAG_NONTEMPORAL | TMAP_FLAG_THREAD_COPY |
+                                 TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WHOLE_BOX | TMAP_FLAG_BAND |
+                                 TMAP_FLAG_WAVE_PER_BOX | TMAP_FLAG_INJECT_BUDGET_MISMATCH | TMAP_FLAG_DEBUG_POISON;
+
 tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
                         const DeviceState &dev, bool band, bool corners, Plan &pl) {
     const uint32_t per_wave_pass = tmap::kWaves * tmap::kBlockBytes;  // bytes one slot per lane covers
@@ -367,6 +374,8 @@ void fill_common(tmap::KArgs &a, const MapImpl &swept, const int32_t *coords, in
 // and complete the kernel arguments for it, short of the status word.
 tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launch_opts *opts,
                     const DeviceState &dev, Plan &pl) {
+    if (opts && (opts->flags & ~kKnownFlags))
+        return fail(TMAP_ERROR_INVALID_VALUE, "unknown flag bits 0x%x", opts->flags & ~kKnownFlags);
     uint32_t g = 0, nb = 0, rows = 0;
     const char *why = nullptr;
     const bool band = band_fits(swept, a, mode == tmap::kRoundtrip, opts ? opts->flags : 0u,
@@ -550,6 +559,7 @@ uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *co
     MapImpl s, d;
     if (!decode(src, s)) return 0;
     if (dst && !decode(dst, d)) return 0;
+    if (opts && (opts->flags & ~kKnownFlags)) return 0;  // the launch would reject them
     tmap::KArgs a;
     std::memset(&a, 0, sizeof a);
     a.src = tmap::kernel_map(s);
