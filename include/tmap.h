@@ -87,7 +87,8 @@ typedef struct tmap_launch_opts {
                              two <= 64 (default: enough boxes side by side to span 512
                              bytes of a row, at least 2 and at most 8; band units: 4 for
                              a round trip, 1 for a load or store; explicit corners: 8,
-                             4 for a wave-per-box store)                                 */
+                             for a wave-per-box store 4, or 2 for boxes of 8 KiB and
+                             more)                                                       */
     uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
                              streams, each sweeping an equal contiguous stretch of the
                              tiles (workgroup i takes stretch i mod regions), so that the
@@ -143,13 +144,15 @@ typedef struct tmap_launch_opts {
  * record ("GPU TMA", "Warp specialization").  Same results.  Needs boxes of
  * at most 32 KiB; `stages` 1 is taken as 2. */
 #define TMAP_FLAG_PRODUCER_WAVE 0x8u
-/* Wave-per-box mode: each of a workgroup's four waves walks its own tiles
- * through its own ring of one-box stages (stages 1 or 2), issuing all of a
+/* Wave-per-box mode: each wave walks its own tiles through its own ring of
+ * one-box stages (stages 1 or 2), issuing all of a
  * box's direct-to-LDS loads under one arrive+expect of its bytes on its own
  * stage record, and draining the box itself once the record's phase flips.
  * The per-box address and bounds work is done once per box instead of once
  * per wave, and no workgroup barrier is needed.  Same results.  Needs boxes
- * of at most 16 KiB; grid_wgs then counts waves.  Excludes the thread-copy
+ * of at most 16 KiB; grid_wgs then counts waves, which run four to a
+ * workgroup for boxes under 8 KiB and one to a workgroup for larger boxes
+ * (as many one-box rings as fit in a CU's LDS).  Excludes the thread-copy
  * and producer-wave modes, TMAP_FLAG_WHOLE_BOX and the band schedule.  The
  * default for explicit corners of boxes up to 8 KiB (unless stages > 2). */
 #define TMAP_FLAG_WAVE_PER_BOX 0x40u

@@ -498,8 +498,15 @@ def test_plan_query_reports_the_schedules():
     assert (p["variant"], p["band_boxes"], p["band_rows"], p["stages"], p["group"], p["regions"]) == \
         ("ring", 16, 8, 1, 1, 2)
     p = plan("pad5d_f32", "store")
-    assert (p["variant"], p["stages"], p["slots"], p["group"]) == ("wave_per_box", 1, 8, 4)
-    assert p["walkers"] == -(-100000 // 4) and p["workgroups"] == -(-p["walkers"] // 4)
+    assert (p["variant"], p["stages"], p["slots"], p["group"]) == ("wave_per_box", 1, 8, 2)
+    # 8 KiB boxes: one wave to a workgroup, each with its own one-box ring
+    assert p["walkers"] == 100000 // 2 and p["workgroups"] == p["walkers"]
+    assert p["lds_bytes"] == 8192 + 32 + 4
+    # 2 KiB boxes: four waves to a workgroup
+    m = T.tmap_encode("f32", 2, 0x7F0000000000, [1000, 1000], [4000], [32, 16])
+    p = T.tmap_plan_launch("load", m, None, True, 1000)
+    assert (p["variant"], p["slots"], p["walkers"]) == ("wave_per_box", 2, 125)
+    assert p["workgroups"] == 32 and p["lds_bytes"] == 4 * 2048 + 4 * 32 + 4
     assert plan("pad5d_f32", "load")["group"] == 8 and plan("pad5d_f32", "roundtrip")["variant"] == "wave_per_box"
     assert plan("pad5d_f32", "load", flags=T.FLAG_WHOLE_BOX)["variant"] == "ring"
     assert plan("pad5d_f32", "load", stages=3)["variant"] == "ring"

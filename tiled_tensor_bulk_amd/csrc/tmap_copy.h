@@ -517,7 +517,7 @@ __device__ __forceinline__ uint32_t logical_chunk_of(const KArgs &a, uint32_t p,
 // one box.  W: waves that share a stage (and a tile sequence) -- the whole
 // 4-wave workgroup, or 1 in wave-per-box mode, where every wave of the
 // workgroup walks its own tiles through its own ring.
-template <int MODE, int S, int NSLOT, int R, bool BAND = false, int W = kWaves>
+template <int MODE, int S, int NSLOT, int R, bool BAND = false, int W = kWaves, int WG = kWaves>
 struct Copier {
     static_assert(W == kWaves || W == 1, "a stage is shared by the workgroup or owned by one wave");
     static_assert(!BAND || NSLOT == kBandSlots, "a band stage is 16 KiB");
@@ -699,13 +699,14 @@ struct Copier {
         parity = 0;
         edge = 0;
         // the tile sequences are dealt to a.grid walkers: the workgroups, or
-        // in wave-per-box mode the waves (workgroup b's wave w is walker
-        // 4b + w; walkers past a.grid in the last workgroup take no tiles).
+        // in wave-per-box mode the waves (wave w of workgroup b, of WG waves
+        // each, is walker WG*b + w; walkers past a.grid in the last
+        // workgroup take no tiles).
         // Walker index -> place in the deal: with R regions the first
         // R*(grid/R) walkers are dealt as R interleaved streams, walker i
         // taking the next place of stretch i mod R (a permutation of
         // 0..grid-1, so every place is still taken once)
-        int64_t g = W == 1 ? (int64_t)blockIdx.x * kWaves + hw : (int64_t)blockIdx.x;
+        int64_t g = W == 1 ? (int64_t)blockIdx.x * WG + hw : (int64_t)blockIdx.x;
         const bool walker = g < (int64_t)a.grid;
         if (a.regions > 1) {
             const uint32_t per = a.grid / a.regions;
@@ -1088,19 +1089,21 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const KArgs a) {
 // completes them once its loads have landed and drains the box after the
 // record's phase flips -- the same byte-count protocol with one arrival per
 // phase, and no workgroup barrier.  The per-box scalar work (corner,
-// address, bounds) is done once per box instead of once per wave, and four
-// boxes are in flight per workgroup and stage.
+// address, bounds) is done once per box instead of once per wave.  A
+// workgroup is wave_group(NSLOT) such waves: four for boxes under 8 KiB, one
+// for larger ones.
 template <int MODE, int S, int NSLOT, int R>
-__global__ __launch_bounds__(kThreads) void wave_kernel(const KArgs a) {
+__global__ __launch_bounds__(64 * wave_group(NSLOT)) void wave_kernel(const KArgs a) {
+    constexpr int WG = wave_group(NSLOT);
     constexpr uint32_t SB = NSLOT * kBlockBytes;
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[kWaves * S * SB];
-    __shared__ uint64_t bars[kWaves * 4];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[WG * S * SB];
+    __shared__ uint64_t bars[WG * 4];
     __shared__ uint32_t abort_flag;
 
     const uint32_t hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    Copier<MODE, S, NSLOT, R, false, 1> cp(a, bars + 4 * hw, &abort_flag);
+    Copier<MODE, S, NSLOT, R, false, 1, WG> cp(a, bars + 4 * hw, &abort_flag);
     if (threadIdx.x == 0) {
-        for (int i = 0; i < kWaves * 4; ++i) bars[i] = 0;
+        for (int i = 0; i < WG * 4; ++i) bars[i] = 0;
         abort_flag = 0;
     }
     cp.setup();
@@ -1537,9 +1540,13 @@ int launch_mode(int stages, int nslot, const KArgs &a, void *stream) {
         case 22: fn = copy_kernel<MODE, 2, kBandSlots, R, true>; break;
         case 23: fn = copy_kernel<MODE, 3, kBandSlots, R, true>; break;
         case 24: fn = copy_kernel<MODE, 4, kBandSlots, R, true>; break;
-        // a.grid counts waves here: four to a workgroup
-        case 31: fn = pick_wave<MODE, 1, R>(nslot); blocks = (a.grid + kWaves - 1) / kWaves; break;
-        case 32: fn = pick_wave<MODE, 2, R>(nslot); blocks = (a.grid + kWaves - 1) / kWaves; break;
+        // a.grid counts waves here: wave_group(nslot) to a workgroup
+        case 31:
+        case 32:
+            fn = stages == 31 ? pick_wave<MODE, 1, R>(nslot) : pick_wave<MODE, 2, R>(nslot);
+            threads = 64 * wave_group(nslot);
+            blocks = (a.grid + wave_group(nslot) - 1) / wave_group(nslot);
+            break;
         default: break;
     }
     if (!fn) return (int)hipErrorInvalidValue;
