@@ -285,6 +285,53 @@ def test_fuzz_random_maps(chunk):
         assert (mm := first_mismatch(dst2.cpu().numpy(), want2, 1 << 40)) is None, ("store", mm)
 
 
+@pytest.mark.parametrize("box_kib", [2, 8, 16])
+def test_wave_per_box_workgroup_shapes(box_kib):
+    """Wave-per-box mode runs four waves to a workgroup for boxes under 8 KiB
+    and one wave to a workgroup from 8 KiB: loads, round trips and stores of
+    scattered corners (in, across and outside the tensor) match the oracle
+    for both shapes, 1 and 2 stages, and grids of waves that do and do not
+    fill the last workgroup."""
+    rng = np.random.default_rng(9300 + box_kib)
+    es = 4
+    box = {2: [16, 8, 4], 8: [32, 8, 8], 16: [64, 8, 8]}[box_kib]
+    dims = [77, 29, 21]
+    strides = [80 * es, 80 * es * 31]
+    alloc = strides[1] * dims[2]
+    swz = (2, 2, 3)
+    om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+    src = dev_tensor(alloc, fill_seed=box_kib)
+    host = src.cpu().numpy()
+    m = enc("f32", src, dims, strides, box, swz)
+    assert T.tmap_box_bytes(m) == box_kib * 1024
+    coords = inputs.random_corners(dims, box, 301, seed=box_kib)
+    want_load = oracle.load_tiles(om, host, coords, len(coords))
+    c = torch.from_numpy(coords).to(DEV)
+    for stages in (1, 2):
+        p = T.tmap_plan_launch("load", m, None, True, len(coords), stages=stages, flags=T.FLAG_WAVE_PER_BOX)
+        assert p["variant"] == "wave_per_box"
+        assert p["workgroups"] == -(-p["walkers"] // (4 if box_kib < 8 else 1))
+        for grid in (0, 1, 3, 6):
+            say(f"wave workgroups: box {box_kib} KiB stages={stages} grid={grid}")
+            opts = dict(stages=stages, grid_wgs=grid, flags=T.FLAG_WAVE_PER_BOX)
+            got = gpu_load(m, coords, len(coords), **opts).cpu().numpy()
+            assert (mm := first_mismatch(got, want_load, box_kib * 1024)) is None, ("load", stages, grid, mm)
+            dst = dev_tensor(alloc, fill_seed=100 + grid)
+            want_dst = dst.cpu().numpy().copy()
+            T.tmap_roundtrip(m, enc("f32", dst, dims, strides, box, swz), c, len(coords), **opts)
+            check_ok()
+            oracle.roundtrip(om, host, om, want_dst, coords, len(coords))
+            assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip", mm)
+            # the loaded images stored back: overlapping boxes carry equal bytes
+            dst2 = dev_tensor(alloc, fill_seed=200 + grid)
+            want2 = dst2.cpu().numpy().copy()
+            T.tmap_store_tiles(enc("f32", dst2, dims, strides, box, swz), c, len(coords),
+                               torch.from_numpy(want_load).to(DEV), **opts)
+            check_ok()
+            oracle.store_tiles(om, want2, coords, len(coords), want_load)
+            assert (mm := first_mismatch(dst2.cpu().numpy(), want2, 1 << 40)) is None, ("store", mm)
+
+
 @pytest.mark.parametrize("chunk", range(2))
 def test_poisoned_stages_still_match(chunk):
     """With every stage filled with 0xDEADBEEF before its loads are issued, a
