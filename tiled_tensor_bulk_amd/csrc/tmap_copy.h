@@ -6,7 +6,8 @@
 // store from packed images, round trip).  Each workgroup (4 waves) walks its
 // share of the tiles (by default one group of neighbouring tiles) through a
 // ring of S LDS stages -- or, in wave-per-box mode, each wave walks its own
-// share through its own ring of one-box stages:
+// share through its own ring of one-box stages (four such waves to a
+// workgroup for boxes under 8 KiB, one for larger boxes):
 //
 //   fill    every lane issues one 16-byte direct-to-LDS buffer load per slot
 //           it owns (buffer_load_dwordx4 ... lds).  The tensor map sits in
