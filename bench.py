@@ -156,7 +156,16 @@ def main():
 
     plan = None
     if args.op == "bulk":
-        schedule = "whole boxes (rank-1 16 KiB tiles)"
+        # the library moves ranges of 256 MiB and more as 64 KiB rows of
+        # 16 x 128 8-byte boxes (the rest as rank-1 16 KiB tiles); the plan
+        # of that 2-D sweep names its schedule
+        schedule = "rank-1 16 KiB tiles"
+        rows = w.alloc_bytes // 65536
+        if w.alloc_bytes >= (256 << 20):
+            mv = T.tmap_encode("u64", 2, src.data_ptr(), [8192, rows], [65536], [16, 128])
+            plan = T.tmap_plan_launch("roundtrip", mv, mv, False, None, **opts)
+            schedule = "64 KiB rows as 16x128 u64 boxes" + (
+                f", band: {plan['band_boxes']} boxes x {plan['band_rows']} rows per stage" if plan["band_boxes"] else "")
     else:
         # the schedule the library chose for these options
         direction = {"load": "load", "store": "store"}.get(args.op, "roundtrip")

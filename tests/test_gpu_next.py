@@ -120,6 +120,23 @@ def test_bulk_copy_sizes(nbytes):
     assert got.tobytes() == want.tobytes()          # the 64 bytes past the range are untouched
 
 
+@pytest.mark.parametrize("nbytes", [(256 << 20) - 16, 256 << 20, (256 << 20) + 37 * 65536 + 4096 + 16])
+def test_bulk_copy_row_view_and_remainder(nbytes):
+    """From 256 MiB the bulk copy moves the whole 64 KiB rows as a 2-D sweep
+    on the band schedule (here with a short last row of boxes) and the rest
+    in 16 KiB tiles; every byte matches the oracle and the bytes past the
+    range stay untouched."""
+    say(f"bulk copy {nbytes} bytes (row view)")
+    src = dev_bytes(nbytes + 64, 13)
+    dst = dev_bytes(nbytes + 64, 14)
+    want = dst.cpu().numpy().copy()
+    T.tmap_bulk_copy(dst, src, nbytes)
+    check_ok()
+    oracle.bulk_copy(want, src.cpu().numpy(), nbytes)
+    got = dst.cpu().numpy()
+    assert np.array_equal(got, want), int(np.flatnonzero(got != want)[0])
+
+
 def test_bulk_copy_2gib_and_argument_rules():
     say("bulk copy 2 GiB")
     src = inputs.device_bytes(inputs.WORKLOADS["sweep2g_u8"], DEV)

@@ -446,6 +446,36 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     return ok();
 }
 
+// A map of 8-byte elements over a contiguous byte range for the bulk copy:
+// rank 1 (dims0 elements, boxes of box0) or rank 2 (rows of dims0 elements
+// at a pitch of dims0 * 8 bytes, boxes of box0 x box1).
+MapImpl bulk_map(uint64_t base, int rank, uint64_t dims0, uint64_t dims1, uint32_t box0, uint32_t box1) {
+    MapImpl m;
+    std::memset(&m, 0, sizeof m);
+    m.base = base;
+    for (int d = 0; d < tmap::kMaxRank; ++d) {
+        m.dims[d] = d == 0 ? dims0 : (d == 1 ? dims1 : 1);
+        m.box[d] = (uint16_t)(d == 0 ? box0 : (d == 1 ? box1 : 1));
+        m.strides[d] = d == 0 ? 8u : (d == 1 && rank > 1 ? dims0 * 8u : 0u);
+    }
+    m.elem_size = 8;
+    m.rank = (uint8_t)rank;
+    m.dtype = TMAP_U64;
+    m.box_bytes = box0 * box1 * 8u;
+    m.span = (uint32_t)(box0 * 8u + (uint64_t)(box1 - 1) * m.strides[1]);
+    m.magic = tmap::kMagic;
+    return m;
+}
+
+tmap_status bulk_launch(const MapImpl &m, const MapImpl &md, const tmap_launch_opts *opts, void *stream) {
+    tmap::KArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.src = tmap::kernel_map(m);
+    a.dst = tmap::kernel_map(md);
+    fill_common(a, m, nullptr, sweep_count(m));
+    return run(tmap::kRoundtrip, m, a, opts, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -685,35 +715,34 @@ tmap_status tmap_bulk_copy(void *dst, const void *src, uint64_t bytes, const tma
     const uint64_t lo_d = (uint64_t)(uintptr_t)dst, lo_s = (uint64_t)(uintptr_t)src;
     if (lo_d < lo_s + bytes && lo_s < lo_d + bytes)
         return fail(TMAP_ERROR_INVALID_VALUE, "src and dst ranges overlap");
-    // A rank-1 map of 8-byte elements with 16 KiB boxes over each side; ranges
-    // above 16 GiB go in several launches so that dims stay within 2^31.
-    const uint64_t kBox = 2048, kMaxElems = 1ull << 31;
     uint64_t done = 0;
+    // Ranges of 256 MiB and more: the whole 64 KiB rows as a 2-D tensor of
+    // 8-byte elements, 8192 to a row, in 16 x 128 boxes (16 KiB), which
+    // takes the band schedule like any sweep of that size (a unit is two
+    // rows of 8 KiB; measured on MI355X over 2 GiB: 0.76 of peak as 16 KiB
+    // tiles in address order, 0.81 as bands).  At most 2^31 rows a launch.
+    if (bytes >= kBandMinSpan) {
+        const uint64_t kRow = 65536, kMaxRows = 1ull << 31;
+        while (bytes - done >= kRow) {
+            const uint64_t rows = std::min<uint64_t>((bytes - done) / kRow, kMaxRows);
+            MapImpl m = bulk_map(lo_s + done, 2, kRow / 8u, rows, 16u, 128u);
+            MapImpl md = m;
+            md.base = lo_d + done;
+            tmap_status st = bulk_launch(m, md, opts, hip_stream);
+            if (st != TMAP_SUCCESS) return st;
+            done += rows * kRow;
+        }
+    }
+    // The rest: a rank-1 map of 8-byte elements with 16 KiB boxes over each
+    // side; ranges above 16 GiB go in several launches so that dims stay
+    // within 2^31.
+    const uint64_t kBox = 2048, kMaxElems = 1ull << 31;
     while (done < bytes) {
         const uint64_t elems = std::min<uint64_t>((bytes - done) / 8u, kMaxElems);
-        MapImpl m;
-        std::memset(&m, 0, sizeof m);
-        m.base = lo_s + done;
-        for (int d = 0; d < tmap::kMaxRank; ++d) {
-            m.dims[d] = d == 0 ? elems : 1;
-            m.strides[d] = d == 0 ? 8u : 0u;
-            m.box[d] = (uint16_t)(d == 0 ? kBox : 1);
-        }
-        m.elem_size = 8;
-        m.rank = 1;
-        m.dtype = TMAP_U64;
-        m.box_bytes = (uint32_t)(kBox * 8u);
-        m.span = m.box_bytes;
-        m.magic = tmap::kMagic;
+        MapImpl m = bulk_map(lo_s + done, 1, elems, 1, (uint32_t)kBox, 1);
         MapImpl md = m;
         md.base = lo_d + done;
-        tmap::KArgs a;
-        std::memset(&a, 0, sizeof a);
-        a.src = tmap::kernel_map(m);
-        a.dst = tmap::kernel_map(md);
-        const int64_t n = sweep_count(m);
-        fill_common(a, m, nullptr, n);
-        tmap_status st = run(tmap::kRoundtrip, m, a, opts, hip_stream);
+        tmap_status st = bulk_launch(m, md, opts, hip_stream);
         if (st != TMAP_SUCCESS) return st;
         done += elems * 8u;
     }
