@@ -62,12 +62,34 @@ def check_ok(stream=None):
     assert st == T.SUCCESS, T.tmap_status_string(st)
 
 
-def first_mismatch(a: np.ndarray, b: np.ndarray, bb: int):
+def first_mismatch(a: np.ndarray, b: np.ndarray, bb: int, where=None):
+    """None if equal, else the first differing byte (its tile and offset in
+    packed images of bb bytes; `where(i)` may add what the byte holds)."""
     idx = np.flatnonzero(a != b)
     if idx.size == 0:
         return None
     i = int(idx[0])
-    return f"byte {i} (tile {i // bb}, offset {i % bb}): got {a[i]:#x} want {b[i]:#x}; {idx.size} bytes differ"
+    extra = f", {where(i)}" if where else ""
+    return (f"byte {i} (tile {i // bb}, offset {i % bb}{extra}): got {a[i]:#x} want {b[i]:#x}; "
+            f"{idx.size} bytes differ")
+
+
+def packed_byte_source(es, box, swz, corners):
+    """For the byte at offset i of packed load images: the box element whose
+    bytes sit there (the swizzle is its own inverse), as a multi-index inside
+    the box and as global coordinates (innermost first)."""
+    n = int(np.prod(box))
+    p = npref.perm(n, swz)
+
+    def where(i):
+        t, e = i // (n * es), int(p[(i % (n * es)) // es])
+        idx = []
+        for d in box:
+            idx.append(e % d)
+            e //= d
+        g = [int(c) + k for c, k in zip(corners[t], idx)] if corners is not None else None
+        return f"box element {tuple(idx)}" + (f", global {tuple(g)}" if g is not None else "")
+    return where
 
 
 def gpu_load(m, coords_np, n, **opts):
@@ -264,7 +286,7 @@ def test_fuzz_random_maps(chunk):
         packed = gpu_load(m, coords, len(coords), **opts)
         want = oracle.load_tiles(om, host, coords, len(coords))
         got = packed.cpu().numpy()
-        assert (mm := first_mismatch(got, want, bb)) is None, mm
+        assert (mm := first_mismatch(got, want, bb, packed_byte_source(es, box, swz, coords))) is None, mm
         # round trip into a sentinel-filled tensor of another layout (same box, swizzle)
         dst = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
         want_dst = dst.cpu().numpy().copy()
