@@ -130,8 +130,17 @@ typedef struct tmap_launch_opts {
  * that a workgroup's tiles in flight are neighbours in memory.  With this
  * flag each workgroup instead takes one contiguous run of tiles. */
 #define TMAP_FLAG_CONTIGUOUS 0x1u
-/* Non-temporal hints on the streaming loads and stores. */
+/* Non-temporal hints on the tensor side of a copy: the loads of a load, the
+ * stores of a store, both of a round trip.  They pay when the tensor is
+ * larger than the 256 MB last-level cache; on smaller tensors, and on the
+ * scattered, partial-line accesses of explicit corners, they cost. */
 #define TMAP_FLAG_NONTEMPORAL 0x2u
+/* Keep the packed images cached.  By default the packed side of a load or
+ * store (the images it writes or reads, each touched once per call) carries
+ * non-temporal hints, so that streaming them does not evict the tensor from
+ * the caches; a caller that reads the images again right away can keep them
+ * with this flag. */
+#define TMAP_FLAG_CACHED_PACKED 0x80u
 /* Thread-copy mode: the lanes load each box into registers and write it into
  * a single LDS stage themselves, publishing it with a workgroup barrier,
  * instead of direct-to-LDS loads counted by the per-stage byte record

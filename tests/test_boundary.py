@@ -248,7 +248,8 @@ def test_band_schedule_choice():
             assert T.tmap_band_boxes(m, flags=fl | B) == 0
         assert T.tmap_band_boxes(m, flags=T.FLAG_NONTEMPORAL | T.FLAG_CONTIGUOUS) == want
         # bits the header does not define: the launch rejects them
-        assert T.tmap_band_boxes(m, flags=B | 0x80) == 0
+        assert T.tmap_band_boxes(m, flags=B | 0x400) == 0
+        assert T.tmap_band_boxes(m, flags=B | T.FLAG_CACHED_PACKED) == forced
         assert T.tmap_band_boxes(m, explicit_coords=True, flags=B) == 0
         assert T.tmap_band_boxes(m, m) == want_rt
     # the size threshold: 256 MiB spanned by the outermost dimension

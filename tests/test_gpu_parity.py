@@ -247,7 +247,8 @@ def _fuzz_case(rng, idx):
     opts = dict(stages=int(rng.integers(1, 5)), grid_wgs=int(rng.choice([0, 1, 2, 3, 7])),
                 flags=int(rng.choice([0, T.FLAG_CONTIGUOUS, T.FLAG_NONTEMPORAL, T.FLAG_THREAD_COPY,
                                       T.FLAG_THREAD_COPY | T.FLAG_CONTIGUOUS, T.FLAG_PRODUCER_WAVE,
-                                      T.FLAG_PRODUCER_WAVE | T.FLAG_CONTIGUOUS])),
+                                      T.FLAG_PRODUCER_WAVE | T.FLAG_CONTIGUOUS, T.FLAG_THREAD_COPY | T.FLAG_CACHED_PACKED,
+                                      T.FLAG_PRODUCER_WAVE | T.FLAG_CACHED_PACKED | T.FLAG_NONTEMPORAL])),
                 group=int(rng.choice([0, 1, 2, 4, 8, 64])),
                 regions=int(rng.choice([0, 1, 2, 3, 8, 64])))
     return es, dims, strides, box, swz, alloc, coords, opts
@@ -262,7 +263,8 @@ def _wave_case(rng, idx):
             break
     opts = case[7]
     opts["stages"] = int(rng.integers(1, 3))
-    opts["flags"] = T.FLAG_WAVE_PER_BOX | int(rng.choice([0, T.FLAG_CONTIGUOUS, T.FLAG_NONTEMPORAL]))
+    opts["flags"] = T.FLAG_WAVE_PER_BOX | int(rng.choice([0, T.FLAG_CONTIGUOUS, T.FLAG_NONTEMPORAL,
+                                                        T.FLAG_CACHED_PACKED]))
     opts["grid_wgs"] = int(rng.choice([0, 0, 1, 2, 3, 5, 9]))
     return case
 
@@ -609,7 +611,7 @@ def test_launch_options_out_of_range_are_rejected():
                 dict(flags=T.FLAG_THREAD_COPY | T.FLAG_PRODUCER_WAVE),
                 dict(flags=T.FLAG_WAVE_PER_BOX | T.FLAG_THREAD_COPY),
                 dict(flags=T.FLAG_WAVE_PER_BOX | T.FLAG_PRODUCER_WAVE), dict(flags=T.FLAG_WAVE_PER_BOX, stages=3),
-                dict(flags=0x80), dict(flags=0x400), dict(flags=T.FLAG_NONTEMPORAL | 0x80000000)):
+                dict(flags=0x400), dict(flags=0x800), dict(flags=T.FLAG_NONTEMPORAL | 0x80000000)):
         with pytest.raises(T.TmapError) as e:
             T.tmap_load_tiles(m, None, n, out, **bad)
         assert e.value.status == T.INVALID_VALUE, bad

@@ -318,6 +318,23 @@ __device__ __forceinline__ uint32_t inbox_offset(const uint32_t i[R], const KMap
     return (uint32_t)o;
 }
 
+// ---------------------------------------------------------------- cache hints
+// Packed images are streamed once per call (written by a load, read by a
+// store), so their side of a copy gets non-temporal hints unless
+// TMAP_FLAG_CACHED_PACKED keeps them cached; the tensor side gets them with
+// TMAP_FLAG_NONTEMPORAL (worth it only when the tensor exceeds the last-level
+// cache).  Measured on MI355X: 10^5 scattered 8 KiB boxes of a 103 MB tensor,
+// load 0.46 -> 0.62 and store 0.56 -> 0.62 of peak with the packed side
+// hinted, and both lower with the tensor side hinted too.
+template <int MODE>
+__device__ __forceinline__ bool nontemporal_loads(uint32_t flags) {
+    return MODE == kStore ? !(flags & TMAP_FLAG_CACHED_PACKED) : (flags & TMAP_FLAG_NONTEMPORAL) != 0;
+}
+template <int MODE>
+__device__ __forceinline__ bool nontemporal_stores(uint32_t flags) {
+    return MODE == kLoad ? !(flags & TMAP_FLAG_CACHED_PACKED) : (flags & TMAP_FLAG_NONTEMPORAL) != 0;
+}
+
 // ---------------------------------------------------------------- barrier record
 // One 8-byte LDS word per stage: bits 0..31 outstanding bytes, bits 32..62
 // arrivals, bit 63 phase.  The operation that leaves (all waves arrived, zero
@@ -526,7 +543,7 @@ struct Copier {
     uint32_t lane, wave, my_bytes, parity;
     uint32_t edge;  // bit X: the tile in stage X needs the element path when it lands
     int64_t cnt;
-    bool nt;
+    bool nt, nts;  // non-temporal hints on this copy's loads / stores
     uint64_t *bars;
     uint32_t *abort_flag;
     Cursor<R> fcur;  // next tile to fill
@@ -696,7 +713,8 @@ struct Copier {
         lane = threadIdx.x & 63u;
         const uint32_t hw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave in the workgroup
         wave = vwave >= 0 ? (uint32_t)vwave : (W == 1 ? 0u : hw);
-        nt = (a.flags & TMAP_FLAG_NONTEMPORAL) != 0;
+        nt = nontemporal_loads<MODE>(a.flags);
+        nts = nontemporal_stores<MODE>(a.flags);
         parity = 0;
         edge = 0;
         // the tile sequences are dealt to a.grid walkers: the workgroups, or
@@ -859,7 +877,7 @@ struct Copier {
 
     template <typename Rs>
     __device__ __forceinline__ void store16(const i32x4 &v, Rs r, uint32_t off) const {
-        if (nt)
+        if (nts)
             __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2);
         else
             __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
@@ -1281,7 +1299,7 @@ struct WsProducer {
         lane = threadIdx.x & 63u;
         eparity = 0;
         edge = 0;
-        nt = (a.flags & TMAP_FLAG_NONTEMPORAL) != 0;
+        nt = nontemporal_loads<MODE>(a.flags);
         cursor_init<R>(a, t0, fcur);
 #pragma unroll
         for (int j = 0; j < NP; ++j) {

@@ -227,7 +227,8 @@ void band_setup(const MapImpl &m, tmap::KArgs &a, uint32_t g, uint32_t nb, uint3
 // different copy.
 constexpr uint32_t kKnownFlags = TMAP_FLAG_CONTIGUOUS | TMAP_FLAG_NONTEMPORAL | TMAP_FLAG_THREAD_COPY |
                                  TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WHOLE_BOX | TMAP_FLAG_BAND |
-                                 TMAP_FLAG_WAVE_PER_BOX | TMAP_FLAG_INJECT_BUDGET_MISMATCH | TMAP_FLAG_DEBUG_POISON;
+                                 TMAP_FLAG_WAVE_PER_BOX | TMAP_FLAG_CACHED_PACKED | TMAP_FLAG_INJECT_BUDGET_MISMATCH |
+                                 TMAP_FLAG_DEBUG_POISON;
 
 tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
                         const DeviceState &dev, bool band, bool corners, Plan &pl) {

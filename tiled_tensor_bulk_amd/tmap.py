@@ -21,6 +21,7 @@ FLAG_NONTEMPORAL = 0x2
 FLAG_THREAD_COPY = 0x4
 FLAG_PRODUCER_WAVE = 0x8
 FLAG_WAVE_PER_BOX = 0x40
+FLAG_CACHED_PACKED = 0x80
 FLAG_WHOLE_BOX = 0x10
 FLAG_BAND = 0x20
 FLAG_INJECT_BUDGET_MISMATCH = 0x100
