@@ -87,8 +87,8 @@ typedef struct tmap_launch_opts {
                              two <= 64 (default: enough boxes side by side to span 512
                              bytes of a row, at least 2 and at most 8; band units: 4 for
                              a round trip, 1 for a load or store; explicit corners: 8,
-                             for a wave-per-box store 4, or 2 for boxes of 8 KiB and
-                             more)                                                       */
+                             for a wave-per-box store 4; wave per box with boxes of
+                             8 KiB and more: 2 for a store, 4 for a load)                */
     uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
                              streams, each sweeping an equal contiguous stretch of the
                              tiles (workgroup i takes stretch i mod regions), so that the

@@ -294,11 +294,17 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     if (group && (group > 64 || (group & (group - 1))))
         return fail(TMAP_ERROR_INVALID_VALUE, "group must be a power of two <= 64 (got %u)", group);
     if (!group && band) group = mode == tmap::kRoundtrip ? 4u : 1u;
-    // explicit corners: 8 tiles to a walker; a wave-per-box store takes 4,
-    // or 2 where each wave is a workgroup of its own (measured best on
-    // MI355X over 10^5 scattered 8 KiB boxes: store 0.539 -> 0.557 of peak)
-    if (!group && corners)
-        group = (wave_box && mode == tmap::kStore) ? (tmap::wave_group(nslot) == 1 ? 2u : 4u) : 8u;
+    // explicit corners: 8 tiles to a walker; a wave-per-box store takes 4.
+    // Where each wave is a workgroup of its own, a store takes 2 and a load
+    // 4 (measured best on MI355X over 10^5 scattered 8 KiB boxes: store
+    // 0.539 -> 0.557 of peak, load 0.625 -> 0.669 with the packed side's
+    // non-temporal hints)
+    if (!group && corners) {
+        if (wave_box && tmap::wave_group(nslot) == 1)
+            group = mode == tmap::kStore ? 2u : (mode == tmap::kLoad ? 4u : 8u);
+        else
+            group = (wave_box && mode == tmap::kStore) ? 4u : 8u;
+    }
     // a workgroup that takes one band unit has nothing to overlap in its ring
     if (band && group == 1 && !(opts && opts->stages)) stages = 1;
     if (!group) {
