@@ -132,8 +132,10 @@ typedef struct tmap_launch_opts {
 #define TMAP_FLAG_CONTIGUOUS 0x1u
 /* Non-temporal hints on the tensor side of a copy: the loads of a load, the
  * stores of a store, both of a round trip.  They pay when the tensor is
- * larger than the 256 MB last-level cache; on smaller tensors, and on the
- * scattered, partial-line accesses of explicit corners, they cost. */
+ * larger than the 256 MB last-level cache, and sweeps (coords == NULL) of
+ * tensors spanning 256 MiB or more (dims[rank-1] * strides[rank-1]) get
+ * them without the flag; on smaller tensors, and on the scattered,
+ * partial-line accesses of explicit corners, they cost. */
 #define TMAP_FLAG_NONTEMPORAL 0x2u
 /* Keep the packed images cached.  By default the packed side of a load or
  * store (the images it writes or reads, each touched once per call) carries

@@ -398,6 +398,11 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     a.grid = pl.grid;
     a.regions = pl.regions;
     a.flags = opts ? opts->flags : 0u;
+    // A sweep of a tensor larger than the last-level cache streams it once:
+    // non-temporal hints on the tensor side too (measured on MI355X over the
+    // 2 GiB u8 round trip: 0.744 of peak without them, 0.815 with them).
+    if (!a.coords && swept.dims[swept.rank - 1] * swept.strides[swept.rank - 1] >= kBandMinSpan)
+        a.flags |= TMAP_FLAG_NONTEMPORAL;
     // each workgroup advances through the tiles by +1 inside a group and by
     // big_step between groups; kernels add the steps' digits with carries
     // instead of dividing per tile
