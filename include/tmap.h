@@ -29,6 +29,9 @@
  *     nothing.  n_tiles == 0 is a successful no-op.
  *   - No call allocates device memory per call.  One 4-byte status word per
  *     device is allocated on first use and kept until process exit.
+ *   - The copy calls can be captured into a HIP graph and replayed: once the
+ *     device's status word exists (after any earlier launch on it), a launch
+ *     only enqueues kernels, with no allocation, copy or memset.
  */
 #ifndef TMAP_H
 #define TMAP_H
