@@ -178,7 +178,7 @@ def test_ragged_bf16_full_size_sampled(opts):
                          ids=["benchmark_launch", "shared_ring_4_stages", "shared_ring_2_stages"])
 def test_pad5d_f32_random_corners_full(opts):
     w = inputs.WORKLOADS["pad5d_f32"]
-    say(f"pad5d_f32: load 1e5 random corners {opts}, full oracle; then store")
+    say(f"pad5d_f32: load 1e5 random corners {opts}, full oracle; then store and round trip")
     src = inputs.device_bytes(w, DEV)
     host = src.cpu().numpy()
     coords = inputs.random_corners(w.dims, w.box, w.n_random, seed=40)
@@ -196,6 +196,13 @@ def test_pad5d_f32_random_corners_full(opts):
     oracle.store_tiles(om, want_dst, coords, len(coords), want)
     got_dst = dst.cpu().numpy()
     assert (mm := first_mismatch(got_dst, want_dst, 1 << 30)) is None, mm
+    # the round trip of the same corners into a third tensor
+    dst3 = dev_tensor(w.alloc_bytes, fill_seed=42)
+    want3 = dst3.cpu().numpy().copy()
+    T.tmap_roundtrip(m, enc("f32", dst3, w.dims, w.strides, w.box), c, len(coords), **opts)
+    check_ok()
+    oracle.roundtrip(om, host, om, want3, coords, len(coords))
+    assert (mm := first_mismatch(dst3.cpu().numpy(), want3, 1 << 30)) is None, ("roundtrip", mm)
 
 
 @pytest.mark.parametrize("opts", [dict(flags=T.FLAG_NONTEMPORAL), dict(stages=4, flags=T.FLAG_NONTEMPORAL),
