@@ -1,5 +1,5 @@
-"""Copies captured in a HIP graph and replayed: every replay matches the
-oracle on the inputs of that replay.
+"""Copies captured in a HIP graph and replayed, and copies running at the same
+time on several streams: every result matches the oracle.
 
 A caller with a launch-bound loop of copies can capture it once and replay
 it.  The library's launches are plain kernel launches on the caller's
@@ -106,3 +106,55 @@ def test_graph_replays_match_the_oracle():
         assert np.array_equal(b.cpu().numpy(), want_b), ("store", rep)
         # the replay changed what it had to: b now holds a's bytes
         assert np.array_equal(want_b.reshape(50, 1216)[:, :1200], host_a.reshape(50, 1216)[:, :1200])
+
+
+def test_concurrent_streams_match_the_oracle():
+    """Three streams (default priority) each repeat a different copy -- a
+    band-schedule load, a wave-per-box round trip and a shared-ring store --
+    with no ordering between them; every output matches the oracle and no
+    readiness wait expires.  Each launch has its own LDS records, so copies on
+    different streams share nothing but the device's status word."""
+    a_dims, a_strides, a_box, a_swz = [1200, 50], [1216], [128, 32], (3, 4, 3)
+    a = torch.empty(1216 * 50, dtype=torch.uint8, device=DEV)
+    fill_random(a, 31)
+    ma = T.tmap_encode("u8", 2, a.data_ptr(), a_dims, a_strides, a_box, None, a_swz)
+    n = T.tmap_sweep_tiles(ma)
+    packed = torch.empty(n * T.tmap_box_bytes(ma), dtype=torch.uint8, device=DEV)
+    c_dims, c_strides, c_box = [300, 150], [1280], [32, 64]
+    c = torch.empty(1280 * 150, dtype=torch.uint8, device=DEV)
+    fill_random(c, 32)
+    d = torch.empty_like(c)
+    fill_random(d, 33)
+    mc = T.tmap_encode("f32", 2, c.data_ptr(), c_dims, c_strides, c_box)
+    md = T.tmap_encode("f32", 2, d.data_ptr(), c_dims, c_strides, c_box)
+    corners = inputs.random_corners(c_dims, c_box, 300, seed=72)
+    corners_dev = torch.from_numpy(corners).to(DEV)
+    # images to store with the shared ring: a's own images, loaded once up front
+    e = torch.empty_like(a)
+    fill_random(e, 34)
+    me = T.tmap_encode("u8", 2, e.data_ptr(), a_dims, a_strides, a_box, None, a_swz)
+    imgs = torch.empty_like(packed)
+    T.tmap_load_tiles(ma, None, n, imgs)
+    assert T.tmap_sync_status() == T.SUCCESS
+    want_e = e.cpu().numpy().copy()
+    want_d = d.cpu().numpy().copy()
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    say("concurrent streams: 3 x 20 launches")
+    for _ in range(20):
+        T.tmap_load_tiles(ma, None, n, packed, stream=streams[0], flags=T.FLAG_BAND)
+        T.tmap_roundtrip(mc, md, corners_dev, len(corners), stream=streams[1])
+        T.tmap_store_tiles(me, None, n, imgs, stream=streams[2], flags=T.FLAG_WHOLE_BOX)
+    torch.cuda.synchronize()
+    for st in streams:
+        assert T.tmap_sync_status(st) == T.SUCCESS
+    oa = Map(es=1, dims=a_dims, strides=a_strides, box=a_box, swizzle=a_swz)
+    host_a = a.cpu().numpy()
+    want_packed = oracle.load_tiles(oa, host_a, None, n)
+    assert np.array_equal(packed.cpu().numpy(), want_packed)
+    assert np.array_equal(imgs.cpu().numpy(), want_packed)
+    oc = Map(es=4, dims=c_dims, strides=c_strides, box=c_box)
+    oracle.roundtrip(oc, c.cpu().numpy(), oc, want_d, corners, len(corners))
+    assert np.array_equal(d.cpu().numpy(), want_d)
+    oracle.store_tiles(oa, want_e, None, n, want_packed)
+    assert np.array_equal(e.cpu().numpy(), want_e)
