@@ -159,9 +159,9 @@ typedef struct tmap_launch_opts {
  * at most 32 KiB; `stages` 1 is taken as 2. */
 #define TMAP_FLAG_PRODUCER_WAVE 0x8u
 /* Wave-per-box mode: each wave walks its own tiles through its own ring of
- * one-box stages (stages 1 or 2), issuing all of a
- * box's direct-to-LDS loads under one arrive+expect of its bytes on its own
- * stage record, and draining the box itself once the record's phase flips.
+ * one-box stages (stages 1 or 2), issuing all of a box's direct-to-LDS loads
+ * under one arrive+expect of its bytes on its own stage record, and draining
+ * the box itself once the record's phase flips.
  * The per-box address and bounds work is done once per box instead of once
  * per wave, and no workgroup barrier is needed.  Same results.  Needs boxes
  * of at most 16 KiB; grid_wgs then counts waves, which run four to a
