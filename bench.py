@@ -180,7 +180,7 @@ def main():
             schedule = "whole boxes" + ("" if plan["variant"] == "ring" else f" ({plan['variant']})")
 
     kernel_name = {"ring": "copy_kernel", "wave_per_box": "wave_kernel", "thread_copy": "thread_kernel",
-                   "producer_wave": "ws_kernel"}[plan["variant"]] if plan else "copy_kernel"
+                   "producer_wave": "ws_kernel", "band": "band_kernel"}[plan["variant"]] if plan else "copy_kernel"
     for _ in range(args.warmup):
         launch()
     st = T.tmap_sync_status(stream)

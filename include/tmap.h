@@ -351,7 +351,10 @@ typedef enum tmap_variant {
     TMAP_VARIANT_RING = 0,          /* workgroup-shared ring of stages (whole boxes or band units) */
     TMAP_VARIANT_THREAD_COPY = 1,   /* TMAP_FLAG_THREAD_COPY                                       */
     TMAP_VARIANT_PRODUCER_WAVE = 2, /* TMAP_FLAG_PRODUCER_WAVE                                     */
-    TMAP_VARIANT_WAVE_PER_BOX = 3   /* TMAP_FLAG_WAVE_PER_BOX, or its default                      */
+    TMAP_VARIANT_WAVE_PER_BOX = 3,  /* TMAP_FLAG_WAVE_PER_BOX, or its default                      */
+    TMAP_VARIANT_BAND = 4           /* band schedule of a sweep whose maps have rank <= 2 and whose
+                                       dimension-0 rows are whole 16-byte chunks: the band ring
+                                       with per-slot offsets fixed per kernel                      */
 } tmap_variant;
 typedef struct tmap_plan {
     uint32_t variant;     /* tmap_variant                                                  */
@@ -391,10 +394,15 @@ const char *tmap_status_string(tmap_status status);
  * (the rule that failed, the argument that was wrong); "" after success. */
 const char *tmap_last_error_detail(void);
 
-/* Wait for hip_stream, then read and clear the device status word that
- * kernels set when a bounded readiness wait expires.  Returns TMAP_SUCCESS
- * or TMAP_ERROR_TIMEOUT (or TMAP_ERROR_LAUNCH if the stream reports an
- * error). */
+/* Wait for hip_stream, then read and clear the current device's status
+ * word that kernels set when a bounded readiness wait expires.  Returns
+ * TMAP_SUCCESS or TMAP_ERROR_TIMEOUT (or TMAP_ERROR_LAUNCH if the stream
+ * reports an error).  The word is per device, not per stream: a timeout
+ * of a copy on one stream is reported to whichever stream of that device is
+ * checked first, and a check clears it for all of them.
+ * ("TMA -- the async bulk copy engine", "Load completion -- the mbarrier and
+ * the byte budget": a wait on a byte budget that never completes must end;
+ * here it ends the kernel and is reported here.) */
 tmap_status tmap_sync_status(void *hip_stream);
 
 #ifdef __cplusplus

@@ -295,3 +295,110 @@ def test_band_rows_that_do_not_fit_are_rejected():
     assert T.tmap_band_boxes(m64, None, False, T.FLAG_BAND, 4) == 64
     with pytest.raises(T.TmapError):
         T.tmap_load_tiles(m64, None, n64, packed, flags=T.FLAG_BAND, band_rows=1)
+
+
+def _lean_case(rng):
+    """A rank-2 band sweep whose dimension-0 rows are whole 16-byte chunks
+    (the case the lean band kernels take): ragged in boxes both ways."""
+    while True:
+        es = int(rng.choice([1, 2, 4, 8]))
+        rc = int(rng.choice([4, 8, 16, 32]))
+        box0 = rc * 16 // es
+        if box0 <= 256:
+            break
+    k = 16 // es
+    box1 = int(rng.choice([16, 32, 64, 128]))
+    while box0 * es * box1 > 65536:
+        box1 //= 2
+    want_rows = int(rng.choice([0, 0, 1, 2, 4, 8, 16, 32]))
+    while want_rows > box1 or want_rows * rc > 1024:
+        want_rows //= 2
+    rows = want_rows or 2
+    g = 1024 // (rows * rc)
+    tiles0 = int(rng.integers(g, 3 * g + 3))
+    dims0 = tiles0 * box0 - k * int(rng.integers(0, box0 // k))
+    dims1 = int(rng.integers(1, 3 * box1 + 2))
+    return es, [dims0, dims1], [box0, box1], _swizzle(rng, es, box0, box1, rows), want_rows
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_band_kernel_random_sweeps(chunk):
+    """Rank-2 band sweeps with whole-chunk rows run the band kernel (the plan
+    says so); load, store, round trip into a destination of another size and
+    pitch (also whole-chunk rows), and for fp32 the +1.0f round trip, each
+    against the oracle, over ring depths 1..4, groups, grids, regions, cache
+    hints and the poison debug flag."""
+    rng = np.random.default_rng(7300 + chunk)
+    for i in range(24):
+        es, dims, box, swz, rows = _lean_case(rng)
+        strides, alloc = _strides(rng, dims, es)
+        opts = _opts(rng, rows)
+        opts["flags"] |= int(rng.choice([0, 0, T.FLAG_DEBUG_POISON, T.FLAG_CACHED_PACKED]))
+        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+        src = dev_bytes(alloc, int(rng.integers(1 << 30)))
+        m = T.tmap_encode(DT[es], 2, src.data_ptr(), dims, strides, box, None, swz)
+        n = T.tmap_sweep_tiles(m)
+        bb = T.tmap_box_bytes(m)
+        say(f"band kernel {chunk}/{i}: es={es} dims={dims} strides={strides} box={box} swz={swz} n={n} {opts}")
+        for direction in ("load", "store"):
+            p = T.tmap_plan_launch(direction, m, None, False, n, **opts)
+            assert p["variant"] == "band", (direction, p)
+        host = src.cpu().numpy()
+        packed = torch.empty(n * bb, dtype=torch.uint8, device=DEV)
+        T.tmap_load_tiles(m, None, n, packed, **opts)
+        check_ok()
+        want = oracle.load_tiles(om, host, None, n)
+        assert (mm := first_mismatch(packed.cpu().numpy(), want)) is None, ("load", mm)
+        imgs = dev_bytes(n * bb, int(rng.integers(1 << 30)))
+        dst = dev_bytes(alloc, int(rng.integers(1 << 30)))
+        want_dst = dst.cpu().numpy().copy()
+        T.tmap_store_tiles(T.tmap_encode(DT[es], 2, dst.data_ptr(), dims, strides, box, None, swz),
+                           None, n, imgs, **opts)
+        check_ok()
+        oracle.store_tiles(om, want_dst, None, n, imgs.cpu().numpy())
+        assert (mm := first_mismatch(dst.cpu().numpy(), want_dst)) is None, ("store", mm)
+        k = 16 // es
+        ddims = [max(k, (dims[0] + k * int(rng.integers(-box[0] // (2 * k), 2 * box[0] // k + 1))) // k * k),
+                 max(1, dims[1] + int(rng.integers(-box[1] // 2, 2 * box[1] + 1)))]
+        dstrides, dalloc = _strides(rng, ddims, es)
+        dst2 = dev_bytes(dalloc, int(rng.integers(1 << 30)))
+        want2 = dst2.cpu().numpy().copy()
+        md = T.tmap_encode(DT[es], 2, dst2.data_ptr(), ddims, dstrides, box, None, swz)
+        assert T.tmap_plan_launch("roundtrip", m, md, False, n, **opts)["variant"] == "band"
+        T.tmap_roundtrip(m, md, None, n, **opts)
+        check_ok()
+        omd = Map(es=es, dims=ddims, strides=dstrides, box=box, swizzle=swz)
+        oracle.roundtrip(om, host, omd, want2, None, n)
+        assert (mm := first_mismatch(dst2.cpu().numpy(), want2)) is None, ("roundtrip", ddims, mm)
+        if es == 4:
+            dst3 = dev_bytes(dalloc, int(rng.integers(1 << 30)))
+            want3 = dst3.cpu().numpy().copy()
+            md3 = T.tmap_encode("f32", 2, dst3.data_ptr(), ddims, dstrides, box, None, swz)
+            T.tmap_roundtrip_add_f32(m, md3, None, n, 1.0, **opts)
+            check_ok()
+            oracle.roundtrip_add_f32(om, host, omd, want3, None, n, 1.0)
+            got3 = dst3.cpu().numpy()
+            nan = np.isnan(want3.view(np.float32))
+            w32, g32 = want3.view(np.uint32), got3.view(np.uint32)
+            assert np.array_equal(g32[~nan], w32[~nan]), "roundtrip +1.0f"
+            assert np.all(np.isnan(got3.view(np.float32)[nan]))
+
+
+def test_band_kernel_budget_mismatch_times_out():
+    """The band kernel's bounded wait: a byte budget 16 bytes above what is
+    delivered never completes a stage; every wave gives up after spin_limit
+    polls and the status reports a timeout; the next launch is correct."""
+    say("budget mismatch -> TIMEOUT (band kernel)")
+    src = dev_bytes(2048 * 64, 3)
+    m = T.tmap_encode("u8", 2, src.data_ptr(), [2048, 64], [2048], [128, 16])
+    n = T.tmap_sweep_tiles(m)
+    out = torch.empty(n * 2048, dtype=torch.uint8, device=DEV)
+    for stages in (1, 3):
+        assert T.tmap_plan_launch("load", m, None, False, n, flags=T.FLAG_BAND, stages=stages)["variant"] == "band"
+        T.tmap_load_tiles(m, None, n, out, stages=stages, group=4,
+                          flags=T.FLAG_INJECT_BUDGET_MISMATCH | T.FLAG_BAND, spin_limit=2000)
+        assert T.tmap_sync_status() == T.TIMEOUT
+    T.tmap_load_tiles(m, None, n, out, flags=T.FLAG_BAND)
+    check_ok()
+    om = Map(es=1, dims=[2048, 64], strides=[2048], box=[128, 16])
+    assert out.cpu().numpy().tobytes() == oracle.load_tiles(om, src.cpu().numpy(), None, n).tobytes()

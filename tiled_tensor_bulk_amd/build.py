@@ -18,10 +18,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtmap.so")
-CEILING = os.path.join(PKG, "stream_ceiling")   # achievable-bandwidth probe (context for the roofline)
 ROOT = os.path.dirname(PKG)
 
-SOURCES = ["tmap_host.cpp"] + [f"tmap_{m}_r{r}.hip" for m in ("load", "store", "roundtrip") for r in (2, 5)]
+SOURCES = (["tmap_host.cpp"] + [f"tmap_{m}_r{r}.hip" for m in ("load", "store", "roundtrip") for r in (2, 5)]
+           + [f"tmap_band_{m}.hip" for m in ("load", "store", "roundtrip")])
 ARCH = "gfx950"
 
 
@@ -81,11 +81,6 @@ def build(jobs: int = 7, verbose: bool = False, incremental: bool = False) -> st
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
-    src = os.path.join(CSRC, "stream_ceiling.hip")
-    if not (incremental and os.path.exists(CEILING) and os.path.getmtime(CEILING) > os.path.getmtime(src)):
-        subprocess.check_call([cc, *common_flags(), src, "-o", CEILING + ".tmp"],
-                              stderr=subprocess.DEVNULL if not verbose else None)
-        os.replace(CEILING + ".tmp", CEILING)
     if verbose:
         print(f"built {LIB} in {time.time() - t0:.1f}s", flush=True)
     return LIB

@@ -327,11 +327,11 @@ __device__ __forceinline__ uint32_t inbox_offset(const uint32_t i[R], const KMap
 // load 0.46 -> 0.62 and store 0.56 -> 0.62 of peak with the packed side
 // hinted, and both lower with the tensor side hinted too.
 template <int MODE>
-__device__ __forceinline__ bool nontemporal_loads(uint32_t flags) {
+__host__ __device__ __forceinline__ bool nontemporal_loads(uint32_t flags) {
     return MODE == kStore ? !(flags & TMAP_FLAG_CACHED_PACKED) : (flags & TMAP_FLAG_NONTEMPORAL) != 0;
 }
 template <int MODE>
-__device__ __forceinline__ bool nontemporal_stores(uint32_t flags) {
+__host__ __device__ __forceinline__ bool nontemporal_stores(uint32_t flags) {
     return MODE == kLoad ? !(flags & TMAP_FLAG_CACHED_PACKED) : (flags & TMAP_FLAG_NONTEMPORAL) != 0;
 }
 

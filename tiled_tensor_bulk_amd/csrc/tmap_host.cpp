@@ -118,6 +118,7 @@ struct Plan {
     uint32_t regions;
     uint32_t lds;                 // bytes per workgroup
     uint32_t band_g, band_rows;   // band schedule (0: whole boxes)
+    bool lean;                    // the band schedule runs the lean rank-2 band kernels
 };
 
 uint32_t log2u(uint32_t v) {
@@ -229,6 +230,18 @@ constexpr uint32_t kKnownFlags = TMAP_FLAG_CONTIGUOUS | TMAP_FLAG_NONTEMPORAL | 
                                  TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WHOLE_BOX | TMAP_FLAG_BAND |
                                  TMAP_FLAG_WAVE_PER_BOX | TMAP_FLAG_CACHED_PACKED | TMAP_FLAG_INJECT_BUDGET_MISMATCH |
                                  TMAP_FLAG_DEBUG_POISON;
+
+// Whether a band-schedule launch runs the lean band kernels (tmap_band.h):
+// both maps have rank <= 2 and every tensor side's dimension-0 row is a whole
+// number of 16-byte chunks, so that the tensor's edge never cuts a chunk
+// (the generic ring's element path is then never needed).
+bool band_lean(int mode, const tmap::KArgs &a, uint32_t band_g) {
+    if (!band_g || a.src.rank > 2 || a.dst.rank > 2) return false;
+    auto whole = [](const tmap::KMap &k) { return ((uint64_t)k.dims[0] * k.elem_size) % 16u == 0; };
+    if (mode != tmap::kStore && !whole(a.src)) return false;
+    if (mode != tmap::kLoad && !whole(a.dst)) return false;
+    return true;
+}
 
 tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
                         const DeviceState &dev, bool band, bool corners, Plan &pl) {
@@ -395,6 +408,7 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     if (st != TMAP_SUCCESS) return st;
     pl.band_g = band ? g : 0u;
     pl.band_rows = band ? rows : 0u;
+    pl.lean = band_lean(mode, a, pl.band_g);
     a.grid = pl.grid;
     a.regions = pl.regions;
     a.flags = opts ? opts->flags : 0u;
@@ -436,6 +450,17 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     // maps of rank <= 2 run the variants that only walk two dimensions
     const bool r2 = a.src.rank <= 2 && a.dst.rank <= 2;
     int rc = (int)hipErrorInvalidValue;
+    if (pl.lean) {
+        const int st = pl.stages - 20;  // band launch codes are 20 + stages
+        rc = mode == tmap::kLoad    ? tmap::launch_band_load(st, a, stream)
+             : mode == tmap::kStore ? tmap::launch_band_store(st, a, stream)
+                                    : tmap::launch_band_roundtrip(st, a, stream);
+        if (rc != 0) {
+            (void)hipGetLastError();
+            return fail(TMAP_ERROR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)rc));
+        }
+        return ok();
+    }
     switch (mode) {
         case tmap::kLoad:
             rc = r2 ? tmap::launch_load_r2(pl.stages, pl.nslot, a, stream)
@@ -825,6 +850,7 @@ tmap_status tmap_plan_launch(tmap_direction direction, const tmap_t *swept, cons
     out->variant = code == 0 ? TMAP_VARIANT_THREAD_COPY
                    : code > 30 ? TMAP_VARIANT_WAVE_PER_BOX
                    : (code > 10 && code < 20) ? TMAP_VARIANT_PRODUCER_WAVE
+                   : pl.lean ? TMAP_VARIANT_BAND
                    : TMAP_VARIANT_RING;
     out->band_boxes = pl.band_g;
     out->band_rows = pl.band_rows;

@@ -136,6 +136,13 @@ int launch_load_r5(int stages, int nslot, const KArgs &a, void *stream);
 int launch_store_r5(int stages, int nslot, const KArgs &a, void *stream);
 int launch_roundtrip_r5(int stages, int nslot, const KArgs &a, void *stream);
 
+// The band schedule of sweeps over maps of rank <= 2 whose dimension-0 rows
+// are whole 16-byte chunks: the lean band kernels (tmap_band.h), stages 1..4,
+// one translation unit per direction (tmap_band_{load,store,roundtrip}.hip).
+int launch_band_load(int stages, const KArgs &a, void *stream);
+int launch_band_store(int stages, const KArgs &a, void *stream);
+int launch_band_roundtrip(int stages, const KArgs &a, void *stream);
+
 // LDS bytes one workgroup of a variant uses: the ring plus the barrier words.
 inline uint32_t variant_lds_bytes(int stages, int nslot) {
     return (uint32_t)stages * (uint32_t)nslot * kWaves * kBlockBytes + 64u;

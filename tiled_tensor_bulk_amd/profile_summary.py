@@ -61,7 +61,7 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-_KERNEL = re.compile(r"\b(copy|wave|thread|ws)_kernel<")
+_KERNEL = re.compile(r"\b(copy|wave|thread|ws|band)_kernel<")
 
 
 def is_copy_kernel(name: str) -> bool:
@@ -79,6 +79,12 @@ def short(name: str) -> str:
     if m:
         mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
         return f"tmap wave_kernel<{mode}, stages={m.group(2)}, nslot={m.group(3)}, dims={m.group(4)}>"
+    m = re.search(r"band_kernel<(\d+), (\d+), (true|false), (true|false), (true|false)>", name)
+    if m:
+        mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
+        extra = ", +addend" if m.group(5) == "true" else ""
+        return (f"tmap band_kernel<{mode}, stages={m.group(2)}, nt loads={m.group(3)}, "
+                f"nt stores={m.group(4)}{extra}>")
     if "copyBuffer" in name:
         return "hip copyBuffer (torch d2d copy)"
     return (name[:60] + "...") if len(name) > 63 else name
