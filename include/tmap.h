@@ -79,7 +79,8 @@ typedef struct tmap_swizzle {
 typedef struct tmap_launch_opts {
     uint32_t stages;      /* LDS ring depth 1..4 (default 2; 1 with explicit corners and
                              when each workgroup takes a single band unit; 3 for round
-                             trips on the band schedule)                                 */
+                             trips on the band schedule, and for every direction of
+                             the band kernel, TMAP_VARIANT_BAND)                         */
     uint32_t grid_wgs;    /* workgroups launched; fewer than there are groups makes each
                              take several (default: one workgroup per group; with
                              TMAP_FLAG_CONTIGUOUS, twice what fits in LDS per CU; in
@@ -88,8 +89,9 @@ typedef struct tmap_launch_opts {
     uint32_t spin_limit;  /* readiness-wait polls before TMAP_ERROR_TIMEOUT (default 2^22) */
     uint32_t group;       /* tiles (band units) dealt to a workgroup at a time, a power of
                              two <= 64 (default: enough boxes side by side to span 512
-                             bytes of a row, at least 2 and at most 8; band units: 4 for
-                             a round trip, 1 for a load or store; explicit corners: 8,
+                             bytes of a row, at least 2 and at most 8; band units: 2 on
+                             the band kernel, else 4 for a round trip and 1 for a load
+                             or store; explicit corners: 8,
                              for a wave-per-box store 4; wave per box with boxes of
                              8 KiB and more: 2 for a store, 4 for a load)                */
     uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
@@ -101,9 +103,10 @@ typedef struct tmap_launch_opts {
                              and stores on the band schedule, else 1)                  */
     uint32_t band_rows;   /* band schedule: box rows per band, a power of two.  A unit is
                              then 16 KiB / (band_rows * box row bytes) boxes side by
-                             side.  Default: 2 for a round trip (units 8 KiB wide), 8
-                             for a load or store (2 KiB wide), or the next taller
-                             height that fits.  An explicit height that does not fit
+                             side.  Default on the band kernel: 8 for a round trip, 16
+                             for a load or store; elsewhere 2 for a round trip (units
+                             8 KiB wide with 128-byte box rows), 8 for a load or store;
+                             or the next taller height that fits.  An explicit height that does not fit
                              the box, the swizzle or the sweep (see below) is
                              TMAP_ERROR_INVALID_VALUE where the band schedule applies,
                              and ignored elsewhere                                       */
@@ -312,23 +315,34 @@ tmap_status tmap_bulk_copy(void *dst, const void *src, uint64_t bytes, const tma
                            void *hip_stream);
 
 /* Bytes of one tile image: product of the box extents times the element
- * size ("Day 76": 64x64 fp32 is 16384 bytes).  0 for a map never encoded. */
+ * size ("Day 76", "An exact round trip": a 64x64 fp32 tile is 16384 bytes,
+ * the byte count its barrier expects).  0 for a map never encoded. */
 uint64_t tmap_box_bytes(const tmap_t *map);
 
-/* Tiles in a full sweep: product over dimensions of ceil(dim / box).
+/* Tiles in a full sweep: product over dimensions of ceil(dim / box), the
+ * count a copy with coords == NULL must be given.  ("Understanding TMA loads
+ * in CuTe DSL", "The work assigned to each block": the 8448 x 1792 fp16
+ * matrix in 64 x 256 boxes is 132 strips of 7 tiles, 924 tile loads; a
+ * ragged last tile in a dimension counts as a whole one, its overhang
+ * zero-filled as "GPU TMA", "Why architecture matters here" describes.)
  * -1 for a map never encoded. */
 int64_t tmap_sweep_tiles(const tmap_t *map);
 
 /* Host-side count of in-bounds box elements over n_tiles corners (host
  * int32 [n_tiles][rank], or NULL for the full sweep): the elements a copy
- * must read or write.  Writes *out_elems; TMAP_ERROR_INVALID_VALUE on bad
- * arguments. */
+ * must read or write, since out-of-bounds elements are zero-filled rather
+ * than read, and never stored ("GPU TMA", "Why architecture matters here").
+ * The copies' algorithmic byte counts are built from it.  Writes
+ * *out_elems; TMAP_ERROR_INVALID_VALUE on bad arguments (the checks of the
+ * copy calls for n_tiles and corners). */
 tmap_status tmap_inbounds_elems(const tmap_t *map, const int32_t *host_coords,
                                 int64_t n_tiles, uint64_t *out_elems);
 
 /* Schedule a copy would take (host only, no device needed): the boxes per
  * stage on the band schedule described at tmap_launch_opts, or 0 when every
- * stage holds one whole box.  src is the swept map of a load or round trip
+ * stage holds one whole box.  (A stage is what "TMA -- the async bulk copy
+ * engine", "Why this only pays off inside a pipeline" calls a pipeline
+ * stage: one byte-counted buffer of the ring.)  src is the swept map of a load or round trip
  * (of a store: the destination map), dst the round trip's destination map or
  * NULL for a load or store; coords is non-NULL for explicit corners (any non-NULL pointer: it is
  * not read); opts are the launch options the copy would get (NULL: the
@@ -337,10 +351,12 @@ tmap_status tmap_inbounds_elems(const tmap_t *map, const int32_t *host_coords,
 uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *coords,
                          const tmap_launch_opts *opts);
 
-/* The schedule a copy would run with (no device memory is touched and
- * nothing is launched; the plan depends on the current device's CU count
- * and LDS size, so a gfx950 device must be current, else
- * TMAP_ERROR_UNSUPPORTED_DEVICE).  Arguments as for the copy call of that
+/* The schedule a copy would run with: variant, band, ring depth, deal of
+ * the tiles to workgroups ("Understanding TMA loads in CuTe DSL", "The work
+ * assigned to each block": which tiles each block walks, in what order).
+ * No device memory is touched and nothing is launched (the plan depends on
+ * the current device's CU count and LDS size, so a gfx950 device must be
+ * current, else TMAP_ERROR_UNSUPPORTED_DEVICE).  Arguments as for the copy call of that
  * direction: `swept` is the source map of a load or round trip and the
  * destination map of a store, `dst` the round trip's destination map (NULL
  * otherwise), `coords` non-NULL for explicit corners (not read), `n_tiles`
@@ -374,7 +390,11 @@ tmap_status tmap_plan_launch(tmap_direction direction, const tmap_t *swept, cons
                              const int32_t *coords, int64_t n_tiles, const tmap_launch_opts *opts,
                              tmap_plan *out);
 
-/* Decoded fields of an encoded map (for inspection and tests). */
+/* Decoded fields of an encoded map (for inspection and tests): what "GPU
+ * TMA", "The architecture: every piece explained" lists a tensor descriptor
+ * as recording -- base address, rank, per-dimension size and stride, tile
+ * shape -- plus the element size and the swizzle.  TMAP_ERROR_INVALID_VALUE
+ * for a NULL or never encoded map or a NULL out. */
 typedef struct tmap_info {
     uint64_t global_address;
     uint64_t dims[5];
@@ -387,11 +407,15 @@ typedef struct tmap_info {
 } tmap_info;
 tmap_status tmap_query(const tmap_t *map, tmap_info *out);
 
-/* Static text for a status code. */
+/* Static text for a status code ("TMAP_ERROR_INVALID_VALUE" and so on; the
+ * names follow the driver results the pages quote, "Day 76", "Pitfalls":
+ * a failed encode rule gives INVALID_VALUE).  Never NULL. */
 const char *tmap_status_string(tmap_status status);
 
 /* Thread-local text describing the last failure of a call on this thread
- * (the rule that failed, the argument that was wrong); "" after success. */
+ * (the rule that failed, the argument that was wrong); "" after success.
+ * An addition: the encode of "Day 76", "Pitfalls" reports a failed rule
+ * only as INVALID_VALUE, with no word on which rule it was. */
 const char *tmap_last_error_detail(void);
 
 /* Wait for hip_stream, then read and clear the current device's status

@@ -228,17 +228,20 @@ def _enc_rows(dt, dims, box, swz=(0, 0, 0), pad_rows=0):
 
 def test_band_schedule_choice():
     """Which sweeps take the band schedule: boxes with 64..512-byte rows and a
-    dimension-1 extent of the band height (16 rows by default) times a power
-    of two, swizzles that map a band onto itself, a row of the sweep holding a
-    whole unit, sweeps only, and not in the thread-copy, producer-wave or
-    whole-box modes; by default only for tensors spanning 256 MiB or more
-    (TMAP_FLAG_BAND lifts that)."""
+    dimension-1 extent of the band height times a power of two, swizzles that
+    map a band onto itself, a row of the sweep holding a whole unit, sweeps
+    only, and not in the thread-copy, producer-wave or whole-box modes; by
+    default only for tensors spanning 256 MiB or more (TMAP_FLAG_BAND lifts
+    that).  Default heights: maps of rank <= 2 whose rows are whole 16-byte
+    chunks (the band kernel) 16 rows for a load or store and 8 for a round
+    trip, or the next taller, else the tallest shorter height that fits;
+    other maps 8 and 2 rows, or the next taller."""
     W = inputs.WORKLOADS
     B = T.FLAG_BAND
-    # (name, boxes per unit of a load or store (8-row bands), of a round trip
-    # (2-row bands), of a load forced onto the band schedule)
-    for name, want, want_rt, forced in [("sweep2g_u8", 16, 64, 16), ("ragged_bf16", 16, 64, 16),
-                                        ("plus1_f32", 8, 32, 8), ("strips_f16", 0, 0, 4),
+    # (name, boxes per unit of a load or store (16-row bands), of a round
+    # trip (8-row bands), of a load forced onto the band schedule)
+    for name, want, want_rt, forced in [("sweep2g_u8", 8, 16, 8), ("ragged_bf16", 8, 16, 8),
+                                        ("plus1_f32", 4, 8, 4), ("strips_f16", 0, 0, 2),
                                         ("tile64_f32", 0, 0, 1), ("pad5d_f32", 0, 0, 0)]:
         w = W[name]
         m = T.tmap_encode(w.dtype, w.rank, BASE, w.dims, w.strides, w.box, None, w.swizzle)
@@ -253,17 +256,23 @@ def test_band_schedule_choice():
         assert T.tmap_band_boxes(m, explicit_coords=True, flags=B) == 0
         assert T.tmap_band_boxes(m, m) == want_rt
     # the size threshold: 256 MiB spanned by the outermost dimension
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65536], [128, 128])) == 16
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65536], [128, 128])) == 8
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128])) == 0
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128]), flags=B) == 16
-    # row width: 64..512 bytes; units of 8 rows (2 KiB wide), or taller bands
-    # when a row of the sweep (20 boxes here) is narrower than that
-    for dt, box0, want in [("u8", 32, 0), ("u8", 64, 16), ("u8", 128, 16), ("u8", 256, 8), ("f16", 256, 4),
-                           ("f32", 128, 4), ("f32", 256, 0), ("f64", 8, 16), ("f64", 64, 4), ("f32", 24, 0)]:
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128]), flags=B) == 8
+    # row width: 64..512 bytes; units of 16 rows, or shorter bands when a
+    # 16-row unit is wider than a row of the sweep (20 boxes here)
+    for dt, box0, want in [("u8", 32, 0), ("u8", 64, 16), ("u8", 128, 8), ("u8", 256, 4), ("f16", 256, 2),
+                           ("f32", 128, 2), ("f32", 256, 0), ("f64", 8, 16), ("f64", 64, 2), ("f32", 24, 0)]:
         assert T.tmap_band_boxes(_enc_rows(dt, [box0 * 20, 100], [box0, 16]), flags=B) == want, (dt, box0)
-    # dimension-1 extent: the band height times a power of two
-    for box1, want in [(4, 0), (8, 16), (16, 16), (24, 0), (32, 16), (48, 0), (64, 16), (128, 16)]:
+    # the generic ring's heights (a rank-3 map): 8 rows, or taller
+    for dt, box0, want in [("u8", 64, 16), ("u8", 128, 16), ("u8", 256, 8), ("f16", 256, 4)]:
+        assert T.tmap_band_boxes(_enc_rows(dt, [box0 * 20, 100, 2], [box0, 16, 1]), flags=B) == want, (dt, box0)
+    # dimension-1 extent: the band height times a power of two (16 rows, or
+    # the tallest shorter height for a shorter box)
+    for box1, want in [(4, 32), (8, 16), (16, 8), (24, 0), (32, 8), (48, 0), (64, 8), (128, 8)]:
         assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, box1]), flags=B) == want, box1
+    for box1, want in [(4, 0), (8, 16), (16, 16), (24, 0), (32, 16)]:            # the generic ring's: 8 or taller
+        assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300, 2], [128, box1, 1]), flags=B) == want, box1
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 4]), flags=B, band_rows=4) == 32
     # the swizzle only changes element-offset bits [m, m+b): a band of
     # 16 * 128 elements must be a whole number of 2^(m+b) blocks
@@ -276,7 +285,7 @@ def test_band_schedule_choice():
     # band height: a power of two dividing box[1], at most a 16 KiB stage, and
     # a unit of 16 KiB / (rows * row bytes) boxes fitting a row of the sweep
     wide = _enc_rows("u8", [65536, 300], [128, 128], (3, 4, 3))
-    for rows, want in [(0, 16), (1, 128), (2, 64), (4, 32), (8, 16), (16, 8), (32, 4), (64, 2), (128, 1), (256, 0),
+    for rows, want in [(0, 8), (1, 128), (2, 64), (4, 32), (8, 16), (16, 8), (32, 4), (64, 2), (128, 1), (256, 0),
                        (3, 0), (48, 0)]:
         assert T.tmap_band_boxes(wide, flags=B, band_rows=rows) == want, rows
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 128]), flags=B, band_rows=1) == 0  # 32 boxes a row

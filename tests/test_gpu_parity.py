@@ -631,11 +631,12 @@ def test_plan_query_reports_the_schedules():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     p = plan("sweep2g_u8", "roundtrip", flags=T.FLAG_NONTEMPORAL)
     assert (p["variant"], p["band_boxes"], p["band_rows"], p["stages"], p["group"], p["regions"]) == \
-        ("band", 64, 2, 3, 4, 1)
-    assert p["units"] == 131072 * 64 // 64 and p["walkers"] == p["workgroups"] == p["units"] // 4
+        ("band", 16, 8, 3, 2, 1)
+    # 512 boxes a row in units of 16, 256 box rows of 16 bands each
+    assert p["units"] == (512 // 16) * 256 * 16 and p["walkers"] == p["workgroups"] == p["units"] // 2
     p = plan("sweep2g_u8", "load", flags=T.FLAG_NONTEMPORAL)
     assert (p["variant"], p["band_boxes"], p["band_rows"], p["stages"], p["group"], p["regions"]) == \
-        ("band", 16, 8, 1, 1, 2)
+        ("band", 8, 16, 3, 2, 2)
     p = plan("pad5d_f32", "store")
     assert (p["variant"], p["stages"], p["slots"], p["group"]) == ("wave_per_box", 1, 8, 2)
     # 8 KiB boxes: one wave to a workgroup, each with its own one-box ring

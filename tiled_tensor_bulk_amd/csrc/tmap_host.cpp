@@ -146,13 +146,17 @@ uint64_t band_span(const tmap::KMap &k, uint32_t g, uint32_t rows) {
 constexpr uint64_t kBandMinSpan = 256ull << 20;
 
 // Default band heights, measured on MI355X over the 2 GiB u8, 1 GiB fp32 and
-// ragged bf16 sweeps: round trips read and write 2-row bands of units 8 KiB
-// wide (with 3 stages and 4 units per workgroup, see plan_launch), loads and
-// stores 8-row bands of units 2 KiB wide (0.5-1.8% faster than 16 rows).
+// ragged bf16 sweeps.  The band kernel of rank-2 sweeps (tmap_band.h): round
+// trips 8-row bands (units 2 KiB wide), loads and stores 16-row bands (units
+// 1 KiB wide for 128-byte box rows); the generic ring: round trips 2-row
+// bands of units 8 KiB wide (with 3 stages and 4 units per workgroup, see
+// plan_launch), loads and stores 8-row bands (0.5-1.8% faster than 16).
 // Where that height does not fit the box or the sweep, the next taller one
 // that does is taken.
 constexpr uint32_t kBandRowsRoundtrip = 2;
 constexpr uint32_t kBandRowsLoadStore = 8;
+constexpr uint32_t kLeanRowsRoundtrip = 8;
+constexpr uint32_t kLeanRowsLoadStore = 16;
 
 // The checks that depend on the band height; nullptr when `rows` fits,
 // else the reason.  rc: 16-byte chunks per box row.
@@ -175,11 +179,24 @@ const char *band_height_misfit(const MapImpl &m, const tmap::KArgs &a, uint32_t 
     return nullptr;
 }
 
-// want_rows: the band height asked for, 0 for the default of the direction.
-// An explicit height that does not fit leaves *why set and returns false;
-// without one the schedule falls back to whole boxes silently.
+// Whether the maps of a copy suit the band kernel of rank-2 sweeps
+// (tmap_band.h): both have rank <= 2 and every tensor side's dimension-0 row
+// is a whole number of 16-byte chunks, so that the tensor's edge never cuts
+// a chunk (the generic ring's element path is then never needed).
+bool band_lean_maps(int mode, const tmap::KArgs &a) {
+    if (a.src.rank > 2 || a.dst.rank > 2) return false;
+    auto whole = [](const tmap::KMap &k) { return ((uint64_t)k.dims[0] * k.elem_size) % 16u == 0; };
+    if (mode != tmap::kStore && !whole(a.src)) return false;
+    if (mode != tmap::kLoad && !whole(a.dst)) return false;
+    return true;
+}
+
+// want_rows: the band height asked for, 0 for the default of the direction
+// (lean: the maps suit the band kernel, whose defaults differ).  An explicit
+// height that does not fit leaves *why set and returns false; without one
+// the schedule falls back to whole boxes silently.
 bool band_fits(const MapImpl &m, const tmap::KArgs &a, bool roundtrip, uint32_t flags, uint32_t want_rows,
-               uint32_t &g, uint32_t &nb, uint32_t &rows, const char **why = nullptr) {
+               uint32_t &g, uint32_t &nb, uint32_t &rows, const char **why = nullptr, bool lean = false) {
     if (a.coords || a.elemwise) return false;
     if (flags & (TMAP_FLAG_THREAD_COPY | TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WAVE_PER_BOX | TMAP_FLAG_WHOLE_BOX))
         return false;
@@ -196,8 +213,15 @@ bool band_fits(const MapImpl &m, const tmap::KArgs &a, bool roundtrip, uint32_t 
         if (w && why) *why = w;
         return w == nullptr;
     }
-    for (rows = roundtrip ? kBandRowsRoundtrip : kBandRowsLoadStore; rows <= m.box[1]; rows *= 2)
+    const uint32_t first = lean ? (roundtrip ? kLeanRowsRoundtrip : kLeanRowsLoadStore)
+                                : (roundtrip ? kBandRowsRoundtrip : kBandRowsLoadStore);
+    for (rows = first; rows <= m.box[1]; rows *= 2)
         if (!band_height_misfit(m, a, rc, rows, g, nb)) return true;
+    // the band kernel's defaults are tall: a shorter box takes the tallest
+    // height below them that fits
+    if (lean)
+        for (rows = first / 2; rows >= 1; rows /= 2)
+            if (!band_height_misfit(m, a, rc, rows, g, nb)) return true;
     return false;
 }
 
@@ -231,20 +255,9 @@ constexpr uint32_t kKnownFlags = TMAP_FLAG_CONTIGUOUS | TMAP_FLAG_NONTEMPORAL | 
                                  TMAP_FLAG_WAVE_PER_BOX | TMAP_FLAG_CACHED_PACKED | TMAP_FLAG_INJECT_BUDGET_MISMATCH |
                                  TMAP_FLAG_DEBUG_POISON;
 
-// Whether a band-schedule launch runs the lean band kernels (tmap_band.h):
-// both maps have rank <= 2 and every tensor side's dimension-0 row is a whole
-// number of 16-byte chunks, so that the tensor's edge never cuts a chunk
-// (the generic ring's element path is then never needed).
-bool band_lean(int mode, const tmap::KArgs &a, uint32_t band_g) {
-    if (!band_g || a.src.rank > 2 || a.dst.rank > 2) return false;
-    auto whole = [](const tmap::KMap &k) { return ((uint64_t)k.dims[0] * k.elem_size) % 16u == 0; };
-    if (mode != tmap::kStore && !whole(a.src)) return false;
-    if (mode != tmap::kLoad && !whole(a.dst)) return false;
-    return true;
-}
-
+// lean: the band schedule runs the band kernel of rank-2 sweeps.
 tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
-                        const DeviceState &dev, bool band, bool corners, Plan &pl) {
+                        const DeviceState &dev, bool band, bool lean, bool corners, Plan &pl) {
     const uint32_t per_wave_pass = tmap::kWaves * tmap::kBlockBytes;  // bytes one slot per lane covers
     const uint32_t need = (m.box_bytes + per_wave_pass - 1) / per_wave_pass;
     int nslot = 1;
@@ -261,6 +274,12 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // 1 GiB fp32 round trips (one placement-sensitive ragged bf16 round trip
     // lost 3%); 4 stages fit one workgroup fewer per CU and lose 10%
     if (band && mode == tmap::kRoundtrip && !(opts && opts->stages)) stages = 3;
+    // the band kernel: 3 stages in every direction, of which its two units
+    // (below) use two; the third stage's LDS holds a CU to three workgroups.
+    // Measured on MI355X with 5 warm-up and 20 timed launches after an idle
+    // gap, 2 GiB u8 round trip: 0.816-0.818 of peak at 3 stages x 2 units,
+    // 0.812-0.815 at 2 x 2 (four workgroups a CU), 0.756-0.764 at 3 x 4
+    if (lean && !(opts && opts->stages)) stages = 3;
     if (stages < 1 || stages > 4)
         return fail(TMAP_ERROR_INVALID_VALUE, "stages must be 1..4 (got %d)", stages);
     const uint32_t flags = opts ? opts->flags : 0u;
@@ -306,6 +325,10 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     uint32_t group = (opts && opts->group) ? opts->group : 0;
     if (group && (group > 64 || (group & (group - 1))))
         return fail(TMAP_ERROR_INVALID_VALUE, "group must be a power of two <= 64 (got %u)", group);
+    // the band kernel: 2 units a workgroup in every direction (its setup is
+    // a few shifts, so short-lived workgroups cost little; measured on the
+    // 2 GiB u8, 1 GiB fp32 and ragged bf16 sweeps, 4 units lose 3-8%)
+    if (!group && lean) group = 2u;
     if (!group && band) group = mode == tmap::kRoundtrip ? 4u : 1u;
     // explicit corners: 8 tiles to a walker; a wave-per-box store takes 4.
     // Where each wave is a workgroup of its own, a store takes 2 and a load
@@ -400,15 +423,17 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
         return fail(TMAP_ERROR_INVALID_VALUE, "unknown flag bits 0x%x", opts->flags & ~kKnownFlags);
     uint32_t g = 0, nb = 0, rows = 0;
     const char *why = nullptr;
+    const bool lean_maps = band_lean_maps(mode, a);
     const bool band = band_fits(swept, a, mode == tmap::kRoundtrip, opts ? opts->flags : 0u,
-                                opts ? opts->band_rows : 0u, g, nb, rows, &why);
+                                opts ? opts->band_rows : 0u, g, nb, rows, &why, lean_maps);
     if (why) return fail(TMAP_ERROR_INVALID_VALUE, "%s", why);
     if (band) band_setup(swept, a, g, nb, rows);
-    tmap_status st = plan_launch(mode, swept, a.n_tiles, opts, dev, band, a.coords != nullptr, pl);
+    const bool lean = band && lean_maps;
+    tmap_status st = plan_launch(mode, swept, a.n_tiles, opts, dev, band, lean, a.coords != nullptr, pl);
     if (st != TMAP_SUCCESS) return st;
     pl.band_g = band ? g : 0u;
     pl.band_rows = band ? rows : 0u;
-    pl.lean = band_lean(mode, a, pl.band_g);
+    pl.lean = lean;
     a.grid = pl.grid;
     a.regions = pl.regions;
     a.flags = opts ? opts->flags : 0u;
@@ -635,8 +660,12 @@ uint32_t tmap_band_boxes(const tmap_t *src, const tmap_t *dst, const int32_t *co
     a.dst = dst ? tmap::kernel_map(d) : a.src;
     fill_common(a, s, coords, 0);
     uint32_t g = 0, nb = 0, rows = 0;
-    return band_fits(s, a, dst != nullptr, opts ? opts->flags : 0u, opts ? opts->band_rows : 0u, g, nb, rows) ? g
-                                                                                                          : 0u;
+    // a load and a store take the same band (the swept map is either side)
+    const bool lean = band_lean_maps(dst ? (int)tmap::kRoundtrip : (int)tmap::kLoad, a);
+    return band_fits(s, a, dst != nullptr, opts ? opts->flags : 0u, opts ? opts->band_rows : 0u, g, nb, rows,
+                     nullptr, lean)
+               ? g
+               : 0u;
 }
 
 tmap_status tmap_query(const tmap_t *map, tmap_info *out) {

@@ -112,6 +112,10 @@ def cmd_stats(a):
         if us:
             out += ["", f"copy kernel, last {len(us)} launches (the bench's timed steps): "
                         f"average {sum(us) / len(us):.1f} us, median {sorted(us)[len(us) // 2]:.1f} us"]
+        if a.list:
+            every = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr]
+            out += ["", f"every copy-kernel launch in order ({len(every)}, us): "
+                        + ", ".join(f"{x:.1f}" for x in every)]
     open(a.out, "w").write("\n".join(out) + "\n")
     print("\n".join(out))
 
@@ -198,6 +202,7 @@ def main():
     s.add_argument("--cmd", required=True)
     s.add_argument("--trace", help="the run's kernel trace csv (adds the average of the last launches)")
     s.add_argument("--last", type=int, default=100)
+    s.add_argument("--list", action="store_true", help="also list every copy-kernel launch duration in order")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
