@@ -284,6 +284,28 @@ tmap_status tmap_roundtrip(const tmap_t *src, const tmap_t *dst, const int32_t *
                            int64_t n_tiles, const tmap_launch_opts *opts, void *hip_stream);
 
 /*
+ * tmap_roundtrip_noalloc -- tmap_roundtrip for callers that cannot allocate
+ * device memory: code being captured into a HIP graph on its first launch,
+ * serving loops and harnesses that forbid hipMalloc.  Same arguments,
+ * checks, schedule and results as tmap_roundtrip; it never allocates or
+ * frees device memory, on its first call included.
+ *
+ * The copy kernels need one 4-byte status word beyond their inputs and
+ * outputs, which they set when a bounded readiness wait expires.  Here it is
+ * a static device array of the library (4 bytes per device, kept until the
+ * process ends) instead of the word tmap_roundtrip allocates on first use;
+ * its need does not grow with the input, so no input size is refused for it.
+ * The device address of the array is looked up once per device, on the
+ * first call there (a gfx950 device must be current, else
+ * TMAP_ERROR_UNSUPPORTED_DEVICE).  Every call on a device shares that
+ * device's word: a timeout stays recorded until tmap_sync_status reads and
+ * clears it, and calls that overlap on one device (on several streams) race
+ * for it, so a timeout cannot be told apart by stream.
+ */
+tmap_status tmap_roundtrip_noalloc(const tmap_t *src, const tmap_t *dst, const int32_t *coords,
+                                   int64_t n_tiles, const tmap_launch_opts *opts, void *hip_stream);
+
+/*
  * tmap_roundtrip_add_f32 -- the round trip with an fp32 update of the tile in
  * on-chip memory: each box is loaded into LDS, every element gets + addend
  * (IEEE single precision, round to nearest even) between the LDS read and the
@@ -419,9 +441,10 @@ const char *tmap_status_string(tmap_status status);
 const char *tmap_last_error_detail(void);
 
 /* Wait for hip_stream, then read and clear the current device's status
- * word that kernels set when a bounded readiness wait expires.  Returns
+ * words that kernels set when a bounded readiness wait expires (the
+ * library-allocated one and that of tmap_roundtrip_noalloc).  Returns
  * TMAP_SUCCESS or TMAP_ERROR_TIMEOUT (or TMAP_ERROR_LAUNCH if the stream
- * reports an error).  The word is per device, not per stream: a timeout
+ * reports an error).  The words are per device, not per stream: a timeout
  * of a copy on one stream is reported to whichever stream of that device is
  * checked first, and a check clears it for all of them.
  * ("TMA -- the async bulk copy engine", "Load completion -- the mbarrier and

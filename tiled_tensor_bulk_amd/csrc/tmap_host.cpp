@@ -463,15 +463,22 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     return TMAP_SUCCESS;
 }
 
+// noalloc: the kernels set the no-allocation entry point's static status
+// word (tmap_noalloc.hip) instead of the device's library-allocated one,
+// which is then neither allocated nor touched.
 tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launch_opts *opts,
-                void *stream) {
+                void *stream, bool noalloc = false) {
     DeviceState *dev = nullptr;
-    tmap_status st = device_for_launch(&dev);
+    tmap_status st = device_for_launch(&dev, !noalloc);
     if (st != TMAP_SUCCESS) return st;
     Plan pl;
     st = prepare(mode, swept, a, opts, *dev, pl);
     if (st != TMAP_SUCCESS) return st;
     a.status = dev->status;
+    if (noalloc) {
+        st = tmap::noalloc_scratch(&a.status);
+        if (st != TMAP_SUCCESS) return st;
+    }
     // maps of rank <= 2 run the variants that only walk two dimensions
     const bool r2 = a.src.rank <= 2 && a.dst.rank <= 2;
     int rc = (int)hipErrorInvalidValue;
@@ -756,7 +763,8 @@ tmap_status tmap_store_tiles(const tmap_t *dst, const int32_t *coords, int64_t n
 }
 
 static tmap_status roundtrip_impl(const tmap_t *src, const tmap_t *dst, const int32_t *coords, int64_t n_tiles,
-                                  bool add, float addend, const tmap_launch_opts *opts, void *hip_stream);
+                                  bool add, float addend, const tmap_launch_opts *opts, void *hip_stream,
+                                  bool noalloc = false);
 
 tmap_status tmap_roundtrip(const tmap_t *src, const tmap_t *dst, const int32_t *coords, int64_t n_tiles,
                            const tmap_launch_opts *opts, void *hip_stream) {
@@ -816,7 +824,8 @@ tmap_status tmap_bulk_copy(void *dst, const void *src, uint64_t bytes, const tma
 }
 
 static tmap_status roundtrip_impl(const tmap_t *src, const tmap_t *dst, const int32_t *coords, int64_t n_tiles,
-                                  bool add, float addend, const tmap_launch_opts *opts, void *hip_stream) {
+                                  bool add, float addend, const tmap_launch_opts *opts, void *hip_stream,
+                                  bool noalloc) {
     MapImpl s, d;
     if (!decode(src, s)) return fail(TMAP_ERROR_INVALID_VALUE, "src map is NULL or not encoded");
     if (!decode(dst, d)) return fail(TMAP_ERROR_INVALID_VALUE, "dst map is NULL or not encoded");
@@ -840,8 +849,21 @@ static tmap_status roundtrip_impl(const tmap_t *src, const tmap_t *dst, const in
     a.add_f32 = add ? 1u : 0u;
     a.addend = addend;
     fill_common(a, s, coords, n_tiles);
-    return run(tmap::kRoundtrip, s, a, opts, hip_stream);
+    return run(tmap::kRoundtrip, s, a, opts, hip_stream, noalloc);
 }
+
+tmap_status tmap_roundtrip_noalloc(const tmap_t *src, const tmap_t *dst, const int32_t *coords, int64_t n_tiles,
+                                   const tmap_launch_opts *opts, void *hip_stream) {
+    return roundtrip_impl(src, dst, coords, n_tiles, false, 0.0f, opts, hip_stream, true);
+}
+
+}  // extern "C"
+
+tmap_status tmap::record_failure(tmap_status st, const char *detail) {
+    return fail(st, "%s", detail);
+}
+
+extern "C" {
 
 tmap_status tmap_plan_launch(tmap_direction direction, const tmap_t *swept, const tmap_t *dst,
                              const int32_t *coords, int64_t n_tiles, const tmap_launch_opts *opts,
@@ -905,22 +927,27 @@ tmap_status tmap_sync_status(void *hip_stream) {
         const hipError_t e = hipGetLastError();
         return fail(TMAP_ERROR_LAUNCH, "stream error: %s", hipGetErrorString(e));
     }
-    uint32_t *word = nullptr;
+    // the library-allocated word and the no-allocation entry point's word
+    uint32_t *words[2] = {nullptr, tmap::noalloc_status(dev)};
     {
         std::lock_guard<std::mutex> lk(g_dev_mu);
-        word = g_dev[dev].status;
+        words[0] = g_dev[dev].status;
     }
-    if (!word) return ok();
-    uint32_t v = 0;
-    if (hipMemcpy(&v, word, 4, hipMemcpyDeviceToHost) != hipSuccess) {
-        const hipError_t e = hipGetLastError();
-        return fail(TMAP_ERROR_LAUNCH, "cannot read the status word: %s", hipGetErrorString(e));
+    uint32_t any = 0;
+    for (uint32_t *word : words) {
+        if (!word) continue;
+        uint32_t v = 0;
+        if (hipMemcpy(&v, word, 4, hipMemcpyDeviceToHost) != hipSuccess) {
+            const hipError_t e = hipGetLastError();
+            return fail(TMAP_ERROR_LAUNCH, "cannot read the status word: %s", hipGetErrorString(e));
+        }
+        if (v) {
+            (void)hipMemset(word, 0, 4);
+            (void)hipDeviceSynchronize();
+            any |= v;
+        }
     }
-    if (v) {
-        (void)hipMemset(word, 0, 4);
-        (void)hipDeviceSynchronize();
-        return fail(TMAP_ERROR_TIMEOUT, "a readiness wait expired (status 0x%x)", v);
-    }
+    if (any) return fail(TMAP_ERROR_TIMEOUT, "a readiness wait expired (status 0x%x)", any);
     return ok();
 }
 

@@ -143,6 +143,15 @@ int launch_band_load(int stages, const KArgs &a, void *stream);
 int launch_band_store(int stages, const KArgs &a, void *stream);
 int launch_band_roundtrip(int stages, const KArgs &a, void *stream);
 
+// The no-allocation entry point's status word (tmap_noalloc.hip): its device
+// address on the current device, looked up on the first call there
+// (noalloc_scratch), or nullptr for a device it was never looked up on
+// (noalloc_status).
+tmap_status noalloc_scratch(uint32_t **out);
+uint32_t *noalloc_status(int dev);
+// Record a failure's status and detail text for tmap_last_error_detail().
+tmap_status record_failure(tmap_status st, const char *detail);
+
 // LDS bytes one workgroup of a variant uses: the ring plus the barrier words.
 inline uint32_t variant_lds_bytes(int stages, int nslot) {
     return (uint32_t)stages * (uint32_t)nslot * kWaves * kBlockBytes + 64u;

@@ -91,6 +91,8 @@ def lib():
             f.restype = ctypes.c_int
         L.tmap_roundtrip.argtypes = [P(tmap_t), P(tmap_t), vp, i64, P(tmap_launch_opts), vp]
         L.tmap_roundtrip.restype = ctypes.c_int
+        L.tmap_roundtrip_noalloc.argtypes = [P(tmap_t), P(tmap_t), vp, i64, P(tmap_launch_opts), vp]
+        L.tmap_roundtrip_noalloc.restype = ctypes.c_int
         L.tmap_roundtrip_add_f32.argtypes = [P(tmap_t), P(tmap_t), vp, i64, ctypes.c_float,
                                              P(tmap_launch_opts), vp]
         L.tmap_roundtrip_add_f32.restype = ctypes.c_int
@@ -226,6 +228,15 @@ def tmap_roundtrip(src: tmap_t, dst: tmap_t, coords, n_tiles: int, stream=None, 
     st = lib().tmap_roundtrip(ctypes.byref(src), ctypes.byref(dst), _ptr(coords), int(n_tiles),
                               _opts(**opts), _stream(stream))
     _check(st, "tmap_roundtrip")
+
+
+def tmap_roundtrip_noalloc(src: tmap_t, dst: tmap_t, coords, n_tiles: int, stream=None, **opts) -> None:
+    """tmap_roundtrip without any device allocation (its status word is a
+    static device array of the library)."""
+    _check_corners(coords, src, n_tiles)
+    st = lib().tmap_roundtrip_noalloc(ctypes.byref(src), ctypes.byref(dst), _ptr(coords), int(n_tiles),
+                                      _opts(**opts), _stream(stream))
+    _check(st, "tmap_roundtrip_noalloc")
 
 
 def tmap_roundtrip_add_f32(src: tmap_t, dst: tmap_t, coords, n_tiles: int, addend: float, stream=None,
