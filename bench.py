@@ -174,13 +174,15 @@ def main():
                                   n, **opts)
         if plan["band_boxes"]:
             schedule = f"band: {plan['band_boxes']} boxes x {plan['band_rows']} rows per stage"
-        elif plan["variant"] == "wave_per_box":
-            schedule = "whole boxes, one wave per box"
+        elif plan["variant"] in ("wave_per_box", "corner"):
+            schedule = "whole boxes, one wave per box" + (", drained box held in registers"
+                                                           if plan["variant"] == "corner" else "")
         else:
             schedule = "whole boxes" + ("" if plan["variant"] == "ring" else f" ({plan['variant']})")
 
     kernel_name = {"ring": "copy_kernel", "wave_per_box": "wave_kernel", "thread_copy": "thread_kernel",
-                   "producer_wave": "ws_kernel", "band": "band_kernel"}[plan["variant"]] if plan else "copy_kernel"
+                   "producer_wave": "ws_kernel", "band": "band_kernel",
+                   "corner": "corner_kernel"}[plan["variant"]] if plan else "copy_kernel"
     for _ in range(args.warmup):
         launch()
     st = T.tmap_sync_status(stream)

@@ -93,7 +93,9 @@ typedef struct tmap_launch_opts {
                              the band kernel, else 4 for a round trip and 1 for a load
                              or store; explicit corners: 8,
                              for a wave-per-box store 4; wave per box with boxes of
-                             8 KiB and more: 2 for a store, 4 for a load)                */
+                             8 KiB and more: 2 for a load or store (4 for a load with
+                             2 stages or a swizzle inside 16-byte chunks), 8 for a
+                             round trip)                                               */
     uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
                              streams, each sweeping an equal contiguous stretch of the
                              tiles (workgroup i takes stretch i mod regions), so that the
@@ -115,10 +117,14 @@ typedef struct tmap_launch_opts {
 /* Band schedule.  A sweep (coords == NULL) of boxes whose rows hold 64 to
  * 512 bytes, whose dimension-1 extent is the band height times a power of
  * two and whose higher extents are 1 runs on it when the tensor spans at
- * least 256 MiB (dims[rank-1] * strides[rank-1]; smaller ones fit in the
- * last-level cache and gain nothing from it) or TMAP_FLAG_BAND asks for it,
- * unless TMAP_FLAG_WHOLE_BOX, thread-copy or producer-wave mode is asked
- * for.  A stage then holds the same band of band_rows rows of the
+ * least 256 MiB (dims[rank-1] * strides[rank-1]), or when TMAP_FLAG_BAND
+ * asks for it, or when its maps suit the band kernel (TMAP_VARIANT_BAND:
+ * rank <= 2, dimension-0 rows of whole 16-byte chunks); unless
+ * TMAP_FLAG_WHOLE_BOX, thread-copy, producer-wave or wave-per-box mode is
+ * asked for.  A smaller tensor stays in the last-level cache, where DRAM
+ * page locality gains nothing: on the band kernel it then takes the tallest
+ * band that fits (often one whole box), 2 stages and one region, and other
+ * maps keep whole boxes.  A stage then holds the same band of band_rows rows of the
  * neighbouring boxes that together fill 16 KiB (a "unit"), each box's band
  * being the contiguous piece of that box's swizzled LDS image that it
  * always is.  The swizzle must map each band onto itself (band_rows * box[0]
@@ -390,9 +396,12 @@ typedef enum tmap_variant {
     TMAP_VARIANT_THREAD_COPY = 1,   /* TMAP_FLAG_THREAD_COPY                                       */
     TMAP_VARIANT_PRODUCER_WAVE = 2, /* TMAP_FLAG_PRODUCER_WAVE                                     */
     TMAP_VARIANT_WAVE_PER_BOX = 3,  /* TMAP_FLAG_WAVE_PER_BOX, or its default                      */
-    TMAP_VARIANT_BAND = 4           /* band schedule of a sweep whose maps have rank <= 2 and whose
+    TMAP_VARIANT_BAND = 4,          /* band schedule of a sweep whose maps have rank <= 2 and whose
                                        dimension-0 rows are whole 16-byte chunks: the band ring
                                        with per-slot offsets fixed per kernel                      */
+    TMAP_VARIANT_CORNER = 5         /* wave per box with one stage, boxes of at most 8 KiB and a
+                                       swizzle that moves whole chunks: each wave holds a drained
+                                       box in registers while the next one loads               */
 } tmap_variant;
 typedef struct tmap_plan {
     uint32_t variant;     /* tmap_variant                                                  */

@@ -24,6 +24,9 @@ int launch_roundtrip_r5(int, int, const KArgs &, void *) { return 1; }
 int launch_band_load(int, const KArgs &, void *) { return 1; }
 int launch_band_store(int, const KArgs &, void *) { return 1; }
 int launch_band_roundtrip(int, const KArgs &, void *) { return 1; }
+int launch_corner_load(int, int, const KArgs &, void *) { return 1; }
+int launch_corner_store(int, int, const KArgs &, void *) { return 1; }
+int launch_corner_roundtrip(int, int, const KArgs &, void *) { return 1; }
 uint32_t *noalloc_status(int) { return nullptr; }
 tmap_status noalloc_scratch(uint32_t **) { return TMAP_ERROR_LAUNCH; }
 }  // namespace tmap

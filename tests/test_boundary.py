@@ -241,8 +241,8 @@ def test_band_schedule_choice():
     # (name, boxes per unit of a load or store (16-row bands), of a round
     # trip (8-row bands), of a load forced onto the band schedule)
     for name, want, want_rt, forced in [("sweep2g_u8", 8, 16, 8), ("ragged_bf16", 8, 16, 8),
-                                        ("plus1_f32", 4, 8, 4), ("strips_f16", 0, 0, 2),
-                                        ("tile64_f32", 0, 0, 1), ("pad5d_f32", 0, 0, 0)]:
+                                        ("plus1_f32", 4, 8, 4), ("strips_f16", 1, 1, 2),
+                                        ("tile64_f32", 1, 1, 1), ("pad5d_f32", 0, 0, 0)]:
         w = W[name]
         m = T.tmap_encode(w.dtype, w.rank, BASE, w.dims, w.strides, w.box, None, w.swizzle)
         assert T.tmap_band_boxes(m) == want, name
@@ -255,9 +255,14 @@ def test_band_schedule_choice():
         assert T.tmap_band_boxes(m, flags=B | T.FLAG_CACHED_PACKED) == forced
         assert T.tmap_band_boxes(m, explicit_coords=True, flags=B) == 0
         assert T.tmap_band_boxes(m, m) == want_rt
-    # the size threshold: 256 MiB spanned by the outermost dimension
+    # the size threshold, 256 MiB spanned by the outermost dimension: below
+    # it the band kernel's maps take the tallest band that fits (here one
+    # whole 128-row box), other maps whole boxes
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65536], [128, 128])) == 8
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128])) == 0
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128])) == 1
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 64])) == 2
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535, 1], [128, 128, 1])) == 0
+    assert T.tmap_band_boxes(_enc_rows("u8", [4097, 60000], [128, 128])) == 0     # rows not whole chunks
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128]), flags=B) == 8
     # row width: 64..512 bytes; units of 16 rows, or shorter bands when a
     # 16-row unit is wider than a row of the sweep (20 boxes here)

@@ -62,7 +62,7 @@ def test_graph_replays_match_the_oracle():
     corners = inputs.random_corners(c_dims, c_box, 200, seed=71)
     corners_dev = torch.from_numpy(corners).to(DEV)
     oc = Map(es=4, dims=c_dims, strides=c_strides, box=c_box)
-    assert T.tmap_plan_launch("roundtrip", mc, md, True, len(corners))["variant"] == "wave_per_box"
+    assert T.tmap_plan_launch("roundtrip", mc, md, True, len(corners))["variant"] == "corner"
     fill_random(b, 1)
     fill_random(d, 2)
 

@@ -136,7 +136,7 @@ def test_strips_f16_load_page_schedule():
     assert n == 924
     om = Map(es=2, dims=w.dims, strides=w.strides, box=w.box, swizzle=w.swizzle)
     want = oracle.load_tiles(om, src.cpu().numpy(), None, n)
-    for opts in (dict(stages=2, grid_wgs=132, flags=T.FLAG_CONTIGUOUS), dict(stages=2), dict()):
+    for opts in (dict(stages=2, grid_wgs=132, flags=T.FLAG_CONTIGUOUS | T.FLAG_WHOLE_BOX), dict(stages=2), dict()):
         got = gpu_load(m, None, n, **opts).cpu().numpy()
         assert (mm := first_mismatch(got, want, 32768)) is None, (opts, mm)
 
@@ -401,7 +401,8 @@ def test_wave_per_box_workgroup_shapes(box_kib):
     c = torch.from_numpy(coords).to(DEV)
     for stages in (1, 2):
         p = T.tmap_plan_launch("load", m, None, True, len(coords), stages=stages, flags=T.FLAG_WAVE_PER_BOX)
-        assert p["variant"] == "wave_per_box"
+        # one stage and boxes up to 8 KiB: the corner kernel
+        assert p["variant"] == ("corner" if stages == 1 and box_kib <= 8 else "wave_per_box")
         assert p["workgroups"] == -(-p["walkers"] // (4 if box_kib < 8 else 1))
         for grid in (0, 1, 3, 6):
             say(f"wave workgroups: box {box_kib} KiB stages={stages} grid={grid}")
@@ -638,21 +639,26 @@ def test_plan_query_reports_the_schedules():
     assert (p["variant"], p["band_boxes"], p["band_rows"], p["stages"], p["group"], p["regions"]) == \
         ("band", 8, 16, 3, 2, 2)
     p = plan("pad5d_f32", "store")
-    assert (p["variant"], p["stages"], p["slots"], p["group"]) == ("wave_per_box", 1, 8, 2)
+    assert (p["variant"], p["stages"], p["slots"], p["group"]) == ("corner", 1, 8, 2)
     # 8 KiB boxes: one wave to a workgroup, each with its own one-box ring
     assert p["walkers"] == 100000 // 2 and p["workgroups"] == p["walkers"]
     assert p["lds_bytes"] == 8192 + 32 + 4
     # 2 KiB boxes: four waves to a workgroup
     m = T.tmap_encode("f32", 2, 0x7F0000000000, [1000, 1000], [4000], [32, 16])
     p = T.tmap_plan_launch("load", m, None, True, 1000)
-    assert (p["variant"], p["slots"], p["walkers"]) == ("wave_per_box", 2, 125)
+    assert (p["variant"], p["slots"], p["walkers"]) == ("corner", 2, 125)
     assert p["workgroups"] == 32 and p["lds_bytes"] == 4 * 2048 + 4 * 32 + 4
-    assert plan("pad5d_f32", "load")["group"] == 4 and plan("pad5d_f32", "roundtrip")["group"] == 8
-    assert plan("pad5d_f32", "roundtrip")["variant"] == "wave_per_box"
+    assert plan("pad5d_f32", "load")["group"] == 2 and plan("pad5d_f32", "roundtrip")["group"] == 4
+    assert plan("pad5d_f32", "roundtrip")["variant"] == "corner"
+    assert plan("pad5d_f32", "roundtrip", stages=2)["variant"] == "wave_per_box"
     assert plan("pad5d_f32", "load", flags=T.FLAG_WHOLE_BOX)["variant"] == "ring"
     assert plan("pad5d_f32", "load", stages=3)["variant"] == "ring"
     assert plan("tile64_f32", "roundtrip")["variant"] == "ring"              # a 16 KiB box: the shared ring
-    assert plan("strips_f16", "load")["band_boxes"] == 0
+    # a cache-resident sweep on the band kernel: the tallest band that fits
+    # (half of a 32 KiB box), 2 stages x 2 units
+    p = plan("strips_f16", "load")
+    assert (p["variant"], p["band_boxes"], p["band_rows"], p["stages"], p["group"], p["regions"]) == \
+        ("band", 1, 32, 2, 2, 1)
     assert plan("strips_f16", "load", flags=T.FLAG_THREAD_COPY)["variant"] == "thread_copy"
     p = plan("sweep2g_u8", "load", flags=T.FLAG_PRODUCER_WAVE)
     assert (p["variant"], p["band_boxes"], p["workgroups"]) == ("producer_wave", 0, 8 * cus)
@@ -762,3 +768,58 @@ def test_other_modes_match_the_oracle(name):
             continue
         check_all_directions(name, alt, which, tag=mode)
     forget(name)
+
+
+@pytest.mark.parametrize("rank", [2, 3, 5])
+def test_corner_round_trip_between_layouts(rank):
+    """Round trips of scattered corners (in, across and outside both tensors)
+    from one tensor into another of a different size and pitch: the corner
+    kernel's instances for destinations that differ from the source, against
+    the oracle, for 8 KiB boxes (a wave to a workgroup) and 2 KiB boxes (four
+    waves to a workgroup), with the fp32 +1.0f update too."""
+    rng = np.random.default_rng(9500 + rank)
+    for box_kib in (2, 8):
+        es = 4
+        if rank == 2:
+            box, dims, ddims = ([32, 16] if box_kib == 2 else [64, 32]), [301, 77], [333, 60]
+        elif rank == 3:
+            box, dims, ddims = ([16, 8, 4] if box_kib == 2 else [32, 8, 8]), [77, 29, 21], [90, 25, 23]
+        else:
+            box, dims, ddims = ([8, 4, 4, 2, 2] if box_kib == 2 else [16, 8, 4, 2, 2]), [37, 11, 9, 5, 3], \
+                [41, 9, 10, 5, 4]
+
+        def layout(d):
+            strides, s = [], (-(-d[0] * es // 16) + 1) * 16
+            for k in range(1, len(d)):
+                strides.append(s)
+                s *= d[k]
+            return strides, s
+        strides, alloc = layout(dims)
+        dstrides, dalloc = layout(ddims)
+        src = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        host = src.cpu().numpy()
+        ms = enc("f32", src, dims, strides, box, (2, 2, 3))
+        corners = inputs.random_corners(dims, box, 700, seed=int(rng.integers(1 << 30)))
+        c = torch.from_numpy(corners).to(DEV)
+        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=(2, 2, 3))
+        omd = Map(es=es, dims=ddims, strides=dstrides, box=box, swizzle=(2, 2, 3))
+        for add in (False, True):
+            say(f"corner round trip between layouts: rank {rank}, box {box_kib} KiB, add={add}")
+            dst = dev_tensor(dalloc, fill_seed=int(rng.integers(1 << 30)))
+            want = dst.cpu().numpy().copy()
+            md = enc("f32", dst, ddims, dstrides, box, (2, 2, 3))
+            assert T.tmap_plan_launch("roundtrip", ms, md, True, len(corners))["variant"] == "corner"
+            if add:
+                T.tmap_roundtrip_add_f32(ms, md, c, len(corners), 1.0)
+                oracle.roundtrip_add_f32(om, host, omd, want, corners, len(corners), 1.0)
+            else:
+                T.tmap_roundtrip(ms, md, c, len(corners))
+                oracle.roundtrip(om, host, omd, want, corners, len(corners))
+            check_ok()
+            got = dst.cpu().numpy()
+            if add:
+                nan = np.isnan(want.view(np.float32))
+                assert np.array_equal(got.view(np.uint32)[~nan], want.view(np.uint32)[~nan]), "round trip +1.0f"
+                assert np.all(np.isnan(got.view(np.float32)[nan]))
+            else:
+                assert (mm := first_mismatch(got, want, 1 << 40)) is None, (rank, box_kib, mm)

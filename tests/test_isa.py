@@ -54,13 +54,13 @@ def kernels(tmp_path_factory):
 
 
 def _family(name):
-    m = re.search(r"(copy|wave|thread|ws|band)_kernel", name)
+    m = re.search(r"(copy|wave|thread|ws|band|corner)_kernel", name)
     return m.group(0) if m else None
 
 
 def test_every_variant_is_present(kernels):
     fams = {_family(k) for k in kernels}
-    assert {"copy_kernel", "wave_kernel", "thread_kernel", "ws_kernel", "band_kernel"} <= fams
+    assert {"copy_kernel", "wave_kernel", "thread_kernel", "ws_kernel", "band_kernel", "corner_kernel"} <= fams
     assert len(kernels) >= 200
 
 
@@ -68,7 +68,7 @@ def test_staged_kernels_load_tiles_straight_into_lds(kernels):
     for name, body in kernels.items():
         fam = _family(name)
         lds_dma = sum(1 for l in body if "buffer_load_dwordx4" in l and re.search(r"\blds\b", l))
-        if fam in ("copy_kernel", "wave_kernel", "ws_kernel", "band_kernel"):
+        if fam in ("copy_kernel", "wave_kernel", "ws_kernel", "band_kernel", "corner_kernel"):
             assert lds_dma > 0, name
         elif fam == "thread_kernel":
             assert lds_dma == 0, name

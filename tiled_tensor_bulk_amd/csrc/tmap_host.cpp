@@ -119,6 +119,7 @@ struct Plan {
     uint32_t lds;                 // bytes per workgroup
     uint32_t band_g, band_rows;   // band schedule (0: whole boxes)
     bool lean;                    // the band schedule runs the lean rank-2 band kernels
+    bool corner;                  // wave per box with one stage runs the corner kernels
 };
 
 uint32_t log2u(uint32_t v) {
@@ -191,6 +192,11 @@ bool band_lean_maps(int mode, const tmap::KArgs &a) {
     return true;
 }
 
+// Whether a tensor's span (outermost dim times its stride) is below the
+// size from which the band pays for DRAM page locality: it then stays in
+// the last-level cache.
+bool resident_span(const MapImpl &m) { return m.dims[m.rank - 1] * m.strides[m.rank - 1] < kBandMinSpan; }
+
 // want_rows: the band height asked for, 0 for the default of the direction
 // (lean: the maps suit the band kernel, whose defaults differ).  An explicit
 // height that does not fit leaves *why set and returns false; without one
@@ -201,8 +207,14 @@ bool band_fits(const MapImpl &m, const tmap::KArgs &a, bool roundtrip, uint32_t 
     if (flags & (TMAP_FLAG_THREAD_COPY | TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WAVE_PER_BOX | TMAP_FLAG_WHOLE_BOX))
         return false;
     if (m.rank < 2) return false;
-    const uint64_t span = m.dims[m.rank - 1] * m.strides[m.rank - 1];
-    if (!(flags & TMAP_FLAG_BAND) && span < kBandMinSpan) return false;
+    // a tensor that fits in the last-level cache takes the band only on the
+    // band kernel (or when TMAP_FLAG_BAND asks for it), and then in the
+    // tallest bands that fit: there the per-unit work, not DRAM page
+    // locality, decides (measured on MI355X over the 30 MB fp16 strips
+    // workload: 0.835 of peak in 32-row bands against 0.70 through registers
+    // and 0.60 for whole boxes on the generic ring)
+    const bool resident = !(flags & TMAP_FLAG_BAND) && resident_span(m);
+    if (resident && !lean) return false;
     for (int d = 2; d < tmap::kMaxRank; ++d)
         if (m.box[d] != 1) return false;
     const uint32_t rc = (uint32_t)m.box[0] * m.elem_size / 16u;  // 16-byte chunks per box row
@@ -212,6 +224,11 @@ bool band_fits(const MapImpl &m, const tmap::KArgs &a, bool roundtrip, uint32_t 
         const char *w = band_height_misfit(m, a, rc, rows, g, nb);
         if (w && why) *why = w;
         return w == nullptr;
+    }
+    if (resident) {
+        for (rows = 1u << 8; rows >= 1; rows /= 2)
+            if (rows <= m.box[1] && !band_height_misfit(m, a, rc, rows, g, nb)) return true;
+        return false;
     }
     const uint32_t first = lean ? (roundtrip ? kLeanRowsRoundtrip : kLeanRowsLoadStore)
                                 : (roundtrip ? kBandRowsRoundtrip : kBandRowsLoadStore);
@@ -256,8 +273,10 @@ constexpr uint32_t kKnownFlags = TMAP_FLAG_CONTIGUOUS | TMAP_FLAG_NONTEMPORAL | 
                                  TMAP_FLAG_DEBUG_POISON;
 
 // lean: the band schedule runs the band kernel of rank-2 sweeps.
+// elemwise: the swizzle moves data inside 16-byte chunks.
 tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
-                        const DeviceState &dev, bool band, bool lean, bool corners, Plan &pl) {
+                        const DeviceState &dev, bool band, bool lean, bool corners, bool elemwise, Plan &pl) {
+    const uint32_t flags0 = opts ? opts->flags : 0u;
     const uint32_t per_wave_pass = tmap::kWaves * tmap::kBlockBytes;  // bytes one slot per lane covers
     const uint32_t need = (m.box_bytes + per_wave_pass - 1) / per_wave_pass;
     int nslot = 1;
@@ -278,8 +297,10 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // (below) use two; the third stage's LDS holds a CU to three workgroups.
     // Measured on MI355X with 5 warm-up and 20 timed launches after an idle
     // gap, 2 GiB u8 round trip: 0.816-0.818 of peak at 3 stages x 2 units,
-    // 0.812-0.815 at 2 x 2 (four workgroups a CU), 0.756-0.764 at 3 x 4
-    if (lean && !(opts && opts->stages)) stages = 3;
+    // 0.812-0.815 at 2 x 2 (four workgroups a CU), 0.756-0.764 at 3 x 4.
+    // A tensor that stays in the last-level cache takes 2 stages (fp16
+    // strips: 0.835 against 0.78 at 3)
+    if (lean && !(opts && opts->stages)) stages = (resident_span(m) && !(flags0 & TMAP_FLAG_BAND)) ? 2 : 3;
     if (stages < 1 || stages > 4)
         return fail(TMAP_ERROR_INVALID_VALUE, "stages must be 1..4 (got %d)", stages);
     const uint32_t flags = opts ? opts->flags : 0u;
@@ -336,8 +357,13 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // 0.539 -> 0.557 of peak, load 0.625 -> 0.669 with the packed side's
     // non-temporal hints)
     if (!group && corners) {
+        // the corner kernel (one stage, whole-chunk swizzles) loads 8 KiB
+        // boxes fastest 2 to a wave (10^5 boxes: 0.71 of peak against 0.66
+        // with 4) and round-trips them 4 to a wave (0.336 against 0.31 with
+        // 8); the wave kernel 4 and 8
+        const bool corner = stages == 1 && !elemwise;
         if (wave_box && tmap::wave_group(nslot) == 1)
-            group = mode == tmap::kStore ? 2u : (mode == tmap::kLoad ? 4u : 8u);
+            group = mode == tmap::kStore ? 2u : (corner ? (mode == tmap::kLoad ? 2u : 4u) : (mode == tmap::kLoad ? 4u : 8u));
         else
             group = (wave_box && mode == tmap::kStore) ? 4u : 8u;
     }
@@ -378,7 +404,9 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // cost the 2 GiB round trip about 1%)
     uint32_t regions = (opts && opts->regions) ? opts->regions : 0u;
     if (regions > 64) return fail(TMAP_ERROR_INVALID_VALUE, "regions must be 1..64 (got %u)", regions);
-    if (!regions) regions = (band && mode != tmap::kRoundtrip) ? 2u : 1u;
+    if (!regions) regions = (band && mode != tmap::kRoundtrip && !(lean && resident_span(m) && !(flags0 & TMAP_FLAG_BAND)))
+                                ? 2u
+                                : 1u;
     pl.lds = lds;
     pl.nslot = nslot;
     pl.stages = thread_copy ? 0
@@ -429,11 +457,16 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     if (why) return fail(TMAP_ERROR_INVALID_VALUE, "%s", why);
     if (band) band_setup(swept, a, g, nb, rows);
     const bool lean = band && lean_maps;
-    tmap_status st = plan_launch(mode, swept, a.n_tiles, opts, dev, band, lean, a.coords != nullptr, pl);
+    tmap_status st =
+        plan_launch(mode, swept, a.n_tiles, opts, dev, band, lean, a.coords != nullptr, a.elemwise != 0, pl);
     if (st != TMAP_SUCCESS) return st;
     pl.band_g = band ? g : 0u;
     pl.band_rows = band ? rows : 0u;
     pl.lean = lean;
+    // explicit corners, one wave per box with one stage, boxes of at most
+    // 8 KiB and a swizzle that moves whole chunks: the corner kernels, which
+    // hold each drained box in registers while the next one loads
+    pl.corner = a.coords && pl.stages == 31 && pl.nslot <= 8 && !a.elemwise;
     a.grid = pl.grid;
     a.regions = pl.regions;
     a.flags = opts ? opts->flags : 0u;
@@ -482,6 +515,17 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     // maps of rank <= 2 run the variants that only walk two dimensions
     const bool r2 = a.src.rank <= 2 && a.dst.rank <= 2;
     int rc = (int)hipErrorInvalidValue;
+    if (pl.corner) {
+        const int dims = r2 ? 2 : 5;
+        rc = mode == tmap::kLoad    ? tmap::launch_corner_load(pl.nslot, dims, a, stream)
+             : mode == tmap::kStore ? tmap::launch_corner_store(pl.nslot, dims, a, stream)
+                                    : tmap::launch_corner_roundtrip(pl.nslot, dims, a, stream);
+        if (rc != 0) {
+            (void)hipGetLastError();
+            return fail(TMAP_ERROR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)rc));
+        }
+        return ok();
+    }
     if (pl.lean) {
         const int st = pl.stages - 20;  // band launch codes are 20 + stages
         rc = mode == tmap::kLoad    ? tmap::launch_band_load(st, a, stream)
@@ -899,6 +943,7 @@ tmap_status tmap_plan_launch(tmap_direction direction, const tmap_t *swept, cons
     if (st != TMAP_SUCCESS) return st;
     const int code = pl.stages;
     out->variant = code == 0 ? TMAP_VARIANT_THREAD_COPY
+                   : pl.corner ? TMAP_VARIANT_CORNER
                    : code > 30 ? TMAP_VARIANT_WAVE_PER_BOX
                    : (code > 10 && code < 20) ? TMAP_VARIANT_PRODUCER_WAVE
                    : pl.lean ? TMAP_VARIANT_BAND
@@ -909,7 +954,9 @@ tmap_status tmap_plan_launch(tmap_direction direction, const tmap_t *swept, cons
     out->slots = (uint32_t)pl.nslot;
     out->group = a.group;
     out->walkers = pl.grid;
-    const uint32_t wg = out->variant == TMAP_VARIANT_WAVE_PER_BOX ? (uint32_t)tmap::wave_group(pl.nslot) : 1u;
+    const uint32_t wg = (out->variant == TMAP_VARIANT_WAVE_PER_BOX || out->variant == TMAP_VARIANT_CORNER)
+                            ? (uint32_t)tmap::wave_group(pl.nslot)
+                            : 1u;
     out->workgroups = (pl.grid + wg - 1) / wg;
     out->regions = pl.regions;
     out->lds_bytes = pl.lds;

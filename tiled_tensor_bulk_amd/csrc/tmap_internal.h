@@ -152,6 +152,14 @@ uint32_t *noalloc_status(int dev);
 // Record a failure's status and detail text for tmap_last_error_detail().
 tmap_status record_failure(tmap_status st, const char *detail);
 
+// Boxes at explicit corners, one wave per box with one stage, boxes of at
+// most 8 KiB, swizzles that move whole chunks: the corner kernels
+// (tmap_corner.h), nslot 1..8, dims 2 for maps of rank <= 2 else 5, one
+// translation unit per direction (tmap_corner_{load,store,roundtrip}.hip).
+int launch_corner_load(int nslot, int dims, const KArgs &a, void *stream);
+int launch_corner_store(int nslot, int dims, const KArgs &a, void *stream);
+int launch_corner_roundtrip(int nslot, int dims, const KArgs &a, void *stream);
+
 // LDS bytes one workgroup of a variant uses: the ring plus the barrier words.
 inline uint32_t variant_lds_bytes(int stages, int nslot) {
     return (uint32_t)stages * (uint32_t)nslot * kWaves * kBlockBytes + 64u;

@@ -61,7 +61,7 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-_KERNEL = re.compile(r"\b(copy|wave|thread|ws|band)_kernel<")
+_KERNEL = re.compile(r"\b(copy|wave|thread|ws|band|corner)_kernel<")
 
 
 def is_copy_kernel(name: str) -> bool:
@@ -85,6 +85,12 @@ def short(name: str) -> str:
         extra = ", +addend" if m.group(5) == "true" else ""
         return (f"tmap band_kernel<{mode}, stages={m.group(2)}, nt loads={m.group(3)}, "
                 f"nt stores={m.group(4)}{extra}>")
+    m = re.search(r"corner_kernel<(\d+), (\d+), (\d+), (true|false), (true|false), (true|false)>", name)
+    if m:
+        mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
+        extra = ", +addend" if m.group(6) == "true" else ""
+        return (f"tmap corner_kernel<{mode}, nslot={m.group(2)}, dims={m.group(3)}, nt loads={m.group(4)}, "
+                f"nt stores={m.group(5)}{extra}>")
     if "copyBuffer" in name:
         return "hip copyBuffer (torch d2d copy)"
     return (name[:60] + "...") if len(name) > 63 else name
