@@ -72,9 +72,17 @@ def test_counters_average_the_copy_kernel_dispatches_only(tmp_path):
 
 def test_copy_kernel_names_cover_every_variant():
     for k in ("copy_kernel<0, 1, 8, 5, false>", "wave_kernel<1, 1, 8, 5>", "thread_kernel<2, 4, 2>",
-              "ws_kernel<0, 2, 4, 2>"):
+              "ws_kernel<0, 2, 4, 2>", "band_kernel<2, 3, true, true, false>",
+              "corner_kernel<2, 8, 5, false, false, false, true>"):
         assert ps.is_copy_kernel(f"void tmap::(anonymous namespace)::{k}(tmap::KArgs)")
     assert not ps.is_copy_kernel("__amd_rocclr_copyBuffer")
+    full = "void tmap::(anonymous namespace)::{}(tmap::KArgs)".format
+    assert ps.short(full("band_kernel<2, 3, true, true, true>")) == \
+        "tmap band_kernel<roundtrip, stages=3, nt loads=true, nt stores=true, +addend>"
+    assert ps.short(full("corner_kernel<0, 8, 5, false, true, false, false>")) == \
+        "tmap corner_kernel<load, nslot=8, dims=5, nt loads=false, nt stores=true>"
+    assert ps.short(full("corner_kernel<2, 8, 5, false, false, false, true>")) == \
+        "tmap corner_kernel<roundtrip, nslot=8, dims=5, nt loads=false, nt stores=false, same maps>"
 
 
 def test_bench_reports_traffic_only_for_the_current_sources(tmp_path, monkeypatch):

@@ -85,10 +85,11 @@ def short(name: str) -> str:
         extra = ", +addend" if m.group(5) == "true" else ""
         return (f"tmap band_kernel<{mode}, stages={m.group(2)}, nt loads={m.group(3)}, "
                 f"nt stores={m.group(4)}{extra}>")
-    m = re.search(r"corner_kernel<(\d+), (\d+), (\d+), (true|false), (true|false), (true|false)>", name)
+    m = re.search(r"corner_kernel<(\d+), (\d+), (\d+), (true|false), (true|false), (true|false)(?:, (true|false))?>",
+                  name)
     if m:
         mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
-        extra = ", +addend" if m.group(6) == "true" else ""
+        extra = (", +addend" if m.group(6) == "true" else "") + (", same maps" if m.group(7) == "true" else "")
         return (f"tmap corner_kernel<{mode}, nslot={m.group(2)}, dims={m.group(3)}, nt loads={m.group(4)}, "
                 f"nt stores={m.group(5)}{extra}>")
     if "copyBuffer" in name:
