@@ -592,6 +592,63 @@ def test_largest_coordinates():
     assert (mm := first_mismatch(d, want_dst, 1 << 40)) is None, mm
 
 
+def test_corner_offsets_far_and_wrapped():
+    """The corner kernel sums corner offsets in 32 bits when both maps lie
+    within 2 GiB of their bases, else in 64.  In the 32-bit case, corners
+    far outside the tensor wrap to meaningless offsets whose boxes must
+    still read as zeros and write nothing; in the 64-bit case, boxes more
+    than 2 GiB from the base must land where they belong.  Load, store and
+    round trip of 8 KiB boxes (rank 5) against the oracle."""
+    big = 1 << 31
+    i32 = np.iinfo(np.int32)
+    for case in ("wrapped", "far"):
+        if case == "wrapped":
+            # the padded 5-D fp32 tensor (103 MB): corners whose offsets overflow 32 bits
+            w = inputs.WORKLOADS["pad5d_f32"]
+            es, dims, strides, box, dtype, alloc = 4, list(w.dims), list(w.strides), list(w.box), "f32", w.alloc_bytes
+            extreme = [[0, i32.max, 0, 0, 0], [5, 0, i32.min, 0, 0], [i32.min, i32.min, 3, 1, 0],
+                       [100, 60, 30, i32.max, 6], [7, 9, 11, 5, i32.min], [i32.max] * 5, [i32.min] * 5,
+                       [-31, -7, -3, -1, 0], [128, 64, 32, 12, 6], [1 << 28, 0, 0, 0, 0], [0, 0, 0, 0, 1 << 29]]
+            rand = inputs.random_corners(dims, box, 500, seed=4242)
+        else:
+            # a 2 GiB u8 tensor seen as 65536 x 256 x 128: boxes up to the last byte
+            es, dims, strides, box, dtype, alloc = 1, [65536, 256, 128], [65536, 65536 * 256], [128, 64, 1], "u8", big
+            extreme = [[65536 - 128, 256 - 64, 127], [65536 - 100, 200, 127], [0, 0, 127], [-64, -32, 127],
+                       [65500, 250, 126], [i32.max, 0, 127], [0, 0, i32.max], [i32.min, 5, 64], [77, 3, 128]]
+            rng = np.random.default_rng(4343)
+            rand = np.stack([rng.integers(-128, 65536, 300), rng.integers(-64, 256, 300),
+                             rng.integers(100, 129, 300)], axis=1)
+        corners = np.ascontiguousarray(np.concatenate([np.array(extreme, np.int64), rand.astype(np.int64)]), np.int32)
+        n = len(corners)
+        c = torch.from_numpy(corners).to(DEV)
+        src = dev_tensor(alloc, fill_seed=91)
+        host = src.cpu().numpy()
+        m = enc(dtype, src, dims, strides, box)
+        om = Map(es=es, dims=dims, strides=strides, box=box)
+        assert T.tmap_plan_launch("load", m, None, True, n)["variant"] == "corner"
+        say(f"corner kernel, {case} offsets: load")
+        got = gpu_load(m, corners, n).cpu().numpy()
+        want = oracle.load_tiles(om, host, corners, n)
+        bb = T.tmap_box_bytes(m)
+        assert (mm := first_mismatch(got, want, bb)) is None, (case, "load", mm)
+        say(f"corner kernel, {case} offsets: store")
+        dst = dev_tensor(alloc, fill_seed=92)
+        want_dst = dst.cpu().numpy().copy()
+        T.tmap_store_tiles(enc(dtype, dst, dims, strides, box), c, n, torch.from_numpy(want).to(DEV))
+        check_ok()
+        oracle.store_tiles(om, want_dst, corners, n, want)
+        assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, (case, "store", mm)
+        say(f"corner kernel, {case} offsets: round trip")
+        dst = dev_tensor(alloc, fill_seed=93)
+        want_dst = dst.cpu().numpy().copy()
+        T.tmap_roundtrip(m, enc(dtype, dst, dims, strides, box), c, n)
+        check_ok()
+        oracle.roundtrip(om, host, om, want_dst, corners, n)
+        assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, (case, "roundtrip", mm)
+        del src, dst, host, want_dst
+        torch.cuda.empty_cache()
+
+
 def test_binding_rejects_buffers_the_copy_would_overrun():
     """Given tensors, the binding checks sizes before launching: a packed
     buffer or corner array too small for n_tiles, a host tensor or int64
@@ -642,13 +699,16 @@ def test_plan_query_reports_the_schedules():
     assert (p["variant"], p["stages"], p["slots"], p["group"]) == ("corner", 1, 8, 2)
     # 8 KiB boxes: one wave to a workgroup, each with its own one-box ring
     assert p["walkers"] == 100000 // 2 and p["workgroups"] == p["walkers"]
-    assert p["lds_bytes"] == 8192 + 32 + 4
+    assert p["lds_bytes"] == 8192 + 8
     # 2 KiB boxes: four waves to a workgroup
     m = T.tmap_encode("f32", 2, 0x7F0000000000, [1000, 1000], [4000], [32, 16])
     p = T.tmap_plan_launch("load", m, None, True, 1000)
     assert (p["variant"], p["slots"], p["walkers"]) == ("corner", 2, 125)
-    assert p["workgroups"] == 32 and p["lds_bytes"] == 4 * 2048 + 4 * 32 + 4
-    assert plan("pad5d_f32", "load")["group"] == 2 and plan("pad5d_f32", "roundtrip")["group"] == 4
+    assert p["workgroups"] == 32 and p["lds_bytes"] == 4 * 2048 + 4 * 8
+    # the 8 KiB load: one box to a wave, 11 KiB of LDS to a workgroup
+    p = plan("pad5d_f32", "load")
+    assert (p["group"], p["lds_bytes"], p["walkers"]) == (1, 11264, 100000)
+    assert plan("pad5d_f32", "roundtrip")["group"] == 2
     assert plan("pad5d_f32", "roundtrip")["variant"] == "corner"
     assert plan("pad5d_f32", "roundtrip", stages=2)["variant"] == "wave_per_box"
     assert plan("pad5d_f32", "load", flags=T.FLAG_WHOLE_BOX)["variant"] == "ring"

@@ -530,29 +530,50 @@ __device__ __forceinline__ void store_chunk_edge_es(uint32_t es, const uint8_t *
     }
 }
 
+// The kernel arguments, read again from the argument segment where this is
+// called: the compiler cannot tell the address from the one it loaded
+// before, so it keeps no register copy of the fields read through it alive
+// across a loop.  For slow paths that need fields the hot loop does not.
+// The kernels take one argument, the KArgs, at the start of the segment.
+__device__ __forceinline__ const KArgs &reread(const KArgs &) {
+    typedef const __attribute__((address_space(4))) uint8_t const_u8;
+    const_u8 *p = (const_u8 *)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    return *(const KArgs *)(const uint8_t *)p;
+}
+
+// n / d for n < 2^16, given magic = ceil(2^32 / d), or 0 for d == 1.
+__device__ __forceinline__ uint32_t div_small(uint32_t n, uint32_t magic) {
+    return magic ? __umulhi(n, magic) : n;
+}
+
 // In-box byte offset (in map m) and packed indices of logical chunk q.
+// The offset wraps modulo 2^32 like every in-box offset (box footprints
+// stay below 2 GiB), so the 32-bit products suffice.
 template <int R>
 __device__ __forceinline__ void chunk_info_of(const KArgs &a, uint32_t q, const KMap &m, uint32_t &off,
                                               uint32_t &w0, uint32_t &w1) {
-    const uint32_t row = q / a.row_chunks;
-    const uint32_t x0 = (q - row * a.row_chunks) * a.k_el;
+    const uint32_t row = div_small(q, a.rc_magic);
+    const uint32_t x0 = (q - row * a.row_chunks) << a.lk_el;
     uint32_t i[kMaxRank] = {x0, 0, 0, 0, 0};
     uint32_t rest = row;
 #pragma unroll
     for (int d = 1; d < R; ++d) {
-        const uint32_t b = m.box[d];
-        const uint32_t qq = rest / b;
-        i[d] = rest - qq * b;
+        const uint32_t qq = div_small(rest, a.box_magic[d]);
+        i[d] = rest - qq * m.box[d];
         rest = qq;
     }
-    off = inbox_offset<R>(i, m);
+    uint32_t o = 0;
+#pragma unroll
+    for (int d = 0; d < R; ++d) o += i[d] * (uint32_t)m.strides[d];
+    off = o;
     w0 = x0 | (i[1] << 16);
     w1 = i[2] | (i[3] << 8) | (i[4] << 16);
 }
 
 // Logical chunk held by LDS slot p (the swizzle is its own inverse).
 __device__ __forceinline__ uint32_t logical_chunk_of(const KArgs &a, uint32_t p, const KMap &m) {
-    return swizzle(p * a.k_el, m.swz_b, m.swz_m, m.swz_s) / a.k_el;
+    return swizzle(p << a.lk_el, m.swz_b, m.swz_m, m.swz_s) >> a.lk_el;
 }
 
 // ---------------------------------------------------------------- the kernel

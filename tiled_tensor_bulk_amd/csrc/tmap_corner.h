@@ -42,10 +42,63 @@
 namespace tmap {
 namespace {
 
+// Byte offset of a box corner from the map's base.  With small offsets (the
+// host has checked that every corner whose box touches the tensor is less
+// than 2 GiB from the base in every direction) the sum is taken in 32 bits:
+// a box that does not touch the tensor gets a meaningless offset, but none
+// of its chunks is read or written.
+template <int R>
+__device__ __forceinline__ int64_t corner_offset(const KArgs &A, const KMap &m, const int32_t (&c)[R]) {
+    if (A.off32) {
+        uint32_t o = 0;
+#pragma unroll
+        for (int d = 0; d < R; ++d) o += (uint32_t)c[d] * (uint32_t)m.strides[d];
+        return (int64_t)(int32_t)o;
+    }
+    int64_t o = 0;
+#pragma unroll
+    for (int d = 0; d < R; ++d) o += (int64_t)c[d] * (int64_t)m.strides[d];
+    return o;
+}
+
+// Whether the box at corner c lies wholly inside the tensor.
+template <int R>
+__device__ __forceinline__ bool corner_inside(const KMap &m, const int32_t (&c)[R]) {
+    bool in = true;
+#pragma unroll
+    for (int d = 0; d < R; ++d) in = in & (c[d] >= 0) & (c[d] <= m.lim[d]);
+    return in;
+}
+
+// Per dimension, the window [lo, hi) of box indices inside the tensor, in
+// 32-bit scalar arithmetic: dims <= 2^31 and box extents <= 256, so every
+// difference taken below fits (a corner below -box or past dims gives an
+// empty window).
+template <int R>
+__device__ __forceinline__ Win<R> corner_window(const KMap &m, const int32_t (&c)[R]) {
+    Win<R> w;
+#pragma unroll
+    for (int d = 0; d < R; ++d) {
+        const int32_t cd = c[d];
+        const uint32_t b = m.box[d];
+        const uint32_t lo = cd >= 0 ? 0u : (cd <= -(int32_t)b ? b : 0u - (uint32_t)cd);
+        const int32_t lim = (int32_t)(m.dims[d] - b);           // dims - box, negative if the box is larger
+        const int32_t hr = (int32_t)(m.dims[d] - (uint32_t)cd);  // dims - c when c > lim: below box
+        w.lo[d] = lo;
+        w.hi[d] = cd <= lim ? b : (hr < (int32_t)lo ? lo : (uint32_t)hr);
+    }
+    return w;
+}
+
 // SAME: a round trip whose destination map has the source's dims and strides
 // (only its base differs), so the drain takes the source map's offsets,
-// interior test and windows, which also frees the scalar registers the
-// destination's fields would take.
+// interior test and windows.
+//
+// Across the loop a wave holds its tile positions, the corners of the box
+// in the stage and of the next one, and per-slot vectors: each phase reads
+// the kernel-argument fields it needs again (scalar loads that hit the
+// constant cache), so that the map fields of both sides do not have to stay
+// in scalar registers for the whole loop.
 template <int MODE, int NSLOT, int R, bool NTL, bool NTS, bool ADD, bool SAME = false>
 struct CornerCopier {
     static_assert(NSLOT <= 8, "the held image takes 4 VGPRs per slot");
@@ -57,7 +110,7 @@ struct CornerCopier {
     // in this wave's sequence, for the box to fill next and the box to drain
     int64_t ft, ct;
     uint32_t fk, ck;
-    int32_t fc[R];  // corner of the box under the fill cursor
+    int32_t fc[R];  // corner of the box under the fill cursor, read one fill ahead
     int32_t sc[R];  // corner of the box in the stage
     bool edge;      // the box in the stage needs its cut chunks patched
     bool behind;    // exactly NSLOT stores (one drain) were issued after the stage's loads
@@ -71,10 +124,10 @@ struct CornerCopier {
 
     __device__ __forceinline__ CornerCopier(const KArgs &args, uint64_t *b) : a(args), bar(b) {}
 
-    __device__ __forceinline__ const KMap &swept() const { return MODE == kStore ? a.dst : a.src; }
+    __device__ __forceinline__ static const KMap &swept(const KArgs &A) { return MODE == kStore ? A.dst : A.src; }
 
-    // The destination's dims, strides and span (its base is always a.dst's).
-    __device__ __forceinline__ const KMap &dst_shape() const { return SAME ? a.src : a.dst; }
+    // The destination's dims, strides and span (its base is always A.dst's).
+    __device__ __forceinline__ static const KMap &dst_shape(const KArgs &A) { return SAME ? A.src : A.dst; }
 
     // the tiles are dealt to the waves as the other variants deal them to
     // their walkers: groups of a.group consecutive tiles, round robin, as
@@ -104,7 +157,7 @@ struct CornerCopier {
         if (!walker) cnt = 0;
         ft = ct = t0;
         fk = ck = 0;
-        const KMap &sw = swept();
+        const KMap &sw = swept(a);
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
             const uint32_t p = (uint32_t)j * 64u + lane;
@@ -128,71 +181,73 @@ struct CornerCopier {
                 }
             }
         }
-        if (cnt > 0) corner_of(ft, fc);
+        if (cnt > 0) corner_of(a, ft, fc);
     }
 
     // Corner of tile t: uniform scalar loads through the constant address
     // space, so they never wait behind the direct-to-LDS loads (vmcnt).
-    __device__ __forceinline__ void corner_of(int64_t t, int32_t (&c)[R]) const {
+    __device__ __forceinline__ static void corner_of(const KArgs &A, int64_t t, int32_t (&c)[R]) {
         typedef const __attribute__((address_space(4))) int32_t const_i32;
-        const int r = swept().rank;
-        const_i32 *p = (const_i32 *)(a.coords) + t * r;
+        const int r = swept(A).rank;
+        const_i32 *p = (const_i32 *)(A.coords) + t * r;
 #pragma unroll
         for (int d = 0; d < R; ++d) c[d] = d < r ? p[d] : 0;
     }
 
     // Next tile of the sequence: +1 inside a group, big_step after its last.
-    __device__ __forceinline__ void advance(int64_t &t, uint32_t &k) const {
-        const bool big = (k & a.group_mask) == a.group_mask;
+    __device__ __forceinline__ static void advance(const KArgs &A, int64_t &t, uint32_t &k) {
+        const bool big = (k & A.group_mask) == A.group_mask;
         k += 1;
-        t += big ? a.big_step : 1;
+        t += big ? A.big_step : 1;
     }
 
     // slot j's direct-to-LDS load: lane l's 16 bytes at voff land at m0 + j KiB + 16 l
-    __device__ __forceinline__ void dma(uint64_t base, uint32_t nrec, uint32_t m0, int j, uint32_t voff) const {
+    __device__ __forceinline__ static void dma(uint64_t base, uint32_t nrec, uint32_t m0, int j, uint32_t voff) {
         dma_lds_hint<NTL>(base, nrec, m0 + (uint32_t)j * kBlockBytes, voff);
     }
 
     // Issue the loads of the box under the fill cursor into the stage.
     __device__ __forceinline__ void fill(uint8_t *stage, int64_t nfill) {
+        const KArgs &A = reread(a);
+#pragma unroll
+        for (int d = 0; d < R; ++d) sc[d] = fc[d];
         if (a.flags & TMAP_FLAG_DEBUG_POISON) poison_blocks(stage, NSLOT, 1, lane);
         const uint32_t budget = a.src.box_bytes + ((a.flags & TMAP_FLAG_INJECT_BUDGET_MISMATCH) ? 16u : 0u);
         bar_arrive_expect(bar, budget, lane, 1);
-#pragma unroll
-        for (int d = 0; d < R; ++d) sc[d] = fc[d];
         const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_t *)stage;
         if (MODE == kStore) {
+            // the packed images' fields stay in registers: the loads issue
+            // without waiting for an argument read
             const uint64_t base = (uint64_t)a.packed + (uint64_t)ft * a.dst.box_bytes;
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) dma(base, a.dst.box_bytes, m0, j, soff[j]);
             edge = false;
         } else {
-            const Place pl = place<R>(a.src, sc);
-            const uint64_t base = a.src.base + (uint64_t)pl.off;
-            if (pl.interior) {
+            const uint64_t base = A.src.base + (uint64_t)corner_offset<R>(A, A.src, sc);
+            if (corner_inside<R>(A.src, sc)) {
 #pragma unroll
-                for (int j = 0; j < NSLOT; ++j) dma(base, a.src.span, m0, j, soff[j]);
+                for (int j = 0; j < NSLOT; ++j) dma(base, A.src.span, m0, j, soff[j]);
                 edge = false;
             } else {
-                const Win<R> w = window<R>(a.src, sc);
+                const Win<R> w = corner_window<R>(A.src, sc);
 #pragma unroll
                 for (int j = 0; j < NSLOT; ++j)
-                    dma(base, a.src.span, m0, j, classify<R>(w0[j], w1[j], w, a.k_el) == kFull ? soff[j] : kOob);
-                edge = cuts_chunks(w);
+                    dma(base, A.src.span, m0, j, classify<R>(w0[j], w1[j], w, A.k_el) == kFull ? soff[j] : kOob);
+                edge = cuts_chunks(A, w);
             }
         }
-        advance(ft, fk);
+        advance(a, ft, fk);
         // read the next corner now, while this box's loads fly (never past
         // this wave's last tile: an explicit-corner array ends there)
-        if (nfill + 1 < cnt) corner_of(ft, fc);
+        if (nfill + 1 < cnt) corner_of(A, ft, fc);
     }
 
     // Whether window w cuts through a 16-byte chunk in dimension 0.
-    __device__ __forceinline__ bool cuts_chunks(const Win<R> &w) const {
+    __device__ __forceinline__ static bool cuts_chunks(const KArgs &A, const Win<R> &w) {
         bool rows = true;
 #pragma unroll
         for (int d = 1; d < R; ++d) rows = rows & (w.lo[d] < w.hi[d]);
-        return rows & (w.lo[0] < w.hi[0]) & (((w.lo[0] | w.hi[0]) & (a.k_el - 1u)) != 0u);
+        return rows & (w.lo[0] < w.hi[0]) & (((w.lo[0] | w.hi[0]) & (A.k_el - 1u)) != 0u);
     }
 
     // Land the box in the stage: wait for its loads, patch its cut chunks,
@@ -208,17 +263,18 @@ struct CornerCopier {
         if (MODE != kStore && edge) {
             // slow path, kept out of the unrolled slot arrays: each slot's
             // chunk is recomputed
-            const Place pl = place<R>(a.src, sc);
-            const Win<R> w = window<R>(a.src, sc);
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(a.src.base + (uint64_t)pl.off, a.src.span);
+            const KArgs &A = reread(a);
+            const Win<R> w = corner_window<R>(A.src, sc);
+            const __amdgpu_buffer_rsrc_t r =
+                make_rsrc(A.src.base + (uint64_t)corner_offset<R>(A, A.src, sc), A.src.span);
 #pragma unroll 1
             for (int j = 0; j < NSLOT; ++j) {
                 const uint32_t p = (uint32_t)j * 64u + lane;
-                if (p >= a.n_chunks) continue;
+                if (p >= A.n_chunks) continue;
                 uint32_t off, u0, u1;
-                chunk_info_of<R>(a, logical_chunk_of(a, p, a.src), a.src, off, u0, u1);
-                if (classify<R>(u0, u1, w, a.k_el) == kPart)
-                    load_chunk_edge_es(a.src.elem_size, stage + p * 16u, off, u0 & 0xFFFFu, w.lo[0], w.hi[0], r);
+                chunk_info_of<R>(A, logical_chunk_of(A, p, A.src), A.src, off, u0, u1);
+                if (classify<R>(u0, u1, w, A.k_el) == kPart)
+                    load_chunk_edge_es(A.src.elem_size, stage + p * 16u, off, u0 & 0xFFFFu, w.lo[0], w.hi[0], r);
             }
         }
         __builtin_amdgcn_s_waitcnt(kWaitLgkm);
@@ -231,73 +287,73 @@ struct CornerCopier {
     }
 
     template <typename Rs>
-    __device__ __forceinline__ void store16(const i32x4 &v, Rs r, uint32_t off) const {
+    __device__ __forceinline__ static void store16(const i32x4 &v, Rs r, uint32_t off) {
         if constexpr (NTS)
             __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2);
         else
             __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
     }
 
-    // Chunks of the box in the stage (corner c) that the destination's
-    // dimension-0 edge cuts through: store their inside elements, read from
-    // the stage, before the stage is refilled (so these stores precede the
-    // next box's loads and the next landing need not count them).  Slow
-    // path, kept out of the unrolled slot arrays.
+    // Chunks of the box in the stage that the destination's dimension-0
+    // edge cuts through: store their inside elements, read from the stage,
+    // before the stage is refilled (so these stores precede the next box's
+    // loads and the next landing need not count them).  Slow path, kept out
+    // of the unrolled slot arrays.
     __device__ __forceinline__ void drain_cut_chunks(const uint8_t *stage, const int32_t (&c)[R]) const {
         if (MODE == kLoad) return;
-        const KMap &dm = dst_shape();
-        const Place pl = place<R>(dm, c);
-        if (pl.interior) return;
-        const Win<R> w = window<R>(dm, c);
-        if (!cuts_chunks(w)) return;
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(a.dst.base + (uint64_t)pl.off, dm.span);
+        const KArgs &A = reread(a);
+        const KMap &dm = dst_shape(A);
+        if (corner_inside<R>(dm, c)) return;
+        const Win<R> w = corner_window<R>(dm, c);
+        if (!cuts_chunks(A, w)) return;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(A.dst.base + (uint64_t)corner_offset<R>(A, dm, c), dm.span);
 #pragma unroll 1
         for (int j = 0; j < NSLOT; ++j) {
             const uint32_t p = (uint32_t)j * 64u + lane;
-            if (p >= a.n_chunks) continue;
+            if (p >= A.n_chunks) continue;
             uint32_t off, u0, u1;
-            chunk_info_of<R>(a, logical_chunk_of(a, p, dm), dm, off, u0, u1);
-            if (classify<R>(u0, u1, w, a.k_el) == kPart)
-                store_chunk_edge_es(a.dst.elem_size, stage + p * 16u, off, u0 & 0xFFFFu, w.lo[0], w.hi[0], r, ADD,
-                                    a.addend);
+            chunk_info_of<R>(A, logical_chunk_of(A, p, dm), dm, off, u0, u1);
+            if (classify<R>(u0, u1, w, A.k_el) == kPart)
+                store_chunk_edge_es(A.dst.elem_size, stage + p * 16u, off, u0 & 0xFFFFu, w.lo[0], w.hi[0], r, ADD,
+                                    A.addend);
         }
     }
 
-    // Store the whole chunks of the held image of the box under the consume
-    // cursor (corner c): always NSLOT stores per lane, chunks with nothing to
-    // write going to the out-of-range offset, so that the next landing can
-    // count them.
+    // Store the whole chunks of the held image of the box under the drain
+    // cursor: always NSLOT stores per lane, chunks with nothing to write
+    // going to the out-of-range offset, so that the next landing can count
+    // them.
     __device__ __forceinline__ void drain(i32x4 (&v)[NSLOT], const int32_t (&c)[R], bool after_fill) {
         // the next landing may leave these NSLOT stores in flight when they
         // are the only operations issued after its loads
         behind = after_fill;
+        const KArgs &A = reread(a);
         if (MODE == kLoad) {
             const __amdgpu_buffer_rsrc_t r =
-                make_rsrc((uint64_t)a.packed + (uint64_t)ct * a.src.box_bytes, a.src.box_bytes);
+                make_rsrc((uint64_t)A.packed + (uint64_t)ct * A.src.box_bytes, A.src.box_bytes);
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) store16(v[j], r, doff[j]);
-            advance(ct, ck);
+            advance(a, ct, ck);
             return;
         }
         if constexpr (ADD) {
             // the tile update of the fused round trip, in the held registers
             typedef __attribute__((ext_vector_type(4))) float f32x4;
 #pragma unroll
-            for (int j = 0; j < NSLOT; ++j) v[j] = __builtin_bit_cast(i32x4, __builtin_bit_cast(f32x4, v[j]) + a.addend);
+            for (int j = 0; j < NSLOT; ++j) v[j] = __builtin_bit_cast(i32x4, __builtin_bit_cast(f32x4, v[j]) + A.addend);
         }
-        const KMap &dm = dst_shape();
-        const Place pl = place<R>(dm, c);
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(a.dst.base + (uint64_t)pl.off, dm.span);
-        if (pl.interior) {
+        const KMap &dm = dst_shape(A);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(A.dst.base + (uint64_t)corner_offset<R>(A, dm, c), dm.span);
+        if (corner_inside<R>(dm, c)) {
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) store16(v[j], r, doff[j]);
         } else {
-            const Win<R> w = window<R>(dm, c);
+            const Win<R> w = corner_window<R>(dm, c);
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j)
-                store16(v[j], r, classify<R>(w0[j], w1[j], w, a.k_el) == kFull ? doff[j] : kOob);
+                store16(v[j], r, classify<R>(w0[j], w1[j], w, A.k_el) == kFull ? doff[j] : kOob);
         }
-        advance(ct, ck);
+        advance(a, ct, ck);
     }
 };
 
@@ -321,6 +377,11 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner_kernel(const KA
     i32x4 held[NSLOT];
     cp.fill(stage, 0);
     for (int64_t k = 0; k < cp.cnt; ++k) {
+        // the per-slot box indices are unpacked where they are tested, not
+        // once before the loop: unpacked, they would take four times the
+        // vector registers for the whole loop
+#pragma unroll
+        for (int j = 0; j < NSLOT; ++j) asm volatile("" : "+v"(cp.w0[j]), "+v"(cp.w1[j]));
         if (!cp.land(stage)) {
             if (cp.lane == 0) __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
@@ -392,8 +453,9 @@ int launch_corner_mode(int nslot, const KArgs &a, void *stream) {
     const uint32_t wg = (uint32_t)wave_group(nslot);
     KArgs copy = a;
     void *args[] = {&copy};
-    return (int)hipLaunchKernel((const void *)fn, dim3((a.grid + wg - 1) / wg), dim3(64 * wg), args, 0,
-                                (hipStream_t)stream);
+    // the reserve is allocated as dynamic LDS the kernel does not touch
+    return (int)hipLaunchKernel((const void *)fn, dim3((a.grid + wg - 1) / wg), dim3(64 * wg), args,
+                                corner_lds_reserve(MODE, nslot), (hipStream_t)stream);
 }
 
 }  // namespace

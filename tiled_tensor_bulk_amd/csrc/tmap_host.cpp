@@ -358,12 +358,12 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // non-temporal hints)
     if (!group && corners) {
         // the corner kernel (one stage, whole-chunk swizzles) loads 8 KiB
-        // boxes fastest 2 to a wave (10^5 boxes: 0.71 of peak against 0.66
-        // with 4) and round-trips them 4 to a wave (0.336 against 0.31 with
-        // 8); the wave kernel 4 and 8
+        // boxes fastest one to a wave (10^5 boxes: 0.730 of peak against
+        // 0.70 with 2) and round-trips them 2 to a wave (0.354; 4: 0.334);
+        // the wave kernel 4 and 8
         const bool corner = stages == 1 && !elemwise;
         if (wave_box && tmap::wave_group(nslot) == 1)
-            group = mode == tmap::kStore ? 2u : (corner ? (mode == tmap::kLoad ? 2u : 4u) : (mode == tmap::kLoad ? 4u : 8u));
+            group = mode == tmap::kStore ? 2u : (corner ? (mode == tmap::kLoad ? 1u : 2u) : (mode == tmap::kLoad ? 4u : 8u));
         else
             group = (wave_box && mode == tmap::kStore) ? 4u : 8u;
     }
@@ -427,6 +427,28 @@ tmap_status check_coords_and_count(const MapImpl &swept, const int32_t *coords, 
     return TMAP_SUCCESS;
 }
 
+// ceil(2^32 / d) for 2 <= d <= 2^16, 0 for d == 1: the multiplier that
+// divides any n < 2^16 by d with one high multiply (the rounding error of
+// the multiplier, below n / 2^32 < 1 / d, never carries past the next
+// integer).
+uint32_t div_magic(uint32_t d) {
+    return d <= 1 ? 0u : (uint32_t)((((uint64_t)1 << 32) + d - 1) / d);
+}
+
+// Whether every corner of a box that touches the tensor of map m (corner
+// coordinates in (-box, dims) per dimension) is less than 2 GiB from the
+// base: then sum_d |c_d| * stride_d < sum_d (dims_d + box_d) * stride_d < 2^31.
+// A map with no rank (the unused side of a load or store) qualifies.
+bool small_offsets(const tmap::KMap &m) {
+    uint64_t s = 0;
+    for (int d = 0; d < tmap::kMaxRank; ++d) {
+        if (m.strides[d] >= ((uint64_t)1 << 31)) return false;
+        s += ((uint64_t)m.dims[d] + m.box[d]) * m.strides[d];
+        if (s >= ((uint64_t)1 << 31)) return false;
+    }
+    return true;
+}
+
 void fill_common(tmap::KArgs &a, const MapImpl &swept, const int32_t *coords, int64_t n_tiles) {
     a.coords = coords;
     a.n_tiles = n_tiles;
@@ -438,6 +460,9 @@ void fill_common(tmap::KArgs &a, const MapImpl &swept, const int32_t *coords, in
     a.n_chunks = swept.box_bytes / 16u;
     a.row_chunks = (uint32_t)swept.box[0] * swept.elem_size / 16u;
     a.k_el = 16u / swept.elem_size;
+    a.lk_el = log2u(a.k_el);
+    a.rc_magic = div_magic(a.row_chunks);
+    for (int d = 0; d < tmap::kMaxRank; ++d) a.box_magic[d] = div_magic(swept.box[d]);
     // The direct-to-LDS path moves whole 16-byte chunks; a swizzle that
     // permutes elements inside a chunk needs the element path for every chunk.
     a.elemwise = (swept.swz_b > 0 && ((1u << swept.swz_m) * swept.elem_size) < 16u) ? 1u : 0u;
@@ -467,6 +492,7 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     // 8 KiB and a swizzle that moves whole chunks: the corner kernels, which
     // hold each drained box in registers while the next one loads
     pl.corner = a.coords && pl.stages == 31 && pl.nslot <= 8 && !a.elemwise;
+    if (pl.corner) pl.lds = tmap::corner_lds_bytes(mode, pl.nslot);
     a.grid = pl.grid;
     a.regions = pl.regions;
     a.flags = opts ? opts->flags : 0u;
@@ -517,6 +543,7 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     int rc = (int)hipErrorInvalidValue;
     if (pl.corner) {
         const int dims = r2 ? 2 : 5;
+        a.off32 = small_offsets(a.src) && small_offsets(a.dst) ? 1u : 0u;
         rc = mode == tmap::kLoad    ? tmap::launch_corner_load(pl.nslot, dims, a, stream)
              : mode == tmap::kStore ? tmap::launch_corner_store(pl.nslot, dims, a, stream)
                                     : tmap::launch_corner_roundtrip(pl.nslot, dims, a, stream);

@@ -96,6 +96,16 @@ struct KArgs {
     uint32_t n_chunks;            // box_bytes / 16
     uint32_t row_chunks;          // box[0]*es / 16
     uint32_t k_el;                // elements per 16-byte chunk (16 / es)
+    uint32_t lk_el;               // log2(k_el)
+    // A chunk's box indices without a division: n / d == mulhi(n, magic(d))
+    // for every n < 2^16 and 2 <= d <= 2^16, with magic(d) = ceil(2^32 / d);
+    // magic 0 stands for d == 1.  Chunk indices stay below 4096 (64 KiB boxes).
+    uint32_t rc_magic;               // magic(row_chunks)
+    uint32_t box_magic[kMaxRank];    // magic(box[d]) of the swept map (a round trip's maps share the box)
+    // 1 when, in both maps, every corner whose box touches the tensor lies
+    // within 2 GiB of the base, so that corner offsets can be summed in 32
+    // bits (explicit-corner kernels)
+    uint32_t off32;
     uint32_t elemwise;            // 1 when the swizzle moves data inside 16-byte chunks
     uint32_t grid;                // workgroups launched
     uint32_t regions;             // interleaved streams the groups are dealt as (1: none)
@@ -178,5 +188,20 @@ constexpr int wave_group(int nslot) { return nslot >= 8 ? 1 : kWaves; }
 inline uint32_t wave_lds_bytes(int stages, int nslot) {
     const uint32_t wg = (uint32_t)wave_group(nslot);
     return wg * (uint32_t)stages * (uint32_t)nslot * kBlockBytes + wg * 32u + 4u;
+}
+
+// LDS the corner kernels reserve per workgroup beyond their stages and
+// barrier words: the load of 8 KiB boxes takes 11 KiB in all, which keeps
+// fourteen such workgroups on a CU instead of eighteen (measured on MI355X
+// over 10^5 scattered 8 KiB boxes: 0.707 -> 0.730 of peak; sixteen 0.725,
+// thirteen 0.68-0.72).  The stores and round trips lose with fewer.
+inline uint32_t corner_lds_reserve(int mode, int nslot) {
+    return (mode == kLoad && nslot == 8) ? 11264u - (8u * kBlockBytes + 8u) : 0u;
+}
+
+// LDS bytes one workgroup of the corner kernels takes.
+inline uint32_t corner_lds_bytes(int mode, int nslot) {
+    const uint32_t wg = (uint32_t)wave_group(nslot);
+    return wg * (uint32_t)nslot * kBlockBytes + wg * 8u + corner_lds_reserve(mode, nslot);
 }
 }  // namespace tmap
