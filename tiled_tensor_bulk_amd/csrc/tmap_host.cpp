@@ -357,13 +357,14 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // 0.539 -> 0.557 of peak, load 0.625 -> 0.669 with the packed side's
     // non-temporal hints)
     if (!group && corners) {
-        // the corner kernel (one stage, whole-chunk swizzles) loads 8 KiB
-        // boxes fastest one to a wave (10^5 boxes: 0.730 of peak against
-        // 0.70 with 2) and round-trips them 2 to a wave (0.354; 4: 0.334);
-        // the wave kernel 4 and 8
+        // the corner kernel (one stage, whole-chunk swizzles) loads and
+        // round-trips 8 KiB boxes fastest one to a wave (10^5 boxes: load
+        // 0.73 of peak against 0.69 with 2, round trip 0.366 against 0.353)
+        // and stores them 2 to a wave (0.633; 4: 0.618); the wave kernel
+        // takes 4 and 8
         const bool corner = stages == 1 && !elemwise;
         if (wave_box && tmap::wave_group(nslot) == 1)
-            group = mode == tmap::kStore ? 2u : (corner ? (mode == tmap::kLoad ? 1u : 2u) : (mode == tmap::kLoad ? 4u : 8u));
+            group = mode == tmap::kStore ? 2u : (corner ? 1u : (mode == tmap::kLoad ? 4u : 8u));
         else
             group = (wave_box && mode == tmap::kStore) ? 4u : 8u;
     }
