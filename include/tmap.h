@@ -91,24 +91,27 @@ typedef struct tmap_launch_opts {
                              two <= 64 (default: enough boxes side by side to span 512
                              bytes of a row, at least 2 and at most 8; band units: 2 on
                              the band kernel, else 4 for a round trip and 1 for a load
-                             or store; explicit corners: 8,
-                             for a wave-per-box store 4; wave per box with boxes of
-                             8 KiB and more: 2 for a load or store (4 for a load with
-                             2 stages or a swizzle inside 16-byte chunks), 8 for a
-                             round trip)                                               */
+                             or store; explicit corners: 8, for a wave-per-box store 4;
+                             wave per box with boxes of 8 KiB and more: on the corner
+                             kernel 1 for a load or round trip and 2 for a store, else
+                             4 for a load, 2 for a store and 8 for a round trip)       */
     uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
                              streams, each sweeping an equal contiguous stretch of the
                              tiles (workgroup i takes stretch i mod regions), so that the
                              tiles in flight lie in that many places of the tensor
                              instead of one.  How the addresses in flight fall on the
                              HBM channels decides which is faster (default: 2 for loads
-                             and stores on the band schedule, else 1)                  */
+                             and stores on the band schedule and for band-kernel round
+                             trips of tensors whose row pitch is not a power of two,
+                             else 1)                                                   */
     uint32_t band_rows;   /* band schedule: box rows per band, a power of two.  A unit is
                              then 16 KiB / (band_rows * box row bytes) boxes side by
-                             side.  Default on the band kernel: 8 for a round trip, 16
-                             for a load or store; elsewhere 2 for a round trip (units
-                             8 KiB wide with 128-byte box rows), 8 for a load or store;
-                             or the next taller height that fits.  An explicit height that does not fit
+                             side.  Default on the band kernel: 8 for a round trip (2
+                             where a tensor's row pitch, the byte stride of dimension
+                             1, is not a power of two), 16 for a load or store;
+                             elsewhere 2 for a round trip (units 8 KiB wide with
+                             128-byte box rows), 8 for a load or store; or the next
+                             taller height that fits.  An explicit height that does not fit
                              the box, the swizzle or the sweep (see below) is
                              TMAP_ERROR_INVALID_VALUE where the band schedule applies,
                              and ignored elsewhere                                       */

@@ -239,8 +239,10 @@ def test_band_schedule_choice():
     W = inputs.WORKLOADS
     B = T.FLAG_BAND
     # (name, boxes per unit of a load or store (16-row bands), of a round
-    # trip (8-row bands), of a load forced onto the band schedule)
-    for name, want, want_rt, forced in [("sweep2g_u8", 8, 16, 8), ("ragged_bf16", 8, 16, 8),
+    # trip (8-row bands; 2-row bands where the row pitch is not a power of
+    # two, as the ragged sweep's 32640 bytes), of a load forced onto the
+    # band schedule)
+    for name, want, want_rt, forced in [("sweep2g_u8", 8, 16, 8), ("ragged_bf16", 8, 64, 8),
                                         ("plus1_f32", 4, 8, 4), ("strips_f16", 1, 1, 2),
                                         ("tile64_f32", 1, 1, 1), ("pad5d_f32", 0, 0, 0)]:
         w = W[name]
@@ -255,6 +257,12 @@ def test_band_schedule_choice():
         assert T.tmap_band_boxes(m, flags=B | T.FLAG_CACHED_PACKED) == forced
         assert T.tmap_band_boxes(m, explicit_coords=True, flags=B) == 0
         assert T.tmap_band_boxes(m, m) == want_rt
+    # a round trip takes 2-row bands unless both tensors' row pitches are
+    # powers of two
+    pow2 = T.tmap_encode("u8", 2, BASE, [32768, 16384], [32768], [128, 128])
+    odd = T.tmap_encode("u8", 2, BASE, [32768, 16384], [33024], [128, 128])
+    assert [T.tmap_band_boxes(pow2, pow2), T.tmap_band_boxes(odd, odd), T.tmap_band_boxes(pow2, odd),
+            T.tmap_band_boxes(odd, pow2), T.tmap_band_boxes(odd)] == [16, 64, 64, 64, 8]
     # the size threshold, 256 MiB spanned by the outermost dimension: below
     # it the band kernel's maps take the tallest band that fits (here one
     # whole 128-row box), other maps whole boxes

@@ -692,6 +692,11 @@ def test_plan_query_reports_the_schedules():
         ("band", 16, 8, 3, 2, 1)
     # 512 boxes a row in units of 16, 256 box rows of 16 bands each
     assert p["units"] == (512 // 16) * 256 * 16 and p["walkers"] == p["workgroups"] == p["units"] // 2
+    # the ragged sweep's 32640-byte pitch is not a power of two: its round
+    # trip takes 2-row bands of 64 boxes, dealt as two streams
+    p = plan("ragged_bf16", "roundtrip", flags=T.FLAG_NONTEMPORAL)
+    assert (p["variant"], p["band_boxes"], p["band_rows"], p["stages"], p["group"], p["regions"]) == \
+        ("band", 64, 2, 3, 2, 2)
     p = plan("sweep2g_u8", "load", flags=T.FLAG_NONTEMPORAL)
     assert (p["variant"], p["band_boxes"], p["band_rows"], p["stages"], p["group"], p["regions"]) == \
         ("band", 8, 16, 3, 2, 2)

@@ -159,6 +159,26 @@ constexpr uint32_t kBandRowsLoadStore = 8;
 constexpr uint32_t kLeanRowsRoundtrip = 8;
 constexpr uint32_t kLeanRowsLoadStore = 16;
 
+// A band-kernel round trip between tensors whose row pitch is not a power of
+// two takes 2-row bands dealt as two interleaved streams instead.  Measured
+// on MI355X (3 stages x 2 units; fraction of 8 TB/s): the ragged bf16 sweep
+// (pitch 32640) 0.796-0.801 at three placements of the destination against
+// 0.68-0.76 in 8-row bands; pitches 33024 and 40960: 0.793 and 0.763
+// against 0.793 and 0.746; 49152: 0.746 against 0.752.  With power-of-two
+// pitches 8-row bands in one stream stay best (2 GiB u8: 0.818 against
+// 0.813, 1 GiB fp32: 0.827 against 0.811, pitch 32768: 0.817 against 0.808).
+constexpr uint32_t kLeanRowsRoundtripSpread = 2;
+
+// Whether every tensor a round trip streams has a power-of-two row pitch
+// (the byte stride of dimension 1).
+bool pow2_pitches(const tmap::KArgs &a) {
+    for (const tmap::KMap *k : {&a.src, &a.dst}) {
+        const uint64_t p = k->strides[1];
+        if (k->rank >= 2 && (p & (p - 1))) return false;
+    }
+    return true;
+}
+
 // The checks that depend on the band height; nullptr when `rows` fits,
 // else the reason.  rc: 16-byte chunks per box row.
 const char *band_height_misfit(const MapImpl &m, const tmap::KArgs &a, uint32_t rc, uint32_t rows, uint32_t &g,
@@ -230,8 +250,9 @@ bool band_fits(const MapImpl &m, const tmap::KArgs &a, bool roundtrip, uint32_t 
             if (rows <= m.box[1] && !band_height_misfit(m, a, rc, rows, g, nb)) return true;
         return false;
     }
-    const uint32_t first = lean ? (roundtrip ? kLeanRowsRoundtrip : kLeanRowsLoadStore)
-                                : (roundtrip ? kBandRowsRoundtrip : kBandRowsLoadStore);
+    const uint32_t first =
+        lean ? (roundtrip ? (pow2_pitches(a) ? kLeanRowsRoundtrip : kLeanRowsRoundtripSpread) : kLeanRowsLoadStore)
+             : (roundtrip ? kBandRowsRoundtrip : kBandRowsLoadStore);
     for (rows = first; rows <= m.box[1]; rows *= 2)
         if (!band_height_misfit(m, a, rc, rows, g, nb)) return true;
     // the band kernel's defaults are tall: a shorter box takes the tallest
@@ -489,6 +510,11 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     pl.band_g = band ? g : 0u;
     pl.band_rows = band ? rows : 0u;
     pl.lean = lean;
+    // the spread round trip of tensors without a power-of-two pitch (see
+    // kLeanRowsRoundtripSpread): two interleaved streams
+    const bool resident = resident_span(swept) && !(opts && (opts->flags & TMAP_FLAG_BAND));
+    if (lean && mode == tmap::kRoundtrip && !(opts && opts->regions) && !resident && !pow2_pitches(a))
+        pl.regions = 2u;
     // explicit corners, one wave per box with one stage, boxes of at most
     // 8 KiB and a swizzle that moves whole chunks: the corner kernels, which
     // hold each drained box in registers while the next one loads
