@@ -70,6 +70,19 @@ def test_counters_average_the_copy_kernel_dispatches_only(tmp_path):
     assert kv["SQ_WAVES"] == "128" and kv["SQ_LDS_BANK_CONFLICT"] == "2"
 
 
+def test_summaries_keep_the_timed_kernel_only(tmp_path):
+    """A store's bench fills its packed images with one load before the
+    timed stores: the summaries average the kernel dispatched most often."""
+    load = KERNEL.replace("<2,", "<0,")
+    path = tmp_path / "c.csv"
+    _write_counters(path, [(1, load, "SQ_WAVES", 5000), (2, KERNEL, "SQ_WAVES", 100), (3, KERNEL, "SQ_WAVES", 300)])
+    out = tmp_path / "c.txt"
+    ps.cmd_counters(types.SimpleNamespace(csv=str(path), workload="w", op="store", out=str(out), cmd="x"))
+    kv = dict(line.strip().split(": ", 1) for line in open(out) if not line.startswith("#"))
+    assert kv["SQ_WAVES"] == "200"
+    assert ps.timed_kernel([load, KERNEL, KERNEL, COPY]) == KERNEL
+
+
 def test_copy_kernel_names_cover_every_variant():
     for k in ("copy_kernel<0, 1, 8, 5, false>", "wave_kernel<1, 1, 8, 5>", "thread_kernel<2, 4, 2>",
               "ws_kernel<0, 2, 4, 2>", "band_kernel<2, 3, true, true, false>",

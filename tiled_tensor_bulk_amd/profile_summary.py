@@ -140,6 +140,16 @@ def per_dispatch(path, counter):
     return [(d, names[d], agg[d]) for d in sorted(agg)]
 
 
+def timed_kernel(names):
+    """The copy kernel the bench times: the one dispatched most often (a
+    store's bench first fills its packed images with one load)."""
+    counts = defaultdict(int)
+    for n in names:
+        if is_copy_kernel(n):
+            counts[n] += 1
+    return max(counts, key=counts.get) if counts else None
+
+
 def cmd_traffic(a):
     from tiled_tensor_bulk_amd import inputs
     w = inputs.WORKLOADS[a.workload]
@@ -148,7 +158,8 @@ def cmd_traffic(a):
     for counter, path in (("FETCH_SIZE", a.fetch), ("WRITE_SIZE", a.write)):
         d = per_dispatch(path, counter)
         copies = [v for (_, n, v) in d if "copyBuffer" in n and v > 0.25 * known_kib]
-        kern = [v for (_, n, v) in d if is_copy_kernel(n)]
+        timed = timed_kernel(n for (_, n, _) in d)
+        kern = [v for (_, n, v) in d if n == timed]
         if not copies or not kern:
             sys.exit(f"{path}: no reference copy or copy kernel dispatches with {counter}")
         factor = known_kib / (sum(copies) / len(copies))
@@ -179,8 +190,9 @@ def cmd_counters(a):
     rows = list(csv.DictReader(open(a.csv)))
     agg = defaultdict(float)
     disp = set()
+    timed = timed_kernel({int(r["Dispatch_Id"]): r["Kernel_Name"] for r in rows}.values())
     for r in rows:
-        if not is_copy_kernel(r["Kernel_Name"]):
+        if r["Kernel_Name"] != timed:
             continue
         disp.add(int(r["Dispatch_Id"]))
         agg[r["Counter_Name"]] += float(r["Counter_Value"])
