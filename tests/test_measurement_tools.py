@@ -94,6 +94,8 @@ def test_copy_kernel_names_cover_every_variant():
         "tmap band_kernel<roundtrip, stages=3, nt loads=true, nt stores=true, +addend>"
     assert ps.short(full("corner_kernel<0, 8, 5, false, true, false, false>")) == \
         "tmap corner_kernel<load, nslot=8, dims=5, nt loads=false, nt stores=true>"
+    assert ps.short(full("thread_kernel<0, 8, 2>")) == "tmap thread_kernel<load, nslot=8, dims=2>"
+    assert ps.short(full("ws_kernel<1, 2, 4, 5>")) == "tmap ws_kernel<store, stages=2, nslot=4, dims=5>"
     assert ps.short(full("corner_kernel<2, 8, 5, false, false, false, true>")) == \
         "tmap corner_kernel<roundtrip, nslot=8, dims=5, nt loads=false, nt stores=false, same maps>"
 

@@ -92,6 +92,14 @@ def short(name: str) -> str:
         extra = (", +addend" if m.group(6) == "true" else "") + (", same maps" if m.group(7) == "true" else "")
         return (f"tmap corner_kernel<{mode}, nslot={m.group(2)}, dims={m.group(3)}, nt loads={m.group(4)}, "
                 f"nt stores={m.group(5)}{extra}>")
+    m = re.search(r"thread_kernel<(\d+), (\d+), (\d+)>", name)
+    if m:
+        mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
+        return f"tmap thread_kernel<{mode}, nslot={m.group(2)}, dims={m.group(3)}>"
+    m = re.search(r"ws_kernel<(\d+), (\d+), (\d+), (\d+)>", name)
+    if m:
+        mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
+        return f"tmap ws_kernel<{mode}, stages={m.group(2)}, nslot={m.group(3)}, dims={m.group(4)}>"
     if "copyBuffer" in name:
         return "hip copyBuffer (torch d2d copy)"
     return (name[:60] + "...") if len(name) > 63 else name
