@@ -1,6 +1,6 @@
 // tmap_corner.h -- the copy of boxes at explicit corners, one wave per box,
-// written for the fewest instructions per box and two boxes in flight per
-// wave.
+// written for the fewest instructions per box; a wave that takes several
+// boxes keeps one loading while it stores the one before.
 //
 // Each wave walks its own share of the corners through one LDS stage of one
 // box (NSLOT KiB, NSLOT <= 8) and its own 8-byte barrier record:
@@ -29,8 +29,8 @@
 //           before it is refilled.
 //
 // So a box's stores are issued after the next box's loads, and the next
-// landing waits for those loads alone (vmcnt leaves the stores in flight):
-// every wave keeps a box loading while it stores the one before.  Per-slot
+// landing waits for those loads alone (vmcnt leaves the stores in flight).
+// Per-slot
 // quantities (box indices, in-box offsets in both maps) are computed once per
 // kernel; per box only the scalar corner, base addresses and bounds change,
 // and an edge box costs a few vector compares per slot.
