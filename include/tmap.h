@@ -458,7 +458,10 @@ const char *tmap_last_error_detail(void);
  * TMAP_SUCCESS or TMAP_ERROR_TIMEOUT (or TMAP_ERROR_LAUNCH if the stream
  * reports an error).  The words are per device, not per stream: a timeout
  * of a copy on one stream is reported to whichever stream of that device is
- * checked first, and a check clears it for all of them.
+ * checked first, and a check clears it for all of them.  The read and the
+ * clear are two steps, so a timeout that a copy still running on another
+ * stream records between them goes unreported; for an exact report, check
+ * once every stream of the device has finished.
  * ("TMA -- the async bulk copy engine", "Load completion -- the mbarrier and
  * the byte budget": a wait on a byte budget that never completes must end;
  * here it ends the kernel and is reported here.) */
