@@ -172,7 +172,9 @@ def main():
         swept = md if args.op == "store" else ms
         plan = T.tmap_plan_launch(direction, swept, md if direction == "roundtrip" else None, coords is not None,
                                   n, **opts)
-        if plan["band_boxes"]:
+        if plan["band_boxes"] and (args.flags & T.FLAG_WHOLE_BOX):
+            schedule = f"whole boxes on the band kernel: {plan['band_boxes']} per stage"
+        elif plan["band_boxes"]:
             schedule = f"band: {plan['band_boxes']} boxes x {plan['band_rows']} rows per stage"
         elif plan["variant"] in ("wave_per_box", "corner"):
             schedule = "whole boxes, one wave per box" + (", drained box held in registers"

@@ -123,8 +123,8 @@ typedef struct tmap_launch_opts {
  * least 256 MiB (dims[rank-1] * strides[rank-1]), or when TMAP_FLAG_BAND
  * asks for it, or when its maps suit the band kernel (TMAP_VARIANT_BAND:
  * rank <= 2, dimension-0 rows of whole 16-byte chunks); unless
- * TMAP_FLAG_WHOLE_BOX, thread-copy, producer-wave or wave-per-box mode is
- * asked for.  A smaller tensor stays in the last-level cache, where DRAM
+ * TMAP_FLAG_WHOLE_BOX (on the band kernel: units of whole boxes),
+ * thread-copy, producer-wave or wave-per-box mode is asked for.  A smaller tensor stays in the last-level cache, where DRAM
  * page locality gains nothing: on the band kernel it then takes the tallest
  * band that fits (often one whole box), 2 stages and one region, and other
  * maps keep whole boxes.  A stage then holds the same band of band_rows rows of the
@@ -182,10 +182,13 @@ typedef struct tmap_launch_opts {
  * and producer-wave modes, TMAP_FLAG_WHOLE_BOX and the band schedule.  The
  * default for explicit corners of boxes up to 8 KiB (unless stages > 2). */
 #define TMAP_FLAG_WAVE_PER_BOX 0x40u
-/* One whole box per stage, shared by the workgroup's four waves (the
- * cooperative ring), even where the band schedule or wave-per-box mode
- * would be the default (for A/B runs, and for a consumer that needs a box's
- * full LDS image at once). */
+/* One whole box per stage, even where the band schedule or wave-per-box
+ * mode would be the default (for A/B runs, and for a consumer that needs a
+ * box's full LDS image at once).  Sweeps whose maps suit the band kernel
+ * (TMAP_VARIANT_BAND) with boxes of at most 16 KiB run there, in units of
+ * the whole boxes that fill 16 KiB (band_rows = box[1]), 3 stages x 2
+ * units, two interleaved streams; other copies run the cooperative ring,
+ * the workgroup's four waves sharing each stage. */
 #define TMAP_FLAG_WHOLE_BOX 0x10u
 /* The band schedule wherever its shape rules allow, whatever the tensor's
  * size.  Excludes TMAP_FLAG_WHOLE_BOX. */
@@ -370,8 +373,10 @@ tmap_status tmap_inbounds_elems(const tmap_t *map, const int32_t *host_coords,
                                 int64_t n_tiles, uint64_t *out_elems);
 
 /* Schedule a copy would take (host only, no device needed): the boxes per
- * stage on the band schedule described at tmap_launch_opts, or 0 when every
- * stage holds one whole box.  (A stage is what "TMA -- the async bulk copy
+ * stage on the band schedule described at tmap_launch_opts (with
+ * TMAP_FLAG_WHOLE_BOX on the band kernel, the whole boxes that fill a
+ * 16 KiB unit), or 0 when every stage of the generic ring holds one whole
+ * box.  (A stage is what "TMA -- the async bulk copy
  * engine", "Why this only pays off inside a pipeline" calls a pipeline
  * stage: one byte-counted buffer of the ring.)  src is the swept map of a load or round trip
  * (of a store: the destination map), dst the round trip's destination map or

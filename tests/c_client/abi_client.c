@@ -118,7 +118,9 @@ static void options_from_c(void) {
     CHECK(tmap_encode(&map, TMAP_U8, 2, (void *)(uintptr_t)0x100000u, dims, strides, box, NULL, swz) ==
           TMAP_SUCCESS);
     memset(&opts, 0, sizeof opts);
-    opts.flags = TMAP_FLAG_WHOLE_BOX;
+    opts.flags = TMAP_FLAG_WHOLE_BOX; /* on the band kernel: one 16 KiB box per unit */
+    CHECK(tmap_band_boxes(&map, &map, NULL, &opts) == 1u);
+    opts.flags = TMAP_FLAG_WHOLE_BOX | TMAP_FLAG_BAND; /* exclusive: the launch would reject them */
     CHECK(tmap_band_boxes(&map, &map, NULL, &opts) == 0u);
     opts.flags = TMAP_FLAG_BAND;
     opts.band_rows = 16;

@@ -242,9 +242,9 @@ def test_band_schedule_choice():
     # trip (8-row bands; 2-row bands where the row pitch is not a power of
     # two, as the ragged sweep's 32640 bytes), of a load forced onto the
     # band schedule)
-    for name, want, want_rt, forced in [("sweep2g_u8", 8, 16, 8), ("ragged_bf16", 8, 64, 8),
-                                        ("plus1_f32", 4, 8, 4), ("strips_f16", 1, 1, 2),
-                                        ("tile64_f32", 1, 1, 1), ("pad5d_f32", 0, 0, 0)]:
+    for name, want, want_rt, forced, whole in [("sweep2g_u8", 8, 16, 8, 1), ("ragged_bf16", 8, 64, 8, 2),
+                                               ("plus1_f32", 4, 8, 4, 1), ("strips_f16", 1, 1, 2, 0),
+                                               ("tile64_f32", 1, 1, 1, 1), ("pad5d_f32", 0, 0, 0, 0)]:
         w = W[name]
         m = T.tmap_encode(w.dtype, w.rank, BASE, w.dims, w.strides, w.box, None, w.swizzle)
         assert T.tmap_band_boxes(m) == want, name
@@ -257,6 +257,11 @@ def test_band_schedule_choice():
         assert T.tmap_band_boxes(m, flags=B | T.FLAG_CACHED_PACKED) == forced
         assert T.tmap_band_boxes(m, explicit_coords=True, flags=B) == 0
         assert T.tmap_band_boxes(m, m) == want_rt
+        # whole boxes: on the band kernel units of whole boxes (as many as
+        # fill 16 KiB: two 8 KiB ragged boxes), where a box fits a stage;
+        # else the generic ring (0)
+        assert T.tmap_band_boxes(m, flags=T.FLAG_WHOLE_BOX) == whole, name
+        assert T.tmap_band_boxes(m, m, flags=T.FLAG_WHOLE_BOX) == whole, name
     # a round trip takes 2-row bands unless both tensors' row pitches are
     # powers of two
     pow2 = T.tmap_encode("u8", 2, BASE, [32768, 16384], [32768], [128, 128])
