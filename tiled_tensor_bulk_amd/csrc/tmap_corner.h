@@ -366,6 +366,8 @@ struct CornerCopier {
     }
 };
 
+// `a` must stay the kernel's only argument: reread() finds it at the start
+// of the argument segment.
 template <int MODE, int NSLOT, int R, bool NTL, bool NTS, bool ADD, bool SAME>
 __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner_kernel(const KArgs a) {
     constexpr int WG = wave_group(NSLOT);
