@@ -340,8 +340,9 @@ def _wave_case(rng, idx):
 @pytest.mark.parametrize("chunk", range(6))
 def test_fuzz_random_maps(chunk):
     """Seeded random maps of every rank, element size and swizzle, random
-    corners in, across and outside the tensor, random launch options; chunks
-    4 and 5 run wave-per-box mode."""
+    corners in, across and outside the tensor, random launch options: load,
+    round trip and store at those corners, and a store through the sweep;
+    chunks 4 and 5 run wave-per-box mode."""
     rng = np.random.default_rng(9000 + chunk)
     for i in range(40):
         es, dims, strides, box, swz, alloc, coords, opts = (_fuzz_case if chunk < 4 else _wave_case)(rng, i)
@@ -365,6 +366,14 @@ def test_fuzz_random_maps(chunk):
         check_ok()
         oracle.roundtrip(om, host, om, want_dst, coords, len(coords))
         assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip", mm)
+        # store of the loaded images back through the same corners (boxes
+        # that overlap write equal bytes: every image holds the source's)
+        dst1 = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        want1 = dst1.cpu().numpy().copy()
+        T.tmap_store_tiles(enc(dt_of(es), dst1, dims, strides, box, swz), c, len(coords), packed, **opts)
+        check_ok()
+        oracle.store_tiles(om, want1, coords, len(coords), want)
+        assert (mm := first_mismatch(dst1.cpu().numpy(), want1, 1 << 40)) is None, ("store at corners", mm)
         # store of random images through a sweep (no two boxes overlap)
         ns = T.tmap_sweep_tiles(m)
         imgs = inputs.sentinel_bytes(ns * bb, int(rng.integers(1 << 30)))
