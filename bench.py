@@ -176,15 +176,15 @@ def main():
             schedule = f"whole boxes on the band kernel: {plan['band_boxes']} per stage"
         elif plan["band_boxes"]:
             schedule = f"band: {plan['band_boxes']} boxes x {plan['band_rows']} rows per stage"
-        elif plan["variant"] in ("wave_per_box", "corner"):
-            schedule = "whole boxes, one wave per box" + (", drained box held in registers"
-                                                           if plan["variant"] == "corner" else "")
+        elif plan["variant"] in ("wave_per_box", "corner", "corner4"):
+            schedule = "whole boxes, one wave per box" + {"corner": ", drained box held in registers",
+                                                          "corner4": ", 4-byte lanes"}.get(plan["variant"], "")
         else:
             schedule = "whole boxes" + ("" if plan["variant"] == "ring" else f" ({plan['variant']})")
 
     kernel_name = {"ring": "copy_kernel", "wave_per_box": "wave_kernel", "thread_copy": "thread_kernel",
                    "producer_wave": "ws_kernel", "band": "band_kernel",
-                   "corner": "corner_kernel"}[plan["variant"]] if plan else "copy_kernel"
+                   "corner": "corner_kernel", "corner4": "corner4_kernel"}[plan["variant"]] if plan else "copy_kernel"
     for _ in range(args.warmup):
         launch()
     st = T.tmap_sync_status(stream)

@@ -27,6 +27,9 @@ int launch_band_roundtrip(int, const KArgs &, void *) { return 1; }
 int launch_corner_load(int, int, const KArgs &, void *) { return 1; }
 int launch_corner_store(int, int, const KArgs &, void *) { return 1; }
 int launch_corner_roundtrip(int, int, const KArgs &, void *) { return 1; }
+int launch_corner4_load(int, int, const KArgs &, void *) { return 1; }
+int launch_corner4_store(int, int, const KArgs &, void *) { return 1; }
+int launch_corner4_roundtrip(int, int, const KArgs &, void *) { return 1; }
 uint32_t *noalloc_status(int) { return nullptr; }
 tmap_status noalloc_scratch(uint32_t **) { return TMAP_ERROR_LAUNCH; }
 }  // namespace tmap

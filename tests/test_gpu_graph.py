@@ -53,7 +53,7 @@ def test_graph_replays_match_the_oracle():
     bb = T.tmap_box_bytes(ma)
     packed = torch.empty(n * bb, dtype=torch.uint8, device=DEV)
     oa = Map(es=1, dims=a_dims, strides=a_strides, box=a_box, swizzle=a_swz)
-    # scattered 8 KiB fp32 boxes (one wave per box and workgroup) for a round trip
+    # scattered 8 KiB fp32 boxes (one wave per box and workgroup, 4-byte lanes) for a round trip
     c_dims, c_strides, c_box = [300, 150], [1280], [32, 64]
     c = torch.empty(1280 * 150, dtype=torch.uint8, device=DEV)
     d = torch.empty_like(c)
@@ -62,7 +62,7 @@ def test_graph_replays_match_the_oracle():
     corners = inputs.random_corners(c_dims, c_box, 200, seed=71)
     corners_dev = torch.from_numpy(corners).to(DEV)
     oc = Map(es=4, dims=c_dims, strides=c_strides, box=c_box)
-    assert T.tmap_plan_launch("roundtrip", mc, md, True, len(corners))["variant"] == "corner"
+    assert T.tmap_plan_launch("roundtrip", mc, md, True, len(corners))["variant"] == "corner4"
     fill_random(b, 1)
     fill_random(d, 2)
 

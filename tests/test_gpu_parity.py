@@ -634,7 +634,8 @@ def test_corner_offsets_far_and_wrapped():
         host = src.cpu().numpy()
         m = enc(dtype, src, dims, strides, box)
         om = Map(es=es, dims=dims, strides=strides, box=box)
-        assert T.tmap_plan_launch("load", m, None, True, n)["variant"] == "corner"
+        # unswizzled fp32 boxes run in 4-byte lanes, the u8 ones in 16-byte lanes
+        assert T.tmap_plan_launch("load", m, None, True, n)["variant"] == ("corner4" if es == 4 else "corner")
         say(f"corner kernel, {case} offsets: load")
         got = gpu_load(m, corners, n).cpu().numpy()
         want = oracle.load_tiles(om, host, corners, n)
@@ -656,6 +657,93 @@ def test_corner_offsets_far_and_wrapped():
         assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, (case, "roundtrip", mm)
         del src, dst, host, want_dst
         torch.cuda.empty_cache()
+
+
+def _corner4_case(rng):
+    """A map the corner kernels run in 4-byte lanes: unswizzled 4- or 8-byte
+    elements, box rows of a power of two from 16 to 256 bytes, at most 64
+    rows and 8 KiB to a box, padded rows and planes; and a second layout of
+    other dims and pitch with the same box."""
+    es = int(rng.choice([4, 8]))
+    rank = int(rng.integers(1, 6))
+    row = int(rng.choice([16, 32, 64, 128, 256]))
+    max_rows = min(64, 8192 // row)
+    box, rows = [row // es], 1
+    for _ in range(1, rank):
+        b = int(rng.integers(1, max_rows // rows + 1))
+        box.append(b)
+        rows *= b
+
+    def layout():
+        dims = [int(rng.integers(1, 2 * box[0] + 40))] + [int(rng.integers(1, 2 * b + 4)) for b in box[1:]]
+        s = (-(-dims[0] * es // 16) + int(rng.integers(0, 3))) * 16
+        strides = []
+        for d in range(1, rank):
+            strides.append(s)
+            s *= dims[d] + int(rng.integers(0, 2))
+        return dims, strides, s
+    return es, box, layout(), layout()
+
+
+@pytest.mark.parametrize("chunk", range(2))
+def test_corner4_random_maps(chunk):
+    """The corner kernels in 4-byte lanes, on seeded random maps they take
+    (every rank, 4- and 8-byte elements, every row width from 16 to 256
+    bytes), random corners in, across and outside the tensor and random
+    deals: load, store of the loaded images at the same corners, round trip
+    into a tensor of the same layout and into one of another layout, and the
+    fp32 +1.0f round trip, against the oracle; some with every stage
+    poisoned before its loads."""
+    rng = np.random.default_rng(9700 + chunk)
+    for i in range(30):
+        es, box, (dims, strides, alloc), (ddims, dstrides, dalloc) = _corner4_case(rng)
+        coords = inputs.random_corners(dims, box, int(rng.integers(1, 400)), int(rng.integers(1 << 30)))
+        n = len(coords)
+        opts = dict(grid_wgs=int(rng.choice([0, 0, 1, 3])), group=int(rng.choice([0, 1, 2, 4])),
+                    regions=int(rng.choice([0, 1, 2, 3])),
+                    flags=int(rng.choice([0, T.FLAG_NONTEMPORAL, T.FLAG_CACHED_PACKED, T.FLAG_DEBUG_POISON])))
+        say(f"corner4 chunk {chunk} case {i}: es={es} dims={dims} strides={strides} box={box} "
+            f"ddims={ddims} dstrides={dstrides} n={n} opts={opts}")
+        dt = dt_of(es)
+        om = Map(es=es, dims=dims, strides=strides, box=box)
+        omd = Map(es=es, dims=ddims, strides=dstrides, box=box)
+        src = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        host = src.cpu().numpy()
+        m = enc(dt, src, dims, strides, box)
+        bb = T.tmap_box_bytes(m)
+        assert T.tmap_plan_launch("load", m, None, True, n, **opts)["variant"] == "corner4"
+        packed = gpu_load(m, coords, n, **opts)
+        want = oracle.load_tiles(om, host, coords, n)
+        assert (mm := first_mismatch(packed.cpu().numpy(), want, bb)) is None, ("load", mm)
+        c = torch.from_numpy(coords).to(DEV)
+        dst = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        want_dst = dst.cpu().numpy().copy()
+        T.tmap_store_tiles(enc(dt, dst, dims, strides, box), c, n, packed, **opts)
+        check_ok()
+        oracle.store_tiles(om, want_dst, coords, n, want)
+        assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("store", mm)
+        for other in (False, True):
+            d_dims, d_strides, d_alloc, od = (ddims, dstrides, dalloc, omd) if other else (dims, strides, alloc, om)
+            dst = dev_tensor(d_alloc, fill_seed=int(rng.integers(1 << 30)))
+            want_dst = dst.cpu().numpy().copy()
+            md = enc(dt, dst, d_dims, d_strides, box)
+            assert T.tmap_plan_launch("roundtrip", m, md, True, n, **opts)["variant"] == "corner4"
+            add = es == 4 and bool(rng.integers(0, 2))
+            if add:
+                T.tmap_roundtrip_add_f32(m, md, c, n, 1.0, **opts)
+                oracle.roundtrip_add_f32(om, host, od, want_dst, coords, n, 1.0)
+            else:
+                T.tmap_roundtrip(m, md, c, n, **opts)
+                oracle.roundtrip(om, host, od, want_dst, coords, n)
+            check_ok()
+            got = dst.cpu().numpy()
+            if add:
+                nan = np.isnan(want_dst.view(np.float32))
+                assert np.array_equal(got.view(np.uint32)[~nan], want_dst.view(np.uint32)[~nan]), \
+                    ("round trip +1.0f", other)
+                assert np.all(np.isnan(got.view(np.float32)[nan]))
+            else:
+                assert (mm := first_mismatch(got, want_dst, 1 << 40)) is None, ("roundtrip", other, mm)
 
 
 def test_binding_rejects_buffers_the_copy_would_overrun():
@@ -709,21 +797,28 @@ def test_plan_query_reports_the_schedules():
     p = plan("sweep2g_u8", "load", flags=T.FLAG_NONTEMPORAL)
     assert (p["variant"], p["band_boxes"], p["band_rows"], p["stages"], p["group"], p["regions"]) == \
         ("band", 8, 16, 3, 2, 2)
-    p = plan("pad5d_f32", "store")
-    assert (p["variant"], p["stages"], p["slots"], p["group"]) == ("corner", 1, 8, 2)
-    # 8 KiB boxes: one wave to a workgroup, each with its own one-box ring
-    assert p["walkers"] == 100000 // 2 and p["workgroups"] == p["walkers"]
-    assert p["lds_bytes"] == 8192 + 8
+    # the padded 5-D fp32 boxes: the corner kernels in 4-byte lanes, one box
+    # to a wave in every direction; 8 KiB boxes: one wave to a workgroup,
+    # each with its own one-box stage
+    for direction in ("load", "store", "roundtrip"):
+        p = plan("pad5d_f32", direction)
+        assert (p["variant"], p["stages"], p["slots"], p["group"]) == ("corner4", 1, 8, 1), direction
+        assert p["walkers"] == 100000 and p["workgroups"] == p["walkers"], direction
+        assert p["lds_bytes"] == 8192 + 8, direction
     # 2 KiB boxes: four waves to a workgroup
     m = T.tmap_encode("f32", 2, 0x7F0000000000, [1000, 1000], [4000], [32, 16])
     p = T.tmap_plan_launch("load", m, None, True, 1000)
-    assert (p["variant"], p["slots"], p["walkers"]) == ("corner", 2, 125)
+    assert (p["variant"], p["slots"], p["walkers"]) == ("corner4", 2, 125)
     assert p["workgroups"] == 32 and p["lds_bytes"] == 4 * 2048 + 4 * 8
-    # the 8 KiB load: one box to a wave, 11 KiB of LDS to a workgroup
-    p = plan("pad5d_f32", "load")
-    assert (p["group"], p["lds_bytes"], p["walkers"]) == (1, 11264, 100000)
-    assert plan("pad5d_f32", "roundtrip")["group"] == 1
-    assert plan("pad5d_f32", "roundtrip")["variant"] == "corner"
+    # 16-bit elements in 128-byte-swizzled 8 KiB boxes: the corner kernel in
+    # 16-byte lanes; its loads reserve 11 KiB of LDS to a workgroup, its
+    # stores take two boxes to a wave
+    m = T.tmap_encode("bf16", 2, 0x7F0000000000, [1000, 1000], [2048], [64, 64], None, (3, 3, 3))
+    p = T.tmap_plan_launch("load", m, None, True, 1000)
+    assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"]) == ("corner", 1, 11264, 1000)
+    p = T.tmap_plan_launch("store", m, None, True, 1000)
+    assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"]) == ("corner", 2, 8192 + 8, 500)
+    assert T.tmap_plan_launch("roundtrip", m, m, True, 1000)["group"] == 1
     assert plan("pad5d_f32", "roundtrip", stages=2)["variant"] == "wave_per_box"
     assert plan("pad5d_f32", "load", flags=T.FLAG_WHOLE_BOX)["variant"] == "ring"
     assert plan("pad5d_f32", "load", stages=3)["variant"] == "ring"
@@ -804,6 +899,36 @@ def test_budget_mismatch_times_out_instead_of_hanging(mode):
     T.tmap_load_tiles(m, coords, 4, out, stages=2, flags=mode)
     check_ok()
     assert torch.equal(out.view(4, -1)[3], src)
+
+
+@pytest.mark.parametrize("dtype", ["u8", "f32"])
+def test_budget_mismatch_times_out_in_the_corner_kernels(dtype):
+    """The same for boxes at explicit corners, one wave per box: the corner
+    kernel in 16-byte lanes (u8) and in 4-byte lanes (fp32), each direction."""
+    es = 1 if dtype == "u8" else 4
+    box = [128 // es, 64]
+    dims = [256 // es, 100]
+    src = dev_tensor(256 * 100, fill_seed=3)
+    dst = dev_tensor(256 * 100, fill_seed=4)
+    m, md = enc(dtype, src, dims, [256], box), enc(dtype, dst, dims, [256], box)
+    assert T.tmap_plan_launch("load", m, None, True, 4)["variant"] == ("corner" if es == 1 else "corner4")
+    coords = torch.tensor([[0, 0], [3, 5], [-7, 60], [200 // es, -10]], dtype=torch.int32, device=DEV)
+    out = dev_tensor(8192 * 4)
+    for direction in ("load", "store", "roundtrip"):
+        say(f"budget mismatch -> TIMEOUT ({dtype} corner kernel, {direction})")
+        for flags in (T.FLAG_INJECT_BUDGET_MISMATCH, 0):
+            if direction == "load":
+                T.tmap_load_tiles(m, coords, 4, out, flags=flags, spin_limit=2000)
+            elif direction == "store":
+                T.tmap_store_tiles(md, coords, 4, out, flags=flags, spin_limit=2000)
+            else:
+                T.tmap_roundtrip(m, md, coords, 4, flags=flags, spin_limit=2000)
+            assert T.tmap_sync_status() == (T.TIMEOUT if flags else T.SUCCESS), (direction, flags)
+    # the library keeps working afterwards
+    T.tmap_load_tiles(m, coords, 4, out)
+    check_ok()
+    om = Map(es=es, dims=dims, strides=[256], box=box)
+    assert out.cpu().numpy().tobytes() == oracle.load_tiles(om, src.cpu().numpy(), coords.cpu().numpy(), 4).tobytes()
 
 
 def test_repeat_is_deterministic():

@@ -7,6 +7,10 @@ kernel:
     producer-wave variants) moves tile data with 16-byte direct-to-LDS
     buffer loads (`buffer_load_dwordx4 ... lds`); the thread-copy variant,
     the register path, has none;
+  - the corner kernels in 4-byte lanes load from the tensor with 4-byte
+    direct-to-LDS loads (`buffer_load_dword ... lds`), fetch each slot's
+    row offset across lanes (`ds_bpermute_b32`) and store to the tensor in
+    4-byte stores;
   - no kernel uses a matrix instruction (there is no contraction);
   - no kernel writes through the scalar data cache (scalar stores, scalar
     atomics, scalar cache write-back): every store is a vector store.
@@ -54,13 +58,14 @@ def kernels(tmp_path_factory):
 
 
 def _family(name):
-    m = re.search(r"(copy|wave|thread|ws|band|corner)_kernel", name)
+    m = re.search(r"(copy|wave|thread|ws|band|corner4|corner)_kernel", name)
     return m.group(0) if m else None
 
 
 def test_every_variant_is_present(kernels):
     fams = {_family(k) for k in kernels}
-    assert {"copy_kernel", "wave_kernel", "thread_kernel", "ws_kernel", "band_kernel", "corner_kernel"} <= fams
+    assert {"copy_kernel", "wave_kernel", "thread_kernel", "ws_kernel", "band_kernel", "corner_kernel",
+            "corner4_kernel"} <= fams
     assert len(kernels) >= 200
 
 
@@ -72,6 +77,26 @@ def test_staged_kernels_load_tiles_straight_into_lds(kernels):
             assert lds_dma > 0, name
         elif fam == "thread_kernel":
             assert lds_dma == 0, name
+
+
+def test_corner4_kernels_move_4_byte_lanes(kernels):
+    seen = set()
+    for name, body in kernels.items():
+        if _family(name) != "corner4_kernel":
+            continue
+        mode = int(re.search(r"corner4_kernelILi(\d)E", name).group(1))
+        seen.add(mode)
+        dword_dma = sum(1 for l in body if re.search(r"buffer_load_dword\s", l) and re.search(r"\blds\b", l))
+        wide_dma = sum(1 for l in body if "buffer_load_dwordx4" in l and re.search(r"\blds\b", l))
+        stores4 = sum(1 for l in body if re.search(r"buffer_store_dword\s", l))
+        bperm = sum(1 for l in body if "ds_bpermute_b32" in l)
+        assert bperm > 0, name
+        if mode == 1:       # store: packed images in 16-byte lanes, the tensor in 4-byte ones
+            assert wide_dma > 0 and dword_dma == 0 and stores4 > 0, name
+        else:               # load and round trip read the tensor in 4-byte lanes
+            assert dword_dma > 0 and wide_dma == 0, name
+            assert (stores4 > 0) == (mode == 2), name
+    assert seen == {0, 1, 2}
 
 
 def test_no_matrix_instructions(kernels):

@@ -86,7 +86,8 @@ def test_summaries_keep_the_timed_kernel_only(tmp_path):
 def test_copy_kernel_names_cover_every_variant():
     for k in ("copy_kernel<0, 1, 8, 5, false>", "wave_kernel<1, 1, 8, 5>", "thread_kernel<2, 4, 2>",
               "ws_kernel<0, 2, 4, 2>", "band_kernel<2, 3, true, true, false>",
-              "corner_kernel<2, 8, 5, false, false, false, true>"):
+              "corner_kernel<2, 8, 5, false, false, false, true>",
+              "corner4_kernel<1, 8, 5, false, true, false, false>"):
         assert ps.is_copy_kernel(f"void tmap::(anonymous namespace)::{k}(tmap::KArgs)")
     assert not ps.is_copy_kernel("__amd_rocclr_copyBuffer")
     full = "void tmap::(anonymous namespace)::{}(tmap::KArgs)".format
@@ -98,6 +99,8 @@ def test_copy_kernel_names_cover_every_variant():
     assert ps.short(full("ws_kernel<1, 2, 4, 5>")) == "tmap ws_kernel<store, stages=2, nslot=4, dims=5>"
     assert ps.short(full("corner_kernel<2, 8, 5, false, false, false, true>")) == \
         "tmap corner_kernel<roundtrip, nslot=8, dims=5, nt loads=false, nt stores=false, same maps>"
+    assert ps.short(full("corner4_kernel<2, 8, 5, false, false, true, true>")) == \
+        "tmap corner4_kernel<roundtrip, nslot=8, dims=5, nt loads=false, nt stores=false, +addend, same maps>"
 
 
 def test_bench_reports_traffic_only_for_the_current_sources(tmp_path, monkeypatch):

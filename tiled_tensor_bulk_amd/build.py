@@ -22,7 +22,8 @@ ROOT = os.path.dirname(PKG)
 
 SOURCES = (["tmap_host.cpp"] + [f"tmap_{m}_r{r}.hip" for m in ("load", "store", "roundtrip") for r in (2, 5)]
            + [f"tmap_band_{m}.hip" for m in ("load", "store", "roundtrip")]
-           + [f"tmap_corner_{m}.hip" for m in ("load", "store", "roundtrip")] + ["tmap_noalloc.hip"])
+           + [f"tmap_corner_{m}.hip" for m in ("load", "store", "roundtrip")]
+           + [f"tmap_corner4_{m}.hip" for m in ("load", "store", "roundtrip")] + ["tmap_noalloc.hip"])
 ARCH = "gfx950"
 
 

@@ -144,6 +144,31 @@ __device__ __forceinline__ void dma_lds_hint(uint64_t base, uint32_t nrec, uint3
             : "memory");
 }
 
+// The same in 4-byte lanes: lane l's 4 bytes at voff land at LDS address
+// lds_addr + 4*l (zeros when voff is past nrec).
+template <bool NT>
+__device__ __forceinline__ void dma_lds_dword(uint64_t base, uint32_t nrec, uint32_t lds_addr, uint32_t voff) {
+    const i32x4 d = {__builtin_amdgcn_readfirstlane((int)(uint32_t)base),
+                     __builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xFFFFu)),
+                     __builtin_amdgcn_readfirstlane((int)nrec), kRsrcWord3};
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((int)lds_addr);
+    uint32_t saved;
+    if constexpr (NT)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
+            "buffer_load_dword %2, %3, 0 offen nt lds\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0), "v"(voff), "s"(d)
+            : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\t"
+            "buffer_load_dword %2, %3, 0 offen lds\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(m0), "v"(voff), "s"(d)
+            : "memory");
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (expcnt and lgkmcnt untouched).  The counter counts loads (direct-to-LDS
 // ones included) and stores alike and retires them in issue order, so after

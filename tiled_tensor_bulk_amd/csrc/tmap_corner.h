@@ -42,6 +42,29 @@
 namespace tmap {
 namespace {
 
+// The tiles of walker g (a wave), dealt as the other variants deal them to
+// their walkers: groups of a.group consecutive tiles, round robin, as
+// a.regions interleaved streams.  cnt tiles from t0 (none for a wave past
+// the grid).
+__device__ __forceinline__ void corner_deal(const KArgs &a, int64_t g, int64_t &cnt, int64_t &t0) {
+    const bool walker = g < (int64_t)a.grid;
+    if (a.regions > 1) {
+        const uint32_t per = a.grid / a.regions;
+        if ((uint32_t)g < per * a.regions) g = (int64_t)((uint32_t)g % a.regions) * per + (uint32_t)g / a.regions;
+    }
+    if (a.group == 0) {
+        cnt = a.deal_q + (g < a.deal_r ? 1 : 0);
+        t0 = g * a.deal_q + (g < a.deal_r ? g : a.deal_r);
+    } else {
+        const int64_t Q = a.group;
+        int64_t last = a.deal_r - g * Q;
+        last = last < 0 ? 0 : (last > Q ? Q : last);
+        cnt = a.deal_q * Q + last;
+        t0 = g * Q;
+    }
+    if (!walker) cnt = 0;
+}
+
 // Byte offset of a box corner from the map's base.  With small offsets (the
 // host has checked that every corner whose box touches the tensor is less
 // than 2 GiB from the base in every direction) the sum is taken in 32 bits:
@@ -138,32 +161,13 @@ struct CornerCopier {
     // The destination's dims, strides and span (its base is always A.dst's).
     __device__ __forceinline__ static const KMap &dst_shape(const KArgs &A) { return SAME ? A.src : A.dst; }
 
-    // the tiles are dealt to the waves as the other variants deal them to
-    // their walkers: groups of a.group consecutive tiles, round robin, as
-    // a.regions interleaved streams
     __device__ __forceinline__ void setup(uint32_t hw, uint32_t wg) {
         lane = threadIdx.x & 63u;
         parity = 0;
         edge = false;
         behind = false;
-        int64_t g = (int64_t)blockIdx.x * wg + hw;
-        const bool walker = g < (int64_t)a.grid;
-        if (a.regions > 1) {
-            const uint32_t per = a.grid / a.regions;
-            if ((uint32_t)g < per * a.regions) g = (int64_t)((uint32_t)g % a.regions) * per + (uint32_t)g / a.regions;
-        }
         int64_t t0;
-        if (a.group == 0) {
-            cnt = a.deal_q + (g < a.deal_r ? 1 : 0);
-            t0 = g * a.deal_q + (g < a.deal_r ? g : a.deal_r);
-        } else {
-            const int64_t Q = a.group;
-            int64_t last = a.deal_r - g * Q;
-            last = last < 0 ? 0 : (last > Q ? Q : last);
-            cnt = a.deal_q * Q + last;
-            t0 = g * Q;
-        }
-        if (!walker) cnt = 0;
+        corner_deal(a, (int64_t)blockIdx.x * wg + hw, cnt, t0);
         ft = ct = t0;
         fk = ck = 0;
         const KMap &sw = swept(a);

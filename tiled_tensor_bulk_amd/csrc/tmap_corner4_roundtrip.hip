@@ -1,0 +1,9 @@
+// The corner kernels in 4-byte lanes (boxes at explicit corners, one wave per
+// box, unswizzled 4- or 8-byte elements) of direction roundtrip; see tmap_corner4.h.
+#include "tmap_corner4.h"
+
+namespace tmap {
+int launch_corner4_roundtrip(int nslot, int dims, const KArgs &a, void *stream) {
+    return dims == 2 ? launch_corner4_mode<kRoundtrip, 2>(nslot, a, stream) : launch_corner4_mode<kRoundtrip, 5>(nslot, a, stream);
+}
+}  // namespace tmap

@@ -120,6 +120,7 @@ struct Plan {
     uint32_t band_g, band_rows;   // band schedule (0: whole boxes)
     bool lean;                    // the band schedule runs the lean rank-2 band kernels
     bool corner;                  // wave per box with one stage runs the corner kernels
+    bool corner4;                 // ... in 4-byte lanes (tmap_corner4.h)
 };
 
 uint32_t log2u(uint32_t v) {
@@ -303,8 +304,10 @@ constexpr uint32_t kKnownFlags = TMAP_FLAG_CONTIGUOUS | TMAP_FLAG_NONTEMPORAL | 
 
 // lean: the band schedule runs the band kernel of rank-2 sweeps.
 // elemwise: the swizzle moves data inside 16-byte chunks.
+// c4: the maps suit the corner kernels in 4-byte lanes (corner4_fits).
 tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
-                        const DeviceState &dev, bool band, bool lean, bool corners, bool elemwise, Plan &pl) {
+                        const DeviceState &dev, bool band, bool lean, bool corners, bool elemwise, bool c4,
+                        Plan &pl) {
     const uint32_t flags0 = opts ? opts->flags : 0u;
     const uint32_t per_wave_pass = tmap::kWaves * tmap::kBlockBytes;  // bytes one slot per lane covers
     const uint32_t need = (m.box_bytes + per_wave_pass - 1) / per_wave_pass;
@@ -389,11 +392,14 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
         // the corner kernel (one stage, whole-chunk swizzles) loads and
         // round-trips 8 KiB boxes fastest one to a wave (10^5 boxes: load
         // 0.73 of peak against 0.69 with 2, round trip 0.366 against 0.353)
-        // and stores them 2 to a wave (0.633; 4: 0.618); the wave kernel
-        // takes 4 and 8
+        // and stores them 2 to a wave (0.633; 4: 0.618); in 4-byte lanes it
+        // takes one box to a wave in every direction (store 0.674 against
+        // 0.667 with 2 and 0.659 with 4; load 0.743 / 0.740 / 0.735; round
+        // trip 0.427 / 0.428 / 0.422); the wave kernel takes 4 and 8
         const bool corner = stages == 1 && !elemwise;
         if (wave_box && tmap::wave_group(nslot) == 1)
-            group = mode == tmap::kStore ? 2u : (corner ? 1u : (mode == tmap::kLoad ? 4u : 8u));
+            group = (mode == tmap::kStore && !(corner && c4)) ? 2u
+                    : (corner ? 1u : (mode == tmap::kLoad ? 4u : 8u));
         else
             group = (wave_box && mode == tmap::kStore) ? 4u : 8u;
     }
@@ -479,6 +485,20 @@ bool small_offsets(const tmap::KMap &m) {
     return true;
 }
 
+// Whether the corner kernels can run in 4-byte lanes (tmap_corner4.h): the
+// swept map (and a round trip's destination, which has its box, element size
+// and swizzle) is unswizzled, has 4- or 8-byte elements, box rows of a power
+// of two from 16 to 256 bytes and at most 64 rows to a box.  Then no lane
+// straddles the tensor's dimension-0 edge, and no chunk needs patching.
+bool corner4_fits(int mode, const tmap::KArgs &a) {
+    const tmap::KMap &m = mode == tmap::kStore ? a.dst : a.src;
+    if (m.elem_size != 4 && m.elem_size != 8) return false;
+    if (m.swz_b != 0 || (mode == tmap::kRoundtrip && a.dst.swz_b != 0)) return false;
+    const uint32_t row = (uint32_t)m.box[0] * m.elem_size;
+    if (row < 16u || row > 256u || (row & (row - 1u))) return false;
+    return m.box_bytes / row <= 64u;
+}
+
 void fill_common(tmap::KArgs &a, const MapImpl &swept, const int32_t *coords, int64_t n_tiles) {
     a.coords = coords;
     a.n_tiles = n_tiles;
@@ -512,8 +532,9 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     if (why) return fail(TMAP_ERROR_INVALID_VALUE, "%s", why);
     if (band) band_setup(swept, a, g, nb, rows);
     const bool lean = band && lean_maps;
+    const bool c4 = a.coords && !band && corner4_fits(mode, a);
     tmap_status st =
-        plan_launch(mode, swept, a.n_tiles, opts, dev, band, lean, a.coords != nullptr, a.elemwise != 0, pl);
+        plan_launch(mode, swept, a.n_tiles, opts, dev, band, lean, a.coords != nullptr, a.elemwise != 0, c4, pl);
     if (st != TMAP_SUCCESS) return st;
     pl.band_g = band ? g : 0u;
     pl.band_rows = band ? rows : 0u;
@@ -533,7 +554,21 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     // 8 KiB and a swizzle that moves whole chunks: the corner kernels, which
     // hold each drained box in registers while the next one loads
     pl.corner = a.coords && pl.stages == 31 && pl.nslot <= 8 && !a.elemwise;
-    if (pl.corner) pl.lds = tmap::corner_lds_bytes(mode, pl.nslot);
+    // ... in 4-byte lanes where the maps allow it: no element-by-element
+    // patching of chunks the tensor's edge cuts, and a row's offset worked
+    // out once per box instead of once per chunk (measured on MI355X over
+    // 10^5 scattered 8 KiB fp32 boxes, fraction of 8 TB/s: round trip 0.351
+    // -> 0.427, store 0.637 -> 0.674, load 0.733 -> 0.743)
+    pl.corner4 = pl.corner && c4;
+    if (pl.corner4) {
+        const uint32_t row = (uint32_t)swept.box[0] * swept.elem_size;
+        a.c4_dshift = log2u(row / 4u);
+        a.c4_eshift = swept.elem_size == 8 ? 1u : 0u;
+        a.c4_rows = swept.box_bytes / row;
+        pl.lds = tmap::corner4_lds_bytes(mode, pl.nslot);
+    } else if (pl.corner) {
+        pl.lds = tmap::corner_lds_bytes(mode, pl.nslot);
+    }
     a.grid = pl.grid;
     a.regions = pl.regions;
     a.flags = opts ? opts->flags : 0u;
@@ -585,9 +620,14 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     if (pl.corner) {
         const int dims = r2 ? 2 : 5;
         a.off32 = small_offsets(a.src) && small_offsets(a.dst) ? 1u : 0u;
-        rc = mode == tmap::kLoad    ? tmap::launch_corner_load(pl.nslot, dims, a, stream)
-             : mode == tmap::kStore ? tmap::launch_corner_store(pl.nslot, dims, a, stream)
-                                    : tmap::launch_corner_roundtrip(pl.nslot, dims, a, stream);
+        if (pl.corner4)
+            rc = mode == tmap::kLoad    ? tmap::launch_corner4_load(pl.nslot, dims, a, stream)
+                 : mode == tmap::kStore ? tmap::launch_corner4_store(pl.nslot, dims, a, stream)
+                                        : tmap::launch_corner4_roundtrip(pl.nslot, dims, a, stream);
+        else
+            rc = mode == tmap::kLoad    ? tmap::launch_corner_load(pl.nslot, dims, a, stream)
+                 : mode == tmap::kStore ? tmap::launch_corner_store(pl.nslot, dims, a, stream)
+                                        : tmap::launch_corner_roundtrip(pl.nslot, dims, a, stream);
         if (rc != 0) {
             (void)hipGetLastError();
             return fail(TMAP_ERROR_LAUNCH, "kernel launch failed: %s", hipGetErrorString((hipError_t)rc));
@@ -1012,6 +1052,7 @@ tmap_status tmap_plan_launch(tmap_direction direction, const tmap_t *swept, cons
     if (st != TMAP_SUCCESS) return st;
     const int code = pl.stages;
     out->variant = code == 0 ? TMAP_VARIANT_THREAD_COPY
+                   : pl.corner4 ? TMAP_VARIANT_CORNER4
                    : pl.corner ? TMAP_VARIANT_CORNER
                    : code > 30 ? TMAP_VARIANT_WAVE_PER_BOX
                    : (code > 10 && code < 20) ? TMAP_VARIANT_PRODUCER_WAVE
@@ -1023,7 +1064,8 @@ tmap_status tmap_plan_launch(tmap_direction direction, const tmap_t *swept, cons
     out->slots = (uint32_t)pl.nslot;
     out->group = a.group;
     out->walkers = pl.grid;
-    const uint32_t wg = (out->variant == TMAP_VARIANT_WAVE_PER_BOX || out->variant == TMAP_VARIANT_CORNER)
+    const uint32_t wg = (out->variant == TMAP_VARIANT_WAVE_PER_BOX || out->variant == TMAP_VARIANT_CORNER ||
+                         out->variant == TMAP_VARIANT_CORNER4)
                             ? (uint32_t)tmap::wave_group(pl.nslot)
                             : 1u;
     out->workgroups = (pl.grid + wg - 1) / wg;

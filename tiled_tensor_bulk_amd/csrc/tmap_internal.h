@@ -127,6 +127,12 @@ struct KArgs {
     uint32_t band_bytes;          // bytes of one box's band
     uint32_t tiles[kMaxRank];     // ceil(dims/box) per dimension of the swept map
     uint32_t ubox[kMaxRank];      // extent of a unit per dimension
+    // Explicit corners in 4-byte lanes (tmap_corner4.h): log2 of the 4-byte
+    // words in a box row (2..6), log2 of the words in an element (0 for
+    // 4-byte, 1 for 8-byte elements) and the rows of a box (<= 64).
+    uint32_t c4_dshift;
+    uint32_t c4_eshift;
+    uint32_t c4_rows;
 };
 
 constexpr int kBandSlots = 4;             // a band stage is 4 slots per lane: 16 KiB
@@ -170,6 +176,15 @@ int launch_corner_load(int nslot, int dims, const KArgs &a, void *stream);
 int launch_corner_store(int nslot, int dims, const KArgs &a, void *stream);
 int launch_corner_roundtrip(int nslot, int dims, const KArgs &a, void *stream);
 
+// The corner kernels in 4-byte lanes (tmap_corner4.h): unswizzled maps of 4-
+// or 8-byte elements whose box rows are a power of two from 16 to 256 bytes,
+// boxes of at most 64 rows and 8 KiB; nslot 1..8 KiB of stage per wave, dims
+// as above, one translation unit per direction
+// (tmap_corner4_{load,store,roundtrip}.hip).
+int launch_corner4_load(int nslot, int dims, const KArgs &a, void *stream);
+int launch_corner4_store(int nslot, int dims, const KArgs &a, void *stream);
+int launch_corner4_roundtrip(int nslot, int dims, const KArgs &a, void *stream);
+
 // LDS bytes one workgroup of a variant uses: the ring plus the barrier words.
 inline uint32_t variant_lds_bytes(int stages, int nslot) {
     return (uint32_t)stages * (uint32_t)nslot * kWaves * kBlockBytes + 64u;
@@ -203,5 +218,16 @@ inline uint32_t corner_lds_reserve(int mode, int nslot) {
 inline uint32_t corner_lds_bytes(int mode, int nslot) {
     const uint32_t wg = (uint32_t)wave_group(nslot);
     return wg * (uint32_t)nslot * kBlockBytes + wg * 8u + corner_lds_reserve(mode, nslot);
+}
+
+// The same for the corner kernels in 4-byte lanes, which reserve nothing.
+inline uint32_t corner4_lds_reserve(int mode, int nslot) {
+    (void)mode;
+    (void)nslot;
+    return 0u;
+}
+inline uint32_t corner4_lds_bytes(int mode, int nslot) {
+    const uint32_t wg = (uint32_t)wave_group(nslot);
+    return wg * (uint32_t)nslot * kBlockBytes + wg * 8u + corner4_lds_reserve(mode, nslot);
 }
 }  // namespace tmap

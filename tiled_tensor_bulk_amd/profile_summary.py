@@ -61,7 +61,7 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-_KERNEL = re.compile(r"\b(copy|wave|thread|ws|band|corner)_kernel<")
+_KERNEL = re.compile(r"\b(copy|wave|thread|ws|band|corner|corner4)_kernel<")
 
 
 def is_copy_kernel(name: str) -> bool:
@@ -91,6 +91,13 @@ def short(name: str) -> str:
         mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
         extra = (", +addend" if m.group(6) == "true" else "") + (", same maps" if m.group(7) == "true" else "")
         return (f"tmap corner_kernel<{mode}, nslot={m.group(2)}, dims={m.group(3)}, nt loads={m.group(4)}, "
+                f"nt stores={m.group(5)}{extra}>")
+    m = re.search(r"corner4_kernel<(\d+), (\d+), (\d+), (true|false), (true|false), (true|false), (true|false)>",
+                  name)
+    if m:
+        mode = {"0": "load", "1": "store", "2": "roundtrip"}[m.group(1)]
+        extra = (", +addend" if m.group(6) == "true" else "") + (", same maps" if m.group(7) == "true" else "")
+        return (f"tmap corner4_kernel<{mode}, nslot={m.group(2)}, dims={m.group(3)}, nt loads={m.group(4)}, "
                 f"nt stores={m.group(5)}{extra}>")
     m = re.search(r"thread_kernel<(\d+), (\d+), (\d+)>", name)
     if m:

@@ -60,7 +60,7 @@ class tmap_plan(ctypes.Structure):
 
 
 DIRECTIONS = {"load": 0, "store": 1, "roundtrip": 2}
-VARIANTS = {0: "ring", 1: "thread_copy", 2: "producer_wave", 3: "wave_per_box", 4: "band", 5: "corner"}
+VARIANTS = {0: "ring", 1: "thread_copy", 2: "producer_wave", 3: "wave_per_box", 4: "band", 5: "corner", 6: "corner4"}
 
 
 class tmap_info(ctypes.Structure):
