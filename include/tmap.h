@@ -93,8 +93,9 @@ typedef struct tmap_launch_opts {
                              the band kernel, else 4 for a round trip and 1 for a load
                              or store; explicit corners: 8, for a wave-per-box store 4;
                              wave per box with boxes of 8 KiB and more: on the corner
-                             kernel 1 for a load or round trip and 2 for a store, else
-                             4 for a load, 2 for a store and 8 for a round trip)       */
+                             kernel 1 for a load or round trip and 2 for a store, 1 in
+                             every direction in 4-byte lanes (TMAP_VARIANT_CORNER4),
+                             else 4 for a load, 2 for a store and 8 for a round trip) */
     uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
                              streams, each sweeping an equal contiguous stretch of the
                              tiles (workgroup i takes stretch i mod regions), so that the
