@@ -607,10 +607,11 @@ def test_corner_offsets_far_and_wrapped():
     far outside the tensor wrap to meaningless offsets whose boxes must
     still read as zeros and write nothing; in the 64-bit case, boxes more
     than 2 GiB from the base must land where they belong.  Load, store and
-    round trip of 8 KiB boxes (rank 5) against the oracle."""
+    round trip of 8 KiB boxes (rank 5) against the oracle, unswizzled (the
+    4-byte lanes) and swizzled (the 16-byte lanes)."""
     big = 1 << 31
     i32 = np.iinfo(np.int32)
-    for case in ("wrapped", "far"):
+    for case, swz in (("wrapped", (0, 0, 0)), ("wrapped", (3, 2, 3)), ("far", (0, 0, 0)), ("far", (3, 4, 3))):
         if case == "wrapped":
             # the padded 5-D fp32 tensor (103 MB): corners whose offsets overflow 32 bits
             w = inputs.WORKLOADS["pad5d_f32"]
@@ -632,10 +633,10 @@ def test_corner_offsets_far_and_wrapped():
         c = torch.from_numpy(corners).to(DEV)
         src = dev_tensor(alloc, fill_seed=91)
         host = src.cpu().numpy()
-        m = enc(dtype, src, dims, strides, box)
-        om = Map(es=es, dims=dims, strides=strides, box=box)
-        # unswizzled fp32 boxes run in 4-byte lanes, the u8 ones in 16-byte lanes
-        assert T.tmap_plan_launch("load", m, None, True, n)["variant"] == ("corner4" if es == 4 else "corner")
+        m = enc(dtype, src, dims, strides, box, swz)
+        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+        assert T.tmap_plan_launch("load", m, None, True, n)["variant"] == ("corner" if swz[0] else "corner4")
+        case = f"{case}, swizzle {swz}"
         say(f"corner kernel, {case} offsets: load")
         got = gpu_load(m, corners, n).cpu().numpy()
         want = oracle.load_tiles(om, host, corners, n)
@@ -644,14 +645,14 @@ def test_corner_offsets_far_and_wrapped():
         say(f"corner kernel, {case} offsets: store")
         dst = dev_tensor(alloc, fill_seed=92)
         want_dst = dst.cpu().numpy().copy()
-        T.tmap_store_tiles(enc(dtype, dst, dims, strides, box), c, n, torch.from_numpy(want).to(DEV))
+        T.tmap_store_tiles(enc(dtype, dst, dims, strides, box, swz), c, n, torch.from_numpy(want).to(DEV))
         check_ok()
         oracle.store_tiles(om, want_dst, corners, n, want)
         assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, (case, "store", mm)
         say(f"corner kernel, {case} offsets: round trip")
         dst = dev_tensor(alloc, fill_seed=93)
         want_dst = dst.cpu().numpy().copy()
-        T.tmap_roundtrip(m, enc(dtype, dst, dims, strides, box), c, n)
+        T.tmap_roundtrip(m, enc(dtype, dst, dims, strides, box, swz), c, n)
         check_ok()
         oracle.roundtrip(om, host, om, want_dst, corners, n)
         assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, (case, "roundtrip", mm)
@@ -660,11 +661,11 @@ def test_corner_offsets_far_and_wrapped():
 
 
 def _corner4_case(rng):
-    """A map the corner kernels run in 4-byte lanes: unswizzled 4- or 8-byte
-    elements, box rows of a power of two from 16 to 256 bytes, at most 64
+    """A map the corner kernels run in 4-byte lanes: unswizzled elements of
+    any size, box rows of a power of two from 16 to 256 bytes, at most 64
     rows and 8 KiB to a box, padded rows and planes; and a second layout of
     other dims and pitch with the same box."""
-    es = int(rng.choice([4, 8]))
+    es = int(rng.choice([1, 2, 4, 8]))
     rank = int(rng.integers(1, 6))
     row = int(rng.choice([16, 32, 64, 128, 256]))
     max_rows = min(64, 8192 // row)
@@ -685,12 +686,12 @@ def _corner4_case(rng):
     return es, box, layout(), layout()
 
 
-@pytest.mark.parametrize("chunk", range(2))
+@pytest.mark.parametrize("chunk", range(3))
 def test_corner4_random_maps(chunk):
     """The corner kernels in 4-byte lanes, on seeded random maps they take
-    (every rank, 4- and 8-byte elements, every row width from 16 to 256
-    bytes), random corners in, across and outside the tensor and random
-    deals: load, store of the loaded images at the same corners, round trip
+    (every rank and element size, every row width from 16 to 256 bytes; with
+    1- and 2-byte elements the tensor's x edge cuts words), random corners
+    in, across and outside the tensor and random deals: load, store of the loaded images at the same corners, round trip
     into a tensor of the same layout and into one of another layout, and the
     fp32 +1.0f round trip, against the oracle; some with every stage
     poisoned before its loads."""
@@ -819,6 +820,21 @@ def test_plan_query_reports_the_schedules():
     p = T.tmap_plan_launch("store", m, None, True, 1000)
     assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"]) == ("corner", 2, 8192 + 8, 500)
     assert T.tmap_plan_launch("roundtrip", m, m, True, 1000)["group"] == 1
+    # what the 4-byte lanes take: unswizzled 4- or 8-byte elements, box rows
+    # of a power of two from 16 to 256 bytes, at most 64 rows to a box
+    def variant(dtype, pitch, box, swz=(0, 0, 0)):
+        strides = [pitch * 1000 ** k for k in range(len(box) - 1)]
+        mm = T.tmap_encode(dtype, len(box), 0x7F0000000000, [1000] * len(box), strides, box, None, swz)
+        return T.tmap_plan_launch("roundtrip", mm, mm, True, 100)["variant"]
+    assert variant("f32", 4000, [32, 64]) == "corner4"            # 128-byte rows, 64 rows
+    assert variant("f64", 8000, [2, 8, 4]) == "corner4"           # 16-byte rows, 32 rows
+    assert variant("f32", 4000, [64, 32]) == "corner4"            # 256-byte rows
+    assert variant("f32", 4000, [128, 16]) == "corner"            # 512-byte rows
+    assert variant("f32", 4000, [4, 128]) == "corner"             # 128 rows
+    assert variant("f32", 4000, [12, 16]) == "corner"             # 48-byte rows
+    assert variant("f32", 4000, [32, 64], (3, 2, 3)) == "corner"  # swizzled
+    assert variant("bf16", 2000, [64, 64]) == "corner4"           # 2-byte elements
+    assert variant("u8", 1008, [16, 8, 4]) == "corner4"           # bytes, 16-byte rows
     assert plan("pad5d_f32", "roundtrip", stages=2)["variant"] == "wave_per_box"
     assert plan("pad5d_f32", "load", flags=T.FLAG_WHOLE_BOX)["variant"] == "ring"
     assert plan("pad5d_f32", "load", stages=3)["variant"] == "ring"
@@ -904,13 +920,15 @@ def test_budget_mismatch_times_out_instead_of_hanging(mode):
 @pytest.mark.parametrize("dtype", ["u8", "f32"])
 def test_budget_mismatch_times_out_in_the_corner_kernels(dtype):
     """The same for boxes at explicit corners, one wave per box: the corner
-    kernel in 16-byte lanes (u8) and in 4-byte lanes (fp32), each direction."""
+    kernel in 16-byte lanes (swizzled u8) and in 4-byte lanes (fp32), each
+    direction."""
     es = 1 if dtype == "u8" else 4
     box = [128 // es, 64]
     dims = [256 // es, 100]
+    swz = (3, 4, 3) if es == 1 else (0, 0, 0)
     src = dev_tensor(256 * 100, fill_seed=3)
     dst = dev_tensor(256 * 100, fill_seed=4)
-    m, md = enc(dtype, src, dims, [256], box), enc(dtype, dst, dims, [256], box)
+    m, md = enc(dtype, src, dims, [256], box, swz), enc(dtype, dst, dims, [256], box, swz)
     assert T.tmap_plan_launch("load", m, None, True, 4)["variant"] == ("corner" if es == 1 else "corner4")
     coords = torch.tensor([[0, 0], [3, 5], [-7, 60], [200 // es, -10]], dtype=torch.int32, device=DEV)
     out = dev_tensor(8192 * 4)
@@ -927,7 +945,7 @@ def test_budget_mismatch_times_out_in_the_corner_kernels(dtype):
     # the library keeps working afterwards
     T.tmap_load_tiles(m, coords, 4, out)
     check_ok()
-    om = Map(es=es, dims=dims, strides=[256], box=box)
+    om = Map(es=es, dims=dims, strides=[256], box=box, swizzle=swz)
     assert out.cpu().numpy().tobytes() == oracle.load_tiles(om, src.cpu().numpy(), coords.cpu().numpy(), 4).tobytes()
 
 

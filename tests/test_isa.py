@@ -10,7 +10,8 @@ kernel:
   - the corner kernels in 4-byte lanes load from the tensor with 4-byte
     direct-to-LDS loads (`buffer_load_dword ... lds`), fetch each slot's
     row offset across lanes (`ds_bpermute_b32`) and store to the tensor in
-    4-byte stores;
+    4-byte stores, with 1- and 2-byte accesses for the words the tensor's
+    edge cuts;
   - no kernel uses a matrix instruction (there is no contraction);
   - no kernel writes through the scalar data cache (scalar stores, scalar
     atomics, scalar cache write-back): every store is a vector store.
@@ -91,11 +92,16 @@ def test_corner4_kernels_move_4_byte_lanes(kernels):
         stores4 = sum(1 for l in body if re.search(r"buffer_store_dword\s", l))
         bperm = sum(1 for l in body if "ds_bpermute_b32" in l)
         assert bperm > 0, name
+        # words the tensor's x edge cuts (1- and 2-byte elements) move element by element
+        narrow_loads = {k for k in ("buffer_load_ubyte", "buffer_load_ushort") if any(k in l for l in body)}
+        narrow_stores = {k for k in ("buffer_store_byte", "buffer_store_short") if any(k in l for l in body)}
         if mode == 1:       # store: packed images in 16-byte lanes, the tensor in 4-byte ones
             assert wide_dma > 0 and dword_dma == 0 and stores4 > 0, name
         else:               # load and round trip read the tensor in 4-byte lanes
             assert dword_dma > 0 and wide_dma == 0, name
             assert (stores4 > 0) == (mode == 2), name
+        assert len(narrow_loads) == (0 if mode == 1 else 2), (name, narrow_loads)
+        assert len(narrow_stores) == (0 if mode == 0 else 2), (name, narrow_stores)
     assert seen == {0, 1, 2}
 
 

@@ -1,16 +1,20 @@
 // tmap_corner4.h -- boxes at explicit corners in 4-byte lanes: the corner
-// path for unswizzled maps of 4- or 8-byte elements whose box rows are a
-// power of two from 16 to 256 bytes, in boxes of at most 64 rows and 8 KiB.
+// path for unswizzled maps whose box rows are a power of two from 16 to 256
+// bytes, in boxes of at most 64 rows and 8 KiB.
 //
 // The 16-byte lanes of the corner kernel (tmap_corner.h) can straddle the
 // tensor's dimension-0 edge, and each chunk cut that way is patched element
-// by element.  A 4-byte lane never holds part of an inside element and part
-// of an outside one (elements are 4 or 8 bytes here), so every lane is
-// wholly in or out, and the hardware does all of the clipping: a load past
-// num_records lands zeros ("GPU TMA", "Why architecture matters here": the
-// copy itself zero-fills out-of-bounds elements) and a store past it is
-// dropped.  The image a wave lands is the same as in 16-byte lanes: slot i
-// of lane l is the box's 4-byte word 64 i + l, at LDS stage + 256 i + 4 l.
+// by element.  A 4-byte lane of 4- or 8-byte elements never holds part of an
+// inside element and part of an outside one, so every lane is wholly in or
+// out, and the hardware does all of the clipping: a load past num_records
+// lands zeros ("GPU TMA", "Why architecture matters here": the copy itself
+// zero-fills out-of-bounds elements) and a store past it is dropped.  With
+// 1- or 2-byte elements the edge can cut a word; only the lanes of the
+// columns it cuts (at most one at each edge of the row) then move their
+// inside elements one by one, in a pass a wave takes only when one of its
+// lanes needs it.  The image a wave lands is the same as in 16-byte lanes:
+// slot i of lane l is the box's 4-byte word 64 i + l, at LDS stage + 256 i
+// + 4 l.
 //
 // A box row is 4 * 2^dshift bytes, so a slot's 64 lanes cover 64 / 2^dshift
 // whole rows and a lane's column (its word in the row) is the same in every
@@ -61,13 +65,95 @@ __device__ __forceinline__ uint32_t c4_row(const KArgs &A, const KMap &m, const 
     return in ? ro : kOob;
 }
 
-// This lane's column: the byte offset of its word in the row, or kOob when
-// the word's element lies outside the window in dimension 0.
+// This lane's column against the window in dimension 0: v, the byte offset
+// of its word in the row when every element of the word lies inside, else
+// kOob; cut, whether the window takes some of the word's elements but not
+// all (1- and 2-byte elements only).
+struct C4Col {
+    uint32_t v;
+    bool cut;
+};
+
 template <int R>
-__device__ __forceinline__ uint32_t c4_col(const KArgs &A, const Win<R> &w, uint32_t lane) {
-    const uint32_t x = lane & ((1u << A.c4_dshift) - 1u);
-    const uint32_t e = x >> A.c4_eshift;
-    return (e - w.lo[0] < w.hi[0] - w.lo[0]) ? x * 4u : kOob;
+__device__ __forceinline__ C4Col c4_col(const KArgs &A, const Win<R> &w, uint32_t lane) {
+    const uint32_t xb = (lane & ((1u << A.c4_dshift) - 1u)) * 4u;
+    const uint32_t e0 = xb >> A.c4_esz, e1 = (xb + 3u) >> A.c4_esz;  // the word's first and last element
+    const bool full = (e0 >= w.lo[0]) && (e1 < w.hi[0]);
+    const bool any = (e0 < w.hi[0]) && (e1 >= w.lo[0]) && (w.lo[0] < w.hi[0]);
+    return {full ? xb : kOob, any && !full};
+}
+
+// The cut word at byte offset row + xb: its elements of ES bytes inside the
+// window [lo0, hi0), loaded one by one, the others zero (what the
+// out-of-range load landed for the whole word).
+template <int ES>
+__device__ __forceinline__ uint32_t c4_cut_word(__amdgpu_buffer_rsrc_t r, uint32_t row, uint32_t xb, uint32_t lo0,
+                                                uint32_t hi0) {
+    uint32_t w = 0;
+#pragma unroll
+    for (uint32_t b = 0; b < 4u; b += ES) {
+        if (((xb + b) / ES) - lo0 >= hi0 - lo0) continue;
+        const uint32_t v = ES == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, row + xb + b, 0, 0)
+                                   : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, row + xb + b, 0, 0);
+        w |= v << (8u * b);
+    }
+    return w;
+}
+
+// The landed stage's cut words (slots whose row is inside, lanes whose
+// column the window cuts), rewritten whole with their inside elements.  In
+// batches of 8 slots, so that a batch's loads are in flight together; every
+// lane takes part in the row fetches, which read other lanes.
+template <int NI, int ES>
+__device__ __forceinline__ void c4_patch_cut(uint8_t *stage, uint32_t lane, bool cut, uint32_t rowv, uint32_t ra,
+                                             uint32_t rstep, __amdgpu_buffer_rsrc_t r, uint32_t xb, uint32_t lo0,
+                                             uint32_t hi0) {
+    constexpr int B = NI < 8 ? NI : 8;
+#pragma unroll 1
+    for (int i0 = 0; i0 < NI; i0 += B) {
+        uint32_t row[B], w[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            row[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(ra + (uint32_t)(i0 + j) * rstep), (int)rowv);
+#pragma unroll
+        for (int j = 0; j < B; ++j) w[j] = (cut && row[j] != kOob) ? c4_cut_word<ES>(r, row[j], xb, lo0, hi0) : 0u;
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (cut && row[j] != kOob) *(uint32_t *)(stage + ((uint32_t)(i0 + j) * 64u + lane) * 4u) = w[j];
+    }
+}
+
+// The stage's cut words stored through the destination: only their
+// elements inside the window [lo0, hi0), one by one.  Batches of 8 slots as
+// above (the words are read again from the stage: 1- and 2-byte elements
+// take no +addend).
+template <int NI, int ES, bool NT>
+__device__ __forceinline__ void c4_store_cut(const uint8_t *stage, uint32_t lane, bool cut, uint32_t rowv, uint32_t ra,
+                                             uint32_t rstep, __amdgpu_buffer_rsrc_t r, uint32_t xb, uint32_t lo0,
+                                             uint32_t hi0) {
+    constexpr int B = NI < 8 ? NI : 8;
+#pragma unroll 1
+    for (int i0 = 0; i0 < NI; i0 += B) {
+        uint32_t row[B], w[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            row[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(ra + (uint32_t)(i0 + j) * rstep), (int)rowv);
+            w[j] = *(const uint32_t *)(stage + ((uint32_t)(i0 + j) * 64u + lane) * 4u);
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            if (!cut || row[j] == kOob) continue;
+#pragma unroll
+            for (uint32_t b = 0; b < 4u; b += ES) {
+                if (((xb + b) / ES) - lo0 >= hi0 - lo0) continue;
+                if constexpr (ES == 1)
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w[j] >> (8u * b)), r, row[j] + xb + b, 0, NT ? 2 : 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w[j] >> (8u * b)), r, row[j] + xb + b, 0,
+                                                          NT ? 2 : 0);
+            }
+        }
+    }
 }
 
 // Slot i's offset: its row's value, fetched from the lane that holds it,
@@ -146,8 +232,11 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
         asm volatile("" : "+v"(ra));
         if (a.flags & TMAP_FLAG_DEBUG_POISON) poison_blocks(stage, NSLOT, 1, lane);
         bar_arrive_expect(bar, budget, lane, 1);
-        // destination offsets of the slots, held until the drain
+        // destination offsets of the slots, held until the drain, and the
+        // row tables and columns of the two sides for the cut words
         uint32_t off[NI];
+        uint32_t srow = kOob, drow = kOob;
+        C4Col scol = {kOob, false}, dcol = {kOob, false};
         if constexpr (MODE == kStore) {
             const uint64_t base = (uint64_t)a.packed + (uint64_t)t * bytes;
 #pragma unroll
@@ -157,14 +246,14 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
             }
         } else {
             const Win<R> w = corner_window<R>(a.src, c);
-            const uint32_t rowv = c4_row<R>(a, a.src, w, lane);
-            const uint32_t colv = c4_col<R>(a, w, lane);
+            srow = c4_row<R>(a, a.src, w, lane);
+            scol = c4_col<R>(a, w, lane);
             const uint64_t base = a.src.base + (uint64_t)corner_offset<R>(a, a.src, c);
             // every slot's offset first, so that the row fetches overlap,
             // then the loads
             uint32_t so[NI];
 #pragma unroll
-            for (int i = 0; i < NI; ++i) so[i] = c4_slot(rowv, colv, ra + (uint32_t)i * rstep);
+            for (int i = 0; i < NI; ++i) so[i] = c4_slot(srow, scol.v, ra + (uint32_t)i * rstep);
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 dma_lds_dword<NTL>(base, a.src.span, m0 + (uint32_t)i * 256u, so[i]);
@@ -177,15 +266,32 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
             // maps' fields would not fit in scalar registers)
             const KArgs &A = MODE == kRoundtrip ? reread(a) : a;
             const Win<R> w = corner_window<R>(A.dst, c);
-            const uint32_t rowv = c4_row<R>(A, A.dst, w, lane);
-            const uint32_t colv = c4_col<R>(A, w, lane);
+            drow = c4_row<R>(A, A.dst, w, lane);
+            dcol = c4_col<R>(A, w, lane);
 #pragma unroll
-            for (int i = 0; i < NI; ++i) off[i] = c4_slot(rowv, colv, ra + (uint32_t)i * rstep);
+            for (int i = 0; i < NI; ++i) off[i] = c4_slot(drow, dcol.v, ra + (uint32_t)i * rstep);
+        } else if constexpr (SAME) {
+            drow = srow;
+            dcol = scol;
         }
 
         // land: every slot's load has written the stage (zeros past the
-        // tensor), then the record's byte count and phase
+        // tensor); the cut words' inside elements; then the record's byte
+        // count and phase
         wait_vmcnt<0>();
+        if constexpr (MODE != kStore) {
+            if (__builtin_amdgcn_ballot_w64(scol.cut)) {
+                const KArgs &A = reread(a);
+                const Win<R> w = corner_window<R>(A.src, c);
+                const __amdgpu_buffer_rsrc_t r =
+                    make_rsrc(A.src.base + (uint64_t)corner_offset<R>(A, A.src, c), A.src.span);
+                const uint32_t xb = (lane & ((1u << A.c4_dshift) - 1u)) * 4u;
+                if (A.c4_esz == 0)
+                    c4_patch_cut<NI, 1>(stage, lane, scol.cut, srow, ra, rstep, r, xb, w.lo[0], w.hi[0]);
+                else
+                    c4_patch_cut<NI, 2>(stage, lane, scol.cut, srow, ra, rstep, r, xb, w.lo[0], w.hi[0]);
+            }
+        }
         __builtin_amdgcn_s_waitcnt(kWaitLgkm);
         asm volatile("" ::: "memory");
         bar_complete(bar, bytes, lane, 1);
@@ -224,6 +330,15 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
                 make_rsrc(A.dst.base + (uint64_t)corner_offset<R>(A, dm, c), dm.span);
 #pragma unroll
             for (int i = 0; i < NI; ++i) c4_store4<NTS>(v[i], r, off[i]);
+            if (__builtin_amdgcn_ballot_w64(dcol.cut)) {
+                // the words the destination's window cuts, element by element
+                const Win<R> w = corner_window<R>(dm, c);
+                const uint32_t xb = (lane & ((1u << A.c4_dshift) - 1u)) * 4u;
+                if (A.c4_esz == 0)
+                    c4_store_cut<NI, 1, NTS>(stage, lane, dcol.cut, drow, ra, rstep, r, xb, w.lo[0], w.hi[0]);
+                else
+                    c4_store_cut<NI, 2, NTS>(stage, lane, dcol.cut, drow, ra, rstep, r, xb, w.lo[0], w.hi[0]);
+            }
         }
         // the stage is free once these reads have completed
         __builtin_amdgcn_s_waitcnt(kWaitLgkm);

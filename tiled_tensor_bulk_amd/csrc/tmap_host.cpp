@@ -487,12 +487,12 @@ bool small_offsets(const tmap::KMap &m) {
 
 // Whether the corner kernels can run in 4-byte lanes (tmap_corner4.h): the
 // swept map (and a round trip's destination, which has its box, element size
-// and swizzle) is unswizzled, has 4- or 8-byte elements, box rows of a power
-// of two from 16 to 256 bytes and at most 64 rows to a box.  Then no lane
-// straddles the tensor's dimension-0 edge, and no chunk needs patching.
+// and swizzle) is unswizzled, has box rows of a power of two from 16 to 256
+// bytes and at most 64 rows to a box.  Then a lane's column is the same in
+// every slot, and only a word of 1- or 2-byte elements that the tensor's
+// dimension-0 edge cuts needs its elements moved one by one.
 bool corner4_fits(int mode, const tmap::KArgs &a) {
     const tmap::KMap &m = mode == tmap::kStore ? a.dst : a.src;
-    if (m.elem_size != 4 && m.elem_size != 8) return false;
     if (m.swz_b != 0 || (mode == tmap::kRoundtrip && a.dst.swz_b != 0)) return false;
     const uint32_t row = (uint32_t)m.box[0] * m.elem_size;
     if (row < 16u || row > 256u || (row & (row - 1u))) return false;
@@ -563,7 +563,7 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     if (pl.corner4) {
         const uint32_t row = (uint32_t)swept.box[0] * swept.elem_size;
         a.c4_dshift = log2u(row / 4u);
-        a.c4_eshift = swept.elem_size == 8 ? 1u : 0u;
+        a.c4_esz = log2u(swept.elem_size);
         a.c4_rows = swept.box_bytes / row;
         pl.lds = tmap::corner4_lds_bytes(mode, pl.nslot);
     } else if (pl.corner) {

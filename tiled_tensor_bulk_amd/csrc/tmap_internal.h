@@ -128,10 +128,10 @@ struct KArgs {
     uint32_t tiles[kMaxRank];     // ceil(dims/box) per dimension of the swept map
     uint32_t ubox[kMaxRank];      // extent of a unit per dimension
     // Explicit corners in 4-byte lanes (tmap_corner4.h): log2 of the 4-byte
-    // words in a box row (2..6), log2 of the words in an element (0 for
-    // 4-byte, 1 for 8-byte elements) and the rows of a box (<= 64).
+    // words in a box row (2..6), log2 of the element size (0..3) and the
+    // rows of a box (<= 64).
     uint32_t c4_dshift;
-    uint32_t c4_eshift;
+    uint32_t c4_esz;
     uint32_t c4_rows;
 };
 
@@ -176,9 +176,9 @@ int launch_corner_load(int nslot, int dims, const KArgs &a, void *stream);
 int launch_corner_store(int nslot, int dims, const KArgs &a, void *stream);
 int launch_corner_roundtrip(int nslot, int dims, const KArgs &a, void *stream);
 
-// The corner kernels in 4-byte lanes (tmap_corner4.h): unswizzled maps of 4-
-// or 8-byte elements whose box rows are a power of two from 16 to 256 bytes,
-// boxes of at most 64 rows and 8 KiB; nslot 1..8 KiB of stage per wave, dims
+// The corner kernels in 4-byte lanes (tmap_corner4.h): unswizzled maps whose
+// box rows are a power of two from 16 to 256 bytes, boxes of at most 64 rows
+// and 8 KiB; nslot 1..8 KiB of stage per wave, dims
 // as above, one translation unit per direction
 // (tmap_corner4_{load,store,roundtrip}.hip).
 int launch_corner4_load(int nslot, int dims, const KArgs &a, void *stream);
@@ -208,8 +208,9 @@ inline uint32_t wave_lds_bytes(int stages, int nslot) {
 // LDS the corner kernels reserve per workgroup beyond their stages and
 // barrier words: the load of 8 KiB boxes takes 11 KiB in all, which keeps
 // fourteen such workgroups on a CU instead of eighteen (measured on MI355X
-// over 10^5 scattered 8 KiB boxes: 0.707 -> 0.730 of peak; sixteen 0.725,
-// thirteen 0.68-0.72).  The stores and round trips lose with fewer.
+// over 10^5 scattered 8 KiB fp32 boxes, before such boxes moved to the
+// 4-byte lanes: 0.707 -> 0.730 of peak; sixteen 0.725, thirteen
+// 0.68-0.72).  The stores and round trips lose with fewer.
 inline uint32_t corner_lds_reserve(int mode, int nslot) {
     return (mode == kLoad && nslot == 8) ? 11264u - (8u * kBlockBytes + 8u) : 0u;
 }
@@ -220,7 +221,9 @@ inline uint32_t corner_lds_bytes(int mode, int nslot) {
     return wg * (uint32_t)nslot * kBlockBytes + wg * 8u + corner_lds_reserve(mode, nslot);
 }
 
-// The same for the corner kernels in 4-byte lanes, which reserve nothing.
+// The same for the corner kernels in 4-byte lanes, which reserve nothing
+// (up to 5 KiB more per workgroup moved the 10^5 scattered 8 KiB fp32 boxes
+// by under 1% in every direction).
 inline uint32_t corner4_lds_reserve(int mode, int nslot) {
     (void)mode;
     (void)nslot;
