@@ -411,11 +411,12 @@ typedef enum tmap_variant {
     TMAP_VARIANT_CORNER = 5,        /* wave per box with one stage, boxes of at most 8 KiB and a
                                        swizzle that moves whole chunks: each wave holds a drained
                                        box in registers while the next one loads               */
-    TMAP_VARIANT_CORNER4 = 6        /* the same boxes in 4-byte lanes, for unswizzled maps with
-                                       box rows of a power of two from 16 to 256 bytes, at most
-                                       64 rows to a box: the hardware's bounds check clips every
-                                       lane, and only words of 1- or 2-byte elements that the
-                                       tensor's edge cuts move element by element              */
+    TMAP_VARIANT_CORNER4 = 6        /* the same boxes in 4-byte lanes, for maps with box rows of a
+                                       power of two from 16 to 256 bytes, at most 64 rows to a
+                                       box, and no swizzle or one that moves whole 16-byte
+                                       chunks within rows: the hardware's bounds check clips
+                                       every lane, and only words of 1- or 2-byte elements that
+                                       the tensor's edge cuts move element by element          */
 } tmap_variant;
 typedef struct tmap_plan {
     uint32_t variant;     /* tmap_variant                                                  */

@@ -410,8 +410,9 @@ def test_wave_per_box_workgroup_shapes(box_kib):
     c = torch.from_numpy(coords).to(DEV)
     for stages in (1, 2):
         p = T.tmap_plan_launch("load", m, None, True, len(coords), stages=stages, flags=T.FLAG_WAVE_PER_BOX)
-        # one stage and boxes up to 8 KiB: the corner kernel
-        assert p["variant"] == ("corner" if stages == 1 and box_kib <= 8 else "wave_per_box")
+        # one stage and boxes up to 8 KiB: the corner kernel in 4-byte lanes
+        # (its rows of 64 and 128 bytes hold the swizzle's XOR)
+        assert p["variant"] == ("corner4" if stages == 1 and box_kib <= 8 else "wave_per_box")
         assert p["workgroups"] == -(-p["walkers"] // (4 if box_kib < 8 else 1))
         for grid in (0, 1, 3, 6):
             say(f"wave workgroups: box {box_kib} KiB stages={stages} grid={grid}")
@@ -608,10 +609,12 @@ def test_corner_offsets_far_and_wrapped():
     still read as zeros and write nothing; in the 64-bit case, boxes more
     than 2 GiB from the base must land where they belong.  Load, store and
     round trip of 8 KiB boxes (rank 5) against the oracle, unswizzled (the
-    4-byte lanes) and swizzled (the 16-byte lanes)."""
+    4-byte lanes), with a swizzle inside the rows (the 4-byte lanes) and
+    with one whose XOR reaches past them (the 16-byte lanes)."""
     big = 1 << 31
     i32 = np.iinfo(np.int32)
-    for case, swz in (("wrapped", (0, 0, 0)), ("wrapped", (3, 2, 3)), ("far", (0, 0, 0)), ("far", (3, 4, 3))):
+    for case, swz in (("wrapped", (0, 0, 0)), ("wrapped", (3, 2, 3)), ("wrapped", (3, 3, 3)),
+                      ("far", (0, 0, 0)), ("far", (3, 4, 3)), ("far", (3, 5, 3))):
         if case == "wrapped":
             # the padded 5-D fp32 tensor (103 MB): corners whose offsets overflow 32 bits
             w = inputs.WORKLOADS["pad5d_f32"]
@@ -635,7 +638,8 @@ def test_corner_offsets_far_and_wrapped():
         host = src.cpu().numpy()
         m = enc(dtype, src, dims, strides, box, swz)
         om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
-        assert T.tmap_plan_launch("load", m, None, True, n)["variant"] == ("corner" if swz[0] else "corner4")
+        past_row = swz in ((3, 3, 3), (3, 5, 3))
+        assert T.tmap_plan_launch("load", m, None, True, n)["variant"] == ("corner" if past_row else "corner4")
         case = f"{case}, swizzle {swz}"
         say(f"corner kernel, {case} offsets: load")
         got = gpu_load(m, corners, n).cpu().numpy()
@@ -683,34 +687,43 @@ def _corner4_case(rng):
             strides.append(s)
             s *= dims[d] + int(rng.integers(0, 2))
         return dims, strides, s
-    return es, box, layout(), layout()
+    # half the maps take a swizzle the 4-byte lanes handle: whole 16-byte
+    # chunks (target bit tb >= 4) moved within a row (tb + B <= log2(row))
+    lg, lrow = es.bit_length() - 1, row.bit_length() - 1
+    swz = (0, 0, 0)
+    if rng.integers(0, 2) and lrow - 4 >= 1:
+        b = int(rng.integers(1, min(4, lrow - 4) + 1))
+        m = int(rng.integers(max(0, 4 - lg), lrow - lg - b + 1))
+        swz = (b, m, int(rng.integers(b, b + 4)))
+    return es, box, swz, layout(), layout()
 
 
-@pytest.mark.parametrize("chunk", range(3))
+@pytest.mark.parametrize("chunk", range(4))
 def test_corner4_random_maps(chunk):
     """The corner kernels in 4-byte lanes, on seeded random maps they take
-    (every rank and element size, every row width from 16 to 256 bytes; with
-    1- and 2-byte elements the tensor's x edge cuts words), random corners
-    in, across and outside the tensor and random deals: load, store of the loaded images at the same corners, round trip
+    (every rank and element size, every row width from 16 to 256 bytes, with
+    and without a swizzle inside the rows; with 1- and 2-byte elements the
+    tensor's x edge cuts words), random corners in, across and outside the
+    tensor and random deals: load, store of the loaded images at the same corners, round trip
     into a tensor of the same layout and into one of another layout, and the
     fp32 +1.0f round trip, against the oracle; some with every stage
     poisoned before its loads."""
     rng = np.random.default_rng(9700 + chunk)
     for i in range(30):
-        es, box, (dims, strides, alloc), (ddims, dstrides, dalloc) = _corner4_case(rng)
+        es, box, swz, (dims, strides, alloc), (ddims, dstrides, dalloc) = _corner4_case(rng)
         coords = inputs.random_corners(dims, box, int(rng.integers(1, 400)), int(rng.integers(1 << 30)))
         n = len(coords)
         opts = dict(grid_wgs=int(rng.choice([0, 0, 1, 3])), group=int(rng.choice([0, 1, 2, 4])),
                     regions=int(rng.choice([0, 1, 2, 3])),
                     flags=int(rng.choice([0, T.FLAG_NONTEMPORAL, T.FLAG_CACHED_PACKED, T.FLAG_DEBUG_POISON])))
-        say(f"corner4 chunk {chunk} case {i}: es={es} dims={dims} strides={strides} box={box} "
+        say(f"corner4 chunk {chunk} case {i}: es={es} dims={dims} strides={strides} box={box} swz={swz} "
             f"ddims={ddims} dstrides={dstrides} n={n} opts={opts}")
         dt = dt_of(es)
-        om = Map(es=es, dims=dims, strides=strides, box=box)
-        omd = Map(es=es, dims=ddims, strides=dstrides, box=box)
+        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+        omd = Map(es=es, dims=ddims, strides=dstrides, box=box, swizzle=swz)
         src = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
         host = src.cpu().numpy()
-        m = enc(dt, src, dims, strides, box)
+        m = enc(dt, src, dims, strides, box, swz)
         bb = T.tmap_box_bytes(m)
         assert T.tmap_plan_launch("load", m, None, True, n, **opts)["variant"] == "corner4"
         packed = gpu_load(m, coords, n, **opts)
@@ -719,7 +732,7 @@ def test_corner4_random_maps(chunk):
         c = torch.from_numpy(coords).to(DEV)
         dst = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
         want_dst = dst.cpu().numpy().copy()
-        T.tmap_store_tiles(enc(dt, dst, dims, strides, box), c, n, packed, **opts)
+        T.tmap_store_tiles(enc(dt, dst, dims, strides, box, swz), c, n, packed, **opts)
         check_ok()
         oracle.store_tiles(om, want_dst, coords, n, want)
         assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("store", mm)
@@ -727,7 +740,7 @@ def test_corner4_random_maps(chunk):
             d_dims, d_strides, d_alloc, od = (ddims, dstrides, dalloc, omd) if other else (dims, strides, alloc, om)
             dst = dev_tensor(d_alloc, fill_seed=int(rng.integers(1 << 30)))
             want_dst = dst.cpu().numpy().copy()
-            md = enc(dt, dst, d_dims, d_strides, box)
+            md = enc(dt, dst, d_dims, d_strides, box, swz)
             assert T.tmap_plan_launch("roundtrip", m, md, True, n, **opts)["variant"] == "corner4"
             add = es == 4 and bool(rng.integers(0, 2))
             if add:
@@ -811,17 +824,18 @@ def test_plan_query_reports_the_schedules():
     p = T.tmap_plan_launch("load", m, None, True, 1000)
     assert (p["variant"], p["slots"], p["walkers"]) == ("corner4", 2, 125)
     assert p["workgroups"] == 32 and p["lds_bytes"] == 4 * 2048 + 4 * 8
-    # 16-bit elements in 128-byte-swizzled 8 KiB boxes: the corner kernel in
-    # 16-byte lanes; its loads reserve 11 KiB of LDS to a workgroup, its
-    # stores take two boxes to a wave
-    m = T.tmap_encode("bf16", 2, 0x7F0000000000, [1000, 1000], [2048], [64, 64], None, (3, 3, 3))
+    # 16-bit elements in 8 KiB boxes with a swizzle whose XOR reaches past a
+    # 128-byte row: the corner kernel in 16-byte lanes; its loads reserve
+    # 11 KiB of LDS to a workgroup, its stores take two boxes to a wave
+    m = T.tmap_encode("bf16", 2, 0x7F0000000000, [1000, 1000], [2048], [64, 64], None, (3, 4, 3))
     p = T.tmap_plan_launch("load", m, None, True, 1000)
     assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"]) == ("corner", 1, 11264, 1000)
     p = T.tmap_plan_launch("store", m, None, True, 1000)
     assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"]) == ("corner", 2, 8192 + 8, 500)
     assert T.tmap_plan_launch("roundtrip", m, m, True, 1000)["group"] == 1
-    # what the 4-byte lanes take: unswizzled 4- or 8-byte elements, box rows
-    # of a power of two from 16 to 256 bytes, at most 64 rows to a box
+    # what the 4-byte lanes take: box rows of a power of two from 16 to 256
+    # bytes, at most 64 rows to a box, no swizzle or one that moves whole
+    # 16-byte chunks within rows with a key of at most 4 bits
     def variant(dtype, pitch, box, swz=(0, 0, 0)):
         strides = [pitch * 1000 ** k for k in range(len(box) - 1)]
         mm = T.tmap_encode(dtype, len(box), 0x7F0000000000, [1000] * len(box), strides, box, None, swz)
@@ -832,7 +846,11 @@ def test_plan_query_reports_the_schedules():
     assert variant("f32", 4000, [128, 16]) == "corner"            # 512-byte rows
     assert variant("f32", 4000, [4, 128]) == "corner"             # 128 rows
     assert variant("f32", 4000, [12, 16]) == "corner"             # 48-byte rows
-    assert variant("f32", 4000, [32, 64], (3, 2, 3)) == "corner"  # swizzled
+    assert variant("f32", 4000, [32, 64], (3, 2, 3)) == "corner4"  # 128-byte swizzle, 128-byte rows
+    assert variant("bf16", 2000, [64, 64], (3, 3, 3)) == "corner4"
+    assert variant("f32", 4000, [16, 64], (3, 2, 3)) == "corner"   # 128-byte swizzle, 64-byte rows
+    assert variant("f32", 4000, [32, 64], (3, 3, 3)) == "corner"   # its XOR reaches past the row
+    assert variant("f32", 4000, [32, 64], (1, 0, 1)) == "wave_per_box"  # moves elements inside chunks
     assert variant("bf16", 2000, [64, 64]) == "corner4"           # 2-byte elements
     assert variant("u8", 1008, [16, 8, 4]) == "corner4"           # bytes, 16-byte rows
     assert plan("pad5d_f32", "roundtrip", stages=2)["variant"] == "wave_per_box"
@@ -925,7 +943,7 @@ def test_budget_mismatch_times_out_in_the_corner_kernels(dtype):
     es = 1 if dtype == "u8" else 4
     box = [128 // es, 64]
     dims = [256 // es, 100]
-    swz = (3, 4, 3) if es == 1 else (0, 0, 0)
+    swz = (3, 5, 3) if es == 1 else (0, 0, 0)     # its XOR reaches past the 128-byte row
     src = dev_tensor(256 * 100, fill_seed=3)
     dst = dev_tensor(256 * 100, fill_seed=4)
     m, md = enc(dtype, src, dims, [256], box, swz), enc(dtype, dst, dims, [256], box, swz)
@@ -1015,16 +1033,19 @@ def test_corner_round_trip_between_layouts(rank):
         dstrides, dalloc = layout(ddims)
         src = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
         host = src.cpu().numpy()
-        ms = enc("f32", src, dims, strides, box, (2, 2, 3))
+        # a 64-byte-granule swizzle whose XOR reaches past every row here:
+        # the corner kernel in 16-byte lanes
+        swz = (3, 4, 3)
+        ms = enc("f32", src, dims, strides, box, swz)
         corners = inputs.random_corners(dims, box, 700, seed=int(rng.integers(1 << 30)))
         c = torch.from_numpy(corners).to(DEV)
-        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=(2, 2, 3))
-        omd = Map(es=es, dims=ddims, strides=dstrides, box=box, swizzle=(2, 2, 3))
+        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+        omd = Map(es=es, dims=ddims, strides=dstrides, box=box, swizzle=swz)
         for add in (False, True):
             say(f"corner round trip between layouts: rank {rank}, box {box_kib} KiB, add={add}")
             dst = dev_tensor(dalloc, fill_seed=int(rng.integers(1 << 30)))
             want = dst.cpu().numpy().copy()
-            md = enc("f32", dst, ddims, dstrides, box, (2, 2, 3))
+            md = enc("f32", dst, ddims, dstrides, box, swz)
             assert T.tmap_plan_launch("roundtrip", ms, md, True, len(corners))["variant"] == "corner"
             if add:
                 T.tmap_roundtrip_add_f32(ms, md, c, len(corners), 1.0)

@@ -26,6 +26,15 @@
 // column stays out of range.  Per box that is one pass of row arithmetic
 // for the whole wave, then two instructions per slot.
 //
+// A swizzle whose XOR lands inside a row (its target bits below the row's
+// size) leaves every word in its row and moves it within the row: the word
+// at column x of row r holds the logical column x ^ key(r) ^ key(x), the
+// keys being the swizzle's source bits of the row and of the column.  The
+// slot fetching the row's entry then also gets the row's key (kept in the
+// entry's low 4 bits: in-box row offsets are multiples of 16), forms its
+// logical column and looks its range test up in a column table (one entry
+// per logical column, a lane each), with a second ds_bpermute.
+//
 // Each wave walks its own share of the corners through its own one-box
 // stage and 8-byte byte record, as the corner kernel does:
 //
@@ -47,11 +56,26 @@
 namespace tmap {
 namespace {
 
-// Row `lane` of a box at the corner whose window is w: its in-box byte
-// offset in map m, or kOob when the row lies outside the tensor or past the
-// box's rows.  In-box offsets are below the map's span (< 2 GiB).
-template <int R>
-__device__ __forceinline__ uint32_t c4_row(const KArgs &A, const KMap &m, const Win<R> &w, uint32_t lane) {
+// Column entries: the byte offset of a word in its row when every element of
+// the word lies inside the window in dimension 0, kOob when none does, and
+// kOob | 1 when the window cuts the word (1- and 2-byte elements only).
+constexpr uint32_t kCut = kOob | 1u;
+
+// One side of the copy (the map a box is loaded from or stored to) for one
+// box, as this lane holds it.
+//   row  the row table entry for row `lane`: the row's in-box byte offset
+//        (with a swizzle, | its swizzle key in bits 0..3), or kOob when the
+//        row lies outside the tensor or past the box's rows;
+//   col  without a swizzle, this lane's column entry; with one, the column
+//        table entry of logical column lane % (words per row);
+//   xb   this lane's column byte (with a swizzle, XOR its own bits' key).
+struct C4Side {
+    uint32_t row, col, xb;
+};
+
+template <int R, bool SWZ>
+__device__ __forceinline__ C4Side c4_side(const KArgs &A, const KMap &m, const Win<R> &w, uint32_t lane) {
+    C4Side s;
     uint32_t r = lane, ro = 0;
     bool in = lane < A.c4_rows;
 #pragma unroll
@@ -62,64 +86,98 @@ __device__ __forceinline__ uint32_t c4_row(const KArgs &A, const KMap &m, const 
         in = in & (id - w.lo[d] < w.hi[d] - w.lo[d]);
         ro += id * (uint32_t)m.strides[d];
     }
-    return in ? ro : kOob;
-}
-
-// This lane's column against the window in dimension 0: v, the byte offset
-// of its word in the row when every element of the word lies inside, else
-// kOob; cut, whether the window takes some of the word's elements but not
-// all (1- and 2-byte elements only).
-struct C4Col {
-    uint32_t v;
-    bool cut;
-};
-
-template <int R>
-__device__ __forceinline__ C4Col c4_col(const KArgs &A, const Win<R> &w, uint32_t lane) {
+    if constexpr (SWZ) ro |= ((lane << (A.c4_dshift + 2u)) >> A.c4_sb) & A.c4_smask;
+    s.row = in ? ro : kOob;
     const uint32_t xb = (lane & ((1u << A.c4_dshift) - 1u)) * 4u;
     const uint32_t e0 = xb >> A.c4_esz, e1 = (xb + 3u) >> A.c4_esz;  // the word's first and last element
     const bool full = (e0 >= w.lo[0]) && (e1 < w.hi[0]);
     const bool any = (e0 < w.hi[0]) && (e1 >= w.lo[0]) && (w.lo[0] < w.hi[0]);
-    return {full ? xb : kOob, any && !full};
+    s.col = full ? xb : (any ? kCut : kOob);
+    s.xb = SWZ ? xb ^ (((xb >> A.c4_sb) & A.c4_smask) << A.c4_tb) : xb;
+    return s;
 }
 
-// The cut word at byte offset row + xb: its elements of ES bytes inside the
+// One slot of this lane: the row table entry of its row (raddr: the lane
+// holding it, times 4), its logical column byte and that column's entry.
+struct C4Slot {
+    uint32_t row, xl, col;
+};
+
+template <bool SWZ>
+__device__ __forceinline__ C4Slot c4_slot(const KArgs &A, const C4Side &s, uint32_t raddr) {
+    C4Slot q;
+    q.row = (uint32_t)__builtin_amdgcn_ds_bpermute((int)raddr, (int)s.row);
+    if constexpr (SWZ) {
+        q.xl = s.xb ^ ((q.row & 15u) << A.c4_tb);
+        q.col = (uint32_t)__builtin_amdgcn_ds_bpermute((int)q.xl, (int)s.col);
+        q.row &= ~15u;
+    } else {
+        q.xl = s.xb;
+        q.col = s.col;
+    }
+    return q;
+}
+
+// The slot's byte offset from the box corner, or >= kOob when its row or
+// column lies outside (the saturating add keeps kOob + anything >= kOob).
+__device__ __forceinline__ uint32_t c4_off(const C4Slot &q) {
+    return __builtin_elementwise_add_sat(q.row, q.col & ~1u);
+}
+
+// Every slot's offset (off[i] for slot i).  With a swizzle each slot takes
+// two table fetches, and each offset is pinned where it is formed: left
+// alone, the compiler would sink the final add to the stores and hold both
+// fetched entries of every slot until then (131 VGPRs for a store, three
+// waves to a SIMD).
+template <int NI, bool SWZ>
+__device__ __forceinline__ void c4_offsets(const KArgs &A, const C4Side &s, uint32_t ra, uint32_t rstep,
+                                           uint32_t (&off)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        off[i] = c4_off(c4_slot<SWZ>(A, s, ra + (uint32_t)i * rstep));
+        if constexpr (SWZ) asm volatile("" : "+v"(off[i]));
+    }
+}
+
+// Whether the window cuts the slot's word inside a row that is inside.
+__device__ __forceinline__ bool c4_cut(const C4Slot &q) { return (q.col == kCut) & (q.row < kOob); }
+
+// The cut word at byte offset row + xl: its elements of ES bytes inside the
 // window [lo0, hi0), loaded one by one, the others zero (what the
 // out-of-range load landed for the whole word).
 template <int ES>
-__device__ __forceinline__ uint32_t c4_cut_word(__amdgpu_buffer_rsrc_t r, uint32_t row, uint32_t xb, uint32_t lo0,
+__device__ __forceinline__ uint32_t c4_cut_word(__amdgpu_buffer_rsrc_t r, uint32_t row, uint32_t xl, uint32_t lo0,
                                                 uint32_t hi0) {
     uint32_t w = 0;
 #pragma unroll
     for (uint32_t b = 0; b < 4u; b += ES) {
-        if (((xb + b) / ES) - lo0 >= hi0 - lo0) continue;
-        const uint32_t v = ES == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, row + xb + b, 0, 0)
-                                   : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, row + xb + b, 0, 0);
+        if (((xl + b) / ES) - lo0 >= hi0 - lo0) continue;
+        const uint32_t v = ES == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, row + xl + b, 0, 0)
+                                   : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, row + xl + b, 0, 0);
         w |= v << (8u * b);
     }
     return w;
 }
 
-// The landed stage's cut words (slots whose row is inside, lanes whose
-// column the window cuts), rewritten whole with their inside elements.  In
-// batches of 8 slots, so that a batch's loads are in flight together; every
-// lane takes part in the row fetches, which read other lanes.
-template <int NI, int ES>
-__device__ __forceinline__ void c4_patch_cut(uint8_t *stage, uint32_t lane, bool cut, uint32_t rowv, uint32_t ra,
-                                             uint32_t rstep, __amdgpu_buffer_rsrc_t r, uint32_t xb, uint32_t lo0,
+// The landed stage's cut words, rewritten whole with their inside elements.
+// In batches of 8 slots, so that a batch's loads are in flight together;
+// every lane takes part in the table fetches, which read other lanes.
+template <int NI, int ES, bool SWZ>
+__device__ __forceinline__ void c4_patch_cut(const KArgs &A, uint8_t *stage, uint32_t lane, const C4Side &s,
+                                             uint32_t ra, uint32_t rstep, __amdgpu_buffer_rsrc_t r, uint32_t lo0,
                                              uint32_t hi0) {
     constexpr int B = NI < 8 ? NI : 8;
 #pragma unroll 1
     for (int i0 = 0; i0 < NI; i0 += B) {
-        uint32_t row[B], w[B];
+        C4Slot q[B];
+        uint32_t w[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) q[j] = c4_slot<SWZ>(A, s, ra + (uint32_t)(i0 + j) * rstep);
+#pragma unroll
+        for (int j = 0; j < B; ++j) w[j] = c4_cut(q[j]) ? c4_cut_word<ES>(r, q[j].row, q[j].xl, lo0, hi0) : 0u;
 #pragma unroll
         for (int j = 0; j < B; ++j)
-            row[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(ra + (uint32_t)(i0 + j) * rstep), (int)rowv);
-#pragma unroll
-        for (int j = 0; j < B; ++j) w[j] = (cut && row[j] != kOob) ? c4_cut_word<ES>(r, row[j], xb, lo0, hi0) : 0u;
-#pragma unroll
-        for (int j = 0; j < B; ++j)
-            if (cut && row[j] != kOob) *(uint32_t *)(stage + ((uint32_t)(i0 + j) * 64u + lane) * 4u) = w[j];
+            if (c4_cut(q[j])) *(uint32_t *)(stage + ((uint32_t)(i0 + j) * 64u + lane) * 4u) = w[j];
     }
 }
 
@@ -127,40 +185,34 @@ __device__ __forceinline__ void c4_patch_cut(uint8_t *stage, uint32_t lane, bool
 // elements inside the window [lo0, hi0), one by one.  Batches of 8 slots as
 // above (the words are read again from the stage: 1- and 2-byte elements
 // take no +addend).
-template <int NI, int ES, bool NT>
-__device__ __forceinline__ void c4_store_cut(const uint8_t *stage, uint32_t lane, bool cut, uint32_t rowv, uint32_t ra,
-                                             uint32_t rstep, __amdgpu_buffer_rsrc_t r, uint32_t xb, uint32_t lo0,
+template <int NI, int ES, bool SWZ, bool NT>
+__device__ __forceinline__ void c4_store_cut(const KArgs &A, const uint8_t *stage, uint32_t lane, const C4Side &s,
+                                             uint32_t ra, uint32_t rstep, __amdgpu_buffer_rsrc_t r, uint32_t lo0,
                                              uint32_t hi0) {
     constexpr int B = NI < 8 ? NI : 8;
 #pragma unroll 1
     for (int i0 = 0; i0 < NI; i0 += B) {
-        uint32_t row[B], w[B];
+        C4Slot q[B];
+        uint32_t w[B];
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            row[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(ra + (uint32_t)(i0 + j) * rstep), (int)rowv);
+            q[j] = c4_slot<SWZ>(A, s, ra + (uint32_t)(i0 + j) * rstep);
             w[j] = *(const uint32_t *)(stage + ((uint32_t)(i0 + j) * 64u + lane) * 4u);
         }
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            if (!cut || row[j] == kOob) continue;
+            if (!c4_cut(q[j])) continue;
 #pragma unroll
             for (uint32_t b = 0; b < 4u; b += ES) {
-                if (((xb + b) / ES) - lo0 >= hi0 - lo0) continue;
+                if (((q[j].xl + b) / ES) - lo0 >= hi0 - lo0) continue;
+                const uint32_t o = q[j].row + q[j].xl + b;
                 if constexpr (ES == 1)
-                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w[j] >> (8u * b)), r, row[j] + xb + b, 0, NT ? 2 : 0);
+                    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w[j] >> (8u * b)), r, o, 0, NT ? 2 : 0);
                 else
-                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w[j] >> (8u * b)), r, row[j] + xb + b, 0,
-                                                          NT ? 2 : 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w[j] >> (8u * b)), r, o, 0, NT ? 2 : 0);
             }
         }
     }
-}
-
-// Slot i's offset: its row's value, fetched from the lane that holds it,
-// plus the column.  The saturating add keeps kOob + anything >= kOob.
-__device__ __forceinline__ uint32_t c4_slot(uint32_t rowv, uint32_t colv, uint32_t raddr) {
-    const uint32_t r = (uint32_t)__builtin_amdgcn_ds_bpermute((int)raddr, (int)rowv);
-    return __builtin_elementwise_add_sat(r, colv);
 }
 
 // Corner of tile t: uniform scalar loads through the constant address space.
@@ -191,9 +243,10 @@ __device__ __forceinline__ void c4_store16(const i32x4 &v, __amdgpu_buffer_rsrc_
 
 // SAME: a round trip whose destination map has the source's dims and
 // strides (only its base differs): the stores reuse the loads' offsets.
+// SWZ: the maps' swizzle moves words within rows (see above).
 // `a` must stay the kernel's only argument: reread() finds it at the start
 // of the argument segment.
-template <int MODE, int NSLOT, int R, bool NTL, bool NTS, bool ADD, bool SAME>
+template <int MODE, int NSLOT, int R, bool NTL, bool NTS, bool ADD, bool SAME, bool SWZ>
 __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const KArgs a) {
     static_assert(!SAME || MODE == kRoundtrip, "a load or store has one tensor map");
     constexpr int WG = wave_group(NSLOT);
@@ -233,10 +286,9 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
         if (a.flags & TMAP_FLAG_DEBUG_POISON) poison_blocks(stage, NSLOT, 1, lane);
         bar_arrive_expect(bar, budget, lane, 1);
         // destination offsets of the slots, held until the drain, and the
-        // row tables and columns of the two sides for the cut words
+        // tables of the two sides for the cut words
         uint32_t off[NI];
-        uint32_t srow = kOob, drow = kOob;
-        C4Col scol = {kOob, false}, dcol = {kOob, false};
+        C4Side ss = {kOob, kOob, 0u}, ds = {kOob, kOob, 0u};
         if constexpr (MODE == kStore) {
             const uint64_t base = (uint64_t)a.packed + (uint64_t)t * bytes;
 #pragma unroll
@@ -246,14 +298,12 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
             }
         } else {
             const Win<R> w = corner_window<R>(a.src, c);
-            srow = c4_row<R>(a, a.src, w, lane);
-            scol = c4_col<R>(a, w, lane);
+            ss = c4_side<R, SWZ>(a, a.src, w, lane);
             const uint64_t base = a.src.base + (uint64_t)corner_offset<R>(a, a.src, c);
-            // every slot's offset first, so that the row fetches overlap,
+            // every slot's offset first, so that the table fetches overlap,
             // then the loads
             uint32_t so[NI];
-#pragma unroll
-            for (int i = 0; i < NI; ++i) so[i] = c4_slot(srow, scol.v, ra + (uint32_t)i * rstep);
+            c4_offsets<NI, SWZ>(a, ss, ra, rstep, so);
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 dma_lds_dword<NTL>(base, a.src.span, m0 + (uint32_t)i * 256u, so[i]);
@@ -266,13 +316,10 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
             // maps' fields would not fit in scalar registers)
             const KArgs &A = MODE == kRoundtrip ? reread(a) : a;
             const Win<R> w = corner_window<R>(A.dst, c);
-            drow = c4_row<R>(A, A.dst, w, lane);
-            dcol = c4_col<R>(A, w, lane);
-#pragma unroll
-            for (int i = 0; i < NI; ++i) off[i] = c4_slot(drow, dcol.v, ra + (uint32_t)i * rstep);
+            ds = c4_side<R, SWZ>(A, A.dst, w, lane);
+            c4_offsets<NI, SWZ>(A, ds, ra, rstep, off);
         } else if constexpr (SAME) {
-            drow = srow;
-            dcol = scol;
+            ds = ss;
         }
 
         // land: every slot's load has written the stage (zeros past the
@@ -280,16 +327,16 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
         // count and phase
         wait_vmcnt<0>();
         if constexpr (MODE != kStore) {
-            if (__builtin_amdgcn_ballot_w64(scol.cut)) {
+            // a wave with a cut column (1- and 2-byte elements only)
+            if (__builtin_amdgcn_ballot_w64(ss.col == kCut)) {
                 const KArgs &A = reread(a);
                 const Win<R> w = corner_window<R>(A.src, c);
                 const __amdgpu_buffer_rsrc_t r =
                     make_rsrc(A.src.base + (uint64_t)corner_offset<R>(A, A.src, c), A.src.span);
-                const uint32_t xb = (lane & ((1u << A.c4_dshift) - 1u)) * 4u;
                 if (A.c4_esz == 0)
-                    c4_patch_cut<NI, 1>(stage, lane, scol.cut, srow, ra, rstep, r, xb, w.lo[0], w.hi[0]);
+                    c4_patch_cut<NI, 1, SWZ>(A, stage, lane, ss, ra, rstep, r, w.lo[0], w.hi[0]);
                 else
-                    c4_patch_cut<NI, 2>(stage, lane, scol.cut, srow, ra, rstep, r, xb, w.lo[0], w.hi[0]);
+                    c4_patch_cut<NI, 2, SWZ>(A, stage, lane, ss, ra, rstep, r, w.lo[0], w.hi[0]);
             }
         }
         __builtin_amdgcn_s_waitcnt(kWaitLgkm);
@@ -330,14 +377,13 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
                 make_rsrc(A.dst.base + (uint64_t)corner_offset<R>(A, dm, c), dm.span);
 #pragma unroll
             for (int i = 0; i < NI; ++i) c4_store4<NTS>(v[i], r, off[i]);
-            if (__builtin_amdgcn_ballot_w64(dcol.cut)) {
+            if (__builtin_amdgcn_ballot_w64(ds.col == kCut)) {
                 // the words the destination's window cuts, element by element
                 const Win<R> w = corner_window<R>(dm, c);
-                const uint32_t xb = (lane & ((1u << A.c4_dshift) - 1u)) * 4u;
                 if (A.c4_esz == 0)
-                    c4_store_cut<NI, 1, NTS>(stage, lane, dcol.cut, drow, ra, rstep, r, xb, w.lo[0], w.hi[0]);
+                    c4_store_cut<NI, 1, SWZ, NTS>(A, stage, lane, ds, ra, rstep, r, w.lo[0], w.hi[0]);
                 else
-                    c4_store_cut<NI, 2, NTS>(stage, lane, dcol.cut, drow, ra, rstep, r, xb, w.lo[0], w.hi[0]);
+                    c4_store_cut<NI, 2, SWZ, NTS>(A, stage, lane, ds, ra, rstep, r, w.lo[0], w.hi[0]);
             }
         }
         // the stage is free once these reads have completed
@@ -351,31 +397,37 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
     __builtin_amdgcn_s_waitcnt(0);
 }
 
-template <int MODE, int NSLOT, int R, bool ADD, bool SAME>
+template <int MODE, int NSLOT, int R, bool ADD, bool SAME, bool SWZ>
 KernelFn pick_corner4_hints(bool ntl, bool nts) {
     if constexpr (MODE == kRoundtrip) {
         // both sides are the tensor's: one hint for both
         (void)nts;
-        return ntl ? corner4_kernel<MODE, NSLOT, R, true, true, ADD, SAME>
-                   : corner4_kernel<MODE, NSLOT, R, false, false, ADD, SAME>;
+        return ntl ? corner4_kernel<MODE, NSLOT, R, true, true, ADD, SAME, SWZ>
+                   : corner4_kernel<MODE, NSLOT, R, false, false, ADD, SAME, SWZ>;
     } else {
         if (ntl)
-            return nts ? corner4_kernel<MODE, NSLOT, R, true, true, ADD, SAME>
-                       : corner4_kernel<MODE, NSLOT, R, true, false, ADD, SAME>;
-        return nts ? corner4_kernel<MODE, NSLOT, R, false, true, ADD, SAME>
-                   : corner4_kernel<MODE, NSLOT, R, false, false, ADD, SAME>;
+            return nts ? corner4_kernel<MODE, NSLOT, R, true, true, ADD, SAME, SWZ>
+                       : corner4_kernel<MODE, NSLOT, R, true, false, ADD, SAME, SWZ>;
+        return nts ? corner4_kernel<MODE, NSLOT, R, false, true, ADD, SAME, SWZ>
+                   : corner4_kernel<MODE, NSLOT, R, false, false, ADD, SAME, SWZ>;
+    }
+}
+
+template <int MODE, int R, bool ADD, bool SAME, bool SWZ>
+KernelFn pick_corner4_slots(int nslot, bool ntl, bool nts) {
+    switch (nslot) {
+        case 1: return pick_corner4_hints<MODE, 1, R, ADD, SAME, SWZ>(ntl, nts);
+        case 2: return pick_corner4_hints<MODE, 2, R, ADD, SAME, SWZ>(ntl, nts);
+        case 4: return pick_corner4_hints<MODE, 4, R, ADD, SAME, SWZ>(ntl, nts);
+        case 8: return pick_corner4_hints<MODE, 8, R, ADD, SAME, SWZ>(ntl, nts);
+        default: return nullptr;
     }
 }
 
 template <int MODE, int R, bool ADD, bool SAME = false>
-KernelFn pick_corner4(int nslot, bool ntl, bool nts) {
-    switch (nslot) {
-        case 1: return pick_corner4_hints<MODE, 1, R, ADD, SAME>(ntl, nts);
-        case 2: return pick_corner4_hints<MODE, 2, R, ADD, SAME>(ntl, nts);
-        case 4: return pick_corner4_hints<MODE, 4, R, ADD, SAME>(ntl, nts);
-        case 8: return pick_corner4_hints<MODE, 8, R, ADD, SAME>(ntl, nts);
-        default: return nullptr;
-    }
+KernelFn pick_corner4(int nslot, bool swz, bool ntl, bool nts) {
+    return swz ? pick_corner4_slots<MODE, R, ADD, SAME, true>(nslot, ntl, nts)
+               : pick_corner4_slots<MODE, R, ADD, SAME, false>(nslot, ntl, nts);
 }
 
 // Launch the 4-byte-lane corner kernel of direction MODE over a.grid waves
@@ -383,16 +435,17 @@ KernelFn pick_corner4(int nslot, bool ntl, bool nts) {
 template <int MODE, int R>
 int launch_corner4_mode(int nslot, const KArgs &a, void *stream) {
     const bool ntl = nontemporal_loads<MODE>(a.flags), nts = nontemporal_stores<MODE>(a.flags);
+    const bool swz = (MODE == kStore ? a.dst : a.src).swz_b != 0;
     KernelFn fn = nullptr;
     if constexpr (MODE == kRoundtrip) {
         if (same_shape(a.src, a.dst))
-            fn = a.add_f32 ? pick_corner4<MODE, R, true, true>(nslot, ntl, nts)
-                           : pick_corner4<MODE, R, false, true>(nslot, ntl, nts);
+            fn = a.add_f32 ? pick_corner4<MODE, R, true, true>(nslot, swz, ntl, nts)
+                           : pick_corner4<MODE, R, false, true>(nslot, swz, ntl, nts);
         else
-            fn = a.add_f32 ? pick_corner4<MODE, R, true>(nslot, ntl, nts)
-                           : pick_corner4<MODE, R, false>(nslot, ntl, nts);
+            fn = a.add_f32 ? pick_corner4<MODE, R, true>(nslot, swz, ntl, nts)
+                           : pick_corner4<MODE, R, false>(nslot, swz, ntl, nts);
     } else {
-        fn = pick_corner4<MODE, R, false>(nslot, ntl, nts);
+        fn = pick_corner4<MODE, R, false>(nslot, swz, ntl, nts);
     }
     if (!fn) return (int)hipErrorInvalidValue;
     const uint32_t wg = (uint32_t)wave_group(nslot);

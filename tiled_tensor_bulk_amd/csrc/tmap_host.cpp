@@ -486,17 +486,21 @@ bool small_offsets(const tmap::KMap &m) {
 }
 
 // Whether the corner kernels can run in 4-byte lanes (tmap_corner4.h): the
-// swept map (and a round trip's destination, which has its box, element size
-// and swizzle) is unswizzled, has box rows of a power of two from 16 to 256
-// bytes and at most 64 rows to a box.  Then a lane's column is the same in
-// every slot, and only a word of 1- or 2-byte elements that the tensor's
-// dimension-0 edge cuts needs its elements moved one by one.
+// swept map (a round trip's destination has its box, element size and
+// swizzle) has box rows of a power of two from 16 to 256 bytes and at most
+// 64 rows to a box.  Then a lane's column is the same in every slot, and
+// only a word of 1- or 2-byte elements that the tensor's dimension-0 edge
+// cuts needs its elements moved one by one.  A swizzle qualifies when it
+// moves whole 16-byte chunks within rows (its XOR's target bits below the
+// row's size) with a key of at most 4 bits.
 bool corner4_fits(int mode, const tmap::KArgs &a) {
     const tmap::KMap &m = mode == tmap::kStore ? a.dst : a.src;
-    if (m.swz_b != 0 || (mode == tmap::kRoundtrip && a.dst.swz_b != 0)) return false;
     const uint32_t row = (uint32_t)m.box[0] * m.elem_size;
     if (row < 16u || row > 256u || (row & (row - 1u))) return false;
-    return m.box_bytes / row <= 64u;
+    if (m.box_bytes / row > 64u) return false;
+    if (m.swz_b == 0) return true;
+    const uint32_t tb = m.swz_m + log2u(m.elem_size);
+    return !a.elemwise && m.swz_b <= 4u && tb + m.swz_b <= log2u(row);
 }
 
 void fill_common(tmap::KArgs &a, const MapImpl &swept, const int32_t *coords, int64_t n_tiles) {
@@ -564,6 +568,9 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
         const uint32_t row = (uint32_t)swept.box[0] * swept.elem_size;
         a.c4_dshift = log2u(row / 4u);
         a.c4_esz = log2u(swept.elem_size);
+        a.c4_tb = swept.swz_m + a.c4_esz;
+        a.c4_sb = swept.swz_m + swept.swz_s + a.c4_esz;
+        a.c4_smask = (1u << swept.swz_b) - 1u;
         a.c4_rows = swept.box_bytes / row;
         pl.lds = tmap::corner4_lds_bytes(mode, pl.nslot);
     } else if (pl.corner) {

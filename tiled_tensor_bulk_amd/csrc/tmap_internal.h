@@ -133,6 +133,12 @@ struct KArgs {
     uint32_t c4_dshift;
     uint32_t c4_esz;
     uint32_t c4_rows;
+    // ... and of a swizzle that moves words within rows: the byte-offset
+    // bit its XOR lands on (tb), the bit it takes its key from (sb), and
+    // the key's mask (2^B - 1, B <= 4)
+    uint32_t c4_tb;
+    uint32_t c4_sb;
+    uint32_t c4_smask;
 };
 
 constexpr int kBandSlots = 4;             // a band stage is 4 slots per lane: 16 KiB
@@ -176,9 +182,9 @@ int launch_corner_load(int nslot, int dims, const KArgs &a, void *stream);
 int launch_corner_store(int nslot, int dims, const KArgs &a, void *stream);
 int launch_corner_roundtrip(int nslot, int dims, const KArgs &a, void *stream);
 
-// The corner kernels in 4-byte lanes (tmap_corner4.h): unswizzled maps whose
-// box rows are a power of two from 16 to 256 bytes, boxes of at most 64 rows
-// and 8 KiB; nslot 1..8 KiB of stage per wave, dims
+// The corner kernels in 4-byte lanes (tmap_corner4.h): maps whose box rows
+// are a power of two from 16 to 256 bytes, boxes of at most 64 rows and 8 KiB,
+// unswizzled or with a swizzle that moves whole words within rows; nslot 1..8 KiB of stage per wave, dims
 // as above, one translation unit per direction
 // (tmap_corner4_{load,store,roundtrip}.hip).
 int launch_corner4_load(int nslot, int dims, const KArgs &a, void *stream);
