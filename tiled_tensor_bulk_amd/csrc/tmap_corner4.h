@@ -1,6 +1,7 @@
 // tmap_corner4.h -- boxes at explicit corners in 4-byte lanes: the corner
-// path for unswizzled maps whose box rows are a power of two from 16 to 256
-// bytes, in boxes of at most 64 rows and 8 KiB.
+// path for maps whose box rows are a power of two from 16 to 256 bytes, in
+// boxes of at most 64 rows and 8 KiB, unswizzled or with a swizzle that moves
+// whole 16-byte chunks within rows.
 //
 // The 16-byte lanes of the corner kernel (tmap_corner.h) can straddle the
 // tensor's dimension-0 edge, and each chunk cut that way is patched element
@@ -24,7 +25,7 @@
 // row's value from the lane that holds it (ds_bpermute) and adds its
 // column's offset with a saturating add, so that an out-of-range row or
 // column stays out of range.  Per box that is one pass of row arithmetic
-// for the whole wave, then two instructions per slot.
+// for the whole wave, then two instructions per slot (without a swizzle).
 //
 // A swizzle whose XOR lands inside a row (its target bits below the row's
 // size) leaves every word in its row and moves it within the row: the word
