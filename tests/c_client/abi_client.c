@@ -16,6 +16,15 @@
 
 static int failed = 0;
 
+/* The plan's variant codes are part of the ABI: a C99 compile-time check
+ * that they keep their values. */
+typedef char variant_codes_keep_their_values[(TMAP_VARIANT_RING == 0 && TMAP_VARIANT_THREAD_COPY == 1 &&
+                                              TMAP_VARIANT_PRODUCER_WAVE == 2 && TMAP_VARIANT_WAVE_PER_BOX == 3 &&
+                                              TMAP_VARIANT_BAND == 4 && TMAP_VARIANT_CORNER == 5 &&
+                                              TMAP_VARIANT_CORNER4 == 6)
+                                                 ? 1
+                                                 : -1];
+
 #define CHECK(cond)                                                        \
     do {                                                                   \
         if (!(cond)) {                                                     \
