@@ -80,7 +80,8 @@ typedef struct tmap_launch_opts {
     uint32_t stages;      /* LDS ring depth 1..4 (default 2; 1 with explicit corners and
                              when each workgroup takes a single band unit; 3 for round
                              trips on the band schedule, and for every direction of
-                             the band kernel, TMAP_VARIANT_BAND)                         */
+                             the band kernel, TMAP_VARIANT_BAND, except 4 for round
+                             trips of whole 16 KiB boxes there)                         */
     uint32_t grid_wgs;    /* workgroups launched; fewer than there are groups makes each
                              take several (default: one workgroup per group; with
                              TMAP_FLAG_CONTIGUOUS, twice what fits in LDS per CU; in
@@ -90,7 +91,8 @@ typedef struct tmap_launch_opts {
     uint32_t group;       /* tiles (band units) dealt to a workgroup at a time, a power of
                              two <= 64 (default: enough boxes side by side to span 512
                              bytes of a row, at least 2 and at most 8; band units: 2 on
-                             the band kernel, else 4 for a round trip and 1 for a load
+                             the band kernel (4 for round trips of whole 16 KiB boxes),
+                             else 4 for a round trip and 1 for a load
                              or store; explicit corners: 8, for a wave-per-box store 4;
                              wave per box with boxes of 8 KiB and more: on the corner
                              kernel 1 for a load or round trip and 2 for a store, 1 in
@@ -102,9 +104,10 @@ typedef struct tmap_launch_opts {
                              tiles in flight lie in that many places of the tensor
                              instead of one.  How the addresses in flight fall on the
                              HBM channels decides which is faster (default: 2 for loads
-                             and stores on the band schedule and for band-kernel round
-                             trips of tensors whose row pitch is not a power of two,
-                             else 1)                                                   */
+                             and stores on the band schedule, for band-kernel round
+                             trips of tensors whose row pitch is not a power of two, and
+                             for whole boxes on the band kernel except round trips of
+                             16 KiB boxes; else 1)                                     */
     uint32_t band_rows;   /* band schedule: box rows per band, a power of two.  A unit is
                              then 16 KiB / (band_rows * box row bytes) boxes side by
                              side.  Default on the band kernel: 8 for a round trip (2

@@ -866,6 +866,14 @@ def test_plan_query_reports_the_schedules():
     p = plan("sweep2g_u8", "load", flags=T.FLAG_PRODUCER_WAVE)
     assert (p["variant"], p["band_boxes"], p["workgroups"]) == ("producer_wave", 0, 8 * cus)
     assert plan("sweep2g_u8", "load", flags=T.FLAG_CONTIGUOUS | T.FLAG_WHOLE_BOX)["group"] == 0
+    # whole boxes on the band kernel: round trips of 16 KiB boxes take 4
+    # stages x 4 units in one stream, everything else 3 x 2 in two streams
+    whole = T.FLAG_NONTEMPORAL | T.FLAG_WHOLE_BOX
+    for name, direction, want in (("sweep2g_u8", "roundtrip", (1, 128, 4, 4, 1)), ("sweep2g_u8", "load", (1, 128, 3, 2, 2)),
+                                  ("plus1_f32", "roundtrip", (1, 64, 4, 4, 1)), ("ragged_bf16", "roundtrip", (2, 64, 3, 2, 2))):
+        p = plan(name, direction, flags=whole)
+        assert p["variant"] == "band", (name, direction)
+        assert (p["band_boxes"], p["band_rows"], p["stages"], p["group"], p["regions"]) == want, (name, direction, p)
 
 
 def test_zero_tiles_launch_nothing():

@@ -333,6 +333,13 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // A tensor that stays in the last-level cache takes 2 stages (fp16
     // strips: 0.835 against 0.78 at 3)
     if (lean && !(opts && opts->stages)) stages = (resident_span(m) && !(flags0 & TMAP_FLAG_BAND)) ? 2 : 3;
+    // whole 16 KiB boxes (one to a unit) in a round trip on the band kernel:
+    // 4 stages x 4 units in one stream (measured on MI355X, fraction of 8
+    // TB/s, against 3 x 2 in two streams: 2 GiB u8 0.738 / 0.705, 1 GiB fp32
+    // +1.0f 0.774 / 0.755; ragged bf16's 8 KiB boxes keep 3 x 2, two streams)
+    const bool whole16 = lean && (flags0 & TMAP_FLAG_WHOLE_BOX) && mode == tmap::kRoundtrip &&
+                         m.box_bytes == 16384u && !resident_span(m);
+    if (whole16 && !(opts && opts->stages)) stages = 4;
     if (stages < 1 || stages > 4)
         return fail(TMAP_ERROR_INVALID_VALUE, "stages must be 1..4 (got %d)", stages);
     const uint32_t flags = opts ? opts->flags : 0u;
@@ -381,6 +388,7 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // the band kernel: 2 units a workgroup in every direction (its setup is
     // a few shifts, so short-lived workgroups cost little; measured on the
     // 2 GiB u8, 1 GiB fp32 and ragged bf16 sweeps, 4 units lose 3-8%)
+    if (!group && whole16) group = 4u;
     if (!group && lean) group = 2u;
     if (!group && band) group = mode == tmap::kRoundtrip ? 4u : 1u;
     // explicit corners: 8 tiles to a walker; a wave-per-box store takes 4.
@@ -553,7 +561,9 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     // round trips 0.705 / 0.761 / 0.785 on the 2 GiB u8, 1 GiB fp32 and
     // ragged bf16 sweeps against 0.699 / 0.755 / 0.697 on the generic ring;
     // loads 0.721 / 0.755 / 0.782)
-    if (lean && (opts && (opts->flags & TMAP_FLAG_WHOLE_BOX)) && !opts->regions && !resident) pl.regions = 2u;
+    if (lean && (opts && (opts->flags & TMAP_FLAG_WHOLE_BOX)) && !opts->regions && !resident &&
+        !(mode == tmap::kRoundtrip && swept.box_bytes == 16384u))
+        pl.regions = 2u;
     // explicit corners, one wave per box with one stage, boxes of at most
     // 8 KiB and a swizzle that moves whole chunks: the corner kernels, which
     // hold each drained box in registers while the next one loads
