@@ -664,6 +664,47 @@ def test_corner_offsets_far_and_wrapped():
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("dtype,swz", [("bf16", (3, 3, 3)), ("u8", (3, 4, 3))], ids=["bf16_128B_swizzle", "u8_128B_swizzle"])
+def test_scattered_narrow_swizzled_boxes_full(dtype, swz):
+    """10^5 scattered 8 KiB boxes of 2- and 1-byte elements with the 128-byte
+    swizzle, on a padded 5-D tensor of the scattered workload's shape (box
+    rows of 128 bytes, row pitch the dims rounded up to 16 bytes): the 4-byte
+    lanes' swizzled instances and their element-by-element pass for words the
+    x edge cuts, at full size.  Every packed image, the store of all of them
+    through the same corners and the round trip, against the oracle."""
+    es = 1 if dtype == "u8" else 2
+    dims = [129, 65, 33, 13, 7]
+    box = [128 // es, 8, 4, 2, 1]
+    pitch = -(-129 * es // 16) * 16
+    strides = [pitch, pitch * 65, pitch * 65 * 33, pitch * 65 * 33 * 13]
+    alloc = strides[-1] * 7
+    say(f"scattered {dtype} boxes, swizzle {swz}: load, store, round trip of 1e5 corners; full oracle")
+    src = dev_tensor(alloc, fill_seed=77 + es)
+    host = src.cpu().numpy()
+    m = enc(dtype, src, dims, strides, box, swz)
+    om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+    corners = inputs.random_corners(dims, box, 100_000, seed=50 + es)
+    n = len(corners)
+    assert T.tmap_plan_launch("load", m, None, True, n)["variant"] == "corner4"
+    packed = gpu_load(m, corners, n)
+    want = oracle.load_tiles(om, host, corners, n)
+    assert (mm := first_mismatch(packed.cpu().numpy(), want, 8192)) is None, ("load", mm)
+    c = torch.from_numpy(corners).to(DEV)
+    dst = dev_tensor(alloc, fill_seed=90 + es)
+    want_dst = dst.cpu().numpy().copy()
+    T.tmap_store_tiles(enc(dtype, dst, dims, strides, box, swz), c, n, packed)
+    check_ok()
+    oracle.store_tiles(om, want_dst, corners, n, want)
+    assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("store", mm)
+    del packed, want
+    dst = dev_tensor(alloc, fill_seed=95 + es)
+    want_dst = dst.cpu().numpy().copy()
+    T.tmap_roundtrip(m, enc(dtype, dst, dims, strides, box, swz), c, n)
+    check_ok()
+    oracle.roundtrip(om, host, om, want_dst, corners, n)
+    assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip", mm)
+
+
 def _corner4_case(rng):
     """A map the corner kernels run in 4-byte lanes: unswizzled elements of
     any size, box rows of a power of two from 16 to 256 bytes, at most 64
