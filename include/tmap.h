@@ -77,8 +77,10 @@ typedef struct tmap_swizzle {
 /* Launch options; pass NULL for the defaults.  Any field left 0 takes its
  * default. */
 typedef struct tmap_launch_opts {
-    uint32_t stages;      /* LDS ring depth 1..4 (default 2; 1 with explicit corners and
-                             when each workgroup takes a single band unit; 3 for round
+    uint32_t stages;      /* LDS ring depth 1..4 (default 2; 1 with explicit corners, for
+                             sweeps the corner kernel in 4-byte lanes takes (see
+                             TMAP_FLAG_WAVE_PER_BOX) and when each workgroup takes a
+                             single band unit; 3 for round
                              trips on the band schedule, and for every direction of
                              the band kernel, TMAP_VARIANT_BAND, except 4 for round
                              trips of whole 16 KiB boxes there)                         */
@@ -96,8 +98,9 @@ typedef struct tmap_launch_opts {
                              or store; explicit corners: 8, for a wave-per-box store 4;
                              wave per box with boxes of 8 KiB and more: on the corner
                              kernel 1 for a load or round trip and 2 for a store, 1 in
-                             every direction in 4-byte lanes (TMAP_VARIANT_CORNER4),
-                             else 4 for a load, 2 for a store and 8 for a round trip) */
+                             every direction in 4-byte lanes (TMAP_VARIANT_CORNER4)
+                             except 8 for the load of a sweep there, else 4 for a load,
+                             2 for a store and 8 for a round trip)                     */
     uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
                              streams, each sweeping an equal contiguous stretch of the
                              tiles (workgroup i takes stretch i mod regions), so that the
@@ -184,7 +187,9 @@ typedef struct tmap_launch_opts {
  * workgroup for boxes under 8 KiB and one to a workgroup for larger boxes
  * (as many one-box rings as fit in a CU's LDS).  Excludes the thread-copy
  * and producer-wave modes, TMAP_FLAG_WHOLE_BOX and the band schedule.  The
- * default for explicit corners of boxes up to 8 KiB (unless stages > 2). */
+ * default for explicit corners of boxes up to 8 KiB (unless stages > 2), and
+ * for sweeps that the band schedule does not take whose maps suit the corner
+ * kernel in 4-byte lanes, TMAP_VARIANT_CORNER4 (unless stages > 1). */
 #define TMAP_FLAG_WAVE_PER_BOX 0x40u
 /* One whole box per stage, even where the band schedule or wave-per-box
  * mode would be the default (for A/B runs, and for a consumer that needs a
@@ -419,7 +424,9 @@ typedef enum tmap_variant {
                                        box, and no swizzle or one that moves whole 16-byte
                                        chunks within rows: the hardware's bounds check clips
                                        every lane, and only words of 1- or 2-byte elements that
-                                       the tensor's edge cuts move element by element          */
+                                       the tensor's edge cuts move element by element.  Also
+                                       sweeps of such maps that the band schedule does not take
+                                       (maps of rank 3 and more, among others)                */
 } tmap_variant;
 typedef struct tmap_plan {
     uint32_t variant;     /* tmap_variant                                                  */

@@ -801,6 +801,57 @@ def test_corner4_random_maps(chunk):
                 assert (mm := first_mismatch(got, want_dst, 1 << 40)) is None, ("roundtrip", other, mm)
 
 
+@pytest.mark.parametrize("chunk", range(2))
+def test_corner4_sweeps(chunk):
+    """Sweeps the band kernel does not take run on the corner kernel in
+    4-byte lanes, their corners walked by the kernel's carry-add cursor:
+    seeded random maps of every rank, element size, row width and in-row
+    swizzle, random deals (groups, streams, grids, contiguous runs) and
+    hints.  Load of every tile, store of random images through the sweep,
+    round trip into the same layout and into another one, against the
+    oracle."""
+    rng = np.random.default_rng(9800 + chunk)
+    for i in range(30):
+        es, box, swz, (dims, strides, alloc), (ddims, dstrides, dalloc) = _corner4_case(rng)
+        if len(box) < 3:
+            # at least rank 3, so that a small tensor never takes the band schedule
+            while len(box) < 3:
+                box, dims, strides = box + [1], dims + [int(rng.integers(1, 4))], strides + [alloc]
+                alloc *= dims[-1]
+            ddims, dstrides, dalloc = dims, strides, alloc
+        opts = dict(grid_wgs=int(rng.choice([0, 0, 1, 3])), group=int(rng.choice([0, 1, 2, 4])),
+                    regions=int(rng.choice([0, 1, 2, 3])),
+                    flags=int(rng.choice([0, T.FLAG_NONTEMPORAL, T.FLAG_CONTIGUOUS, T.FLAG_DEBUG_POISON])))
+        dt = dt_of(es)
+        src = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        host = src.cpu().numpy()
+        m = enc(dt, src, dims, strides, box, swz)
+        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+        n = T.tmap_sweep_tiles(m)
+        bb = T.tmap_box_bytes(m)
+        say(f"corner4 sweep {chunk}/{i}: es={es} dims={dims} strides={strides} box={box} swz={swz} n={n} opts={opts}")
+        assert T.tmap_plan_launch("load", m, None, False, n, **opts)["variant"] == "corner4"
+        packed = gpu_load(m, None, n, **opts)
+        want = oracle.load_tiles(om, host, None, n)
+        assert (mm := first_mismatch(packed.cpu().numpy(), want, bb)) is None, ("load", mm)
+        imgs = inputs.sentinel_bytes(n * bb, int(rng.integers(1 << 30)))
+        dst = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        want_dst = dst.cpu().numpy().copy()
+        T.tmap_store_tiles(enc(dt, dst, dims, strides, box, swz), None, n, torch.from_numpy(imgs).to(DEV), **opts)
+        check_ok()
+        oracle.store_tiles(om, want_dst, None, n, imgs)
+        assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("store", mm)
+        for other in (False, True):
+            d_dims, d_strides, d_alloc = (ddims, dstrides, dalloc) if other else (dims, strides, alloc)
+            od = Map(es=es, dims=d_dims, strides=d_strides, box=box, swizzle=swz)
+            dst = dev_tensor(d_alloc, fill_seed=int(rng.integers(1 << 30)))
+            want_dst = dst.cpu().numpy().copy()
+            T.tmap_roundtrip(m, enc(dt, dst, d_dims, d_strides, box, swz), None, n, **opts)
+            check_ok()
+            oracle.roundtrip(om, host, od, want_dst, None, n)
+            assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip", other, mm)
+
+
 def test_binding_rejects_buffers_the_copy_would_overrun():
     """Given tensors, the binding checks sizes before launching: a packed
     buffer or corner array too small for n_tiles, a host tensor or int64
@@ -874,6 +925,16 @@ def test_plan_query_reports_the_schedules():
     p = T.tmap_plan_launch("store", m, None, True, 1000)
     assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"]) == ("corner", 2, 8192 + 8, 500)
     assert T.tmap_plan_launch("roundtrip", m, m, True, 1000)["group"] == 1
+    # sweeps of rank 5 (never the band schedule) whose boxes suit the 4-byte
+    # lanes run there, one stage; a load walks 8 boxes to a wave, a round
+    # trip or store one; two stages keep the shared ring
+    w = W["pad5d_f32"]
+    m5 = T.tmap_encode(w.dtype, w.rank, 0x7F0000000000, w.dims, w.strides, w.box)
+    n5 = T.tmap_sweep_tiles(m5)
+    for direction, group in (("load", 8), ("roundtrip", 1), ("store", 1)):
+        p = T.tmap_plan_launch(direction, m5, m5 if direction == "roundtrip" else None, False, n5)
+        assert (p["variant"], p["stages"], p["group"]) == ("corner4", 1, group), (direction, p)
+    assert T.tmap_plan_launch("load", m5, None, False, n5, stages=2)["variant"] == "ring"
     # what the 4-byte lanes take: box rows of a power of two from 16 to 256
     # bytes, at most 64 rows to a box, no swizzle or one that moves whole
     # 16-byte chunks within rows with a key of at most 4 bits

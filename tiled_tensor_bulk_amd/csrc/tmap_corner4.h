@@ -36,8 +36,10 @@
 // logical column and looks its range test up in a column table (one entry
 // per logical column, a lane each), with a second ds_bpermute.
 //
-// Each wave walks its own share of the corners through its own one-box
-// stage and 8-byte byte record, as the corner kernel does:
+// Each wave walks its own share of the tiles through its own one-box stage
+// and 8-byte byte record, as the corner kernel does.  The tiles are explicit
+// corners, or those of a sweep (maps of rank 3 and more, and others the band
+// kernel does not take), whose corners the carry-add cursor walks:
 //
 //   fill    arrive on the record with the box's byte budget and issue one
 //           4-byte direct-to-LDS load per slot from the tensor (a store: one
@@ -216,16 +218,6 @@ __device__ __forceinline__ void c4_store_cut(const KArgs &A, const uint8_t *stag
     }
 }
 
-// Corner of tile t: uniform scalar loads through the constant address space.
-template <int R>
-__device__ __forceinline__ void c4_corner(const KArgs &A, const KMap &swept, int64_t t, int32_t (&c)[R]) {
-    typedef const __attribute__((address_space(4))) int32_t const_i32;
-    const int r = swept.rank;
-    const_i32 *p = (const_i32 *)(A.coords) + t * r;
-#pragma unroll
-    for (int d = 0; d < R; ++d) c[d] = d < r ? p[d] : 0;
-}
-
 template <bool NT>
 __device__ __forceinline__ void c4_store4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
     if constexpr (NT)
@@ -275,11 +267,20 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
     const uint32_t rstep = (64u >> a.c4_dshift) * 4u;
     const uint32_t bytes = sw.box_bytes;
     const uint32_t budget = bytes + ((a.flags & TMAP_FLAG_INJECT_BUDGET_MISMATCH) ? 16u : 0u);
-    uint32_t parity = 0, k = 0;
+    uint32_t parity = 0;
+    // the wave's tiles: explicit corners are read per tile; a sweep walks
+    // its tiles' digits with the carry-add cursor, divided out once here
+    Cursor<R> cur;
+    if (a.coords) {
+        cur.t = t;
+        cur.k = 0;
+    } else {
+        cursor_init<R>(a, t, cur);
+    }
 
     for (int64_t n = 0; n < cnt; ++n) {
         int32_t c[R];
-        c4_corner<R>(a, sw, t, c);
+        cursor_corner<R>(a, sw, cur, c);
         // the slots' row-fetch addresses are formed per box, not held across
         // the loop in NI registers
         uint32_t ra = raddr;
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
         uint32_t off[NI];
         C4Side ss = {kOob, kOob, 0u}, ds = {kOob, kOob, 0u};
         if constexpr (MODE == kStore) {
-            const uint64_t base = (uint64_t)a.packed + (uint64_t)t * bytes;
+            const uint64_t base = (uint64_t)a.packed + (uint64_t)cur.t * bytes;
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
                 const uint32_t p = (uint32_t)j * 64u + lane;
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
             i32x4 v[NSLOT];
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) v[j] = *(const i32x4 *)(stage + ((uint32_t)j * 64u + lane) * 16u);
-            const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)t * bytes, bytes);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc((uint64_t)a.packed + (uint64_t)cur.t * bytes, bytes);
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) {
                 const uint32_t p = (uint32_t)j * 64u + lane;
@@ -390,9 +391,7 @@ __global__ __launch_bounds__(64 * wave_group(NSLOT)) void corner4_kernel(const K
         // the stage is free once these reads have completed
         __builtin_amdgcn_s_waitcnt(kWaitLgkm);
         asm volatile("" ::: "memory");
-        const bool big = (k & a.group_mask) == a.group_mask;
-        k += 1;
-        t += big ? a.big_step : 1;
+        cursor_advance<R>(a, cur);
     }
     // nothing may still be writing LDS or memory when the wave ends
     __builtin_amdgcn_s_waitcnt(0);

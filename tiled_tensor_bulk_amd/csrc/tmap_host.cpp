@@ -304,7 +304,8 @@ constexpr uint32_t kKnownFlags = TMAP_FLAG_CONTIGUOUS | TMAP_FLAG_NONTEMPORAL | 
 
 // lean: the band schedule runs the band kernel of rank-2 sweeps.
 // elemwise: the swizzle moves data inside 16-byte chunks.
-// c4: the maps suit the corner kernels in 4-byte lanes (corner4_fits).
+// c4: the maps suit the corner kernels in 4-byte lanes (corner4_fits) and
+// the band schedule is not taken.
 tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
                         const DeviceState &dev, bool band, bool lean, bool corners, bool elemwise, bool c4,
                         Plan &pl) {
@@ -357,6 +358,20 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     if (corners && !band && m.box_bytes <= 8192u && !(opts && opts->stages > 2) &&
         !(flags & (TMAP_FLAG_THREAD_COPY | TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WHOLE_BOX)))
         wave_box = true;
+    // sweeps the band kernel does not take (maps of rank 3 and more, and
+    // others) whose boxes suit the corner kernel in 4-byte lanes run there
+    // too, one stage, their corners walked by the kernel's cursor (measured
+    // on MI355X, padded 5-D fp32 tensor tiled by three shapes of 8 KiB box,
+    // fraction of 8 TB/s against the shared ring: round trips 0.45 / 0.53 /
+    // 0.45 against 0.23 / 0.17 / 0.22, loads 0.65 / 0.76 / 0.66 against
+    // 0.38 / 0.31 / 0.38, stores 0.63 / 0.69 / 0.63 against 0.47 / 0.40 /
+    // 0.47)
+    const bool sweep_c4 = !corners && !band && c4 && m.box_bytes <= 8192u && !(opts && opts->stages > 1) &&
+                          !(flags & (TMAP_FLAG_THREAD_COPY | TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WHOLE_BOX));
+    if (sweep_c4) {
+        wave_box = true;
+        stages = 1;
+    }
     if (opts && (opts->flags & TMAP_FLAG_BAND) && (opts->flags & TMAP_FLAG_WHOLE_BOX))
         return fail(TMAP_ERROR_INVALID_VALUE, "TMAP_FLAG_BAND and TMAP_FLAG_WHOLE_BOX exclude each other");
     if (thread_copy) stages = 1;  // one LDS stage; the next tile waits in registers
@@ -396,7 +411,7 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // 4 (measured best on MI355X over 10^5 scattered 8 KiB boxes: store
     // 0.539 -> 0.557 of peak, load 0.625 -> 0.669 with the packed side's
     // non-temporal hints)
-    if (!group && corners) {
+    if (!group && (corners || sweep_c4)) {
         // the corner kernel (one stage, whole-chunk swizzles) loads and
         // round-trips 8 KiB boxes fastest one to a wave (10^5 boxes: load
         // 0.73 of peak against 0.69 with 2, round trip 0.366 against 0.353)
@@ -410,6 +425,11 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
                     : (corner ? 1u : (mode == tmap::kLoad ? 4u : 8u));
         else
             group = (wave_box && mode == tmap::kStore) ? 4u : 8u;
+        // a sweep's load in 4-byte lanes walks 8 neighbouring boxes to a
+        // wave (padded 5-D fp32 tensor tiled by three 8 KiB box shapes:
+        // 0.650 / 0.762 / 0.656 of peak against 0.624 / 0.717 / 0.633 with
+        // one; its round trips and stores lose 4-12% with 8)
+        if (sweep_c4 && tmap::wave_group(nslot) == 1 && mode == tmap::kLoad) group = 8u;
     }
     // a workgroup that takes one band unit has nothing to overlap in its ring
     if (band && group == 1 && !(opts && opts->stages)) stages = 1;
@@ -544,7 +564,7 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     if (why) return fail(TMAP_ERROR_INVALID_VALUE, "%s", why);
     if (band) band_setup(swept, a, g, nb, rows);
     const bool lean = band && lean_maps;
-    const bool c4 = a.coords && !band && corner4_fits(mode, a);
+    const bool c4 = !band && corner4_fits(mode, a);
     tmap_status st =
         plan_launch(mode, swept, a.n_tiles, opts, dev, band, lean, a.coords != nullptr, a.elemwise != 0, c4, pl);
     if (st != TMAP_SUCCESS) return st;
@@ -567,7 +587,8 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     // explicit corners, one wave per box with one stage, boxes of at most
     // 8 KiB and a swizzle that moves whole chunks: the corner kernels, which
     // hold each drained box in registers while the next one loads
-    pl.corner = a.coords && pl.stages == 31 && pl.nslot <= 8 && !a.elemwise;
+    // (a sweep runs there only in 4-byte lanes)
+    pl.corner = (a.coords || c4) && pl.stages == 31 && pl.nslot <= 8 && !a.elemwise;
     // ... in 4-byte lanes where the maps allow it: no element-by-element
     // patching of chunks the tensor's edge cuts, and a row's offset worked
     // out once per box instead of once per chunk (measured on MI355X over
