@@ -264,31 +264,33 @@ def main():
 
 def cpu_baseline(w, op, src, budget_s):
     """The CPU oracle (single thread, as it stands) on a bounded sample: whole
-    tile rows of the sweep, one after another, until ~budget_s of oracle time.
-    Reported in the same algorithmic GB/s as the GPU line."""
+    tile rows of the sweep (slabs one box deep in the outermost dimension),
+    one after another, until ~budget_s of oracle time.  Reported in the same
+    algorithmic GB/s as the GPU line."""
     import numpy as np
 
     import oracle
 
     if w.coords != "sweep":
         return _cpu_baseline_corners(w, op, src, budget_s)
-    if w.rank != 2:
+    if w.rank < 2:
         return None
-    row_bytes = w.strides[0] * w.box[1]                       # one tile row of the tensor
+    row_bytes = w.strides[-1] * w.box[-1]                     # one tile row of the tensor
     rows_per_chunk = 4
     total_t = 0.0
     total_bytes = 0
     tiles = 0
     chunk = 0
-    n_rows = -(-w.dims[1] // w.box[1])
+    n_rows = -(-w.dims[-1] // w.box[-1])
     while total_t < budget_s and chunk * rows_per_chunk < n_rows:
         r0 = chunk * rows_per_chunk
         r1 = min(n_rows, r0 + rows_per_chunk)
         lo = r0 * row_bytes
         hi = min(w.alloc_bytes, r1 * row_bytes)
         host = src[lo:hi].cpu().numpy()
-        sub_rows = min(w.dims[1], r1 * w.box[1]) - r0 * w.box[1]
-        m = oracle.Map(es=w.es, dims=[w.dims[0], sub_rows], strides=w.strides, box=w.box, swizzle=w.swizzle)
+        sub_rows = min(w.dims[-1], r1 * w.box[-1]) - r0 * w.box[-1]
+        m = oracle.Map(es=w.es, dims=list(w.dims[:-1]) + [sub_rows], strides=w.strides, box=w.box,
+                       swizzle=w.swizzle)
         nt = oracle.sweep_count(m)
         t0 = time.perf_counter()
         if op == "bulk":
@@ -319,7 +321,7 @@ def cpu_baseline(w, op, src, budget_s):
         chunk += 1
     return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "tiles_per_s": round(tiles / total_t, 1),
-            "sample": f"{tiles} tiles ({chunk * rows_per_chunk} tile rows from the top) of {w.name}, "
+            "sample": f"{tiles} tiles ({min(n_rows, chunk * rows_per_chunk)} of {n_rows} tile rows, from the top) of {w.name}, "
                       f"{op}, {total_t:.1f} s of single-thread oracle time",
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 

@@ -298,6 +298,17 @@ def test_pad5d_f32_random_corners_full(opts):
     check_all_directions("pad5d_f32", opts, tag=str(opts))
 
 
+@pytest.mark.parametrize("opts", [dict(), dict(group=4), dict(stages=2)],
+                         ids=["benchmark_launch", "corner4_group_4", "shared_ring_2_stages"])
+def test_pad5d_sweep_f32_full(opts):
+    """The padded 5-D tensor swept whole (19845 boxes, ragged in four
+    dimensions): one stage on the 4-byte-lane corner kernel by default, the
+    shared ring with two stages."""
+    say(f"pad5d_sweep_f32: load, store, round trip of the whole sweep {opts}; full oracle")
+    check_all_directions("pad5d_sweep_f32", opts, tag=str(opts))
+    forget("pad5d_sweep_f32")
+
+
 # ----------------------------------------------------------------- seeded fuzz
 def _fuzz_case(rng, idx):
     mp = inputs.random_map(rng)
@@ -928,9 +939,10 @@ def test_plan_query_reports_the_schedules():
     # sweeps of rank 5 (never the band schedule) whose boxes suit the 4-byte
     # lanes run there, one stage; a load walks 8 boxes to a wave, a round
     # trip or store one; two stages keep the shared ring
-    w = W["pad5d_f32"]
+    w = W["pad5d_sweep_f32"]
     m5 = T.tmap_encode(w.dtype, w.rank, 0x7F0000000000, w.dims, w.strides, w.box)
     n5 = T.tmap_sweep_tiles(m5)
+    assert n5 == 5 * 9 * 9 * 7 * 7
     for direction, group in (("load", 8), ("roundtrip", 1), ("store", 1)):
         p = T.tmap_plan_launch(direction, m5, m5 if direction == "roundtrip" else None, False, n5)
         assert (p["variant"], p["stages"], p["group"]) == ("corner4", 1, group), (direction, p)
@@ -1088,7 +1100,7 @@ def test_repeat_is_deterministic():
         assert torch.equal(a, b), st
 
 
-@pytest.mark.parametrize("name", ["tile64_f32", "strips_f16", "ragged_bf16", "pad5d_f32", "sweep2g_u8"])
+@pytest.mark.parametrize("name", ["tile64_f32", "strips_f16", "ragged_bf16", "pad5d_f32", "pad5d_sweep_f32", "sweep2g_u8"])
 def test_other_modes_match_the_oracle(name):
     """The register-path, producer-wave and wave-per-box variants, the ring
     on whole boxes, and other deals of the groups to the grid (regions), at

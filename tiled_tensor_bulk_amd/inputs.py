@@ -12,7 +12,8 @@ Shapes follow the pages' examples:
     in CuTe DSL", "The work assigned to each block"),
 and three larger synthetic cases: a ragged bf16 sweep with a 128-byte XOR
 swizzle, a padded 5-D fp32 tensor read at random (partly out-of-bounds)
-corners, and a 2 GiB byte tensor swept with a 128-byte swizzle.
+corners and swept whole, and a 2 GiB byte tensor swept with a 128-byte
+swizzle.
 All dims, boxes and coordinates are innermost dimension first.
 """
 from __future__ import annotations
@@ -75,6 +76,11 @@ WORKLOADS = {
     # 2 GiB byte tensor 32768 rows x 65536 cols, 128x128 boxes, 128-byte swizzle
     "sweep2g_u8": Workload("sweep2g_u8", "u8", (65536, 32768), (65536,), (128, 128), (3, 4, 3),
                            "sweep", stages=4, values="bytes", seed=5),
+    # the same padded 5-D fp32 tensor swept whole: 5 x 9 x 9 x 7 x 7 boxes,
+    # ragged in every dimension but the outermost
+    "pad5d_sweep_f32": Workload("pad5d_sweep_f32", "f32", (129, 65, 33, 13, 7),
+                                (528, 528 * 65, 528 * 65 * 33, 528 * 65 * 33 * 13),
+                                (32, 8, 4, 2, 1), (0, 0, 0), "sweep", stages=1, values="u32", seed=7),
     # the round-trip program's 64x64 fp32 boxes over a 1 GiB matrix (16384 x 16384),
     # 128-byte swizzle, for the fused +1.0f update
     "plus1_f32": Workload("plus1_f32", "f32", (16384, 16384), (65536,), (64, 64), (3, 2, 3),
