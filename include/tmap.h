@@ -98,19 +98,23 @@ typedef struct tmap_launch_opts {
                              or store; explicit corners: 8, for a wave-per-box store 4;
                              wave per box with boxes of 8 KiB and more: on the corner
                              kernel 1 for a load or round trip and 2 for a store, 1 in
-                             every direction in 4-byte lanes (TMAP_VARIANT_CORNER4)
-                             except 8 for the load of a sweep there, else 4 for a load,
-                             2 for a store and 8 for a round trip)                     */
+                             every direction in 4-byte lanes (TMAP_VARIANT_CORNER4),
+                             else 4 for a load, 2 for a store and 8 for a round trip) */
     uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
                              streams, each sweeping an equal contiguous stretch of the
-                             tiles (workgroup i takes stretch i mod regions), so that the
-                             tiles in flight lie in that many places of the tensor
-                             instead of one.  How the addresses in flight fall on the
-                             HBM channels decides which is faster (default: 2 for loads
-                             and stores on the band schedule, for band-kernel round
-                             trips of tensors whose row pitch is not a power of two, and
-                             for whole boxes on the band kernel except round trips of
-                             16 KiB boxes; else 1)                                     */
+                             tiles (workgroup i takes stretch i mod regions; in
+                             wave-per-box mode and on the corner kernels, wave i), so
+                             that the tiles in flight lie in that many places of the
+                             tensor instead of one.  How the addresses in flight fall
+                             on the HBM channels and the L2 caches decides which is
+                             faster (default: 8 on the corner kernels, TMAP_VARIANT_CORNER
+                             and TMAP_VARIANT_CORNER4, where a workgroup is one wave
+                             (boxes of 8 KiB), so that the workgroups on one of the
+                             GPU's 8 XCDs, which share an L2, take neighbouring
+                             tiles; 2 for loads and stores on the band schedule, for
+                             band-kernel round trips of tensors whose row pitch is not
+                             a power of two, and for whole boxes on the band kernel
+                             except round trips of 16 KiB boxes; else 1)               */
     uint32_t band_rows;   /* band schedule: box rows per band, a power of two.  A unit is
                              then 16 KiB / (band_rows * box row bytes) boxes side by
                              side.  Default on the band kernel: 8 for a round trip (2

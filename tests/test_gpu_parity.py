@@ -298,12 +298,13 @@ def test_pad5d_f32_random_corners_full(opts):
     check_all_directions("pad5d_f32", opts, tag=str(opts))
 
 
-@pytest.mark.parametrize("opts", [dict(), dict(group=4), dict(stages=2)],
-                         ids=["benchmark_launch", "corner4_group_4", "shared_ring_2_stages"])
+@pytest.mark.parametrize("opts", [dict(), dict(group=4), dict(regions=1), dict(stages=2)],
+                         ids=["benchmark_launch", "corner4_group_4", "corner4_one_stream", "shared_ring_2_stages"])
 def test_pad5d_sweep_f32_full(opts):
     """The padded 5-D tensor swept whole (19845 boxes, ragged in four
-    dimensions): one stage on the 4-byte-lane corner kernel by default, the
-    shared ring with two stages."""
+    dimensions): one stage on the 4-byte-lane corner kernel by default (one
+    box to a wave, the waves dealt to the XCDs as 8 streams), 4 boxes to a
+    wave, one stream, and the shared ring with two stages."""
     say(f"pad5d_sweep_f32: load, store, round trip of the whole sweep {opts}; full oracle")
     check_all_directions("pad5d_sweep_f32", opts, tag=str(opts))
     forget("pad5d_sweep_f32")
@@ -917,36 +918,40 @@ def test_plan_query_reports_the_schedules():
     # the padded 5-D fp32 boxes: the corner kernels in 4-byte lanes, one box
     # to a wave in every direction; 8 KiB boxes: one wave to a workgroup,
     # each with its own one-box stage
+    # the waves, one to a workgroup, are dealt as 8 interleaved streams, one
+    # to each XCD's workgroups; four-wave workgroups keep one stream
     for direction in ("load", "store", "roundtrip"):
         p = plan("pad5d_f32", direction)
-        assert (p["variant"], p["stages"], p["slots"], p["group"]) == ("corner4", 1, 8, 1), direction
+        assert (p["variant"], p["stages"], p["slots"], p["group"], p["regions"]) == ("corner4", 1, 8, 1, 8), direction
         assert p["walkers"] == 100000 and p["workgroups"] == p["walkers"], direction
         assert p["lds_bytes"] == 8192 + 8, direction
     # 2 KiB boxes: four waves to a workgroup
     m = T.tmap_encode("f32", 2, 0x7F0000000000, [1000, 1000], [4000], [32, 16])
     p = T.tmap_plan_launch("load", m, None, True, 1000)
-    assert (p["variant"], p["slots"], p["walkers"]) == ("corner4", 2, 125)
+    assert (p["variant"], p["slots"], p["walkers"], p["regions"]) == ("corner4", 2, 125, 1)
+    assert T.tmap_plan_launch("load", m, None, True, 1000, regions=3)["regions"] == 3
     assert p["workgroups"] == 32 and p["lds_bytes"] == 4 * 2048 + 4 * 8
     # 16-bit elements in 8 KiB boxes with a swizzle whose XOR reaches past a
     # 128-byte row: the corner kernel in 16-byte lanes; its loads reserve
     # 11 KiB of LDS to a workgroup, its stores take two boxes to a wave
     m = T.tmap_encode("bf16", 2, 0x7F0000000000, [1000, 1000], [2048], [64, 64], None, (3, 4, 3))
     p = T.tmap_plan_launch("load", m, None, True, 1000)
-    assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"]) == ("corner", 1, 11264, 1000)
+    assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"], p["regions"]) == ("corner", 1, 11264, 1000, 8)
     p = T.tmap_plan_launch("store", m, None, True, 1000)
     assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"]) == ("corner", 2, 8192 + 8, 500)
     assert T.tmap_plan_launch("roundtrip", m, m, True, 1000)["group"] == 1
     # sweeps of rank 5 (never the band schedule) whose boxes suit the 4-byte
-    # lanes run there, one stage; a load walks 8 boxes to a wave, a round
-    # trip or store one; two stages keep the shared ring
+    # lanes run there, one stage, one box to a wave, the waves dealt to the
+    # XCDs; two stages keep the shared ring
     w = W["pad5d_sweep_f32"]
     m5 = T.tmap_encode(w.dtype, w.rank, 0x7F0000000000, w.dims, w.strides, w.box)
     n5 = T.tmap_sweep_tiles(m5)
     assert n5 == 5 * 9 * 9 * 7 * 7
-    for direction, group in (("load", 8), ("roundtrip", 1), ("store", 1)):
+    for direction in ("load", "roundtrip", "store"):
         p = T.tmap_plan_launch(direction, m5, m5 if direction == "roundtrip" else None, False, n5)
-        assert (p["variant"], p["stages"], p["group"]) == ("corner4", 1, group), (direction, p)
-    assert T.tmap_plan_launch("load", m5, None, False, n5, stages=2)["variant"] == "ring"
+        assert (p["variant"], p["stages"], p["group"], p["regions"]) == ("corner4", 1, 1, 8), (direction, p)
+    p = T.tmap_plan_launch("load", m5, None, False, n5, stages=2)
+    assert (p["variant"], p["regions"]) == ("ring", 1)
     # what the 4-byte lanes take: box rows of a power of two from 16 to 256
     # bytes, at most 64 rows to a box, no swizzle or one that moves whole
     # 16-byte chunks within rows with a key of at most 4 bits

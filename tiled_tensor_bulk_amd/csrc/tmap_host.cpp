@@ -170,6 +170,10 @@ constexpr uint32_t kLeanRowsLoadStore = 16;
 // 0.813, 1 GiB fp32: 0.827 against 0.811, pitch 32768: 0.817 against 0.808).
 constexpr uint32_t kLeanRowsRoundtripSpread = 2;
 
+// The accelerator complex dies (XCDs) of an MI355X: each has its own L2, and
+// the dispatcher hands consecutive workgroups to them in turn.
+constexpr uint32_t kXcds = 8;
+
 // Whether every tensor a round trip streams has a power-of-two row pitch
 // (the byte stride of dimension 1).
 bool pow2_pitches(const tmap::KArgs &a) {
@@ -425,11 +429,6 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
                     : (corner ? 1u : (mode == tmap::kLoad ? 4u : 8u));
         else
             group = (wave_box && mode == tmap::kStore) ? 4u : 8u;
-        // a sweep's load in 4-byte lanes walks 8 neighbouring boxes to a
-        // wave (padded 5-D fp32 tensor tiled by three 8 KiB box shapes:
-        // 0.650 / 0.762 / 0.656 of peak against 0.624 / 0.717 / 0.633 with
-        // one; its round trips and stores lose 4-12% with 8)
-        if (sweep_c4 && tmap::wave_group(nslot) == 1 && mode == tmap::kLoad) group = 8u;
     }
     // a workgroup that takes one band unit has nothing to overlap in its ring
     if (band && group == 1 && !(opts && opts->stages)) stages = 1;
@@ -595,6 +594,20 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     // 10^5 scattered 8 KiB fp32 boxes, fraction of 8 TB/s: round trip 0.351
     // -> 0.427, store 0.637 -> 0.674, load 0.733 -> 0.743)
     pl.corner4 = pl.corner && c4;
+    // Where each wave is a workgroup of its own (8 KiB boxes), the corner
+    // kernels deal the waves as one interleaved stream per XCD: the
+    // dispatcher hands workgroups to the XCDs in turn, so workgroups b and
+    // b + 8 share an L2 and get neighbouring boxes, and the cache lines that
+    // neighbouring boxes share (box rows that do not start on a line) are
+    // fetched into one L2 instead of two.  Measured on MI355X, sweeps of the
+    // padded 5-D fp32 tensor by three 8 KiB box shapes, fraction of 8 TB/s:
+    // round trips 0.732 / 0.736 / 0.729 against 0.447 / 0.528 / 0.450 with
+    // one stream, loads 0.871 / 0.886 / 0.879 against 0.621 / 0.716 / 0.629,
+    // stores 0.706 / 0.721 / 0.708 against 0.624 / 0.692 / 0.633; the same
+    // sweep's corners as a list alike; 10^5 random corners 0.8-1.9% faster.
+    // Four-wave workgroups of smaller boxes keep one stream (8 KiB-wide
+    // deals gained their sweeps 1-7% but cost random corners up to 7%).
+    if (pl.corner && tmap::wave_group(pl.nslot) == 1 && !(opts && opts->regions)) pl.regions = kXcds;
     if (pl.corner4) {
         const uint32_t row = (uint32_t)swept.box[0] * swept.elem_size;
         a.c4_dshift = log2u(row / 4u);
