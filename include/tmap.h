@@ -78,7 +78,7 @@ typedef struct tmap_swizzle {
  * default. */
 typedef struct tmap_launch_opts {
     uint32_t stages;      /* LDS ring depth 1..4 (default 2; 1 with explicit corners, for
-                             sweeps the corner kernel in 4-byte lanes takes (see
+                             sweeps the corner kernels take (see
                              TMAP_FLAG_WAVE_PER_BOX) and when each workgroup takes a
                              single band unit; 3 for round
                              trips on the band schedule, and for every direction of
@@ -192,8 +192,9 @@ typedef struct tmap_launch_opts {
  * (as many one-box rings as fit in a CU's LDS).  Excludes the thread-copy
  * and producer-wave modes, TMAP_FLAG_WHOLE_BOX and the band schedule.  The
  * default for explicit corners of boxes up to 8 KiB (unless stages > 2), and
- * for sweeps that the band schedule does not take whose maps suit the corner
- * kernel in 4-byte lanes, TMAP_VARIANT_CORNER4 (unless stages > 1). */
+ * for sweeps of such boxes that the band schedule does not take, on the
+ * corner kernels, TMAP_VARIANT_CORNER and TMAP_VARIANT_CORNER4 (unless
+ * stages > 1 or the swizzle moves data inside 16-byte chunks). */
 #define TMAP_FLAG_WAVE_PER_BOX 0x40u
 /* One whole box per stage, even where the band schedule or wave-per-box
  * mode would be the default (for A/B runs, and for a consumer that needs a
@@ -421,8 +422,10 @@ typedef enum tmap_variant {
                                        dimension-0 rows are whole 16-byte chunks: the band ring
                                        with per-slot offsets fixed per kernel                      */
     TMAP_VARIANT_CORNER = 5,        /* wave per box with one stage, boxes of at most 8 KiB and a
-                                       swizzle that moves whole chunks: each wave holds a drained
-                                       box in registers while the next one loads               */
+                                       swizzle that moves whole chunks, at explicit corners or
+                                       over a sweep the band schedule does not take: each wave
+                                       holds a drained box in registers while the next one
+                                       loads                                                   */
     TMAP_VARIANT_CORNER4 = 6        /* the same boxes in 4-byte lanes, for maps with box rows of a
                                        power of two from 16 to 256 bytes, at most 64 rows to a
                                        box, and no swizzle or one that moves whole 16-byte

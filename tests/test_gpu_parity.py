@@ -831,37 +831,112 @@ def test_corner4_sweeps(chunk):
                 box, dims, strides = box + [1], dims + [int(rng.integers(1, 4))], strides + [alloc]
                 alloc *= dims[-1]
             ddims, dstrides, dalloc = dims, strides, alloc
-        opts = dict(grid_wgs=int(rng.choice([0, 0, 1, 3])), group=int(rng.choice([0, 1, 2, 4])),
-                    regions=int(rng.choice([0, 1, 2, 3])),
-                    flags=int(rng.choice([0, T.FLAG_NONTEMPORAL, T.FLAG_CONTIGUOUS, T.FLAG_DEBUG_POISON])))
-        dt = dt_of(es)
-        src = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
-        host = src.cpu().numpy()
-        m = enc(dt, src, dims, strides, box, swz)
-        om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
-        n = T.tmap_sweep_tiles(m)
-        bb = T.tmap_box_bytes(m)
-        say(f"corner4 sweep {chunk}/{i}: es={es} dims={dims} strides={strides} box={box} swz={swz} n={n} opts={opts}")
-        assert T.tmap_plan_launch("load", m, None, False, n, **opts)["variant"] == "corner4"
-        packed = gpu_load(m, None, n, **opts)
-        want = oracle.load_tiles(om, host, None, n)
-        assert (mm := first_mismatch(packed.cpu().numpy(), want, bb)) is None, ("load", mm)
-        imgs = inputs.sentinel_bytes(n * bb, int(rng.integers(1 << 30)))
-        dst = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+        _check_sweep(rng, f"corner4 sweep {chunk}/{i}", "corner4", es, box, swz,
+                     (dims, strides, alloc), (ddims, dstrides, dalloc))
+
+
+def _corner16_case(rng):
+    """A map of rank 3 to 5 with boxes of at most 8 KiB that the corner
+    kernel takes in 16-byte lanes only: box rows that are not a power of two
+    from 16 to 256 bytes, more than 64 rows, or a swizzle of whole chunks
+    whose XOR reaches past the row; and a second layout with the same box."""
+    while True:
+        es = int(rng.choice([1, 2, 4, 8]))
+        lg = es.bit_length() - 1
+        rank = int(rng.integers(3, 6))
+        kind = int(rng.integers(0, 3))
+        swz = (0, 0, 0)
+        if kind == 0:
+            row = 16 * int(rng.choice([3, 5, 6, 7, 9, 12, 32]))
+            max_rows = 8192 // row
+        elif kind == 1:
+            row = int(rng.choice([16, 32]))
+            max_rows = 8192 // row
+        else:
+            row = int(rng.choice([16, 32, 64]))
+            max_rows = min(64, 8192 // row)
+        if row // es > 256:
+            continue
+        box, rows = [row // es], 1
+        for d in range(1, rank):
+            b = int(rng.integers(1, min(256, max_rows // rows) + 1))
+            if kind == 1 and d == 1:
+                b = int(rng.integers(65, min(256, max_rows) + 1))
+            box.append(b)
+            rows *= b
+        if kind == 1 and rows <= 64:
+            continue
+        if all(b == 1 for b in box[2:]):
+            continue  # the band schedule could take it
+        if kind == 2:
+            lrow = row.bit_length() - 1
+            n_el = int(np.prod(box))
+            picks = [(b, m) for b in (1, 2, 3) for m in range(max(0, 4 - lg), 6)
+                     if m + lg + b > lrow and n_el % (1 << (m + b)) == 0]
+            if not picks:
+                continue
+            b, m = picks[int(rng.integers(0, len(picks)))]
+            swz = (b, m, int(rng.integers(b, b + 4)))
+
+        def layout():
+            dims = [int(rng.integers(1, 2 * box[0] + 40))] + [int(rng.integers(1, 2 * b + 4)) for b in box[1:]]
+            st = (-(-dims[0] * es // 16) + int(rng.integers(0, 3))) * 16
+            strides = []
+            for d in range(1, rank):
+                strides.append(st)
+                st *= dims[d] + int(rng.integers(0, 2))
+            return dims, strides, st
+        return es, box, swz, layout(), layout()
+
+
+@pytest.mark.parametrize("chunk", range(2))
+def test_corner_sweeps_in_16_byte_lanes(chunk):
+    """Sweeps of rank 3 to 5 whose boxes the 4-byte lanes do not take run on
+    the corner kernel in 16-byte lanes, their corners walked by the same
+    cursor: random row widths, row counts and chunk swizzles, random deals
+    and hints; load, store and round trips against the oracle."""
+    rng = np.random.default_rng(9900 + chunk)
+    for i in range(20):
+        es, box, swz, lay, dlay = _corner16_case(rng)
+        _check_sweep(rng, f"corner sweep {chunk}/{i}", "corner", es, box, swz, lay, dlay)
+
+
+def _check_sweep(rng, tag, variant, es, box, swz, lay, dlay):
+    """Load, store and round trips (into the same layout and into dlay) of
+    the whole sweep of one map under random deals and hints, every byte
+    against the oracle; the plan must name `variant`."""
+    dims, strides, alloc = lay
+    opts = dict(grid_wgs=int(rng.choice([0, 0, 1, 3])), group=int(rng.choice([0, 1, 2, 4])),
+                regions=int(rng.choice([0, 1, 2, 3, 8])),
+                flags=int(rng.choice([0, T.FLAG_NONTEMPORAL, T.FLAG_CONTIGUOUS, T.FLAG_DEBUG_POISON])))
+    dt = dt_of(es)
+    src = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+    host = src.cpu().numpy()
+    m = enc(dt, src, dims, strides, box, swz)
+    om = Map(es=es, dims=dims, strides=strides, box=box, swizzle=swz)
+    n = T.tmap_sweep_tiles(m)
+    bb = T.tmap_box_bytes(m)
+    say(f"{tag}: es={es} dims={dims} strides={strides} box={box} swz={swz} n={n} opts={opts}")
+    assert T.tmap_plan_launch("load", m, None, False, n, **opts)["variant"] == variant
+    packed = gpu_load(m, None, n, **opts)
+    want = oracle.load_tiles(om, host, None, n)
+    assert (mm := first_mismatch(packed.cpu().numpy(), want, bb)) is None, ("load", mm)
+    imgs = inputs.sentinel_bytes(n * bb, int(rng.integers(1 << 30)))
+    dst = dev_tensor(alloc, fill_seed=int(rng.integers(1 << 30)))
+    want_dst = dst.cpu().numpy().copy()
+    T.tmap_store_tiles(enc(dt, dst, dims, strides, box, swz), None, n, torch.from_numpy(imgs).to(DEV), **opts)
+    check_ok()
+    oracle.store_tiles(om, want_dst, None, n, imgs)
+    assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("store", mm)
+    for other in (False, True):
+        d_dims, d_strides, d_alloc = dlay if other else lay
+        od = Map(es=es, dims=d_dims, strides=d_strides, box=box, swizzle=swz)
+        dst = dev_tensor(d_alloc, fill_seed=int(rng.integers(1 << 30)))
         want_dst = dst.cpu().numpy().copy()
-        T.tmap_store_tiles(enc(dt, dst, dims, strides, box, swz), None, n, torch.from_numpy(imgs).to(DEV), **opts)
+        T.tmap_roundtrip(m, enc(dt, dst, d_dims, d_strides, box, swz), None, n, **opts)
         check_ok()
-        oracle.store_tiles(om, want_dst, None, n, imgs)
-        assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("store", mm)
-        for other in (False, True):
-            d_dims, d_strides, d_alloc = (ddims, dstrides, dalloc) if other else (dims, strides, alloc)
-            od = Map(es=es, dims=d_dims, strides=d_strides, box=box, swizzle=swz)
-            dst = dev_tensor(d_alloc, fill_seed=int(rng.integers(1 << 30)))
-            want_dst = dst.cpu().numpy().copy()
-            T.tmap_roundtrip(m, enc(dt, dst, d_dims, d_strides, box, swz), None, n, **opts)
-            check_ok()
-            oracle.roundtrip(om, host, od, want_dst, None, n)
-            assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip", other, mm)
+        oracle.roundtrip(om, host, od, want_dst, None, n)
+        assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip", other, mm)
 
 
 def test_binding_rejects_buffers_the_copy_would_overrun():

@@ -1,11 +1,13 @@
-// tmap_corner.h -- the copy of boxes at explicit corners, one wave per box,
-// written for the fewest instructions per box; a wave that takes several
-// boxes keeps one loading while it stores the one before.
+// tmap_corner.h -- the copy of boxes at explicit corners, or over a sweep,
+// one wave per box, written for the fewest instructions per box; a wave that
+// takes several boxes keeps one loading while it stores the one before.
 //
-// Each wave walks its own share of the corners through one LDS stage of one
-// box (NSLOT KiB, NSLOT <= 8) and its own 8-byte barrier record:
+// Each wave walks its own share of the corners (or of the sweep's boxes,
+// with the carry-add cursor of the other kernels) through one LDS stage of
+// one box (NSLOT KiB, NSLOT <= 8) and its own 8-byte barrier record:
 //
-//   fill    read the corner (scalar loads), rebase the buffer resource to it,
+//   fill    take the corner (scalar loads from the corner list, or the
+//           cursor's digits times the box), rebase the buffer resource to it,
 //           and issue one 16-byte direct-to-LDS load per slot: slot p takes
 //           the logical chunk swizzle(p), so the swizzle is applied as the
 //           bytes land ("TMA -- the async bulk copy engine", "The descriptor
@@ -129,10 +131,12 @@ struct CornerCopier {
     const KArgs &a;
     uint32_t lane, parity;
     int64_t cnt;
-    // explicit corners need no sweep digits: a tile index and the position
-    // in this wave's sequence, for the box to fill next and the box to drain
-    int64_t ft, ct;
-    uint32_t fk, ck;
+    // the box to fill next: a tile index, the position in this wave's
+    // sequence and, over a sweep, the tile's digits; the box to drain needs
+    // only its tile index and position (for its packed image)
+    Cursor<R> fcur;
+    int64_t ct;
+    uint32_t ck;
     int32_t fc[R];  // corner of the box under the fill cursor, read one fill ahead
     int32_t sc[R];  // corner of the box in the stage
     bool edge;      // the box in the stage needs its cut chunks patched
@@ -168,8 +172,14 @@ struct CornerCopier {
         behind = false;
         int64_t t0;
         corner_deal(a, (int64_t)blockIdx.x * wg + hw, cnt, t0);
-        ft = ct = t0;
-        fk = ck = 0;
+        ct = t0;
+        ck = 0;
+        if (a.coords) {
+            fcur.t = t0;
+            fcur.k = 0;
+        } else {
+            cursor_init<R>(a, t0, fcur);
+        }
         const KMap &sw = swept(a);
 #pragma unroll
         for (int j = 0; j < NSLOT; ++j) {
@@ -194,20 +204,11 @@ struct CornerCopier {
                 }
             }
         }
-        if (cnt > 0) corner_of(a, ft, fc);
+        if (cnt > 0) cursor_corner<R>(a, sw, fcur, fc);
     }
 
-    // Corner of tile t: uniform scalar loads through the constant address
-    // space, so they never wait behind the direct-to-LDS loads (vmcnt).
-    __device__ __forceinline__ static void corner_of(const KArgs &A, int64_t t, int32_t (&c)[R]) {
-        typedef const __attribute__((address_space(4))) int32_t const_i32;
-        const int r = swept(A).rank;
-        const_i32 *p = (const_i32 *)(A.coords) + t * r;
-#pragma unroll
-        for (int d = 0; d < R; ++d) c[d] = d < r ? p[d] : 0;
-    }
-
-    // Next tile of the sequence: +1 inside a group, big_step after its last.
+    // Next tile of the drain's sequence: +1 inside a group, big_step after
+    // its last.
     __device__ __forceinline__ static void advance(const KArgs &A, int64_t &t, uint32_t &k) {
         const bool big = (k & A.group_mask) == A.group_mask;
         k += 1;
@@ -231,7 +232,7 @@ struct CornerCopier {
         if (MODE == kStore) {
             // the packed images' fields stay in registers: the loads issue
             // without waiting for an argument read
-            const uint64_t base = (uint64_t)a.packed + (uint64_t)ft * a.dst.box_bytes;
+            const uint64_t base = (uint64_t)a.packed + (uint64_t)fcur.t * a.dst.box_bytes;
 #pragma unroll
             for (int j = 0; j < NSLOT; ++j) dma(base, a.dst.box_bytes, m0, j, soff[j]);
             edge = false;
@@ -249,10 +250,10 @@ struct CornerCopier {
                 edge = cuts_chunks(A, w);
             }
         }
-        advance(a, ft, fk);
-        // read the next corner now, while this box's loads fly (never past
+        cursor_advance<R>(a, fcur);
+        // take the next corner now, while this box's loads fly (never past
         // this wave's last tile: an explicit-corner array ends there)
-        if (nfill + 1 < cnt) corner_of(A, ft, fc);
+        if (nfill + 1 < cnt) cursor_corner<R>(A, swept(A), fcur, fc);
     }
 
     // Whether window w cuts through a 16-byte chunk in dimension 0.

@@ -363,16 +363,18 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
         !(flags & (TMAP_FLAG_THREAD_COPY | TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WHOLE_BOX)))
         wave_box = true;
     // sweeps the band kernel does not take (maps of rank 3 and more, and
-    // others) whose boxes suit the corner kernel in 4-byte lanes run there
-    // too, one stage, their corners walked by the kernel's cursor (measured
-    // on MI355X, padded 5-D fp32 tensor tiled by three shapes of 8 KiB box,
+    // others) with boxes of up to 8 KiB and a swizzle that moves whole
+    // chunks run on the corner kernels too, one stage, their corners walked
+    // by the kernels' cursor (measured on MI355X, padded 5-D fp32 tensor
+    // tiled by three shapes of 8 KiB box, in 4-byte lanes, one stream,
     // fraction of 8 TB/s against the shared ring: round trips 0.45 / 0.53 /
     // 0.45 against 0.23 / 0.17 / 0.22, loads 0.65 / 0.76 / 0.66 against
     // 0.38 / 0.31 / 0.38, stores 0.63 / 0.69 / 0.63 against 0.47 / 0.40 /
     // 0.47)
-    const bool sweep_c4 = !corners && !band && c4 && m.box_bytes <= 8192u && !(opts && opts->stages > 1) &&
-                          !(flags & (TMAP_FLAG_THREAD_COPY | TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WHOLE_BOX));
-    if (sweep_c4) {
+    const bool sweep_corner = !corners && !band && !elemwise && m.box_bytes <= 8192u &&
+                              !(opts && opts->stages > 1) &&
+                              !(flags & (TMAP_FLAG_THREAD_COPY | TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WHOLE_BOX));
+    if (sweep_corner) {
         wave_box = true;
         stages = 1;
     }
@@ -415,7 +417,7 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // 4 (measured best on MI355X over 10^5 scattered 8 KiB boxes: store
     // 0.539 -> 0.557 of peak, load 0.625 -> 0.669 with the packed side's
     // non-temporal hints)
-    if (!group && (corners || sweep_c4)) {
+    if (!group && (corners || sweep_corner)) {
         // the corner kernel (one stage, whole-chunk swizzles) loads and
         // round-trips 8 KiB boxes fastest one to a wave (10^5 boxes: load
         // 0.73 of peak against 0.69 with 2, round trip 0.366 against 0.353)
@@ -583,11 +585,11 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     if (lean && (opts && (opts->flags & TMAP_FLAG_WHOLE_BOX)) && !opts->regions && !resident &&
         !(mode == tmap::kRoundtrip && swept.box_bytes == 16384u))
         pl.regions = 2u;
-    // explicit corners, one wave per box with one stage, boxes of at most
-    // 8 KiB and a swizzle that moves whole chunks: the corner kernels, which
-    // hold each drained box in registers while the next one loads
-    // (a sweep runs there only in 4-byte lanes)
-    pl.corner = (a.coords || c4) && pl.stages == 31 && pl.nslot <= 8 && !a.elemwise;
+    // one wave per box with one stage, boxes of at most 8 KiB and a swizzle
+    // that moves whole chunks, at explicit corners or over a sweep: the
+    // corner kernels, which hold each drained box in registers while the
+    // next one loads
+    pl.corner = pl.stages == 31 && pl.nslot <= 8 && !a.elemwise;
     // ... in 4-byte lanes where the maps allow it: no element-by-element
     // patching of chunks the tensor's edge cuts, and a row's offset worked
     // out once per box instead of once per chunk (measured on MI355X over
