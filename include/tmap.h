@@ -27,10 +27,11 @@
  *     stream) and return without waiting.  Argument errors are reported
  *     synchronously, before anything is launched; a failed call launches
  *     nothing.  n_tiles == 0 is a successful no-op.
- *   - No call allocates device memory per call.  One 4-byte status word per
- *     device is allocated on first use and kept until process exit.
+ *   - No call allocates device memory per call.  One 1 KiB table of status
+ *     words per device (a word for each stream that launches a copy there)
+ *     is allocated on first use and kept until process exit.
  *   - The copy calls can be captured into a HIP graph and replayed: once the
- *     device's status word exists (after any earlier launch on it), a launch
+ *     device's status words exist (after any earlier launch on it), a launch
  *     only enqueues kernels, with no allocation, copy or memset.
  */
 #ifndef TMAP_H
@@ -319,7 +320,8 @@ tmap_status tmap_roundtrip(const tmap_t *src, const tmap_t *dst, const int32_t *
  * The copy kernels need one 4-byte status word beyond their inputs and
  * outputs, which they set when a bounded readiness wait expires.  Here it is
  * a static device array of the library (4 bytes per device, kept until the
- * process ends) instead of the word tmap_roundtrip allocates on first use;
+ * process ends) instead of the per-stream words tmap_roundtrip allocates on
+ * first use;
  * its need does not grow with the input, so no input size is refused for it.
  * The device address of the array is looked up once per device, on the
  * first call there (a gfx950 device must be current, else
@@ -481,16 +483,18 @@ const char *tmap_status_string(tmap_status status);
  * only as INVALID_VALUE, with no word on which rule it was. */
 const char *tmap_last_error_detail(void);
 
-/* Wait for hip_stream, then read and clear the current device's status
- * words that kernels set when a bounded readiness wait expires (the
- * library-allocated one and that of tmap_roundtrip_noalloc).  Returns
- * TMAP_SUCCESS or TMAP_ERROR_TIMEOUT (or TMAP_ERROR_LAUNCH if the stream
- * reports an error).  The words are per device, not per stream: a timeout
- * of a copy on one stream is reported to whichever stream of that device is
- * checked first, and a check clears it for all of them.  The read and the
- * clear are two steps, so a timeout that a copy still running on another
- * stream records between them goes unreported; for an exact report, check
- * once every stream of the device has finished.
+/* Wait for hip_stream, then read and clear the status words that kernels
+ * set when a bounded readiness wait expires: the current device's word for
+ * this stream, and the one word of tmap_roundtrip_noalloc on the device.
+ * Returns TMAP_SUCCESS or TMAP_ERROR_TIMEOUT (or TMAP_ERROR_LAUNCH if the
+ * stream reports an error).  Each stream that launches copies on a device
+ * gets a word of its own there (the first 255 streams; later ones share a
+ * word), so a timeout is reported to the stream whose copy it was, and a
+ * copy still running on another stream cannot set the word being read and
+ * cleared.  tmap_roundtrip_noalloc's word is shared by every stream of the
+ * device: its timeouts are reported to whichever stream checks first, and
+ * one recorded by a copy on another stream between this call's read and
+ * clear goes unreported.
  * ("TMA -- the async bulk copy engine", "Load completion -- the mbarrier and
  * the byte budget": a wait on a byte budget that never completes must end;
  * here it ends the kernel and is reported here.) */

@@ -1137,6 +1137,30 @@ def test_budget_mismatch_times_out_instead_of_hanging(mode):
     assert torch.equal(out.view(4, -1)[3], src)
 
 
+def test_timeouts_are_reported_to_their_own_stream():
+    """Each stream that launches copies has its own status word: a copy
+    whose readiness wait expires on one stream is reported to that stream
+    alone, and checking another stream neither sees it nor clears it."""
+    say("timeouts per stream")
+    src = dev_tensor(256 * 100, fill_seed=3)
+    dims, box = [64, 100], [64, 32]
+    m = enc("f32", src, dims, [256], box)
+    coords = torch.tensor([[0, 0], [0, 50], [-9, 90]], dtype=torch.int32, device=DEV)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    out_a, out_b = dev_tensor(8192 * 3), dev_tensor(8192 * 3)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        T.tmap_load_tiles(m, coords, 3, out_a, flags=T.FLAG_INJECT_BUDGET_MISMATCH, spin_limit=2000, stream=sa)
+        T.tmap_load_tiles(m, coords, 3, out_b, stream=sb)
+        assert T.tmap_sync_status(sb) == T.SUCCESS
+        assert T.tmap_sync_status() == T.SUCCESS       # the current stream launched nothing
+        assert T.tmap_sync_status(sa) == T.TIMEOUT
+        assert T.tmap_sync_status(sa) == T.SUCCESS     # read and cleared
+    om = Map(es=4, dims=dims, strides=[256], box=box)
+    want = oracle.load_tiles(om, src.cpu().numpy(), coords.cpu().numpy(), 3)
+    assert out_b.cpu().numpy().tobytes() == want.tobytes()
+
+
 @pytest.mark.parametrize("dtype", ["u8", "f32"])
 def test_budget_mismatch_times_out_in_the_corner_kernels(dtype):
     """The same for boxes at explicit corners, one wave per box: the corner

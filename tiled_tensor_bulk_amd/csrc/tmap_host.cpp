@@ -14,6 +14,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <unordered_map>
 
 #include "tmap_internal.h"
 
@@ -56,12 +57,19 @@ bool decode(const tmap_t *map, MapImpl &m) {
 }
 
 // ------------------------------------------------------------------ device
+// The status words kernels set when a bounded readiness wait expires: one
+// per stream that has launched on the device, so that a timeout is reported
+// to the stream whose copy it was.  Word 0 is shared by the streams beyond
+// the first kStatusSlots - 1.
+constexpr uint32_t kStatusSlots = 256;
+
 struct DeviceState {
     bool probed = false;
     bool supported = false;
     int cus = 0;
     uint32_t lds_per_cu = 0;
-    uint32_t *status = nullptr;  // one word, allocated on first launch
+    uint32_t *status = nullptr;  // kStatusSlots words, allocated on first launch
+    std::unordered_map<void *, uint32_t> slot_of;  // stream -> its word
 };
 std::mutex g_dev_mu;
 DeviceState g_dev[64];
@@ -94,15 +102,28 @@ tmap_status device_for_launch(DeviceState **out, bool need_status = true) {
         return fail(TMAP_ERROR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
     if (need_status && !d.status) {
         void *p = nullptr;
-        if (hipMalloc(&p, 4) != hipSuccess || hipMemset(p, 0, 4) != hipSuccess) {
+        const size_t bytes = kStatusSlots * sizeof(uint32_t);
+        if (hipMalloc(&p, bytes) != hipSuccess || hipMemset(p, 0, bytes) != hipSuccess ||
+            hipDeviceSynchronize() != hipSuccess) {
             (void)hipGetLastError();
             if (p) (void)hipFree(p);
-            return fail(TMAP_ERROR_LAUNCH, "cannot allocate the 4-byte status word");
+            return fail(TMAP_ERROR_LAUNCH, "cannot allocate the status words");
         }
         d.status = (uint32_t *)p;
     }
     *out = &d;
     return TMAP_SUCCESS;
+}
+
+// The status word of `stream` on device d: its own while fewer than
+// kStatusSlots - 1 streams have launched there, else the shared word 0.
+uint32_t status_slot(DeviceState &d, void *stream) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    auto it = d.slot_of.find(stream);
+    if (it != d.slot_of.end()) return it->second;
+    const uint32_t slot = d.slot_of.size() + 1 < kStatusSlots ? (uint32_t)d.slot_of.size() + 1 : 0u;
+    d.slot_of.emplace(stream, slot);
+    return slot;
 }
 
 int64_t sweep_count(const MapImpl &m) {
@@ -662,7 +683,7 @@ tmap_status run(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_launc
     Plan pl;
     st = prepare(mode, swept, a, opts, *dev, pl);
     if (st != TMAP_SUCCESS) return st;
-    a.status = dev->status;
+    if (!noalloc) a.status = dev->status + status_slot(*dev, stream);
     if (noalloc) {
         st = tmap::noalloc_scratch(&a.status);
         if (st != TMAP_SUCCESS) return st;
@@ -1138,11 +1159,14 @@ tmap_status tmap_sync_status(void *hip_stream) {
         const hipError_t e = hipGetLastError();
         return fail(TMAP_ERROR_LAUNCH, "stream error: %s", hipGetErrorString(e));
     }
-    // the library-allocated word and the no-allocation entry point's word
+    // this stream's word of the library's table (none if it never launched
+    // a copy on this device) and the no-allocation entry point's word
     uint32_t *words[2] = {nullptr, tmap::noalloc_status(dev)};
     {
         std::lock_guard<std::mutex> lk(g_dev_mu);
-        words[0] = g_dev[dev].status;
+        const DeviceState &d = g_dev[dev];
+        const auto it = d.slot_of.find(hip_stream);
+        if (d.status && it != d.slot_of.end()) words[0] = d.status + it->second;
     }
     uint32_t any = 0;
     for (uint32_t *word : words) {
