@@ -96,11 +96,12 @@ typedef struct tmap_launch_opts {
                              bytes of a row, at least 2 and at most 8; band units: 2 on
                              the band kernel (4 for round trips of whole 16 KiB boxes),
                              else 4 for a round trip and 1 for a load
-                             or store; explicit corners: 8, for a wave-per-box store 4;
-                             wave per box with boxes of 8 KiB and more: on the corner
-                             kernel 1 for a load or round trip and 2 for a store, 1 in
-                             every direction in 4-byte lanes (TMAP_VARIANT_CORNER4),
-                             else 4 for a load, 2 for a store and 8 for a round trip) */
+                             or store; on the corner kernels, TMAP_VARIANT_CORNER and
+                             TMAP_VARIANT_CORNER4: about 4 KiB of boxes, 1 for boxes of
+                             4 KiB and more, 2 of 2 KiB, 4 of 1 KiB; other explicit
+                             corners: 8, for a wave-per-box
+                             store 4, and with boxes of 8 KiB and more 4 for a
+                             wave-per-box load, 2 for a store and 8 for a round trip) */
     uint32_t regions;     /* 1..64: deal the groups to the grid as that many interleaved
                              streams, each sweeping an equal contiguous stretch of the
                              tiles (workgroup i takes stretch i mod regions; in
@@ -108,11 +109,12 @@ typedef struct tmap_launch_opts {
                              that the tiles in flight lie in that many places of the
                              tensor instead of one.  How the addresses in flight fall
                              on the HBM channels and the L2 caches decides which is
-                             faster (default: 8 on the corner kernels, TMAP_VARIANT_CORNER
-                             and TMAP_VARIANT_CORNER4, where a workgroup is one wave
-                             (boxes of 8 KiB), so that the workgroups on one of the
-                             GPU's 8 XCDs, which share an L2, take neighbouring
-                             tiles; 2 for loads and stores on the band schedule, for
+                             faster (default on the corner kernels, TMAP_VARIANT_CORNER
+                             and TMAP_VARIANT_CORNER4: 8 where a workgroup is one wave
+                             (boxes of 8 KiB), 32 where its four waves take one box at a
+                             time (4 KiB boxes), so that the workgroups on one of the
+                             GPU's 8 XCDs, which share an L2, take neighbouring tiles;
+                             else 1; 2 for loads and stores on the band schedule, for
                              band-kernel round trips of tensors whose row pitch is not
                              a power of two, and for whole boxes on the band kernel
                              except round trips of 16 KiB boxes; else 1)               */

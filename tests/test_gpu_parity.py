@@ -1000,20 +1000,30 @@ def test_plan_query_reports_the_schedules():
         assert (p["variant"], p["stages"], p["slots"], p["group"], p["regions"]) == ("corner4", 1, 8, 1, 8), direction
         assert p["walkers"] == 100000 and p["workgroups"] == p["walkers"], direction
         assert p["lds_bytes"] == 8192 + 8, direction
-    # 2 KiB boxes: four waves to a workgroup
+    # 2 KiB boxes: four waves to a workgroup, two boxes to a wave, one
+    # stream; 4 KiB boxes one box to a wave, dealt as 32 streams (one per XCD
+    # and wave slot); 1 KiB boxes four to a wave
     m = T.tmap_encode("f32", 2, 0x7F0000000000, [1000, 1000], [4000], [32, 16])
     p = T.tmap_plan_launch("load", m, None, True, 1000)
-    assert (p["variant"], p["slots"], p["walkers"], p["regions"]) == ("corner4", 2, 125, 1)
+    assert (p["variant"], p["slots"], p["group"], p["walkers"], p["regions"]) == ("corner4", 2, 2, 500, 1)
     assert T.tmap_plan_launch("load", m, None, True, 1000, regions=3)["regions"] == 3
-    assert p["workgroups"] == 32 and p["lds_bytes"] == 4 * 2048 + 4 * 8
+    assert p["workgroups"] == 125 and p["lds_bytes"] == 4 * 2048 + 4 * 8
+    m = T.tmap_encode("f32", 2, 0x7F0000000000, [1000, 1000], [4000], [32, 32])
+    for direction in ("load", "store", "roundtrip"):
+        p = T.tmap_plan_launch(direction, m, m if direction == "roundtrip" else None, True, 1000)
+        assert (p["variant"], p["slots"], p["group"], p["walkers"], p["workgroups"], p["regions"]) == \
+            ("corner4", 4, 1, 1000, 250, 32), direction
+    m = T.tmap_encode("f32", 2, 0x7F0000000000, [1000, 1000], [4000], [32, 8])
+    p = T.tmap_plan_launch("store", m, None, True, 1000)
+    assert (p["variant"], p["slots"], p["group"], p["walkers"], p["regions"]) == ("corner4", 1, 4, 250, 1)
     # 16-bit elements in 8 KiB boxes with a swizzle whose XOR reaches past a
     # 128-byte row: the corner kernel in 16-byte lanes; its loads reserve
-    # 11 KiB of LDS to a workgroup, its stores take two boxes to a wave
+    # 11 KiB of LDS to a workgroup; one box to a wave in every direction
     m = T.tmap_encode("bf16", 2, 0x7F0000000000, [1000, 1000], [2048], [64, 64], None, (3, 4, 3))
     p = T.tmap_plan_launch("load", m, None, True, 1000)
     assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"], p["regions"]) == ("corner", 1, 11264, 1000, 8)
     p = T.tmap_plan_launch("store", m, None, True, 1000)
-    assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"]) == ("corner", 2, 8192 + 8, 500)
+    assert (p["variant"], p["group"], p["lds_bytes"], p["walkers"]) == ("corner", 1, 8192 + 8, 1000)
     assert T.tmap_plan_launch("roundtrip", m, m, True, 1000)["group"] == 1
     # sweeps of rank 5 (never the band schedule) whose boxes suit the 4-byte
     # lanes run there, one stage, one box to a wave, the waves dealt to the

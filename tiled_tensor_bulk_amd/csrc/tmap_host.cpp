@@ -329,11 +329,8 @@ constexpr uint32_t kKnownFlags = TMAP_FLAG_CONTIGUOUS | TMAP_FLAG_NONTEMPORAL | 
 
 // lean: the band schedule runs the band kernel of rank-2 sweeps.
 // elemwise: the swizzle moves data inside 16-byte chunks.
-// c4: the maps suit the corner kernels in 4-byte lanes (corner4_fits) and
-// the band schedule is not taken.
 tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_launch_opts *opts,
-                        const DeviceState &dev, bool band, bool lean, bool corners, bool elemwise, bool c4,
-                        Plan &pl) {
+                        const DeviceState &dev, bool band, bool lean, bool corners, bool elemwise, Plan &pl) {
     const uint32_t flags0 = opts ? opts->flags : 0u;
     const uint32_t per_wave_pass = tmap::kWaves * tmap::kBlockBytes;  // bytes one slot per lane covers
     const uint32_t need = (m.box_bytes + per_wave_pass - 1) / per_wave_pass;
@@ -433,23 +430,35 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     if (!group && whole16) group = 4u;
     if (!group && lean) group = 2u;
     if (!group && band) group = mode == tmap::kRoundtrip ? 4u : 1u;
-    // explicit corners: 8 tiles to a walker; a wave-per-box store takes 4.
-    // Where each wave is a workgroup of its own, a store takes 2 and a load
-    // 4 (measured best on MI355X over 10^5 scattered 8 KiB boxes: store
-    // 0.539 -> 0.557 of peak, load 0.625 -> 0.669 with the packed side's
-    // non-temporal hints)
+    // explicit corners and the sweeps that run like them: 8 tiles to a
+    // walker; a wave-per-box store takes 4.  Where each wave is a workgroup
+    // of its own, the wave kernel's stores take 2 and its loads 4 (measured
+    // best on MI355X over 10^5 scattered 8 KiB boxes: store 0.539 -> 0.557
+    // of peak, load 0.625 -> 0.669 with the packed side's non-temporal hints)
     if (!group && (corners || sweep_corner)) {
-        // the corner kernel (one stage, whole-chunk swizzles) loads and
-        // round-trips 8 KiB boxes fastest one to a wave (10^5 boxes: load
-        // 0.73 of peak against 0.69 with 2, round trip 0.366 against 0.353)
-        // and stores them 2 to a wave (0.633; 4: 0.618); in 4-byte lanes it
-        // takes one box to a wave in every direction (store 0.674 against
-        // 0.667 with 2 and 0.659 with 4; load 0.743 / 0.740 / 0.735; round
-        // trip 0.427 / 0.428 / 0.422); the wave kernel takes 4 and 8
-        const bool corner = stages == 1 && !elemwise;
-        if (wave_box && tmap::wave_group(nslot) == 1)
-            group = (mode == tmap::kStore && !(corner && c4)) ? 2u
-                    : (corner ? 1u : (mode == tmap::kLoad ? 4u : 8u));
+        // the corner kernels (one stage, whole-chunk swizzles): about 4 KiB
+        // of boxes to a wave, in every direction: one box from 4 KiB up, two
+        // of 2 KiB, four of 1 KiB.  Measured on MI355X over the padded 5-D
+        // tensor, fraction of 8 TB/s, sweeps and 10^5 random corners: 8 KiB
+        // boxes in 4-byte lanes, one box against 2 and 4: load 0.743 / 0.740
+        // / 0.735, store 0.674 / 0.667 / 0.659, round trip 0.427 / 0.428 /
+        // 0.422 (random); in 16-byte lanes, stores of sweeps 0.583 / 0.544 /
+        // 0.504 and of random corners 0.551 / 0.534 / 0.528; 4 KiB boxes, one
+        // against the 8 (stores 4) that four-wave workgroups took before:
+        // sweeps' round trips 0.605 against 0.404 in 4-byte lanes and 0.419
+        // against 0.305 in 16-byte lanes, loads 0.757 against 0.633, random
+        // corners 1-8% faster; 2 KiB boxes, two against 1 and 8 (stores 4):
+        // sweeps' round trips 0.539 against 0.443 and 0.443, random loads
+        // 0.677 against 0.620 and 0.590; 1 KiB boxes, four against 2 and 1:
+        // sweeps' round trips 0.354 / 0.314 / 0.247, loads 0.442 / 0.389 /
+        // 0.305, random round trips 0.246 / 0.235 / 0.198
+        const bool corner = wave_box && stages == 1 && !elemwise && nslot <= 8;
+        if (corner) {
+            group = 1;
+            while (group < 64 && 2 * group * m.box_bytes <= 4096u) group *= 2;
+        }
+        else if (wave_box && tmap::wave_group(nslot) == 1)
+            group = mode == tmap::kStore ? 2u : (mode == tmap::kLoad ? 4u : 8u);
         else
             group = (wave_box && mode == tmap::kStore) ? 4u : 8u;
     }
@@ -588,7 +597,7 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     const bool lean = band && lean_maps;
     const bool c4 = !band && corner4_fits(mode, a);
     tmap_status st =
-        plan_launch(mode, swept, a.n_tiles, opts, dev, band, lean, a.coords != nullptr, a.elemwise != 0, c4, pl);
+        plan_launch(mode, swept, a.n_tiles, opts, dev, band, lean, a.coords != nullptr, a.elemwise != 0, pl);
     if (st != TMAP_SUCCESS) return st;
     pl.band_g = band ? g : 0u;
     pl.band_rows = band ? rows : 0u;
@@ -618,7 +627,9 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     // -> 0.427, store 0.637 -> 0.674, load 0.733 -> 0.743)
     pl.corner4 = pl.corner && c4;
     // Where each wave is a workgroup of its own (8 KiB boxes), the corner
-    // kernels deal the waves as one interleaved stream per XCD: the
+    // kernels deal the waves as one interleaved stream per XCD, and where a
+    // four-wave workgroup's waves take one box at a time (4 KiB boxes), as
+    // one per XCD and wave slot: the
     // dispatcher hands workgroups to the XCDs in turn, so workgroups b and
     // b + 8 share an L2 and get neighbouring boxes, and the cache lines that
     // neighbouring boxes share (box rows that do not start on a line) are
@@ -628,9 +639,18 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     // one stream, loads 0.871 / 0.886 / 0.879 against 0.621 / 0.716 / 0.629,
     // stores 0.706 / 0.721 / 0.708 against 0.624 / 0.692 / 0.633; the same
     // sweep's corners as a list alike; 10^5 random corners 0.8-1.9% faster.
-    // Four-wave workgroups of smaller boxes keep one stream (8 KiB-wide
-    // deals gained their sweeps 1-7% but cost random corners up to 7%).
-    if (pl.corner && tmap::wave_group(pl.nslot) == 1 && !(opts && opts->regions)) pl.regions = kXcds;
+    // 4 KiB boxes dealt as 32 streams: sweeps' loads 0.877 against 0.757 in
+    // 4-byte lanes and 0.697 against 0.641 in 16-byte lanes, round trips
+    // 0.637 against 0.606, random corners within 0.5%.  Walkers that take
+    // several boxes at a time (smaller boxes) keep one stream: 32 streams
+    // cost 2 KiB boxes 1-7%.
+    if (pl.corner && !(opts && opts->regions)) {
+        const uint32_t wg = (uint32_t)tmap::wave_group(pl.nslot);
+        if (wg == 1)
+            pl.regions = kXcds;
+        else if (pl.group == 1)
+            pl.regions = kXcds * wg;
+    }
     if (pl.corner4) {
         const uint32_t row = (uint32_t)swept.box[0] * swept.elem_size;
         a.c4_dshift = log2u(row / 4u);
