@@ -79,9 +79,9 @@ typedef struct tmap_swizzle {
  * default. */
 typedef struct tmap_launch_opts {
     uint32_t stages;      /* LDS ring depth 1..4 (default 2; 1 with explicit corners, for
-                             sweeps the corner kernels take (see
-                             TMAP_FLAG_WAVE_PER_BOX) and when each workgroup takes a
-                             single band unit; 3 for round
+                             sweeps of whole boxes (on the corner kernels, see
+                             TMAP_FLAG_WAVE_PER_BOX, or on the cooperative ring) and
+                             when each workgroup takes a single band unit; 3 for round
                              trips on the band schedule, and for every direction of
                              the band kernel, TMAP_VARIANT_BAND, except 4 for round
                              trips of whole 16 KiB boxes there)                         */

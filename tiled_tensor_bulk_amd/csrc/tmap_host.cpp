@@ -396,6 +396,18 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
         wave_box = true;
         stages = 1;
     }
+    // the other sweeps of whole boxes on the cooperative ring (boxes over
+    // 8 KiB, swizzles that move elements inside chunks, TMAP_FLAG_WHOLE_BOX
+    // where the band kernel does not apply): one stage, which fits twice the
+    // workgroups on a CU (measured on MI355X, padded 5-D fp32 tensor swept
+    // by 16 and 32 KiB boxes, fraction of 8 TB/s: loads 0.615 / 0.589
+    // against 0.485 / 0.448 with two stages, round trips 0.274 / 0.273
+    // against 0.248 / 0.201, stores 0.565 / 0.540 against 0.562 / 0.520;
+    // 8 KiB whole boxes: load 0.462 against 0.381; 8 KiB boxes under a
+    // swizzle of 4-byte granules: load 0.196 against 0.172)
+    if (!(opts && opts->stages) && !corners && !band && !sweep_corner &&
+        !(flags & (TMAP_FLAG_THREAD_COPY | TMAP_FLAG_PRODUCER_WAVE | TMAP_FLAG_WAVE_PER_BOX)))
+        stages = 1;
     if (opts && (opts->flags & TMAP_FLAG_BAND) && (opts->flags & TMAP_FLAG_WHOLE_BOX))
         return fail(TMAP_ERROR_INVALID_VALUE, "TMAP_FLAG_BAND and TMAP_FLAG_WHOLE_BOX exclude each other");
     if (thread_copy) stages = 1;  // one LDS stage; the next tile waits in registers
