@@ -432,10 +432,11 @@ typedef enum tmap_variant {
                                        loads                                                   */
     TMAP_VARIANT_CORNER4 = 6        /* the same boxes in 4-byte lanes, for maps with box rows of a
                                        power of two from 16 to 256 bytes, at most 64 rows to a
-                                       box, and no swizzle or one that moves whole 16-byte
-                                       chunks within rows: the hardware's bounds check clips
-                                       every lane, and only words of 1- or 2-byte elements that
-                                       the tensor's edge cuts move element by element.  Also
+                                       box, and no swizzle or one that moves whole words (4-byte
+                                       granules or larger) within rows: the hardware's bounds
+                                       check clips every lane, and only words of 1- or 2-byte
+                                       elements that the tensor's edge cuts move element by
+                                       element.  Also
                                        sweeps of such maps that the band schedule does not take
                                        (maps of rank 3 and more, among others)                */
 } tmap_variant;

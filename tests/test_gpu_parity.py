@@ -740,13 +740,15 @@ def _corner4_case(rng):
             strides.append(s)
             s *= dims[d] + int(rng.integers(0, 2))
         return dims, strides, s
-    # half the maps take a swizzle the 4-byte lanes handle: whole 16-byte
-    # chunks (target bit tb >= 4) moved within a row (tb + B <= log2(row))
+    # half the maps take a swizzle the 4-byte lanes handle: whole words
+    # (target bit tb >= 2) moved within a row (tb + B <= log2(row))
     lg, lrow = es.bit_length() - 1, row.bit_length() - 1
     swz = (0, 0, 0)
-    if rng.integers(0, 2) and lrow - 4 >= 1:
-        b = int(rng.integers(1, min(4, lrow - 4) + 1))
-        m = int(rng.integers(max(0, 4 - lg), lrow - lg - b + 1))
+    tb_min = 4 if rng.integers(0, 2) and lrow - max(lg, 4) >= 1 else 2   # whole chunks, or word granules
+    b_max = min(4, lrow - max(lg, tb_min))     # m >= max(0, tb_min - lg) and m + lg + b <= lrow
+    if rng.integers(0, 2) and b_max >= 1:
+        b = int(rng.integers(1, b_max + 1))
+        m = int(rng.integers(max(0, tb_min - lg), lrow - lg - b + 1))
         swz = (b, m, int(rng.integers(b, b + 4)))
     return es, box, swz, layout(), layout()
 
@@ -1054,7 +1056,11 @@ def test_plan_query_reports_the_schedules():
     assert variant("bf16", 2000, [64, 64], (3, 3, 3)) == "corner4"
     assert variant("f32", 4000, [16, 64], (3, 2, 3)) == "corner"   # 128-byte swizzle, 64-byte rows
     assert variant("f32", 4000, [32, 64], (3, 3, 3)) == "corner"   # its XOR reaches past the row
-    assert variant("f32", 4000, [32, 64], (1, 0, 1)) == "wave_per_box"  # moves elements inside chunks
+    assert variant("f32", 4000, [32, 64], (1, 0, 1)) == "corner4"  # 4-byte granules: whole words
+    assert variant("f64", 8000, [16, 64], (2, 0, 3)) == "corner4"  # 8-byte granules
+    assert variant("bf16", 2000, [64, 64], (1, 1, 2)) == "corner4"  # 4-byte granules of 2 elements
+    assert variant("bf16", 2000, [64, 64], (1, 0, 1)) == "wave_per_box"  # 2-byte granules: inside words
+    assert variant("u8", 1008, [128, 64], (2, 1, 3)) == "wave_per_box"
     assert variant("bf16", 2000, [64, 64]) == "corner4"           # 2-byte elements
     assert variant("u8", 1008, [16, 8, 4]) == "corner4"           # bytes, 16-byte rows
     assert plan("pad5d_f32", "roundtrip", stages=2)["variant"] == "wave_per_box"

@@ -562,8 +562,10 @@ bool small_offsets(const tmap::KMap &m) {
 // 64 rows to a box.  Then a lane's column is the same in every slot, and
 // only a word of 1- or 2-byte elements that the tensor's dimension-0 edge
 // cuts needs its elements moved one by one.  A swizzle qualifies when it
-// moves whole 16-byte chunks within rows (its XOR's target bits below the
-// row's size) with a key of at most 4 bits.
+// moves whole words within rows (granules of 4 bytes or more: its XOR's
+// target bits from bit 2 of the byte offset up to below the row's size)
+// with a key of at most 4 bits.  Granules of 4 and 8 bytes, which the other
+// kernels move element by element, are whole words here.
 bool corner4_fits(int mode, const tmap::KArgs &a) {
     const tmap::KMap &m = mode == tmap::kStore ? a.dst : a.src;
     const uint32_t row = (uint32_t)m.box[0] * m.elem_size;
@@ -571,7 +573,7 @@ bool corner4_fits(int mode, const tmap::KArgs &a) {
     if (m.box_bytes / row > 64u) return false;
     if (m.swz_b == 0) return true;
     const uint32_t tb = m.swz_m + log2u(m.elem_size);
-    return !a.elemwise && m.swz_b <= 4u && tb + m.swz_b <= log2u(row);
+    return tb >= 2u && m.swz_b <= 4u && tb + m.swz_b <= log2u(row);
 }
 
 void fill_common(tmap::KArgs &a, const MapImpl &swept, const int32_t *coords, int64_t n_tiles) {
@@ -609,7 +611,7 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     const bool lean = band && lean_maps;
     const bool c4 = !band && corner4_fits(mode, a);
     tmap_status st =
-        plan_launch(mode, swept, a.n_tiles, opts, dev, band, lean, a.coords != nullptr, a.elemwise != 0, pl);
+        plan_launch(mode, swept, a.n_tiles, opts, dev, band, lean, a.coords != nullptr, a.elemwise != 0 && !c4, pl);
     if (st != TMAP_SUCCESS) return st;
     pl.band_g = band ? g : 0u;
     pl.band_rows = band ? rows : 0u;
@@ -631,7 +633,7 @@ tmap_status prepare(int mode, const MapImpl &swept, tmap::KArgs &a, const tmap_l
     // that moves whole chunks, at explicit corners or over a sweep: the
     // corner kernels, which hold each drained box in registers while the
     // next one loads
-    pl.corner = pl.stages == 31 && pl.nslot <= 8 && !a.elemwise;
+    pl.corner = pl.stages == 31 && pl.nslot <= 8 && (!a.elemwise || c4);
     // ... in 4-byte lanes where the maps allow it: no element-by-element
     // patching of chunks the tensor's edge cuts, and a row's offset worked
     // out once per box instead of once per chunk (measured on MI355X over
