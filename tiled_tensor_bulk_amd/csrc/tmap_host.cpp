@@ -524,6 +524,42 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     return TMAP_SUCCESS;
 }
 
+// A sweep whose boxes have extent 1 in a dimension d >= 2, over planes that
+// are dense in dimension d - 1 (strides[d] == dims[d-1] * strides[d-1]) and
+// a whole number of boxes tall there (dims[d-1] % box[d-1] == 0), is the
+// same sweep with dimension d folded into d - 1: a batch of matrices swept
+// by 2-D boxes is one taller matrix.  The tiles come in the same order, each
+// covering the same elements with the same bounds, so every image and every
+// stored byte is unchanged; the folded maps can take the kernels of lower
+// ranks (the band kernel takes rank 2).  A round trip's destination folds
+// with the source, with the same plane height, or neither folds.
+void fold_sweep(MapImpl &m, MapImpl *m2) {
+    auto foldable = [](const MapImpl &x, int d) {
+        return x.box[d] == 1 && x.dims[d - 1] % x.box[d - 1] == 0 &&
+               x.strides[d] == x.dims[d - 1] * x.strides[d - 1] && x.dims[d - 1] * x.dims[d] < (1ull << 31);
+    };
+    for (int d = 2; d < m.rank;) {
+        if (!foldable(m, d) || (m2 && (!foldable(*m2, d) || m2->dims[d - 1] != m.dims[d - 1]))) {
+            ++d;
+            continue;
+        }
+        for (MapImpl *x : {&m, m2}) {
+            if (!x) continue;
+            x->dims[d - 1] *= x->dims[d];
+            for (int k = d; k + 1 < x->rank; ++k) {
+                x->dims[k] = x->dims[k + 1];
+                x->strides[k] = x->strides[k + 1];
+                x->box[k] = x->box[k + 1];
+            }
+            const int last = x->rank - 1;
+            x->dims[last] = 1;
+            x->strides[last] = 0;
+            x->box[last] = 1;
+            x->rank = (uint8_t)last;
+        }
+    }
+}
+
 tmap_status check_coords_and_count(const MapImpl &swept, const int32_t *coords, int64_t n_tiles) {
     if (n_tiles < 0) return fail(TMAP_ERROR_INVALID_VALUE, "n_tiles is negative");
     if (!coords && n_tiles != sweep_count(swept))
@@ -996,6 +1032,7 @@ tmap_status tmap_load_tiles(const tmap_t *src, const int32_t *coords, int64_t n_
     if (!packed_out || ((uintptr_t)packed_out & 15u))
         return fail(TMAP_ERROR_INVALID_VALUE, "packed_out is NULL or not 16-byte aligned");
     if (n_tiles == 0) return ok();
+    if (!coords) fold_sweep(s, nullptr);
     tmap::KArgs a;
     std::memset(&a, 0, sizeof a);
     a.src = tmap::kernel_map(s);
@@ -1014,6 +1051,7 @@ tmap_status tmap_store_tiles(const tmap_t *dst, const int32_t *coords, int64_t n
     if (!packed_in || ((uintptr_t)packed_in & 15u))
         return fail(TMAP_ERROR_INVALID_VALUE, "packed_in is NULL or not 16-byte aligned");
     if (n_tiles == 0) return ok();
+    if (!coords) fold_sweep(d, nullptr);
     tmap::KArgs a;
     std::memset(&a, 0, sizeof a);
     a.src = tmap::kernel_map(d);
@@ -1102,6 +1140,7 @@ static tmap_status roundtrip_impl(const tmap_t *src, const tmap_t *dst, const in
     tmap_status st = check_coords_and_count(s, coords, n_tiles);
     if (st != TMAP_SUCCESS) return st;
     if (n_tiles == 0) return ok();
+    if (!coords) fold_sweep(s, &d);
     tmap::KArgs a;
     std::memset(&a, 0, sizeof a);
     a.src = tmap::kernel_map(s);
@@ -1147,6 +1186,10 @@ tmap_status tmap_plan_launch(tmap_direction direction, const tmap_t *swept, cons
     if (st != TMAP_SUCCESS) return st;
     std::memset(out, 0, sizeof *out);
     if (n_tiles == 0) return ok();  // nothing would be launched
+    if (!coords) {
+        fold_sweep(s, direction == TMAP_DIR_ROUNDTRIP ? &d : nullptr);
+        if (direction != TMAP_DIR_ROUNDTRIP) d = s;
+    }
     DeviceState *dev = nullptr;
     st = device_for_launch(&dev, false);
     if (st != TMAP_SUCCESS) return st;
