@@ -81,10 +81,11 @@ typedef struct tmap_launch_opts {
     uint32_t stages;      /* LDS ring depth 1..4 (default 2; 1 with explicit corners, for
                              sweeps of whole boxes (on the corner kernels, see
                              TMAP_FLAG_WAVE_PER_BOX, or on the cooperative ring) and
-                             when each workgroup takes a single band unit; 3 for round
-                             trips on the band schedule, and for every direction of
-                             the band kernel, TMAP_VARIANT_BAND, except 4 for round
-                             trips of whole 16 KiB boxes there)                         */
+                             when each workgroup takes a single band unit, and for
+                             loads and stores on the band schedule outside the band
+                             kernel; 3 for every direction of the band kernel,
+                             TMAP_VARIANT_BAND, except 4 for round trips of whole
+                             16 KiB boxes there)                                         */
     uint32_t grid_wgs;    /* workgroups launched; fewer than there are groups makes each
                              take several (default: one workgroup per group; with
                              TMAP_FLAG_CONTIGUOUS, twice what fits in LDS per CU; in
@@ -95,7 +96,7 @@ typedef struct tmap_launch_opts {
                              two <= 64 (default: enough boxes side by side to span 512
                              bytes of a row, at least 2 and at most 8; band units: 2 on
                              the band kernel (4 for round trips of whole 16 KiB boxes),
-                             else 4 for a round trip and 1 for a load
+                             else 4 for a round trip and 2 for a load
                              or store; on the corner kernels, TMAP_VARIANT_CORNER and
                              TMAP_VARIANT_CORNER4: about 4 KiB of boxes, 1 for boxes of
                              4 KiB and more, 2 of 2 KiB, 4 of 1 KiB; other explicit

@@ -343,11 +343,16 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // leaves little to overlap and the smaller footprint fits more
     // workgroups (measured best on MI355X)
     int stages = (opts && opts->stages) ? (int)opts->stages : (corners ? 1 : 2);
-    // band round trips: a ring of 3 stages over 4 units per workgroup (the
-    // group, below) measured 1-4% faster than 2 over 2 on the 2 GiB u8 and
-    // 1 GiB fp32 round trips (one placement-sensitive ragged bf16 round trip
-    // lost 3%); 4 stages fit one workgroup fewer per CU and lose 10%
-    if (band && mode == tmap::kRoundtrip && !(opts && opts->stages)) stages = 3;
+    // band sweeps on the generic ring (maps the band kernel does not take,
+    // such as batches of planes that do not fold into one matrix): round
+    // trips 2 stages over 4 units per workgroup, loads and stores 1 stage
+    // over 2 units (measured on MI355X over batches of 32 planes that do not
+    // fold, u8 1000 rows in 128 x 128 boxes, bf16 1000 rows and fp32 500
+    // rows in 64 x 64 boxes, fraction of 8 TB/s: round trips 0.685 / 0.765
+    // / 0.766 against 0.662 / 0.657 / 0.658 with 3 stages, loads 0.798 /
+    // 0.782 / 0.791 against 0.652 / 0.649 / 0.641 with 1 unit, stores 0.782
+    // / 0.781 / 0.770 against 0.745 / 0.753 / 0.750)
+    if (band && mode == tmap::kRoundtrip && !(opts && opts->stages)) stages = 2;
     // the band kernel: 3 stages in every direction, of which its two units
     // (below) use two; the third stage's LDS holds a CU to three workgroups.
     // Measured on MI355X with 5 warm-up and 20 timed launches after an idle
@@ -441,7 +446,8 @@ tmap_status plan_launch(int mode, const MapImpl &m, int64_t n_tiles, const tmap_
     // 2 GiB u8, 1 GiB fp32 and ragged bf16 sweeps, 4 units lose 3-8%)
     if (!group && whole16) group = 4u;
     if (!group && lean) group = 2u;
-    if (!group && band) group = mode == tmap::kRoundtrip ? 4u : 1u;
+    if (!group && band) group = mode == tmap::kRoundtrip ? 4u : 2u;
+    if (band && !lean && mode != tmap::kRoundtrip && !(opts && opts->stages)) stages = 1;
     // explicit corners and the sweeps that run like them: 8 tiles to a
     // walker; a wave-per-box store takes 4.  Where each wave is a workgroup
     // of its own, the wave kernel's stores take 2 and its loads 4 (measured
