@@ -357,7 +357,7 @@ tmap_status tmap_roundtrip_add_f32(const tmap_t *src, const tmap_t *dst, const i
  * swizzle ("TMA -- the async bulk copy engine", "The real toolchain": the
  * plain bulk copy moves a contiguous byte range).  src and dst are device
  * pointers, 16-byte aligned, not overlapping; bytes is a multiple of 16
- * (bytes == 0 is a no-op).  From 256 MiB the whole 64 KiB rows are moved as
+ * (bytes == 0 is a no-op).  From 16 MiB the whole 64 KiB rows are moved as
  * a 2-D sweep of 16 KiB boxes, 128 rows of 128 bytes, on the band schedule
  * described at tmap_launch_opts (HBM serves short, wide bands faster than
  * one long stream of tiles); the rest, and smaller ranges, are moved in

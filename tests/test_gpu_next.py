@@ -120,9 +120,10 @@ def test_bulk_copy_sizes(nbytes):
     assert got.tobytes() == want.tobytes()          # the 64 bytes past the range are untouched
 
 
-@pytest.mark.parametrize("nbytes", [(256 << 20) - 16, 256 << 20, (256 << 20) + 37 * 65536 + 4096 + 16])
+@pytest.mark.parametrize("nbytes", [(16 << 20) - 16, 16 << 20, (16 << 20) + 37 * 65536 + 4096 + 16,
+                                    (256 << 20) + 37 * 65536 + 4096 + 16])
 def test_bulk_copy_row_view_and_remainder(nbytes):
-    """From 256 MiB the bulk copy moves the whole 64 KiB rows as a 2-D sweep
+    """From 16 MiB the bulk copy moves the whole 64 KiB rows as a 2-D sweep
     on the band schedule (here with a short last row of boxes) and the rest
     in 16 KiB tiles; every byte matches the oracle and the bytes past the
     range stay untouched."""

@@ -1095,12 +1095,15 @@ tmap_status tmap_bulk_copy(void *dst, const void *src, uint64_t bytes, const tma
     if (lo_d < lo_s + bytes && lo_s < lo_d + bytes)
         return fail(TMAP_ERROR_INVALID_VALUE, "src and dst ranges overlap");
     uint64_t done = 0;
-    // Ranges of 256 MiB and more: the whole 64 KiB rows as a 2-D tensor of
+    // Ranges of 16 MiB and more: the whole 64 KiB rows as a 2-D tensor of
     // 8-byte elements, 8192 to a row, in 16 x 128 boxes (16 KiB), which
-    // takes the band schedule like any sweep of that size (a unit is two
-    // rows of 8 KiB; measured on MI355X over 2 GiB: 0.76 of peak as 16 KiB
-    // tiles in address order, 0.81 as bands).  At most 2^31 rows a launch.
-    if (bytes >= kBandMinSpan) {
+    // takes the band schedule like a sweep of that size (a unit is two rows
+    // of 8 KiB; measured on MI355X over 2 GiB: 0.76 of peak as 16 KiB tiles
+    // in address order, 0.81 as bands; over 16 / 32 / 64 / 128 MiB, 0.531
+    // / 0.678 / 0.750 / 0.795 against 0.407 / 0.560 / 0.679 / 0.750 as
+    // tiles; 200 MiB 0.655 against 0.660).  At most 2^31 rows a launch.
+    constexpr uint64_t kBulkBandMin = 16ull << 20;
+    if (bytes >= kBulkBandMin) {
         const uint64_t kRow = 65536, kMaxRows = 1ull << 31;
         while (bytes - done >= kRow) {
             const uint64_t rows = std::min<uint64_t>((bytes - done) / kRow, kMaxRows);
