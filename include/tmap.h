@@ -425,10 +425,11 @@ typedef enum tmap_variant {
     TMAP_VARIANT_WAVE_PER_BOX = 3,  /* TMAP_FLAG_WAVE_PER_BOX, or its default                      */
     TMAP_VARIANT_BAND = 4,          /* band schedule of a sweep whose maps have rank <= 2 and whose
                                        dimension-0 rows are whole 16-byte chunks: the band ring
-                                       with per-slot offsets fixed per kernel.  A sweep of boxes
-                                       of extent 1 in dimensions 2 and up over dense planes a
-                                       whole number of boxes tall (a batch of matrices) is the
-                                       same sweep over one taller matrix, and runs here too     */
+                                       with per-slot offsets fixed per kernel.  Also batches of
+                                       such planes: maps of rank 3 with boxes of extent 1 in
+                                       dimension 2, walked plane by plane, and sweeps of higher
+                                       rank over dense planes a whole number of boxes tall,
+                                       which are the same sweep over one taller matrix          */
     TMAP_VARIANT_CORNER = 5,        /* wave per box with one stage, boxes of at most 8 KiB and a
                                        swizzle that moves whole chunks, at explicit corners or
                                        over a sweep the band schedule does not take: each wave

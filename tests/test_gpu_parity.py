@@ -946,21 +946,24 @@ def _check_sweep(rng, tag, variant, es, box, swz, lay, dlay):
         assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip", other, mm)
 
 
-def test_batched_sweeps_fold_into_taller_matrices():
-    """A sweep of 2-D boxes over a batch of matrices (boxes of extent 1 in
-    dimension 2) whose planes are dense and a whole number of boxes tall is
-    the same sweep over one taller matrix: it takes the band kernel.  Ragged
-    plane heights, padded planes and a round trip into another plane height
-    do not fold.  Every direction against the oracle."""
+def test_batched_sweeps_run_on_the_band_kernel():
+    """Sweeps of 2-D boxes over a batch of matrices (boxes of extent 1 above
+    dimension 1): dense planes a whole number of boxes tall fold into one
+    taller matrix; other batches of rank 3 walk their planes with the band
+    kernel's third cursor digit (ragged plane heights, padded planes, a
+    round trip into planes of another height or into fewer planes); a
+    padded batch of rank 4 runs elsewhere.  Every direction against the
+    oracle."""
     say("batched sweeps")
-    cases = [  # dims, strides (bytes), band expected
-        ([512, 256, 6], [1024, 1024 * 256], True),
-        ([512, 256, 3, 2], [1024, 1024 * 256, 1024 * 256 * 3], True),
-        ([512, 250, 6], [1024, 1024 * 250], False),           # 250 rows: not a whole number of boxes
-        ([512, 256, 6], [1024, 1024 * 256 + 512], False),     # padded planes
+    cases = [  # dims, strides (bytes), variant
+        ([512, 256, 6], [1024, 1024 * 256], "band"),
+        ([512, 256, 3, 2], [1024, 1024 * 256, 1024 * 256 * 3], "band"),
+        ([512, 250, 6], [1024, 1024 * 250], "band"),           # 250 rows: the last tile row of a plane is ragged
+        ([512, 256, 6], [1024, 1024 * 256 + 512], "band"),     # padded planes
+        ([512, 250, 3, 2], [1024, 1024 * 256, 1024 * 256 * 4], "corner4"),  # rank 4: 8 KiB boxes, 4-byte lanes
     ]
     box, swz = [64, 64, 1], (3, 3, 3)
-    for dims, strides, band in cases:
+    for dims, strides, variant in cases:
         bx = box + [1] * (len(dims) - 3)
         alloc = dims[-1] * strides[-1]
         src = dev_tensor(alloc, fill_seed=len(dims) + dims[1])
@@ -970,7 +973,7 @@ def test_batched_sweeps_fold_into_taller_matrices():
         n = T.tmap_sweep_tiles(m)
         for direction in ("load", "store", "roundtrip"):
             p = T.tmap_plan_launch(direction, m, m if direction == "roundtrip" else None, False, n)
-            assert (p["variant"] == "band") == band, (dims, strides, direction, p)
+            assert p["variant"] == variant, (dims, strides, direction, p)
         packed = gpu_load(m, None, n)
         want = oracle.load_tiles(om, host, None, n)
         assert (mm := first_mismatch(packed.cpu().numpy(), want, T.tmap_box_bytes(m))) is None, ("load", dims, mm)
@@ -986,20 +989,21 @@ def test_batched_sweeps_fold_into_taller_matrices():
         check_ok()
         oracle.roundtrip(om, host, om, want_dst, None, n)
         assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip", dims, mm)
-    # a round trip into planes of another height: neither map folds
+    # round trips into planes of another height, and into fewer planes
+    # (those past the destination's last are not written)
     dims, strides = [512, 256, 6], [1024, 1024 * 256]
-    ddims, dstrides = [512, 320, 6], [1024, 1024 * 320]
     src = dev_tensor(dims[-1] * strides[-1], fill_seed=11)
-    dst = dev_tensor(ddims[-1] * dstrides[-1], fill_seed=12)
-    m, md = enc("bf16", src, dims, strides, box, swz), enc("bf16", dst, ddims, dstrides, box, swz)
-    n = T.tmap_sweep_tiles(m)
-    assert T.tmap_plan_launch("roundtrip", m, md, False, n)["variant"] != "band"
-    want_dst = dst.cpu().numpy().copy()
-    T.tmap_roundtrip(m, md, None, n)
-    check_ok()
-    oracle.roundtrip(Map(es=2, dims=dims, strides=strides, box=box, swizzle=swz), src.cpu().numpy(),
-                     Map(es=2, dims=ddims, strides=dstrides, box=box, swizzle=swz), want_dst, None, n)
-    assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip between heights", mm)
+    for ddims, dstrides in (([512, 320, 6], [1024, 1024 * 320]), ([512, 200, 4], [1024, 1024 * 208])):
+        dst = dev_tensor(ddims[-1] * dstrides[-1], fill_seed=12)
+        m, md = enc("bf16", src, dims, strides, box, swz), enc("bf16", dst, ddims, dstrides, box, swz)
+        n = T.tmap_sweep_tiles(m)
+        assert T.tmap_plan_launch("roundtrip", m, md, False, n)["variant"] == "band"
+        want_dst = dst.cpu().numpy().copy()
+        T.tmap_roundtrip(m, md, None, n)
+        check_ok()
+        oracle.roundtrip(Map(es=2, dims=dims, strides=strides, box=box, swizzle=swz), src.cpu().numpy(),
+                         Map(es=2, dims=ddims, strides=dstrides, box=box, swizzle=swz), want_dst, None, n)
+        assert (mm := first_mismatch(dst.cpu().numpy(), want_dst, 1 << 40)) is None, ("roundtrip into", ddims, mm)
 
 
 def test_binding_rejects_buffers_the_copy_would_overrun():

@@ -1,4 +1,5 @@
-// tmap_band.h -- the band-schedule copy for maps of rank <= 2, written for
+// tmap_band.h -- the band-schedule copy for maps of rank <= 2 (and batches
+// of such planes: rank 3 with boxes of extent 1 in dimension 2), written for
 // the fewest instructions per byte.
 //
 // A sweep of boxes with rows of 64..512 bytes runs on the band schedule: a
@@ -6,8 +7,9 @@
 // are neighbours in dimension 0 (G * H * row bytes = 16 KiB), each box's band
 // being the contiguous piece of that box's swizzled LDS image it always is.
 // For maps of rank <= 2 whose rows are whole 16-byte chunks (so no chunk is
-// ever cut by the tensor's dimension-0 edge) this kernel replaces the generic
-// ring of tmap_copy.h on that schedule.  Same steps, same results:
+// ever cut by the tensor's dimension-0 edge), and batches of such planes
+// walked plane after plane, this kernel replaces the generic ring of
+// tmap_copy.h on that schedule.  Same steps, same results:
 //
 //   fill    every lane issues one 16-byte direct-to-LDS buffer load per slot
 //           it owns (4 slots: 16 KiB over 256 lanes); slot p receives the
@@ -139,7 +141,7 @@ struct BandCopier {
     // shapes (log2): 16-byte chunks per box row, per box band; band rows; boxes per unit
     uint32_t lrc, lbc, lh, lg, lk;
     int64_t cnt;
-    Cursor<2> fcur, ccur;
+    Cursor<3> fcur, ccur;
     // producer slots (filled by this lane): source offsets in the unit, and
     // column | row << 16 for the bounds test (packed offsets for a store)
     uint32_t poff[kBandSlots], pxy[kBandSlots];
@@ -182,7 +184,7 @@ struct BandCopier {
             t0 = g * Q;
         }
         if (g >= (int64_t)a.grid) cnt = 0;
-        cursor_init<2>(a, t0, fcur);
+        cursor_init<3>(a, t0, fcur);
         ccur = fcur;
         const uint32_t cw = (wave + 1u) & (kWaves - 1u);
         const uint32_t bb = sw.box_bytes;
@@ -211,19 +213,23 @@ struct BandCopier {
     // The tensor side of the unit under cur in map m; `boxes` caps the
     // columns at the unit's existing boxes (a round trip's destination may
     // reach past the swept source's last box).
-    __device__ __forceinline__ Side tensor_side(const KMap &m, const Cursor<2> &cur, uint32_t boxes) const {
+    __device__ __forceinline__ Side tensor_side(const KMap &m, const Cursor<3> &cur, uint32_t boxes) const {
         Side s;
-        const uint32_t ux = cur.dig[0], v = cur.dig[1];
+        const uint32_t ux = cur.dig[0], v = cur.dig[1], z = cur.dig[2];
         const uint32_t width = boxes << lrc;  // 16-byte columns of the unit's existing boxes
         const uint32_t x0 = ux << (lg + lrc), y0 = v << lh, h = 1u << lh;
-        s.base = m.base + (uint64_t)y0 * m.strides[1] + ((uint64_t)x0 << 4);
+        // a map of rank 3 is a batch of planes (boxes of extent 1 in
+        // dimension 2): the third digit is the plane; rank 2 keeps it 0
+        s.base = m.base + (uint64_t)z * m.strides[2] + (uint64_t)y0 * m.strides[1] + ((uint64_t)x0 << 4);
         s.nrec = m.span;
         // 16-byte columns and rows of the map (dims[0] * elem_size is a
         // multiple of 16, checked on the host; both fit 31 bits, and so do
         // x0 and y0, which stay within a unit of the sweep's end)
         const uint32_t xc = m.dims[0] >> lk, yc = m.dims[1];
         const uint32_t xl = x0 >= xc ? 0u : (xc - x0 < width ? xc - x0 : width);
-        const uint32_t rl = y0 >= yc ? 0u : (yc - y0 < h ? yc - y0 : h);
+        // rows past the plane's height, or a plane past a round trip's
+        // destination, hold nothing
+        const uint32_t rl = (y0 >= yc || z >= m.dims[2]) ? 0u : (yc - y0 < h ? yc - y0 : h);
         s.xl = (int32_t)xl;
         s.rl = (int32_t)rl;
         s.inside = xl == (a.band_g << lrc) && rl == h;
@@ -232,17 +238,18 @@ struct BandCopier {
 
     // Boxes of the unit under cur that exist (the last unit of a row of the
     // sweep can reach past the row's last box).
-    __device__ __forceinline__ uint32_t unit_boxes(const Cursor<2> &cur) const {
+    __device__ __forceinline__ uint32_t unit_boxes(const Cursor<3> &cur) const {
         const uint32_t left = a.tiles[0] - (cur.dig[0] << lg);
         return left < a.band_g ? left : a.band_g;
     }
 
     // The packed side: the unit's bands in the images of its boxes.  Records
     // end after the last existing box's band.
-    __device__ __forceinline__ Side packed_side(const Cursor<2> &cur, uint32_t boxes) const {
+    __device__ __forceinline__ Side packed_side(const Cursor<3> &cur, uint32_t boxes) const {
         const KMap &sw = swept();
         const uint32_t lnb = a.band_lnb;
-        const uint64_t t = (uint64_t)(cur.dig[1] >> lnb) * a.tiles[0] + ((uint64_t)cur.dig[0] << lg);
+        const uint64_t t = ((uint64_t)cur.dig[2] * a.tiles[1] + (cur.dig[1] >> lnb)) * a.tiles[0] +
+                           ((uint64_t)cur.dig[0] << lg);
         const uint32_t j = cur.dig[1] & ((1u << lnb) - 1u);
         Side s;
         s.base = (uint64_t)a.packed + t * sw.box_bytes + (uint64_t)j * a.band_bytes;
@@ -255,7 +262,7 @@ struct BandCopier {
     // Band j of a box is staged in band 0's arrangement: its image position
     // is the slot's position XOR x_j (bytes) -- see the band schedule notes
     // at tmap_launch_opts.
-    __device__ __forceinline__ uint32_t band_xor(const Cursor<2> &cur) const {
+    __device__ __forceinline__ uint32_t band_xor(const Cursor<3> &cur) const {
         const KMap &sw = swept();
         const uint32_t jb = (cur.dig[1] & ((1u << a.band_lnb) - 1u)) << a.band_lbe;
         return (swizzle(jb, sw.swz_b, sw.swz_m, sw.swz_s) ^ jb) * sw.elem_size;
@@ -290,7 +297,7 @@ struct BandCopier {
             }
         }
         dma4<NTL>(s.base, s.nrec, (uint32_t)(uintptr_t)(lds_void_t *)(stage + wave * kBlockBytes), v);
-        cursor_advance<2>(a, fcur);
+        cursor_advance<3>(a, fcur);
     }
 
     template <typename Rs>
@@ -338,7 +345,7 @@ struct BandCopier {
                     store16(v[jj], r, slot_inside(cxy[jj], s.xl, s.rl) ? coff[jj] : kOob);
             }
         }
-        cursor_advance<2>(a, ccur);
+        cursor_advance<3>(a, ccur);
     }
 
     // One step: unit k sits in stage X; the unit k+S-1 goes into the stage

@@ -227,11 +227,15 @@ const char *band_height_misfit(const MapImpl &m, const tmap::KArgs &a, uint32_t 
 }
 
 // Whether the maps of a copy suit the band kernel of rank-2 sweeps
-// (tmap_band.h): both have rank <= 2 and every tensor side's dimension-0 row
-// is a whole number of 16-byte chunks, so that the tensor's edge never cuts
-// a chunk (the generic ring's element path is then never needed).
+// (tmap_band.h): both have rank <= 2, or are batches of such planes, and
+// every tensor side's dimension-0 row is a whole number of 16-byte chunks,
+// so that the tensor's edge never cuts a chunk (the generic ring's element
+// path is then never needed).
 bool band_lean_maps(int mode, const tmap::KArgs &a) {
-    if (a.src.rank > 2 || a.dst.rank > 2) return false;
+    // rank 2, or a batch of planes: rank 3 with boxes of extent 1 in
+    // dimension 2 (the kernel's third cursor digit walks the planes)
+    auto planes = [](const tmap::KMap &k) { return k.rank <= 2 || (k.rank == 3 && k.box[2] == 1); };
+    if (!planes(a.src) || !planes(a.dst)) return false;
     auto whole = [](const tmap::KMap &k) { return ((uint64_t)k.dims[0] * k.elem_size) % 16u == 0; };
     if (mode != tmap::kStore && !whole(a.src)) return false;
     if (mode != tmap::kLoad && !whole(a.dst)) return false;
