@@ -274,7 +274,8 @@ def test_band_schedule_choice():
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65536], [128, 128])) == 8
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128])) == 1
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 64])) == 2
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535, 1], [128, 128, 1])) == 0
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535, 1], [128, 128, 1])) == 1   # a batch of planes
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535, 1, 1], [128, 128, 1, 1])) == 0
     assert T.tmap_band_boxes(_enc_rows("u8", [4097, 60000], [128, 128])) == 0     # rows not whole chunks
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 65535], [128, 128]), flags=B) == 8
     # row width: 64..512 bytes; units of 16 rows, or shorter bands when a
@@ -282,15 +283,18 @@ def test_band_schedule_choice():
     for dt, box0, want in [("u8", 32, 0), ("u8", 64, 16), ("u8", 128, 8), ("u8", 256, 4), ("f16", 256, 2),
                            ("f32", 128, 2), ("f32", 256, 0), ("f64", 8, 16), ("f64", 64, 2), ("f32", 24, 0)]:
         assert T.tmap_band_boxes(_enc_rows(dt, [box0 * 20, 100], [box0, 16]), flags=B) == want, (dt, box0)
-    # the generic ring's heights (a rank-3 map): 8 rows, or taller
+    # the generic ring's heights (a rank-4 map; rank 3 is a batch of planes
+    # for the band kernel): 8 rows, or taller
     for dt, box0, want in [("u8", 64, 16), ("u8", 128, 16), ("u8", 256, 8), ("f16", 256, 4)]:
-        assert T.tmap_band_boxes(_enc_rows(dt, [box0 * 20, 100, 2], [box0, 16, 1]), flags=B) == want, (dt, box0)
+        assert T.tmap_band_boxes(_enc_rows(dt, [box0 * 20, 100, 2, 1], [box0, 16, 1, 1]), flags=B) == want, (dt, box0)
+        assert T.tmap_band_boxes(_enc_rows(dt, [box0 * 20, 100, 2], [box0, 16, 1]), flags=B) == \
+            T.tmap_band_boxes(_enc_rows(dt, [box0 * 20, 100], [box0, 16]), flags=B), (dt, box0)
     # dimension-1 extent: the band height times a power of two (16 rows, or
     # the tallest shorter height for a shorter box)
     for box1, want in [(4, 32), (8, 16), (16, 8), (24, 0), (32, 8), (48, 0), (64, 8), (128, 8)]:
         assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, box1]), flags=B) == want, box1
     for box1, want in [(4, 0), (8, 16), (16, 16), (24, 0), (32, 16)]:            # the generic ring's: 8 or taller
-        assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300, 2], [128, box1, 1]), flags=B) == want, box1
+        assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300, 2, 1], [128, box1, 1, 1]), flags=B) == want, box1
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 300], [128, 4]), flags=B, band_rows=4) == 32
     # the swizzle only changes element-offset bits [m, m+b): a band of
     # 16 * 128 elements must be a whole number of 2^(m+b) blocks
@@ -320,7 +324,9 @@ def test_band_schedule_choice():
     assert T.tmap_band_boxes(_enc_rows("u8", [7 * 128, 64], [128, 16]), flags=B) == 0
     assert T.tmap_band_boxes(_enc_rows("u8", [7 * 128 + 1, 64], [128, 16]), flags=B) == 8
     # higher box extents must be 1
-    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 1]), flags=B) == 16
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3, 2], [128, 16, 1, 1]), flags=B) == 16   # the ring
+    assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 1]), flags=B) == \
+        T.tmap_band_boxes(_enc_rows("u8", [4096, 64], [128, 16]), flags=B)   # planes on the band kernel
     assert T.tmap_band_boxes(_enc_rows("u8", [4096, 64, 3], [128, 16, 2]), flags=B) == 0
     assert T.tmap_band_boxes(_enc_rows("u8", [4096], [128]), flags=B) == 0
     # a unit must stay within 2^31 bytes of its corner, in both maps: with
